@@ -1,0 +1,69 @@
+"""Build libfa_bwd.so in-tree for gfx950.
+
+The host planner (csrc/fa_bwd_api.cpp) is plain C++ built with g++; the
+kernels (csrc/fa_bwd_kernels.hip) are built with hipcc for gfx950 only; the
+two objects are linked into flashattention_backward_fa_amd/lib/libfa_bwd.so.
+
+Usage: python -m flashattention_backward_fa_amd.build
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(PKG, "lib")
+BUILDDIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(LIBDIR, "libfa_bwd.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+# Packed fp32 VALU instructions are kept out of the generated code.
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _hipcc():
+    for cand in (os.path.join(ROCM, "bin", "hipcc"), shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; set ROCM_PATH")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose=False):
+    """Compile every source and link lib/libfa_bwd.so.  Always rebuilds."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(BUILDDIR, exist_ok=True)
+    hipcc = _hipcc()
+    api_o = os.path.join(BUILDDIR, "fa_bwd_api.o")
+    ker_o = os.path.join(BUILDDIR, "fa_bwd_kernels.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
+          "-c", os.path.join(CSRC, "fa_bwd_api.cpp"), "-o", api_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_kernels.hip"),
+          "-o", ker_o], verbose)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,238 @@
+// Host side of libfa_bwd.so: validation, planning, workspace sizing and the
+// C ABI declared in include/fa_bwd.h.  Plain C++ (no HIP headers): every
+// device call goes through the launchers of fa_bwd_kernels.hip.
+//
+// The checks follow page "CANN ops-transformer FlashAttnGrad 算子详解",
+// section 四 4.6 (constraints) and section 五 5.1 (host tiling: parse, check,
+// plan, write back).
+
+#include "fa_bwd.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "fa_bwd_internal.h"
+
+using fabwd::KernelArgs;
+
+struct fa_bwd_plan_s {
+  fa_bwd_desc desc;
+  KernelArgs args;         // pointers left NULL; filled per run
+  int64_t q_elems;         // elements of q (and of the fp32 dQ accumulator)
+  int64_t lse_elems;       // elements of softmax_lse / sfmg
+  size_t off_dq_acc, off_sfmg, ws_bytes;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool log_enabled() {
+  const char* e = std::getenv("FA_BWD_LOG");
+  return e && e[0] == '1';
+}
+
+// Validate host cu_seqlens: B+1 entries, cu[0] = 0, non-decreasing, cu[B] = T.
+// Returns the longest sequence or -1 when invalid.
+int64_t check_cu(const int32_t* cu, int B, int64_t T) {
+  if (cu[0] != 0) return -1;
+  int64_t mx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (cu[b + 1] < cu[b]) return -1;
+    int64_t len = (int64_t)cu[b + 1] - cu[b];
+    if (len > mx) mx = len;
+  }
+  if ((int64_t)cu[B] != T) return -1;
+  return mx;
+}
+
+int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
+  if (d.abi_version != FA_BWD_ABI_VERSION) return FA_ERR_PARAM_INVALID;
+  if (d.dtype != FA_DTYPE_BF16 && d.dtype != FA_DTYPE_FP16) return FA_ERR_PARAM_INVALID;
+  if (d.layout < FA_LAYOUT_BSND || d.layout > FA_LAYOUT_TND) return FA_ERR_PARAM_INVALID;
+  if (d.mask_mode < FA_MASK_NONE || d.mask_mode > FA_MASK_WINDOW) return FA_ERR_PARAM_INVALID;
+  if (!std::isfinite(d.softmax_scale)) return FA_ERR_PARAM_INVALID;
+  if (d.flags & ~FA_FLAG_DETERMINISTIC) return FA_ERR_PARAM_INVALID;
+
+  // section 四 4.6: positive sizes, 0 < B < 65536, N1 % N2 == 0, 0 < Dv <= D <= 192
+  if (d.B <= 0 || d.B >= 65536) return FA_ERR_SHAPE;
+  if (d.N1 <= 0 || d.N2 <= 0 || d.N1 % d.N2 != 0) return FA_ERR_SHAPE;
+  if (d.D <= 0 || d.Dv <= 0 || d.Dv > d.D || d.D > 192) return FA_ERR_SHAPE;
+  // dense attention iff mask_mode 0 with no window; causal closes the right side
+  if (d.win_left < -1 || d.win_right < -1) return FA_ERR_SHAPE;
+  if (d.mask_mode == FA_MASK_NONE && (d.win_left != -1 || d.win_right != -1)) return FA_ERR_SHAPE;
+  if (d.mask_mode == FA_MASK_CAUSAL && d.win_right > 0) return FA_ERR_SHAPE;
+
+  const bool tnd = d.layout == FA_LAYOUT_TND;
+  int64_t S1 = d.S1, S2 = d.S2;
+  if (tnd) {
+    if (d.T1 <= 0 || d.T2 <= 0) return FA_ERR_SHAPE;
+    if (d.T1 > INT32_MAX || d.T2 > INT32_MAX) return FA_ERR_SHAPE;
+    if ((d.host_cu_seqlens_q == nullptr) != (d.host_cu_seqlens_kv == nullptr)) return FA_ERR_SHAPE;
+    if (d.host_cu_seqlens_q) {
+      int64_t m1 = check_cu(d.host_cu_seqlens_q, d.B, d.T1);
+      int64_t m2 = check_cu(d.host_cu_seqlens_kv, d.B, d.T2);
+      if (m1 < 0 || m2 < 0) return FA_ERR_SHAPE;
+      if (S1 == -1) S1 = m1; else if (S1 < m1) return FA_ERR_SHAPE;
+      if (S2 == -1) S2 = m2; else if (S2 < m2) return FA_ERR_SHAPE;
+    } else if (S1 == -1 || S2 == -1) {
+      return FA_ERR_SHAPE;  // max lengths needed when no host copy is given
+    }
+    if (S1 < 0 || S2 < 0 || S1 > d.T1 || S2 > d.T2) return FA_ERR_SHAPE;
+  } else {
+    if (d.host_cu_seqlens_q || d.host_cu_seqlens_kv) return FA_ERR_SHAPE;
+    if (S1 <= 0 || S2 <= 0) return FA_ERR_SHAPE;
+  }
+
+  // valid on the page, not built here
+  if (d.dtype == FA_DTYPE_FP16) return FA_ERR_UNSUPPORTED;
+  if (d.flags & FA_FLAG_DETERMINISTIC) return FA_ERR_UNSUPPORTED;
+  if (!fabwd::main_instantiated(d.D, d.Dv)) return FA_ERR_UNSUPPORTED;
+
+  KernelArgs& a = p.args;
+  std::memset(&a, 0, sizeof(a));
+  a.B = d.B; a.N1 = d.N1; a.N2 = d.N2; a.G = d.N1 / d.N2;
+  a.S1 = (int32_t)S1; a.S2 = (int32_t)S2;
+  a.D = d.D; a.Dv = d.Dv;
+  a.varlen = tnd ? 1 : 0;
+  a.layout = d.layout;
+  a.T1 = tnd ? d.T1 : 0; a.T2 = tnd ? d.T2 : 0;
+  const int64_t N1 = d.N1, N2 = d.N2, D = d.D, Dv = d.Dv;
+  switch (d.layout) {
+    case FA_LAYOUT_BSND:
+      a.q_sb = S1 * N1 * D;  a.q_ss = N1 * D;  a.q_sn = D;
+      a.k_sb = S2 * N2 * D;  a.k_ss = N2 * D;  a.k_sn = D;
+      a.v_sb = S2 * N2 * Dv; a.v_ss = N2 * Dv; a.v_sn = Dv;
+      a.o_sb = S1 * N1 * Dv; a.o_ss = N1 * Dv; a.o_sn = Dv;
+      a.l_sb = N1 * S1;      a.l_sn = S1;
+      break;
+    case FA_LAYOUT_BNSD:
+      a.q_sb = N1 * S1 * D;  a.q_ss = D;  a.q_sn = S1 * D;
+      a.k_sb = N2 * S2 * D;  a.k_ss = D;  a.k_sn = S2 * D;
+      a.v_sb = N2 * S2 * Dv; a.v_ss = Dv; a.v_sn = S2 * Dv;
+      a.o_sb = N1 * S1 * Dv; a.o_ss = Dv; a.o_sn = S1 * Dv;
+      a.l_sb = N1 * S1;      a.l_sn = S1;
+      break;
+    default:  // TND
+      a.q_sb = 0; a.q_ss = N1 * D;  a.q_sn = D;
+      a.k_sb = 0; a.k_ss = N2 * D;  a.k_sn = D;
+      a.v_sb = 0; a.v_ss = N2 * Dv; a.v_sn = Dv;
+      a.o_sb = 0; a.o_ss = N1 * Dv; a.o_sn = Dv;
+      a.l_sb = 0; a.l_sn = d.T1;
+      break;
+  }
+  const double scale = d.softmax_scale != 0.0f ? (double)d.softmax_scale : 1.0 / std::sqrt((double)d.D);
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  if (d.mask_mode == FA_MASK_NONE) { a.win_left = -1; a.win_right = -1; }
+  else if (d.mask_mode == FA_MASK_CAUSAL) { a.win_left = d.win_left; a.win_right = 0; }
+  else { a.win_left = d.win_left; a.win_right = d.win_right; }
+  a.has_mask = (a.win_left >= 0 || a.win_right >= 0) ? 1 : 0;
+
+  p.q_elems = tnd ? d.T1 * N1 * D : (int64_t)d.B * S1 * N1 * D;
+  p.lse_elems = tnd ? N1 * d.T1 : (int64_t)d.B * N1 * S1;
+  p.off_dq_acc = 0;
+  p.off_sfmg = align_up((size_t)p.q_elems * sizeof(float));
+  p.ws_bytes = p.off_sfmg + align_up((size_t)p.lse_elems * sizeof(float));
+  p.desc = d;
+  p.desc.S1 = (int32_t)S1;
+  p.desc.S2 = (int32_t)S2;
+  p.desc.host_cu_seqlens_q = nullptr;   // host copies are not kept
+  p.desc.host_cu_seqlens_kv = nullptr;
+  return FA_OK;
+}
+
+int check_run_pointers(const fa_bwd_plan_s& p, const int32_t* cu_q, const int32_t* cu_kv) {
+  const bool tnd = p.desc.layout == FA_LAYOUT_TND;
+  if (tnd && (!cu_q || !cu_kv)) return FA_ERR_SHAPE;
+  if (!tnd && (cu_q || cu_kv)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_bytes) {
+  if (!desc || !plan || !workspace_bytes) return FA_ERR_NULLPTR;
+  *plan = nullptr;
+  fa_bwd_plan_s* p = new (std::nothrow) fa_bwd_plan_s();
+  if (!p) return FA_ERR_RUNTIME;
+  int st = validate_and_plan(*desc, *p);
+  if (st != FA_OK) {
+    delete p;
+    return st;
+  }
+  *plan = p;
+  *workspace_bytes = p->ws_bytes;
+  if (log_enabled()) {
+    const KernelArgs& a = p->args;
+    std::fprintf(stderr,
+                 "[fa_bwd] plan layout=%d B=%d N1=%d N2=%d S1=%d S2=%d D=%d Dv=%d T1=%lld T2=%lld "
+                 "scale=%g window=(%d,%d) kv_tile=%d q_tile=%d workspace=%zu B\n",
+                 p->desc.layout, a.B, a.N1, a.N2, a.S1, a.S2, a.D, a.Dv, (long long)a.T1,
+                 (long long)a.T2, (double)a.scale, a.win_left, a.win_right, fabwd::KV_TILE,
+                 fabwd::Q_TILE, p->ws_bytes);
+  }
+  return FA_OK;
+}
+
+int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, const void* dout,
+               const void* attn_out, const float* softmax_lse, const int32_t* cu_seqlens_q,
+               const int32_t* cu_seqlens_kv, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !dout || !attn_out || !softmax_lse || !dq || !dk || !dv)
+    return FA_ERR_NULLPTR;
+  int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < plan->ws_bytes) return FA_ERR_WORKSPACE;
+
+  KernelArgs a = plan->args;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out = attn_out; a.lse = softmax_lse;
+  a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dq_acc);
+  a.sfmg = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_sfmg);
+
+  if (fabwd::launch_preprocess(a, true, stream) != 0) return FA_ERR_RUNTIME;
+  if (fabwd::launch_main(a, stream) != 0) return FA_ERR_RUNTIME;
+  if (fabwd::launch_dq_finalize(a, stream) != 0) return FA_ERR_RUNTIME;
+  return FA_OK;
+}
+
+int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
+                const int32_t* cu_seqlens_q, float* sfmg, void* stream) {
+  if (!plan || !dout || !attn_out || !sfmg) return FA_ERR_NULLPTR;
+  const bool tnd = plan->desc.layout == FA_LAYOUT_TND;
+  if (tnd != (cu_seqlens_q != nullptr)) return FA_ERR_SHAPE;
+  KernelArgs a = plan->args;
+  a.dout = dout; a.out = attn_out; a.cu_q = cu_seqlens_q; a.sfmg = sfmg;
+  if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
+  return FA_OK;
+}
+
+int fa_bwd_destroy(fa_bwd_plan plan) {
+  delete plan;
+  return FA_OK;
+}
+
+const char* fa_bwd_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULLPTR: return "a required pointer is NULL";
+    case FA_ERR_PARAM_INVALID: return "invalid parameter (dtype, layout, mask_mode, flags, abi_version or scale)";
+    case FA_ERR_SHAPE: return "shape constraint violated (sizes, N1 % N2, Dv <= D <= 192, window, cu_seqlens)";
+    case FA_ERR_UNSUPPORTED: return "combination not built in this library";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_RUNTIME: return "HIP runtime or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int fa_bwd_abi_version(void) { return FA_BWD_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal contract between the host planner (fa_bwd_api.cpp, plain C++) and
+// the gfx950 kernels (fa_bwd_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fabwd {
+
+// Tile shape of the main kernel: each workgroup owns KV_TILE keys of one
+// sequence and one key/value head (4 wavefronts x 32 keys); query rows stream
+// through LDS Q_TILE at a time.
+constexpr int KV_TILE = 128;
+constexpr int Q_TILE = 64;
+
+// Everything a launch needs, plain old data, passed by value to the kernels.
+struct KernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const void* out;
+  const float* lse;
+  const int32_t* cu_q;   // TND only (device)
+  const int32_t* cu_kv;  // TND only (device)
+  float* dq_acc;         // fp32, q's layout
+  float* sfmg;           // fp32, lse's layout
+  void* dq;
+  void* dk;
+  void* dv;
+
+  int32_t B, N1, N2, G;
+  int32_t S1, S2;        // dense lengths, or max lengths for TND
+  int32_t D, Dv;
+  int64_t T1, T2;
+  int32_t varlen;        // 1 for TND
+  int32_t layout;        // FA_LAYOUT_* of include/fa_bwd.h
+
+  // element strides: batch (dense layouts), sequence row, head
+  int64_t q_sb, q_ss, q_sn;   // q, dq, dq_acc
+  int64_t k_sb, k_ss, k_sn;   // k, dk
+  int64_t v_sb, v_ss, v_sn;   // v, dv
+  int64_t o_sb, o_ss, o_sn;   // dout, attn_out
+  int64_t l_sb, l_sn;         // lse, sfmg (row stride 1)
+
+  float scale;           // softmax scale actually used
+  float scale_log2;      // scale * log2(e)
+  int32_t win_left;      // -1 = unbounded
+  int32_t win_right;     // -1 = unbounded
+  int32_t has_mask;      // any bound present
+};
+
+// Launchers (fa_bwd_kernels.hip).  Each returns 0 or a hipError_t value.
+int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream);
+int launch_main(const KernelArgs& a, void* stream);
+int launch_dq_finalize(const KernelArgs& a, void* stream);
+bool main_instantiated(int D, int Dv);
+
+}  // namespace fabwd

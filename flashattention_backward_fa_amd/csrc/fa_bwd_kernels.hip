@@ -1,0 +1,440 @@
+// gfx950 (MI355X) kernels of the FlashAttention backward.
+//
+// Formulas: page "CANN ops-transformer FlashAttnGrad 算子详解", section 一
+// (P = exp(scale*QK^T - softmax_lse), dV = P^T dY, dP = dY V^T,
+// sfmg = rowsum(dY (.) Y), dS = P (.) (dP - sfmg), dQ = scale*dS K,
+// dK = scale*dS^T Q).  Section 五 5.2 describes the page's own kernel as five
+// cube matmuls plus vector stages, with dQ reduced through an fp32 workspace by
+// atomic adds and dK/dV accumulated on chip across query blocks; the design
+// below keeps those two ideas and is otherwise laid out for CDNA4:
+//
+//   preprocess  sfmg = rowsum(dY (.) Y) in fp32, one 16-byte load per lane,
+//               cross-lane sums; also clears the fp32 dQ accumulator.
+//   main        one workgroup = 4 wavefronts = 128 keys of one key/value head
+//               (32 keys per wavefront).  K and V fragments stay in VGPRs for
+//               the whole kernel; Q and dY stream through LDS 64 rows at a
+//               time.  Per block of 64 query rows each wavefront computes
+//               S = Q K^T and dP = dY V^T for its 32 keys with
+//               v_mfma_f32_32x32x16_bf16 (query rows as M, keys as N), so every
+//               lane holds one key and 16 query rows.  That accumulator layout is
+//               exactly the A-operand layout of the key-major products, so P and
+//               dS feed dV += P^T dY and dK += dS^T Q from registers; the
+//               B operands (dY and Q read down their columns) come from LDS with
+//               ds_read_b64_tr_b16.  dS^T goes to LDS once and the four
+//               wavefronts then form dQ = dS K for the block and add it into the
+//               fp32 accumulator with hardware float atomics.  The G query heads
+//               of a GQA group run inside the same workgroup, so dK/dV are
+//               complete in registers when the loop ends.
+//   finalize    dq = bf16(scale * dq_acc).
+//
+// exp is v_exp_f32 (base 2) with log2(e) folded into the scale and the lse.
+
+#include <hip/hip_runtime.h>
+
+#include "fa_bwd_internal.h"
+
+namespace fabwd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// (i % 4) of the 8 bytes addressed by lane 4*e + i/4, for e = 0..3.  With lane
+// i of the group pointing at row (r0 + i/4), column (c0 + 4*(i%4)) of a
+// row-major bf16 tile, lane i gets column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ shortx4 lds_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join(shortx4 lo, shortx4 hi) {
+  shortx8 s = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, s);
+}
+
+// ---------------------------------------------------------------- preprocess
+
+// One row = Dv contiguous bf16 of dout / attn_out.  DV/8 lanes per row, each
+// with one 16-byte load of each tensor.
+template <int DV>
+__global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t rows, int zero_dq,
+                                                          int64_t dq_elems) {
+  constexpr int LPR = DV / 8;             // lanes per row
+  constexpr int RPB = 256 / LPR;          // rows per block
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const int part = tid % LPR;
+  float s = 0.f;
+  if (row < rows) {
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + row * DV + part * 8);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + row * DV + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)g[e] * (float)y[e];
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
+  if (row < rows && part == 0) {
+    int64_t o;
+    if (a.layout == 0) {  // BSND: row = (b*S1 + s)*N1 + n  ->  [b][n][s]
+      const int64_t n = row % a.N1, bs = row / a.N1;
+      const int64_t b = bs / a.S1, si = bs % a.S1;
+      o = b * a.l_sb + n * a.l_sn + si;
+    } else if (a.layout == 1) {  // BNSD: row = (b*N1 + n)*S1 + s  ->  same order
+      o = row;
+    } else {  // TND: row = t*N1 + n  ->  [n][t]
+      const int64_t n = row % a.N1, t = row / a.N1;
+      o = n * a.l_sn + t;
+    }
+    a.sfmg[o] = s;
+  }
+  if (zero_dq) {
+    floatx4* p = reinterpret_cast<floatx4*>(a.dq_acc);
+    const int64_t n4 = dq_elems / 4;
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n4; i += (int64_t)gridDim.x * 256) p[i] = z;
+  }
+}
+
+// ---------------------------------------------------------------- finalize
+
+__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
+                                                          int64_t n8, float scale) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const floatx4 x0 = reinterpret_cast<const floatx4*>(acc)[2 * i];
+    const floatx4 x1 = reinterpret_cast<const floatx4*>(acc)[2 * i + 1];
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = (bf16)(x0[e] * scale);
+      o[e + 4] = (bf16)(x1[e] * scale);
+    }
+    reinterpret_cast<bf16x8*>(dq)[i] = o;
+  }
+}
+
+// ---------------------------------------------------------------- main
+
+template <int HD, int HDV>
+__global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
+  constexpr int BC = KV_TILE;   // keys per workgroup
+  constexpr int BR = Q_TILE;    // query rows per step
+  constexpr int QP = HD + 8;    // padded LDS row pitch (elements) of K and Q tiles
+  constexpr int YP = HDV + 8;   // dY tile
+  constexpr int SP = BR + 8;    // dS^T tile (rows = keys)
+  constexpr int NMB = BR / 32;  // 32-row query blocks per step
+  constexpr int NKQ = HD / 16;  // k-steps over D
+  constexpr int NKV = HDV / 16; // k-steps over Dv
+  constexpr int NDQ = NMB * (HD / 32);  // dQ output tiles per step
+
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BC * QP];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BR * QP];
+  __shared__ __attribute__((aligned(16))) bf16 Ys[BR * YP];
+  __shared__ __attribute__((aligned(16))) bf16 St[BC * SP];
+  __shared__ __attribute__((aligned(16))) float lse_s[BR];
+  __shared__ __attribute__((aligned(16))) float sfm_s[BR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // workgroup -> (key tile, key/value head, sequence).  The key tile varies
+  // slowest, so the tiles with the most causal work are dispatched first.
+  const int bid = blockIdx.x;
+  const int per_tile = a.N2 * a.B;
+  const int tile = bid / per_tile;
+  const int rem = bid - tile * per_tile;
+  const int n2 = rem % a.N2;
+  const int b = rem / a.N2;
+
+  int s1, s2;
+  int64_t qbase, kbase, vbase, obase, lbase;
+  if (a.varlen) {
+    const int q0 = a.cu_q[b], k0 = a.cu_kv[b];
+    s1 = a.cu_q[b + 1] - q0;
+    s2 = a.cu_kv[b + 1] - k0;
+    qbase = (int64_t)q0 * a.q_ss;
+    obase = (int64_t)q0 * a.o_ss;
+    kbase = (int64_t)k0 * a.k_ss;
+    vbase = (int64_t)k0 * a.v_ss;
+    lbase = q0;
+  } else {
+    s1 = a.S1;
+    s2 = a.S2;
+    qbase = (int64_t)b * a.q_sb;
+    obase = (int64_t)b * a.o_sb;
+    kbase = (int64_t)b * a.k_sb;
+    vbase = (int64_t)b * a.v_sb;
+    lbase = (int64_t)b * a.l_sb;
+  }
+  const int j0 = tile * BC;
+  if (j0 >= s2) return;  // whole workgroup: this sequence has fewer keys
+  const int j1 = min(j0 + BC, s2);
+  const int off = s2 - s1;
+  const int wl = a.win_left, wr = a.win_right;
+
+  const bf16* __restrict__ Kg = static_cast<const bf16*>(a.k) + kbase + (int64_t)n2 * a.k_sn;
+  const bf16* __restrict__ Vg = static_cast<const bf16*>(a.v) + vbase + (int64_t)n2 * a.v_sn;
+
+  // K tile -> LDS (row-major, zero rows past the sequence end)
+  for (int c = tid; c < BC * (HD / 8); c += 256) {
+    const int r = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+    bf16x8 val = {};
+    if (j0 + r < s2) val = *reinterpret_cast<const bf16x8*>(Kg + (int64_t)(j0 + r) * a.k_ss + cc);
+    *reinterpret_cast<bf16x8*>(&Ks[r * QP + cc]) = val;
+  }
+  // V fragments (B operand of dP = dY V^T): lane holds key kw, dims 16*kk + 8*hi + 0..7
+  const int kw = wave * 32 + l32;
+  bf16x8 vf[NKV];
+#pragma unroll
+  for (int kk = 0; kk < NKV; ++kk) {
+    bf16x8 val = {};
+    if (j0 + kw < s2) val = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)(j0 + kw) * a.v_ss + 16 * kk + 8 * hi);
+    vf[kk] = val;
+  }
+  __syncthreads();
+  bf16x8 kf[NKQ];  // B operand of S = Q K^T
+#pragma unroll
+  for (int kk = 0; kk < NKQ; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(&Ks[kw * QP + 16 * kk + 8 * hi]);
+
+  floatx16 dk_acc[HD / 32], dv_acc[HDV / 32];
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) dk_acc[i] = floatx16{};
+#pragma unroll
+  for (int i = 0; i < HDV / 32; ++i) dv_acc[i] = floatx16{};
+
+  // lane offsets of the transposing reads
+  const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-wide block
+  const int tr_r4 = 4 * hi + ((lane & 15) >> 2);             // row pattern of P/dS-ordered chunks
+  const int tr_r8 = 8 * hi + ((lane & 15) >> 2);             // row pattern of contiguous chunks
+
+  // query rows that see at least one key of [j0, j1)
+  int i_lo = 0, i_hi = s1;
+  if (wr >= 0) i_lo = max(0, j0 - off - wr);
+  if (wl >= 0) i_hi = min(s1, j1 - off + wl);
+
+  for (int g = 0; g < a.G; ++g) {
+    const int n1 = n2 * a.G + g;
+    const bf16* __restrict__ Qg = static_cast<const bf16*>(a.q) + qbase + (int64_t)n1 * a.q_sn;
+    const bf16* __restrict__ Yg = static_cast<const bf16*>(a.dout) + obase + (int64_t)n1 * a.o_sn;
+    float* __restrict__ dQa = a.dq_acc + qbase + (int64_t)n1 * a.q_sn;
+    const float* __restrict__ Lg = a.lse + lbase + (int64_t)n1 * a.l_sn;
+    const float* __restrict__ Fg = a.sfmg + lbase + (int64_t)n1 * a.l_sn;
+
+    for (int i0 = (i_lo / BR) * BR; i0 < i_hi; i0 += BR) {
+      // ---- stage Q, dY, lse, sfmg of rows [i0, i0 + BR) in LDS
+      for (int c = tid; c < BR * (HD / 8); c += 256) {
+        const int r = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+        bf16x8 val = {};
+        if (i0 + r < s1) val = *reinterpret_cast<const bf16x8*>(Qg + (int64_t)(i0 + r) * a.q_ss + cc);
+        *reinterpret_cast<bf16x8*>(&Qs[r * QP + cc]) = val;
+      }
+      for (int c = tid; c < BR * (HDV / 8); c += 256) {
+        const int r = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+        bf16x8 val = {};
+        if (i0 + r < s1) val = *reinterpret_cast<const bf16x8*>(Yg + (int64_t)(i0 + r) * a.o_ss + cc);
+        *reinterpret_cast<bf16x8*>(&Ys[r * YP + cc]) = val;
+      }
+      if (tid < BR) {
+        const int i = i0 + tid;
+        float l2 = __builtin_inff(), f = 0.f;
+        if (i < s1) {
+          const float l = Lg[i];
+          // a row with no visible key (lse = -inf) must give P = 0
+          l2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
+          f = Fg[i];
+        }
+        lse_s[tid] = l2;
+        sfm_s[tid] = f;
+      }
+      __syncthreads();
+
+      // ---- S = Q K^T and dP = dY V^T for this wavefront's 32 keys
+      floatx16 sacc[NMB], pacc[NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        sacc[mb] = floatx16{};
+        pacc[mb] = floatx16{};
+#pragma unroll
+        for (int kk = 0; kk < NKQ; ++kk) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[(mb * 32 + l32) * QP + 16 * kk + 8 * hi]);
+          sacc[mb] = mfma32(qa, kf[kk], sacc[mb]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+          const bf16x8 ya = *reinterpret_cast<const bf16x8*>(&Ys[(mb * 32 + l32) * YP + 16 * kk + 8 * hi]);
+          pacc[mb] = mfma32(ya, vf[kk], pacc[mb]);
+        }
+      }
+
+      // ---- P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), both packed as bf16
+      const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) &&
+                        (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
+                        (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
+      const int jk = j0 + kw;
+      bf16x8 pa[2 * NMB], da[2 * NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ib = mb * 32 + r4 * 8 + hi * 4;  // first of 4 consecutive query rows
+          const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[ib]);
+          const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[ib]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = r4 * 4 + e;
+            float p = __builtin_amdgcn_exp2f(sacc[mb][r] * a.scale_log2 - l4[e]);
+            if (!full) {
+              const int i = i0 + ib + e;
+              const bool vis = (i < s1) && (jk < s2) && (wl < 0 || jk >= i + off - wl) &&
+                               (wr < 0 || jk <= i + off + wr);
+              p = vis ? p : 0.f;
+            }
+            const float ds = p * (pacc[mb][r] - f4[e]);
+            pa[mb * 2 + (r >> 3)][r & 7] = (bf16)p;
+            da[mb * 2 + (r >> 3)][r & 7] = (bf16)ds;
+          }
+        }
+      }
+
+      // ---- dV += P^T dY and dK += dS^T Q  (M = keys, N = head dim, K = query rows)
+#pragma unroll
+      for (int kc = 0; kc < 2 * NMB; ++kc) {
+#pragma unroll
+        for (int nb = 0; nb < HDV / 32; ++nb) {
+          const bf16* p0 = &Ys[(16 * kc + tr_r4) * YP + nb * 32 + tr_c];
+          const bf16x8 yb = join(lds_tr(p0), lds_tr(p0 + 8 * YP));
+          dv_acc[nb] = mfma32(pa[kc], yb, dv_acc[nb]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < HD / 32; ++nb) {
+          const bf16* p0 = &Qs[(16 * kc + tr_r4) * QP + nb * 32 + tr_c];
+          const bf16x8 qb = join(lds_tr(p0), lds_tr(p0 + 8 * QP));
+          dk_acc[nb] = mfma32(da[kc], qb, dk_acc[nb]);
+        }
+      }
+
+      // ---- dS^T -> LDS: row = key, 4 consecutive query rows per 8-byte store
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int kc = mb * 2 + (r4 >> 1);
+          const int e0 = (r4 & 1) * 4;
+          shortx4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(short, da[kc][e0 + e]);
+          *reinterpret_cast<shortx4*>(&St[kw * SP + mb * 32 + r4 * 8 + hi * 4]) = w;
+        }
+      }
+      __syncthreads();
+
+      // ---- dQ(rows i0..) += dS K, added into the fp32 accumulator
+#pragma unroll
+      for (int t = wave; t < NDQ; t += 4) {
+        const int mq = t % NMB, nd = t / NMB;
+        floatx16 acc = {};
+#pragma unroll
+        for (int kc = 0; kc < BC / 16; ++kc) {
+          const bf16* pa0 = &St[(16 * kc + tr_r8) * SP + mq * 32 + tr_c];
+          const bf16* pb0 = &Ks[(16 * kc + tr_r8) * QP + nd * 32 + tr_c];
+          const bf16x8 av = join(lds_tr(pa0), lds_tr(pa0 + 4 * SP));
+          const bf16x8 bv = join(lds_tr(pb0), lds_tr(pb0 + 4 * QP));
+          acc = mfma32(av, bv, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + mq * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          if (i < s1) unsafeAtomicAdd(dQa + (int64_t)i * a.q_ss + nd * 32 + l32, acc[r]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- write dK = scale * acc and dV (bf16); keys past the sequence end are skipped
+  bf16* __restrict__ dKg = static_cast<bf16*>(a.dk) + kbase + (int64_t)n2 * a.k_sn;
+  bf16* __restrict__ dVg = static_cast<bf16*>(a.dv) + vbase + (int64_t)n2 * a.v_sn;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = j0 + wave * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+    if (j < s2) {
+#pragma unroll
+      for (int nb = 0; nb < HD / 32; ++nb) dKg[(int64_t)j * a.k_ss + nb * 32 + l32] = (bf16)(dk_acc[nb][r] * a.scale);
+#pragma unroll
+      for (int nb = 0; nb < HDV / 32; ++nb) dVg[(int64_t)j * a.v_ss + nb * 32 + l32] = (bf16)dv_acc[nb][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+namespace {
+int64_t q_elems(const KernelArgs& a) {
+  return a.varlen ? a.T1 * a.N1 * a.D : (int64_t)a.B * a.S1 * a.N1 * a.D;
+}
+int64_t out_rows(const KernelArgs& a) {
+  return a.varlen ? a.T1 * a.N1 : (int64_t)a.B * a.S1 * a.N1;
+}
+}  // namespace
+
+int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream) {
+  const int64_t rows = out_rows(a);
+  const int lpr = a.Dv / 8;
+  const int64_t rpb = 256 / lpr;
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  if (blocks <= 0) return 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t dqe = zero_dq_acc ? q_elems(a) : 0;
+  if (a.Dv == 128)
+    hipLaunchKernelGGL(preprocess_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a, rows, zero_dq_acc ? 1 : 0, dqe);
+  else if (a.Dv == 64)
+    hipLaunchKernelGGL(preprocess_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, rows, zero_dq_acc ? 1 : 0, dqe);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_dq_finalize(const KernelArgs& a, void* stream) {
+  const int64_t n8 = q_elems(a) / 8;
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks <= 0) return 0;
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     a.dq_acc, static_cast<bf16*>(a.dq), n8, a.scale);
+  return (int)hipGetLastError();
+}
+
+bool main_instantiated(int D, int Dv) {
+  return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128)) || (D == 192 && (Dv == 64 || Dv == 128));
+}
+
+int launch_main(const KernelArgs& a, void* stream) {
+  const int64_t tiles = (a.S2 + KV_TILE - 1) / KV_TILE;
+  const int64_t blocks = tiles * a.N2 * a.B;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (a.D == 64 && a.Dv == 64) hipLaunchKernelGGL((bwd_main_kernel<64, 64>), grid, block, 0, s, a);
+  else if (a.D == 128 && a.Dv == 64) hipLaunchKernelGGL((bwd_main_kernel<128, 64>), grid, block, 0, s, a);
+  else if (a.D == 128 && a.Dv == 128) hipLaunchKernelGGL((bwd_main_kernel<128, 128>), grid, block, 0, s, a);
+  else if (a.D == 192 && a.Dv == 64) hipLaunchKernelGGL((bwd_main_kernel<192, 64>), grid, block, 0, s, a);
+  else if (a.D == 192 && a.Dv == 128) hipLaunchKernelGGL((bwd_main_kernel<192, 128>), grid, block, 0, s, a);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+}  // namespace fabwd

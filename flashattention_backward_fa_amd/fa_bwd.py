@@ -1,0 +1,301 @@
+"""Thin Python binding of libfa_bwd.so (include/fa_bwd.h).
+
+Argument marshalling only: every step of the backward runs in the library's
+HIP kernels.  PyTorch provides device memory (outputs, workspace) and the
+current stream.  If the library is missing this module raises on use; there
+is no fallback.
+
+The signature of flash_attn_grad follows the page "CANN ops-transformer
+FlashAttnGrad 算子详解", section 四 4.2 (function prototype), without the
+options this library does not build (seqused_q/kv, sinks, attn_mask,
+metadata) and with one layout for q, kv and out (section 四 4.6 requires them
+equal).
+"""
+
+import ctypes
+import enum
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libfa_bwd.so")
+
+ABI_VERSION = 1
+
+FA_OK = 0
+FA_ERR_NULLPTR = 1
+FA_ERR_PARAM_INVALID = 2
+FA_ERR_SHAPE = 3
+FA_ERR_UNSUPPORTED = 4
+FA_ERR_WORKSPACE = 5
+FA_ERR_RUNTIME = 6
+
+LAYOUTS = {"BSND": 0, "BNSD": 1, "TND": 2}
+FLAG_DETERMINISTIC = 0x1
+
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_bwd_destroy",
+            "fa_bwd_strerror", "fa_bwd_abi_version")
+
+
+class MaskMode(enum.IntEnum):
+    """mask_mode (section 四 4.3: IntEnum, int, or case-insensitive name)."""
+    NONE = 0
+    CAUSAL = 1
+    WINDOW = 2
+
+
+def mask_mode_value(m):
+    if isinstance(m, str):
+        try:
+            return int(MaskMode[m.upper()])
+        except KeyError:
+            raise ValueError(f"unknown mask_mode name {m!r}") from None
+    return int(m)
+
+
+class FaBwdDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("B", ctypes.c_int32),
+        ("N1", ctypes.c_int32),
+        ("N2", ctypes.c_int32),
+        ("S1", ctypes.c_int32),
+        ("S2", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("Dv", ctypes.c_int32),
+        ("T1", ctypes.c_int64),
+        ("T2", ctypes.c_int64),
+        ("host_cu_seqlens_q", ctypes.POINTER(ctypes.c_int32)),
+        ("host_cu_seqlens_kv", ctypes.POINTER(ctypes.c_int32)),
+        ("softmax_scale", ctypes.c_float),
+        ("mask_mode", ctypes.c_int32),
+        ("win_left", ctypes.c_int32),
+        ("win_right", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class FaBwdError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {strerror(status)}")
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libfa_bwd.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m flashattention_backward_fa_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.fa_bwd_create.argtypes = [ctypes.POINTER(FaBwdDesc), ctypes.POINTER(vp), ctypes.POINTER(sz)]
+    lib.fa_bwd_create.restype = ctypes.c_int
+    lib.fa_bwd_run.argtypes = [vp] * 9 + [vp] * 3 + [vp, sz, vp]
+    lib.fa_bwd_run.restype = ctypes.c_int
+    lib.fa_bwd_sfmg.argtypes = [vp] * 6
+    lib.fa_bwd_sfmg.restype = ctypes.c_int
+    lib.fa_bwd_destroy.argtypes = [vp]
+    lib.fa_bwd_destroy.restype = ctypes.c_int
+    lib.fa_bwd_strerror.argtypes = [ctypes.c_int]
+    lib.fa_bwd_strerror.restype = ctypes.c_char_p
+    lib.fa_bwd_abi_version.argtypes = []
+    lib.fa_bwd_abi_version.restype = ctypes.c_int
+    if lib.fa_bwd_abi_version() != ABI_VERSION:
+        raise RuntimeError("libfa_bwd.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def strerror(status):
+    return load_library().fa_bwd_strerror(int(status)).decode()
+
+
+def make_desc(layout, B, N1, N2, S1, S2, D, Dv, T1=0, T2=0, softmax_scale=0.0, mask_mode=0,
+              win_left=-1, win_right=-1, flags=0, host_cu_q=None, host_cu_kv=None, dtype=0):
+    """Fill an fa_bwd_desc.  host_cu_q/kv: optional int32 ctypes arrays kept
+    alive by the caller until fa_bwd_create returns."""
+    d = FaBwdDesc()
+    d.abi_version = ABI_VERSION
+    d.dtype = dtype
+    d.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    d.B, d.N1, d.N2, d.S1, d.S2, d.D, d.Dv = B, N1, N2, S1, S2, D, Dv
+    d.T1, d.T2 = T1, T2
+    P = ctypes.POINTER(ctypes.c_int32)
+    d.host_cu_seqlens_q = ctypes.cast(host_cu_q, P) if host_cu_q is not None else P()
+    d.host_cu_seqlens_kv = ctypes.cast(host_cu_kv, P) if host_cu_kv is not None else P()
+    d.softmax_scale = softmax_scale
+    d.mask_mode = mask_mode_value(mask_mode)
+    d.win_left, d.win_right = win_left, win_right
+    d.flags = flags
+    return d
+
+
+class Plan:
+    """Owns an fa_bwd_plan handle; the library validates and sizes in create."""
+
+    def __init__(self, desc):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        st = lib.fa_bwd_create(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws))
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_create")
+        self.handle = h
+        self.workspace_bytes = ws.value
+        self.layout = desc.layout
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.fa_bwd_destroy(h)
+            self.handle = None
+
+    def run(self, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv, workspace, workspace_bytes, stream):
+        st = load_library().fa_bwd_run(self.handle, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv,
+                                       workspace, workspace_bytes, stream)
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_run")
+
+    def sfmg(self, dout, attn_out, cu_q, out, stream):
+        st = load_library().fa_bwd_sfmg(self.handle, dout, attn_out, cu_q, out, stream)
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_sfmg")
+
+
+# ------------------------------------------------------------------ torch-facing API
+
+_plans = {}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _shapes(q, k, v, layout):
+    if layout == "TND":
+        T1, N1, D = q.shape
+        T2, N2, _ = k.shape
+        return dict(N1=N1, N2=N2, D=D, Dv=v.shape[-1], T1=T1, T2=T2)
+    if layout == "BSND":
+        B, S1, N1, D = q.shape
+        _, S2, N2, _ = k.shape
+    else:
+        B, N1, S1, D = q.shape
+        _, N2, S2, _ = k.shape
+    return dict(B=B, N1=N1, N2=N2, S1=S1, S2=S2, D=D, Dv=v.shape[-1])
+
+
+def _check(name, t, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0,
+             mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1,
+             deterministic=False, host_cu_seqlens=None):
+    """Create (or reuse) the plan for these shapes and attributes."""
+    sh = _shapes(q, k, v, layout)
+    flags = FLAG_DETERMINISTIC if deterministic else 0
+    mm = mask_mode_value(mask_mode)
+    if layout == "TND":
+        if cu_seqlens_q is None or cu_seqlens_kv is None:
+            raise ValueError("TND needs cu_seqlens_q and cu_seqlens_kv")
+        B = cu_seqlens_q.numel() - 1
+        hq = hk = None
+        if host_cu_seqlens is not None:
+            hq, hk = host_cu_seqlens
+        elif max_seqlen_q < 0 or max_seqlen_kv < 0:
+            # deriving the max lengths needs a host copy (this synchronises)
+            hq = [int(x) for x in cu_seqlens_q.cpu().tolist()]
+            hk = [int(x) for x in cu_seqlens_kv.cpu().tolist()]
+        key = ("TND", B, sh["N1"], sh["N2"], sh["D"], sh["Dv"], sh["T1"], sh["T2"], max_seqlen_q,
+               max_seqlen_kv, tuple(hq) if hq else None, tuple(hk) if hk else None, float(softmax_scale),
+               mm, win_left, win_right, flags)
+        if key not in _plans:
+            aq = (ctypes.c_int32 * len(hq))(*hq) if hq else None
+            ak = (ctypes.c_int32 * len(hk))(*hk) if hk else None
+            d = make_desc("TND", B, sh["N1"], sh["N2"], max_seqlen_q, max_seqlen_kv, sh["D"], sh["Dv"],
+                          sh["T1"], sh["T2"], softmax_scale, mm, win_left, win_right, flags, aq, ak)
+            _plans[key] = Plan(d)
+        return _plans[key]
+    if cu_seqlens_q is not None or cu_seqlens_kv is not None:
+        raise ValueError("cu_seqlens are only accepted with the TND layout")
+    key = (layout, sh["B"], sh["N1"], sh["N2"], sh["S1"], sh["S2"], sh["D"], sh["Dv"], float(softmax_scale), mm,
+           win_left, win_right, flags)
+    if key not in _plans:
+        d = make_desc(layout, sh["B"], sh["N1"], sh["N2"], sh["S1"], sh["S2"], sh["D"], sh["Dv"], 0, 0,
+                      softmax_scale, mm, win_left, win_right, flags)
+        _plans[key] = Plan(d)
+    return _plans[key]
+
+
+def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None,
+                    softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
+                    max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None):
+    """dq, dk, dv of attention (bf16) on the current HIP stream.
+
+    q, k, v, dout, attn_out: bf16 CUDA(HIP) tensors in `layout`; softmax_lse:
+    float32, (B, N1, S1) or (N1, T1); cu_seqlens_*: int32 device tensors for
+    TND only.  Non-contiguous inputs are made contiguous first.  `workspace`
+    (uint8 tensor) and `out` ((dq, dk, dv)) may be passed to avoid allocation.
+    """
+    import torch
+
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("attn_out", attn_out)):
+        _check(name, t, torch.bfloat16, dev)
+    _check("softmax_lse", softmax_lse, torch.float32, dev)
+    q, k, v, dout, attn_out, softmax_lse = (t.contiguous() for t in (q, k, v, dout, attn_out, softmax_lse))
+    if cu_seqlens_q is not None:
+        _check("cu_seqlens_q", cu_seqlens_q, torch.int32, dev)
+        _check("cu_seqlens_kv", cu_seqlens_kv, torch.int32, dev)
+        cu_seqlens_q, cu_seqlens_kv = cu_seqlens_q.contiguous(), cu_seqlens_kv.contiguous()
+    if dout.shape != attn_out.shape:
+        raise ValueError("dout and attn_out must have the same shape")
+    plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
+                    max_seqlen_q, max_seqlen_kv, deterministic)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    if workspace is None or workspace.numel() < plan.workspace_bytes:
+        workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    plan.run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(attn_out), _ptr(softmax_lse), _ptr(cu_seqlens_q),
+             _ptr(cu_seqlens_kv), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stream)
+    return dq, dk, dv
+
+
+def sfmg(dout, attn_out, layout="BSND", cu_seqlens_q=None, N2=None, max_seqlen_q=-1):
+    """The preprocess kernel alone: float32 rowsum(dout * attn_out) in
+    softmax_lse's layout."""
+    import torch
+
+    # a plan needs key shapes; use a self-attention stand-in with N2 = N1 / 1
+    if layout == "TND":
+        T1, N1, Dv = dout.shape
+        q = torch.empty((T1, N1, Dv), dtype=torch.bfloat16, device="meta")
+        plan = get_plan(q, q, q, "TND", cu_seqlens_q, cu_seqlens_q, max_seqlen_q=max_seqlen_q,
+                        max_seqlen_kv=max_seqlen_q)
+        res = torch.empty((N1, T1), dtype=torch.float32, device=dout.device)
+    else:
+        if layout == "BSND":
+            B, S1, N1, Dv = dout.shape
+        else:
+            B, N1, S1, Dv = dout.shape
+        q = torch.empty(tuple(dout.shape), dtype=torch.bfloat16, device="meta")
+        plan = get_plan(q, q, q, layout)
+        res = torch.empty((B, N1, S1), dtype=torch.float32, device=dout.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dout.device).cuda_stream)
+    plan.sfmg(_ptr(dout.contiguous()), _ptr(attn_out.contiguous()), _ptr(cu_seqlens_q), _ptr(res), stream)
+    return res

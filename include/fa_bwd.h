@@ -1,0 +1,156 @@
+/*
+ * fa_bwd.h — C ABI of the MI355X (gfx950) FlashAttention backward library
+ * (libfa_bwd.so).
+ *
+ * What it computes (page "CANN ops-transformer FlashAttnGrad 算子详解",
+ * section 一, forward formulas and backward formulas): from the forward's
+ * inputs q, k, v, its output attn_out (Y) and its per-row log-sum-exp
+ * softmax_lse, and the upstream gradient dout (dY), the library rebuilds
+ *     P = exp(scale * Q K^T - softmax_lse)            (never stored whole)
+ * tile by tile and returns
+ *     dV = P^T dY,  dP = dY V^T,  sfmg = rowsum(dY (.) Y),
+ *     dS = P (.) (dP - sfmg),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ * Under GQA (N1 a multiple of N2) query head n1 uses key/value head
+ * n1 / (N1/N2), and dK, dV of a key/value head sum over its N1/N2 query heads.
+ *
+ * The interface follows the page's PyTorch signature (section 四 4.2) and its
+ * two-stage "size the workspace, then execute on a stream" aclnn pattern
+ * (section 六): fa_bwd_create validates the problem, plans the launch and
+ * reports the workspace size; fa_bwd_run enqueues the kernels on a stream.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, row-major, contiguous, in device memory, owned by
+ *    the caller.  Inputs are only read.  dq, dk, dv are fully overwritten
+ *    (rows that receive no gradient are written as zeros).
+ *  - bf16 is the only element type built (the page also lists fp16).
+ *  - Return value: FA_OK (0) or one of the FA_ERR_* codes below; nothing
+ *    is thrown across the ABI and nothing is printed unless FA_BWD_LOG=1.
+ *  - Plans hold host memory only; a plan may be used by one stream at a time.
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_BWD_ABI_VERSION 1
+
+/* Status codes.  The classes mirror the aclnn error families that page
+ * "aclnnFusedFloydAttentionGrad" lists (null pointer 161001, invalid
+ * parameter 161002, inner/tiling error 561002, runtime error 361001). */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULLPTR = 1,       /* a required pointer is NULL                      */
+  FA_ERR_PARAM_INVALID = 2, /* unknown dtype / layout / mask_mode / flag, bad
+                               abi_version, non-finite softmax_scale          */
+  FA_ERR_SHAPE = 3,         /* a shape constraint of section 四 4.6 is broken,
+                               or cu_seqlens are inconsistent                  */
+  FA_ERR_UNSUPPORTED = 4,   /* valid on the page but not built here (fp16,
+                               head dims outside the built set, flags)         */
+  FA_ERR_WORKSPACE = 5,     /* workspace pointer NULL or smaller than needed   */
+  FA_ERR_RUNTIME = 6        /* a HIP call or kernel launch failed              */
+};
+
+enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
+
+/* Layouts of section 四 4.6; q, k, v, dout, attn_out, dq, dk, dv share one.
+ *   BSND: q [B, S1, N1, D]   k [B, S2, N2, D]   v [B, S2, N2, Dv]
+ *   BNSD: q [B, N1, S1, D]   k [B, N2, S2, D]   v [B, N2, S2, Dv]
+ *   TND : q [T1, N1, D]      k [T2, N2, D]      v [T2, N2, Dv]
+ * dout and attn_out have q's shape with Dv; dq/dk/dv have q/k/v's shapes.
+ * softmax_lse (float32) is [B, N1, S1] for BSND and BNSD, [N1, T1] for TND. */
+enum { FA_LAYOUT_BSND = 0, FA_LAYOUT_BNSD = 1, FA_LAYOUT_TND = 2 };
+
+/* mask_mode (section 四 4.3; its value table was lost, this is the reading
+ * used throughout): the diagonal of query i is key i + (s2 - s1) of the same
+ * sequence (bottom-right alignment), and key j is visible to query i iff
+ *   j >= i + (s2 - s1) - win_left   (skipped when win_left  == -1) and
+ *   j <= i + (s2 - s1) + win_right  (skipped when win_right == -1).
+ *   FA_MASK_NONE   : dense; win_left = win_right = -1 required.
+ *   FA_MASK_CAUSAL : win_right forced to 0 (must be -1 or 0); win_left >= -1
+ *                    optionally bounds the left side (a causal sliding window).
+ *   FA_MASK_WINDOW : both bounds from win_left / win_right (each >= -1). */
+enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 };
+
+/* flags */
+#define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable dQ (not built: FA_ERR_UNSUPPORTED) */
+
+typedef struct fa_bwd_plan_s* fa_bwd_plan; /* opaque, host memory only */
+
+/* Problem description (the page's attributes and shapes, section 四 4.2/4.6). */
+typedef struct fa_bwd_desc {
+  int32_t abi_version;   /* FA_BWD_ABI_VERSION                                    */
+  int32_t dtype;         /* FA_DTYPE_BF16                                          */
+  int32_t layout;        /* FA_LAYOUT_*                                            */
+  int32_t B;             /* batch (BSND/BNSD) or number of sequences (TND); 0 < B < 65536 */
+  int32_t N1, N2;        /* query heads, key/value heads; N1 % N2 == 0           */
+  int32_t S1, S2;        /* BSND/BNSD: sequence lengths (> 0).  TND: max_seqlen_q /
+                            max_seqlen_kv, or -1 to derive them from the host
+                            cu_seqlens copies below                              */
+  int32_t D, Dv;         /* head dims, 0 < Dv <= D <= 192                         */
+  int64_t T1, T2;        /* TND: total query / key rows (> 0); ignored otherwise  */
+  const int32_t* host_cu_seqlens_q;  /* TND, optional: host copy of cu_seqlens_q
+                                        (B+1 entries) used to validate and plan;
+                                        read only during fa_bwd_create           */
+  const int32_t* host_cu_seqlens_kv; /* TND, optional: same for cu_seqlens_kv    */
+  float softmax_scale;   /* 0 selects 1/sqrt(D) (section 一, scale rule)         */
+  int32_t mask_mode;     /* FA_MASK_*                                             */
+  int32_t win_left, win_right; /* window bounds, -1 = unbounded                  */
+  uint32_t flags;        /* FA_FLAG_* ; 0 for the default (fp32 atomic dQ)       */
+} fa_bwd_desc;
+
+/* Validate `desc` (all rules of section 四 4.6 that this library enforces) and
+ * build a plan.  On success *plan receives a new plan and *workspace_bytes the
+ * device workspace size fa_bwd_run needs.  Pure host code: no HIP call, no
+ * device memory.  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
+ * FA_ERR_PARAM_INVALID, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED; *plan is left NULL. */
+int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_bytes);
+
+/* Enqueue the backward on `stream` (a hipStream_t; NULL = the null stream).
+ * Asynchronous: no allocation, no host synchronisation.
+ *   q, k, v, dout, attn_out : bf16 in the plan's layout (see above)
+ *   softmax_lse             : float32, [B, N1, S1] or [N1, T1]; -inf marks a
+ *                             query row with no visible key (its dq row is 0)
+ *   cu_seqlens_q/kv         : device int32 [B+1] prefix sums; required for TND
+ *                             (cu[0] = 0, non-decreasing, cu[B] = T), NULL
+ *                             otherwise (section 四 4.6)
+ *   dq, dk, dv              : bf16 outputs, shapes of q, k, v
+ *   workspace               : device memory of at least *workspace_bytes from
+ *                             fa_bwd_create, exclusively owned by this call
+ *                             until it completes on `stream`
+ * Errors: FA_ERR_NULLPTR (plan or a tensor pointer NULL), FA_ERR_SHAPE
+ * (cu_seqlens given or missing against the layout), FA_ERR_WORKSPACE,
+ * FA_ERR_RUNTIME (a launch failed).  Device cu_seqlens are trusted: they must
+ * agree with T1/T2 and the max lengths in the plan. */
+int fa_bwd_run(fa_bwd_plan plan,
+               const void* q, const void* k, const void* v,
+               const void* dout, const void* attn_out, const float* softmax_lse,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+               void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* The preprocess step alone (the page's first vector stage, section 五 5.2:
+ * sfmg = rowsum(dY (.) Y)): writes float32 sfmg in softmax_lse's layout
+ * ([B, N1, S1] or [N1, T1]) to `sfmg`, a caller buffer of that size.
+ * Same pointer rules and errors as fa_bwd_run. */
+int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
+                const int32_t* cu_seqlens_q, float* sfmg, void* stream);
+
+/* Free a plan.  NULL is a no-op.  Returns FA_OK. */
+int fa_bwd_destroy(fa_bwd_plan plan);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_bwd_strerror(int status);
+
+/* FA_BWD_ABI_VERSION of the loaded library. */
+int fa_bwd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BWD_H */

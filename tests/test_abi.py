@@ -1,0 +1,186 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa_bwd.h declares, and fa_bwd_create enforces the constraints of page
+"CANN ops-transformer FlashAttnGrad 算子详解", section 四 4.6, with the error
+classes of the header.  fa_bwd_run's pointer and workspace checks return
+before any device call, so they are exercised here too."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from flashattention_backward_fa_amd import fa_bwd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fb.LIB_PATH):
+        from flashattention_backward_fa_amd import build
+        build.build()
+    return fb.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa_bwd.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|void)\s+(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(fb.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.fa_bwd_abi_version() == 1
+    for st in range(0, 7):
+        assert len(fb.strerror(st)) > 0
+    assert fb.strerror(99) == "unknown status"
+
+
+def create(lib, **kw):
+    base = dict(layout="BSND", B=2, N1=8, N2=2, S1=128, S2=128, D=128, Dv=128)
+    base.update(kw)
+    d = fb.make_desc(**base)
+    h = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    st = lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws))
+    if st == fb.FA_OK:
+        lib.fa_bwd_destroy(h)
+    else:
+        assert not h.value
+    return st, ws.value
+
+
+def test_valid_problem_and_workspace_size(lib):
+    st, ws = create(lib)
+    assert st == fb.FA_OK
+    q_elems = 2 * 128 * 8 * 128
+    lse = 2 * 8 * 128
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert ws == rnd(q_elems * 4) + rnd(lse * 4)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), fb.FA_ERR_SHAPE),
+    (dict(B=65536), fb.FA_ERR_SHAPE),
+    (dict(N1=6, N2=4), fb.FA_ERR_SHAPE),            # N1 % N2
+    (dict(N2=0), fb.FA_ERR_SHAPE),
+    (dict(D=128, Dv=192), fb.FA_ERR_SHAPE),          # Dv <= D
+    (dict(D=256, Dv=128), fb.FA_ERR_SHAPE),          # D <= 192
+    (dict(S1=0), fb.FA_ERR_SHAPE),
+    (dict(mask_mode=0, win_left=5), fb.FA_ERR_SHAPE),  # dense needs no window
+    (dict(mask_mode=1, win_right=3), fb.FA_ERR_SHAPE),
+    (dict(mask_mode=2, win_left=-2), fb.FA_ERR_SHAPE),
+    (dict(mask_mode=3), fb.FA_ERR_PARAM_INVALID),
+    (dict(layout=3), fb.FA_ERR_PARAM_INVALID),
+    (dict(dtype=2), fb.FA_ERR_PARAM_INVALID),
+    (dict(flags=0x10), fb.FA_ERR_PARAM_INVALID),
+    (dict(softmax_scale=float("nan")), fb.FA_ERR_PARAM_INVALID),
+    (dict(dtype=1), fb.FA_ERR_UNSUPPORTED),          # fp16 is on the page, not built
+    (dict(D=96, Dv=96), fb.FA_ERR_UNSUPPORTED),      # head dim not instantiated
+    (dict(flags=fb.FLAG_DETERMINISTIC), fb.FA_ERR_UNSUPPORTED),
+])
+def test_create_rejects(lib, kw, code):
+    assert create(lib, **kw)[0] == code
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mask_mode=1), dict(mask_mode=1, win_left=1024, win_right=0), dict(mask_mode=2, win_left=3, win_right=7),
+    dict(mask_mode="causal"), dict(mask_mode=fb.MaskMode.WINDOW, win_left=-1, win_right=-1),
+    dict(D=192, Dv=128), dict(D=64, Dv=64), dict(N1=32, N2=8), dict(softmax_scale=0.25),
+])
+def test_create_accepts(lib, kw):
+    assert create(lib, **kw)[0] == fb.FA_OK
+
+
+def test_abi_version_mismatch(lib):
+    d = fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64)
+    d.abi_version = 7
+    h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_ERR_PARAM_INVALID
+
+
+def test_null_pointers(lib):
+    d = fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64)
+    h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.fa_bwd_create(None, ctypes.byref(h), ctypes.byref(ws)) == fb.FA_ERR_NULLPTR
+    assert lib.fa_bwd_create(ctypes.byref(d), None, ctypes.byref(ws)) == fb.FA_ERR_NULLPTR
+    assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), None) == fb.FA_ERR_NULLPTR
+    assert lib.fa_bwd_destroy(None) == fb.FA_OK
+
+
+def tnd_create(lib, lens_q, lens_kv, S1=-1, S2=-1, host=True, T1=None, T2=None, **kw):
+    cq = [0]
+    for x in lens_q:
+        cq.append(cq[-1] + x)
+    ck = [0]
+    for x in lens_kv:
+        ck.append(ck[-1] + x)
+    aq = (ctypes.c_int32 * len(cq))(*cq)
+    ak = (ctypes.c_int32 * len(ck))(*ck)
+    d = fb.make_desc("TND", len(lens_q), 4, 2, S1, S2, 128, 128, cq[-1] if T1 is None else T1,
+                     ck[-1] if T2 is None else T2, host_cu_q=aq if host else None, host_cu_kv=ak if host else None,
+                     **kw)
+    h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+    st = lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws))
+    if st == fb.FA_OK:
+        lib.fa_bwd_destroy(h)
+    return st
+
+
+def test_tnd_rules(lib):
+    assert tnd_create(lib, [5, 0, 9], [3, 4, 9]) == fb.FA_OK
+    assert tnd_create(lib, [5, 0, 9], [3, 4, 9], S1=9, S2=9) == fb.FA_OK
+    assert tnd_create(lib, [5, 0, 9], [3, 4, 9], S1=8, S2=9) == fb.FA_ERR_SHAPE   # max_seqlen too small
+    assert tnd_create(lib, [5, 9], [3, 9], T1=15) == fb.FA_ERR_SHAPE              # cu[B] != T
+    assert tnd_create(lib, [5, 9], [3, 9], host=False) == fb.FA_ERR_SHAPE         # no lengths at all
+    assert tnd_create(lib, [5, 9], [3, 9], host=False, S1=9, S2=9) == fb.FA_OK
+    # host cu_seqlens are refused for dense layouts
+    aq = (ctypes.c_int32 * 2)(0, 4)
+    d = fb.make_desc("BSND", 1, 2, 2, 4, 4, 64, 64, host_cu_q=aq, host_cu_kv=aq)
+    h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_ERR_SHAPE
+
+
+def test_tnd_decreasing_cu_rejected(lib):
+    aq = (ctypes.c_int32 * 3)(0, 6, 4)
+    d = fb.make_desc("TND", 2, 2, 2, -1, -1, 64, 64, 4, 4, host_cu_q=aq, host_cu_kv=aq)
+    h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_ERR_SHAPE
+
+
+def test_run_checks_before_any_device_call(lib):
+    plan = fb.Plan(fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64))
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every check below fails first
+    args = [fake] * 6 + [None, None] + [fake] * 3
+    st = lib.fa_bwd_run(plan.handle, *args, None, plan.workspace_bytes, None)
+    assert st == fb.FA_ERR_WORKSPACE
+    st = lib.fa_bwd_run(plan.handle, *args, fake, plan.workspace_bytes - 1, None)
+    assert st == fb.FA_ERR_WORKSPACE
+    st = lib.fa_bwd_run(plan.handle, *([fake] * 6), fake, fake, *([fake] * 3), fake, plan.workspace_bytes, None)
+    assert st == fb.FA_ERR_SHAPE   # cu_seqlens given for a dense layout
+    st = lib.fa_bwd_run(plan.handle, None, *args[1:], fake, plan.workspace_bytes, None)
+    assert st == fb.FA_ERR_NULLPTR
+    assert lib.fa_bwd_run(None, *args, fake, plan.workspace_bytes, None) == fb.FA_ERR_NULLPTR
+    assert lib.fa_bwd_sfmg(plan.handle, None, fake, None, fake, None) == fb.FA_ERR_NULLPTR
+
+
+def test_mask_mode_names():
+    assert fb.mask_mode_value("Causal") == 1
+    assert fb.mask_mode_value("window") == 2
+    assert fb.mask_mode_value(fb.MaskMode.NONE) == 0
+    with pytest.raises(ValueError):
+        fb.mask_mode_value("diagonal")
+
+
+def test_default_scale_is_reported_in_plan(lib):
+    # scale 0 -> 1/sqrt(D) is a host decision; a plan must accept it
+    assert create(lib, softmax_scale=0.0, D=192, Dv=128)[0] == fb.FA_OK
+    assert math.isclose(1 / math.sqrt(192), 0.07216878364870322)

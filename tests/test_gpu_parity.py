@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance (bf16 outputs, per tensor, against the stored-mode oracle):
+relative Frobenius error <= 1e-2 and max |err| <= 2e-2 * max |ref|.
+Small cases compare every element; the four large workloads compare the
+sfmg preprocess on every row and dq/dk/dv on sampled rows that the oracle
+evaluates one by one (backward_rows), in the same launch configuration the
+benchmark times."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from flashattention_backward_fa_amd import workloads as W
+
+from gpu_helpers import (assert_close, case_inputs, f64, gpu_backward, oracle_backward, oracle_inputs, say,
+                         max_lengths)
+
+pytestmark = pytest.mark.gpu
+
+EDGE_CASES = {
+    "tiny_full": W.CONFIGS["tiny"],
+    "bsnd_causal_gqa4_ragged": W.custom("BSND", B=1, N1=8, N2=2, S1=300, S2=300, D=128, Dv=128, mask_mode=1),
+    "bsnd_dense_ragged_d64": W.custom("BSND", B=2, N1=2, N2=2, S1=200, S2=333, D=64, Dv=64, softmax_scale=0.2),
+    "bnsd_causal_s1_lt_s2_d192": W.custom("BNSD", B=1, N1=2, N2=1, S1=100, S2=260, D=192, Dv=128, mask_mode=1),
+    "bnsd_causal_s1_gt_s2_empty_rows": W.custom("BNSD", B=1, N1=2, N2=2, S1=260, S2=100, D=128, Dv=128, mask_mode=1),
+    "bsnd_window_37_11": W.custom("BSND", B=1, N1=4, N2=2, S1=250, S2=250, D=128, Dv=128, mask_mode=2,
+                                  win_left=37, win_right=11),
+    "bsnd_causal_left70": W.custom("BSND", B=1, N1=2, N2=2, S1=333, S2=333, D=128, Dv=128, mask_mode=1,
+                                   win_left=70, win_right=0),
+    "tnd_mixed_lengths": W.custom("TND", N1=4, N2=2, D=128, Dv=128, mask_mode=1, lengths=[1, 0, 130, 257, 64],
+                                  lengths_kv=[1, 5, 130, 200, 0]),
+    "tnd_window_dense_heads": W.custom("TND", N1=2, N2=2, D=64, Dv=64, mask_mode=2, win_left=20, win_right=5,
+                                       lengths=[77, 128, 3], lengths_kv=[77, 128, 3]),
+    "bsnd_gqa8_dv64": W.custom("BSND", B=1, N1=8, N2=1, S1=192, S2=192, D=128, Dv=64, mask_mode=0,
+                               softmax_scale=0.05),
+    "bsnd_d192_dv64_window": W.custom("BSND", B=1, N1=2, N2=1, S1=160, S2=140, D=192, Dv=64, mask_mode=2,
+                                      win_left=-1, win_right=30),
+    "bnsd_batch3_causal": W.custom("BNSD", B=3, N1=4, N2=4, S1=129, S2=129, D=64, Dv=64, mask_mode=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_CASES))
+def test_parity_full_output(name):
+    cfg = EDGE_CASES[name]
+    say(f"[parity] {name}: {cfg}")
+    x = case_inputs(cfg, seed=sorted(EDGE_CASES).index(name))
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    say(f"[parity] {name}: launching")
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    assert_close(gq, rq, "dq")
+    assert_close(gk, rk, "dk")
+    assert_close(gv, rv, "dv")
+    # gradient rows that must vanish (no visible key / no attending query) are exact zeros
+    for got, ref in ((gq, rq), (gk, rk), (gv, rv)):
+        empty = np.all(ref == 0, axis=-1)
+        assert not np.any(got[empty])
+
+
+def test_zero_upstream_gradient_gives_exact_zeros():
+    cfg = W.custom("BSND", B=1, N1=4, N2=2, S1=150, S2=150, D=128, Dv=128, mask_mode=1)
+    x = case_inputs(cfg, 3)
+    x["dout"].zero_()
+    Yst, lst = oracle_inputs(cfg, x)
+    say("[parity] zero dout")
+    for g in gpu_backward(cfg, x, Yst, lst):
+        assert not np.any(g)
+
+
+def _metamorphic_inputs():
+    cfg = W.custom("BSND", B=1, N1=4, N2=2, S1=200, S2=200, D=128, Dv=128, mask_mode=1)
+    x = case_inputs(cfg, 4)
+    Yst, lst = oracle_inputs(cfg, x)
+    return cfg, x, Yst, lst
+
+
+def test_doubling_dout_doubles_dk_dv_bitwise():
+    cfg, x, Yst, lst = _metamorphic_inputs()
+    say("[meta] dout x2")
+    g1 = gpu_backward(cfg, x, Yst, lst)
+    x2 = dict(x, dout=x["dout"] * 2)
+    g2 = gpu_backward(cfg, x2, Yst, lst)
+    assert np.array_equal(2 * g1[1], g2[1]) and np.array_equal(2 * g1[2], g2[2])
+    assert np.allclose(2 * g1[0], g2[0], rtol=0, atol=2e-2 * np.abs(g1[0]).max())
+
+
+def test_default_scale_equals_explicit_scale_bitwise():
+    cfg, x, Yst, lst = _metamorphic_inputs()
+    cfg0 = dict(cfg, softmax_scale=0.0)
+    cfg1 = dict(cfg, softmax_scale=1 / math.sqrt(128))
+    say("[meta] scale 0 vs 1/sqrt(D)")
+    a = gpu_backward(cfg0, x, Yst, lst)
+    b = gpu_backward(cfg1, x, Yst, lst)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
+def test_layouts_agree_bitwise_on_dk_dv():
+    import torch
+    cfg, x, Yst, lst = _metamorphic_inputs()
+    say("[meta] BSND vs BNSD vs TND")
+    g_bsnd = gpu_backward(cfg, x, Yst, lst)
+    tr = lambda t: t.transpose(1, 2).contiguous()  # noqa: E731
+    xb = dict(x, q=tr(x["q"]), k=tr(x["k"]), v=tr(x["v"]), dout=tr(x["dout"]))
+    g_bnsd = gpu_backward(dict(cfg, layout="BNSD"), xb, np.ascontiguousarray(Yst.transpose(0, 2, 1, 3)), lst)
+    for a, b in zip(g_bsnd[1:], g_bnsd[1:]):
+        assert np.array_equal(a, b.transpose(0, 2, 1, 3))
+    cu = np.array([0, 200], dtype=np.int32)
+    xt = dict(x, q=x["q"][0], k=x["k"][0], v=x["v"][0], dout=x["dout"][0], cu_q=cu, cu_kv=cu.copy())
+    g_tnd = gpu_backward(dict(cfg, layout="TND", lengths=[200]), xt, Yst[0], lst[0])
+    for a, b in zip(g_bsnd[1:], g_tnd[1:]):
+        assert np.array_equal(a[0], b)
+    del torch
+
+
+# ------------------------------------------------------------------ large workloads
+
+_cache = {}
+
+
+def big(name):
+    if name not in _cache:
+        cfg = W.CONFIGS[name]
+        x = W.make_inputs(cfg)
+        say(f"[parity] {name}: oracle forward")
+        Yst, lst = oracle_inputs(cfg, x)
+        _cache.clear()
+        _cache[name] = (cfg, x, Yst, lst)
+    return _cache[name]
+
+
+def sample_rows(cfg, x, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    if cfg["layout"] == "TND":
+        lq, lk = np.diff(x["cu_q"]), np.diff(x["cu_kv"])
+    else:
+        lq, lk = [cfg["S1"]] * cfg["B"], [cfg["S2"]] * cfg["B"]
+    B = len(lq)
+    q_rows, kv_rows = [], []
+    for t in range(n):
+        b = int(rng.integers(B))
+        picks_q = [0, int(lq[b]) - 1, 63, 64, 127, 128] + [int(rng.integers(lq[b]))]
+        picks_k = [0, int(lk[b]) - 1, 127, 128] + [int(rng.integers(lk[b]))]
+        q_rows.append((b, int(rng.integers(cfg["N1"])), min(picks_q[t % len(picks_q)], int(lq[b]) - 1)))
+        kv_rows.append((b, int(rng.integers(cfg["N2"])), min(picks_k[t % len(picks_k)], int(lk[b]) - 1)))
+    return q_rows, kv_rows
+
+
+def pick(arr, cfg, x, b, n, i, kind):
+    L = cfg["layout"]
+    if L == "TND":
+        cu = x["cu_q"] if kind == "q" else x["cu_kv"]
+        return arr[cu[b] + i, n]
+    if L == "BSND":
+        return arr[b, i, n]
+    return arr[b, n, i]
+
+
+@pytest.mark.parametrize("name", ["mha_causal", "gqa_causal", "varlen_window", "wide_qk"])
+def test_parity_large_workload_sampled(name):
+    import torch
+    cfg, x, Yst, lst = big(name)
+    say(f"[parity] {name}: sfmg preprocess")
+    import flashattention_backward_fa_amd as fa
+    dev = torch.device("cuda", 0)
+    cu = torch.from_numpy(x["cu_q"]).to(dev) if cfg["layout"] == "TND" else None
+    mq, _ = max_lengths(cfg, x)
+    attn_out = torch.from_numpy(Yst).to(torch.bfloat16).to(dev)
+    s_gpu = fa.sfmg(x["dout"].to(dev), attn_out, cfg["layout"], cu, max_seqlen_q=mq).cpu().double().numpy()
+    s_ref = oracle.sfmg(f64(x["dout"]), Yst, cfg["layout"], x["cu_q"])
+    bound = 1e-5 * oracle.sfmg(np.abs(f64(x["dout"])), np.abs(Yst), cfg["layout"], x["cu_q"]) + 1e-30
+    assert np.all(np.abs(s_gpu - s_ref) <= bound)
+
+    say(f"[parity] {name}: backward")
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    q_rows, kv_rows = sample_rows(cfg, x)
+    rq, rk, rv = oracle.backward_rows(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"]), Yst, lst, q_rows,
+                                      kv_rows, cfg["layout"], x["cu_q"], x["cu_kv"], cfg["softmax_scale"],
+                                      cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
+    got_q = np.stack([pick(gq, cfg, x, b, n, i, "q") for (b, n, i) in q_rows])
+    got_k = np.stack([pick(gk, cfg, x, b, n, j, "kv") for (b, n, j) in kv_rows])
+    got_v = np.stack([pick(gv, cfg, x, b, n, j, "kv") for (b, n, j) in kv_rows])
+    assert_close(got_q, np.stack(rq), "dq (sampled rows)")
+    assert_close(got_k, np.stack(rk), "dk (sampled rows)")
+    assert_close(got_v, np.stack(rv), "dv (sampled rows)")
+    assert np.all(np.isfinite(gq)) and np.all(np.isfinite(gk)) and np.all(np.isfinite(gv))

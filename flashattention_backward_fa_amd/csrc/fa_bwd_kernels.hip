@@ -41,6 +41,8 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -326,18 +328,15 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
         }
       }
 
-      // ---- dS^T -> LDS: row = key, 4 consecutive query rows per 8-byte store
+      // ---- dS^T -> LDS: row = key, 4 consecutive query rows per 8-byte store.
+      // (Whole-vector bit casts only: this compiler mis-lowers a bit cast of a
+      // single bf16 vector element.)
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int kc = mb * 2 + (r4 >> 1);
-          const int e0 = (r4 & 1) * 4;
-          shortx4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(short, da[kc][e0 + e]);
-          *reinterpret_cast<shortx4*>(&St[kw * SP + mb * 32 + r4 * 8 + hi * 4]) = w;
-        }
+      for (int kc = 0; kc < 2 * NMB; ++kc) {
+        const uintx4 u = __builtin_bit_cast(uintx4, da[kc]);
+        bf16* row = &St[kw * SP + kc * 16 + hi * 4];
+        *reinterpret_cast<uintx2*>(row) = uintx2{u[0], u[1]};
+        *reinterpret_cast<uintx2*>(row + 8) = uintx2{u[2], u[3]};
       }
       __syncthreads();
 

@@ -66,6 +66,31 @@ def gpu_backward(cfg, x, Yst, lst, **extra):
     return f64(dq.cpu()), f64(dk.cpu()), f64(dv.cpu())
 
 
+def empty_rows(cfg, x, q_shape, k_shape):
+    """Boolean arrays over the row axes of q and k: True for query rows that
+    see no key and key rows that no query sees (their gradients must be
+    exactly zero)."""
+    L, R = oracle.mask_bounds(cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
+    lay = cfg["layout"]
+    qe = np.zeros(q_shape[:-1], dtype=bool)
+    ke = np.zeros(k_shape[:-1], dtype=bool)
+    if lay == "TND":
+        cq, ck = x["cu_q"], x["cu_kv"]
+        for b in range(len(cq) - 1):
+            ok = oracle.allowed_matrix(int(cq[b + 1] - cq[b]), int(ck[b + 1] - ck[b]), L, R)
+            qe[cq[b]:cq[b + 1], :] = ~ok.any(axis=1)[:, None]
+            ke[ck[b]:ck[b + 1], :] = ~ok.any(axis=0)[:, None]
+        return qe, ke
+    ok = oracle.allowed_matrix(cfg["S1"], cfg["S2"], L, R)
+    if lay == "BSND":
+        qe[:] = ~ok.any(axis=1)[None, :, None]
+        ke[:] = ~ok.any(axis=0)[None, :, None]
+    else:
+        qe[:] = ~ok.any(axis=1)[None, None, :]
+        ke[:] = ~ok.any(axis=0)[None, None, :]
+    return qe, ke
+
+
 def errors(got, ref):
     err = got - ref
     nref = np.linalg.norm(ref)
@@ -75,11 +100,15 @@ def errors(got, ref):
     return rel, mx
 
 
-def assert_close(got, ref, name):
-    rel, mx = errors(got, ref)
-    say(f"    {name}: rel_fro={rel:.3e} max_abs_ratio={mx:.3e}")
-    assert rel <= REL_FRO_TOL, f"{name}: relative Frobenius error {rel:.3e} > {REL_FRO_TOL}"
-    assert mx <= MAX_ABS_TOL, f"{name}: max-abs error ratio {mx:.3e} > {MAX_ABS_TOL}"
+def assert_all_close(triples):
+    """Report every tensor's errors, then fail on the first one out of tolerance."""
+    bad = []
+    for got, ref, name in triples:
+        rel, mx = errors(got, ref)
+        say(f"    {name}: rel_fro={rel:.3e} max_abs_ratio={mx:.3e}")
+        if rel > REL_FRO_TOL or mx > MAX_ABS_TOL:
+            bad.append(f"{name}: rel_fro {rel:.3e} (tol {REL_FRO_TOL}), max_abs_ratio {mx:.3e} (tol {MAX_ABS_TOL})")
+    assert not bad, "; ".join(bad)
 
 
 def case_inputs(cfg, seed=0):

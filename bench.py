@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention backward on one MI355X.
+
+One step = one fa_bwd_run over one batch of the workload: the sfmg
+preprocess, the main kernel (S/P recompute, dP, dS, dV, dK, dQ) and the dQ
+finalize, with every input already resident in HBM.  attn_out and
+softmax_lse come from the library's own GPU forward (fa_fwd_run), made once
+before timing.  The default workload is the GQA causal one (B=1, N1=32, N2=8,
+S=4096, D=Dv=128, BSND).
+
+Prints one JSON line: whole-step throughput in TFLOP/s under the standard
+FLOP count (2*(3D+2Dv) per visible (query, key) pair per query head; causal
+with S1 = S2 counted as exactly half of S1*S2), the main kernel's roofline
+entry from HIP events recorded around it inside the timed region, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload gqa_causal]
+                    [--no-cpu-baseline] [--copy-calibration]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FA-bwd TFLOP/s and % of MI355X bf16 MFMA peak (S=4096, D=128, GQA, causal)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc", "fa_bwd_kernels.hip")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def visible_pairs(cfg):
+    """Visible (query, key) pairs per query head, summed over sequences.
+    Causal with equal lengths and no left bound counts S*S/2 (the usual
+    'halved' convention); every other mask counts exactly."""
+    if cfg["layout"] == "TND":
+        lens_q = list(cfg["lengths"])
+        lens_k = list(cfg.get("lengths_kv", cfg["lengths"]))
+    else:
+        lens_q, lens_k = [cfg["S1"]] * cfg["B"], [cfg["S2"]] * cfg["B"]
+    mode, wl, wr = cfg["mask_mode"], cfg["win_left"], cfg["win_right"]
+    if mode == 0:
+        wl, wr = -1, -1
+    elif mode == 1:
+        wr = 0
+    total = 0
+    for s1, s2 in zip(lens_q, lens_k):
+        if mode == 1 and wl < 0 and s1 == s2:
+            total += s1 * s2 / 2
+            continue
+        off = s2 - s1
+        for i in range(s1):
+            lo = 0 if wl < 0 else max(0, i + off - wl)
+            hi = s2 - 1 if wr < 0 else min(s2 - 1, i + off + wr)
+            if hi >= lo:
+                total += hi - lo + 1
+    return total
+
+
+def algorithmic_flops(cfg):
+    return 2.0 * (3 * cfg["D"] + 2 * cfg["Dv"]) * cfg["N1"] * visible_pairs(cfg)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per main-kernel launch from the committed rocprofv3 --pmc
+    summary, if it was taken from the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"bwd_main_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, max_heads, name=""):
+    """The fp64 oracle's backward, untuned, on the first KV-head groups of
+    the workload (its forward is run first, untimed, to make Y and lse)."""
+    import numpy as np
+    import oracle
+    from flashattention_backward_fa_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    G = cfg["N1"] // cfg["N2"]
+    groups = max(1, min(cfg["N2"], max_heads // G))
+    sub = dict(cfg, N1=groups * G, N2=groups)
+    x = W.make_inputs(cfg)
+    lay = cfg["layout"]
+    # head slice of the full workload's tensors
+    if lay == "BSND":
+        sl = lambda t, n: t[:, :, :n]  # noqa: E731
+    elif lay == "BNSD":
+        sl = lambda t, n: t[:, :n]  # noqa: E731
+    else:
+        sl = lambda t, n: t[:, :n]  # noqa: E731
+    q = sl(x["q"], sub["N1"]).double().numpy()
+    k = sl(x["k"], sub["N2"]).double().numpy()
+    v = sl(x["v"], sub["N2"]).double().numpy()
+    dy = sl(x["dout"], sub["N1"]).double().numpy()
+    args = (lay, x["cu_q"], x["cu_kv"], cfg["softmax_scale"], cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
+    Y, lse = oracle.forward(q, k, v, *args)
+    Yst, lst = oracle.store(Y, lse)
+    t0 = time.perf_counter()
+    oracle.backward(q, k, v, dy, Yst, lst, *args)
+    dt = time.perf_counter() - t0
+    flops = algorithmic_flops(sub)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"{sub['N1']} of {cfg['N1']} query heads ({groups} KV-head group(s)) of the {name} workload, "
+                   f"full sequence; oracle backward (dense fp64 NumPy, masked work not skipped) took {dt:.2f} s; "
+                   f"value = algorithmic FLOP of the sample / time"),
+    }
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings to bytes."""
+    import torch
+
+    n = 256 << 20  # 256 MiB
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the kernel shards over "
+              "KV-head groups with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    from flashattention_backward_fa_amd import fa_bwd as fb
+    from flashattention_backward_fa_amd import workloads as W
+
+    name = args.workload or W.BENCH_WORKLOAD
+    cfg = W.CONFIGS[name]
+    dev = torch.device("cuda", 0)
+    x = W.make_inputs(cfg)
+    q, k, v, dout = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    cu_q = cu_kv = None
+    mq = mk = -1
+    if cfg["layout"] == "TND":
+        cu_q = torch.from_numpy(x["cu_q"]).to(dev)
+        cu_kv = torch.from_numpy(x["cu_kv"]).to(dev)
+        mq = mk = int(max(cfg["lengths"]))
+    kw = dict(softmax_scale=cfg["softmax_scale"], mask_mode=cfg["mask_mode"], win_left=cfg["win_left"],
+              win_right=cfg["win_right"], max_seqlen_q=mq, max_seqlen_kv=mk, layout=cfg["layout"])
+    attn_out, lse = fb.flash_attn(q, k, v, cu_q, cu_kv, **kw)
+    plan = fb.get_plan(q, k, v, cfg["layout"], cu_q, cu_kv, kw["softmax_scale"], kw["mask_mode"], kw["win_left"],
+                       kw["win_right"], mq, mk)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fb.flash_attn_grad(q, k, v, dout, attn_out, lse, cu_q, cu_kv, workspace=ws, out=(dq, dk, dv), **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan.profile_enable(max(args.steps, 1))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / max(args.steps, 1)
+    main_ms = plan.profile_read(args.steps)
+    plan.profile_enable(0)
+    main_avg = sum(main_ms) / max(len(main_ms), 1)
+
+    flops = algorithmic_flops(cfg)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (main_avg * 1e-3) / 1e12
+    traffic = committed_traffic(name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": name, "layout": cfg["layout"], "B": cfg.get("B", len(cfg.get("lengths", [])) or None),
+            "N1": cfg["N1"], "N2": cfg["N2"], "S1": cfg.get("S1"), "S2": cfg.get("S2"), "D": cfg["D"],
+            "Dv": cfg["Dv"], "mask_mode": cfg["mask_mode"], "win_left": cfg["win_left"],
+            "win_right": cfg["win_right"], "global_batch": cfg.get("B", len(cfg.get("lengths", []))),
+            "seq_len": cfg.get("S1", int(sum(cfg.get("lengths", [0])))), "parallelism": "single-gpu",
+            "algorithmic_gflop": round(flops / 1e9, 3), "dq_mode": "fp32 atomics",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "bwd_main_kernel", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic, "avg_launch_ms": round(main_avg, 5), "launches_timed": len(main_ms),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads, name)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

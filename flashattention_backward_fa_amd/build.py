@@ -1,8 +1,10 @@
 """Build libfa_bwd.so in-tree for gfx950.
 
 The host planner (csrc/fa_bwd_api.cpp) is plain C++ built with g++; the
-kernels (csrc/fa_bwd_kernels.hip) are built with hipcc for gfx950 only; the
-two objects are linked into flashattention_backward_fa_amd/lib/libfa_bwd.so.
+kernels (csrc/fa_bwd_kernels.hip: backward; csrc/fa_fwd_kernels.hip: the
+forward that produces attn_out and softmax_lse) are built with hipcc for
+gfx950 only; the objects are linked into
+flashattention_backward_fa_amd/lib/libfa_bwd.so.
 
 Usage: python -m flashattention_backward_fa_amd.build
 """
@@ -55,12 +57,15 @@ def build(verbose=False):
     hipcc = _hipcc()
     api_o = os.path.join(BUILDDIR, "fa_bwd_api.o")
     ker_o = os.path.join(BUILDDIR, "fa_bwd_kernels.o")
+    fwd_o = os.path.join(BUILDDIR, "fa_fwd_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
           "-c", os.path.join(CSRC, "fa_bwd_api.cpp"), "-o", api_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_kernels.hip"),
           "-o", ker_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_fwd_kernels.hip"),
+          "-o", fwd_o], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o], verbose)
     os.replace(tmp, LIB)
     return LIB
 

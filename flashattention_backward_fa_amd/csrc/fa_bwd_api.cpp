@@ -24,6 +24,7 @@ struct fa_bwd_plan_s {
   int64_t q_elems;         // elements of q (and of the fp32 dQ accumulator)
   int64_t lse_elems;       // elements of softmax_lse / sfmg
   size_t off_dq_acc, off_sfmg, ws_bytes;
+  fabwd::Profiler* prof = nullptr;  // timing hook, off by default
 };
 
 namespace {
@@ -199,9 +200,40 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   a.sfmg = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_sfmg);
 
   if (fabwd::launch_preprocess(a, true, stream) != 0) return FA_ERR_RUNTIME;
+  if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
   if (fabwd::launch_main(a, stream) != 0) return FA_ERR_RUNTIME;
+  if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
   if (fabwd::launch_dq_finalize(a, stream) != 0) return FA_ERR_RUNTIME;
   return FA_OK;
+}
+
+int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+               const int32_t* cu_seqlens_kv, void* attn_out, float* softmax_lse, void* stream) {
+  if (!plan || !q || !k || !v || !attn_out || !softmax_lse) return FA_ERR_NULLPTR;
+  int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
+  if (st != FA_OK) return st;
+  KernelArgs a = plan->args;
+  a.q = q; a.k = k; a.v = v;
+  a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
+  if (fabwd::launch_forward(a, attn_out, softmax_lse, stream) != 0) return FA_ERR_RUNTIME;
+  return FA_OK;
+}
+
+int fa_bwd_profile_enable(fa_bwd_plan plan, int slots) {
+  if (!plan) return FA_ERR_NULLPTR;
+  if (slots < 0 || slots > 65536) return FA_ERR_PARAM_INVALID;
+  fabwd::profiler_destroy(plan->prof);
+  plan->prof = nullptr;
+  if (slots == 0) return FA_OK;
+  plan->prof = fabwd::profiler_create(slots);
+  return plan->prof ? FA_OK : FA_ERR_RUNTIME;
+}
+
+int fa_bwd_profile_read(fa_bwd_plan plan, float* ms, int cap, int* count) {
+  if (!plan || !ms || !count) return FA_ERR_NULLPTR;
+  *count = 0;
+  if (!plan->prof) return FA_OK;
+  return fabwd::profiler_read(plan->prof, ms, cap, count) == 0 ? FA_OK : FA_ERR_RUNTIME;
 }
 
 int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
@@ -216,6 +248,7 @@ int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
 }
 
 int fa_bwd_destroy(fa_bwd_plan plan) {
+  if (plan) fabwd::profiler_destroy(plan->prof);
   delete plan;
   return FA_OK;
 }

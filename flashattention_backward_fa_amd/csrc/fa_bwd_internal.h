@@ -54,6 +54,15 @@ struct KernelArgs {
 int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream);
 int launch_main(const KernelArgs& a, void* stream);
 int launch_dq_finalize(const KernelArgs& a, void* stream);
+int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream);
 bool main_instantiated(int D, int Dv);
+
+// Ring of HIP event pairs bracketing the main kernel (timing hook).
+struct Profiler;
+Profiler* profiler_create(int slots);   // nullptr on failure
+void profiler_destroy(Profiler* p);
+int profiler_begin(Profiler* p, void* stream);
+int profiler_end(Profiler* p, void* stream);
+int profiler_read(Profiler* p, float* ms, int cap, int* count);
 
 }  // namespace fabwd

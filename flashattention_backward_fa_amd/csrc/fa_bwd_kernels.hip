@@ -31,6 +31,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <new>
+
 #include "fa_bwd_internal.h"
 
 namespace fabwd {
@@ -434,6 +436,68 @@ int launch_main(const KernelArgs& a, void* stream) {
   else if (a.D == 192 && a.Dv == 128) hipLaunchKernelGGL((bwd_main_kernel<192, 128>), grid, block, 0, s, a);
   else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------- timing hook
+
+struct Profiler {
+  int slots = 0;
+  int next = 0;    // slot of the next begin/end pair
+  int count = 0;   // recorded pairs not yet read
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+};
+
+Profiler* profiler_create(int slots) {
+  Profiler* p = new (std::nothrow) Profiler();
+  if (!p) return nullptr;
+  p->start = new (std::nothrow) hipEvent_t[slots]();
+  p->stop = new (std::nothrow) hipEvent_t[slots]();
+  if (!p->start || !p->stop) { profiler_destroy(p); return nullptr; }
+  for (int i = 0; i < slots; ++i) {
+    if (hipEventCreate(&p->start[i]) != hipSuccess || hipEventCreate(&p->stop[i]) != hipSuccess) {
+      p->slots = i + 1;
+      profiler_destroy(p);
+      return nullptr;
+    }
+  }
+  p->slots = slots;
+  return p;
+}
+
+void profiler_destroy(Profiler* p) {
+  if (!p) return;
+  for (int i = 0; i < p->slots; ++i) {
+    if (p->start && p->start[i]) (void)hipEventDestroy(p->start[i]);
+    if (p->stop && p->stop[i]) (void)hipEventDestroy(p->stop[i]);
+  }
+  delete[] p->start;
+  delete[] p->stop;
+  delete p;
+}
+
+int profiler_begin(Profiler* p, void* stream) {
+  return (int)hipEventRecord(p->start[p->next], static_cast<hipStream_t>(stream));
+}
+
+int profiler_end(Profiler* p, void* stream) {
+  const int e = (int)hipEventRecord(p->stop[p->next], static_cast<hipStream_t>(stream));
+  p->next = (p->next + 1) % p->slots;
+  if (p->count < p->slots) ++p->count;
+  return e;
+}
+
+int profiler_read(Profiler* p, float* ms, int cap, int* count) {
+  const int n = p->count < cap ? p->count : cap;
+  const int first = (p->next - p->count + p->slots) % p->slots;  // oldest recorded slot
+  for (int i = 0; i < n; ++i) {
+    const int k = (first + (p->count - n) + i) % p->slots;     // newest n, oldest first
+    if (hipEventSynchronize(p->stop[k]) != hipSuccess) return 1;
+    if (hipEventElapsedTime(&ms[i], p->start[k], p->stop[k]) != hipSuccess) return 1;
+  }
+  *count = n;
+  p->count = 0;
+  return 0;
 }
 
 }  // namespace fabwd

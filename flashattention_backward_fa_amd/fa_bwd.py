@@ -32,8 +32,8 @@ FA_ERR_RUNTIME = 6
 LAYOUTS = {"BSND": 0, "BNSD": 1, "TND": 2}
 FLAG_DETERMINISTIC = 0x1
 
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_bwd_destroy",
-            "fa_bwd_strerror", "fa_bwd_abi_version")
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_profile_enable",
+            "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version")
 
 
 class MaskMode(enum.IntEnum):
@@ -100,6 +100,13 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd_run.restype = ctypes.c_int
     lib.fa_bwd_sfmg.argtypes = [vp] * 6
     lib.fa_bwd_sfmg.restype = ctypes.c_int
+    lib.fa_fwd_run.argtypes = [vp] * 9
+    lib.fa_fwd_run.restype = ctypes.c_int
+    lib.fa_bwd_profile_enable.argtypes = [vp, ctypes.c_int]
+    lib.fa_bwd_profile_enable.restype = ctypes.c_int
+    lib.fa_bwd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int)]
+    lib.fa_bwd_profile_read.restype = ctypes.c_int
     lib.fa_bwd_destroy.argtypes = [vp]
     lib.fa_bwd_destroy.restype = ctypes.c_int
     lib.fa_bwd_strerror.argtypes = [ctypes.c_int]
@@ -161,6 +168,24 @@ class Plan:
                                        workspace, workspace_bytes, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_run")
+
+    def forward(self, q, k, v, cu_q, cu_kv, attn_out, lse, stream):
+        st = load_library().fa_fwd_run(self.handle, q, k, v, cu_q, cu_kv, attn_out, lse, stream)
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_fwd_run")
+
+    def profile_enable(self, slots):
+        st = load_library().fa_bwd_profile_enable(self.handle, int(slots))
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_profile_enable")
+
+    def profile_read(self, cap):
+        buf = (ctypes.c_float * max(int(cap), 1))()
+        n = ctypes.c_int()
+        st = load_library().fa_bwd_profile_read(self.handle, buf, int(cap), ctypes.byref(n))
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_profile_read")
+        return [buf[i] for i in range(n.value)]
 
     def sfmg(self, dout, attn_out, cu_q, out, stream):
         st = load_library().fa_bwd_sfmg(self.handle, dout, attn_out, cu_q, out, stream)
@@ -274,6 +299,31 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
     plan.run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(attn_out), _ptr(softmax_lse), _ptr(cu_seqlens_q),
              _ptr(cu_seqlens_kv), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stream)
     return dq, dk, dv
+
+
+def flash_attn(q, k, v, cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0, mask_mode=0, win_left=-1,
+               win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1, layout="BSND"):
+    """Forward (attn_out bf16, softmax_lse float32) with the same conventions
+    as flash_attn_grad; its outputs are what flash_attn_grad expects."""
+    import torch
+
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, torch.bfloat16, dev)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
+                    max_seqlen_q, max_seqlen_kv)
+    sh = _shapes(q, k, v, layout)
+    out = torch.empty(tuple(q.shape[:-1]) + (sh["Dv"],), dtype=torch.bfloat16, device=dev)
+    if layout == "TND":
+        lse = torch.empty((sh["N1"], sh["T1"]), dtype=torch.float32, device=dev)
+    else:
+        lse = torch.empty((sh["B"], sh["N1"], sh["S1"]), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    plan.forward(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out), _ptr(lse), stream)
+    return out, lse
 
 
 def sfmg(dout, attn_out, layout="BSND", cu_seqlens_q=None, N2=None, max_seqlen_q=-1):

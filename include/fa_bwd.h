@@ -140,7 +140,31 @@ int fa_bwd_run(fa_bwd_plan plan,
 int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
                 const int32_t* cu_seqlens_q, float* sfmg, void* stream);
 
-/* Free a plan.  NULL is a no-op.  Returns FA_OK. */
+/* Attention forward producing the two tensors the backward consumes
+ * (section 一, S = scale*Q K^T, P = exp(S - softmax_lse), Y = P V, with
+ * softmax_lse the natural-log row log-sum-exp): writes bf16 attn_out (q's
+ * layout with Dv) and float32 softmax_lse ([B, N1, S1] or [N1, T1]) for the
+ * plan's problem, masks and layout.  A query row with no visible key gets
+ * attn_out = 0 and softmax_lse = -inf.  Same pointer rules and errors as
+ * fa_bwd_run; needs no workspace. */
+int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,
+               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+               void* attn_out, float* softmax_lse, void* stream);
+
+/* Timing hook.  With slots > 0, every later fa_bwd_run records one pair of
+ * HIP events on its stream immediately before and after the main kernel,
+ * into a ring of `slots` pairs owned by the plan (slots = 0 frees them and
+ * stops recording).  Errors: FA_ERR_NULLPTR, FA_ERR_PARAM_INVALID
+ * (slots < 0 or > 65536), FA_ERR_RUNTIME (event creation failed). */
+int fa_bwd_profile_enable(fa_bwd_plan plan, int slots);
+
+/* Wait for the recorded runs and write the main kernel's duration of each,
+ * in milliseconds, oldest first, into ms[0 .. *count) (at most cap and at
+ * most `slots` entries); the ring is then emptied.  Errors: FA_ERR_NULLPTR,
+ * FA_ERR_RUNTIME (an event query failed). */
+int fa_bwd_profile_read(fa_bwd_plan plan, float* ms, int cap, int* count);
+
+/* Free a plan (and its timing events).  NULL is a no-op.  Returns FA_OK. */
 int fa_bwd_destroy(fa_bwd_plan plan);
 
 /* Static, human-readable text for a status code (never NULL). */

@@ -23,7 +23,7 @@ struct fa_bwd_plan_s {
   KernelArgs args;         // pointers left NULL; filled per run
   int64_t q_elems;         // elements of q (and of the fp32 dQ accumulator)
   int64_t lse_elems;       // elements of softmax_lse / sfmg
-  size_t off_dq_acc, off_sfmg, ws_bytes;
+  size_t off_dq_acc, off_sfmg, off_dk_acc, off_dv_acc, ws_bytes;
   fabwd::Profiler* prof = nullptr;  // timing hook, off by default
 };
 
@@ -134,11 +134,28 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   else { a.win_left = d.win_left; a.win_right = d.win_right; }
   a.has_mask = (a.win_left >= 0 || a.win_right >= 0) ? 1 : 0;
 
+  // Main kernel choice: the 8-wavefront kernel where its register budget
+  // allows (D <= 128); there a GQA group's query heads go to separate
+  // workgroups (better balance of causal work) and dK/dV are summed in fp32.
+  a.variant = fabwd::main_v2_instantiated(d.D, d.Dv) ? 1 : 0;
+  a.heads_per_job = (a.variant == 1) ? 1 : a.G;
+  if (const char* e = std::getenv("FA_BWD_VARIANT")) {  // tuning override: 0 or 1
+    if (e[0] == '0') { a.variant = 0; a.heads_per_job = a.G; }
+  }
+
   p.q_elems = tnd ? d.T1 * N1 * D : (int64_t)d.B * S1 * N1 * D;
   p.lse_elems = tnd ? N1 * d.T1 : (int64_t)d.B * N1 * S1;
+  const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
+  const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
   p.off_dq_acc = 0;
   p.off_sfmg = align_up((size_t)p.q_elems * sizeof(float));
-  p.ws_bytes = p.off_sfmg + align_up((size_t)p.lse_elems * sizeof(float));
+  p.off_dk_acc = p.off_sfmg + align_up((size_t)p.lse_elems * sizeof(float));
+  p.off_dv_acc = p.off_dk_acc;
+  p.ws_bytes = p.off_dk_acc;
+  if (fabwd::split_heads(a)) {
+    p.off_dv_acc = p.off_dk_acc + align_up((size_t)k_elems * sizeof(float));
+    p.ws_bytes = p.off_dv_acc + align_up((size_t)v_elems * sizeof(float));
+  }
   p.desc = d;
   p.desc.S1 = (int32_t)S1;
   p.desc.S2 = (int32_t)S2;
@@ -174,10 +191,10 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
     const KernelArgs& a = p->args;
     std::fprintf(stderr,
                  "[fa_bwd] plan layout=%d B=%d N1=%d N2=%d S1=%d S2=%d D=%d Dv=%d T1=%lld T2=%lld "
-                 "scale=%g window=(%d,%d) kv_tile=%d q_tile=%d workspace=%zu B\n",
+                 "scale=%g window=(%d,%d) kv_tile=%d variant=%d heads_per_job=%d workspace=%zu B\n",
                  p->desc.layout, a.B, a.N1, a.N2, a.S1, a.S2, a.D, a.Dv, (long long)a.T1,
                  (long long)a.T2, (double)a.scale, a.win_left, a.win_right, fabwd::KV_TILE,
-                 fabwd::Q_TILE, p->ws_bytes);
+                 a.variant, a.heads_per_job, p->ws_bytes);
   }
   return FA_OK;
 }
@@ -198,6 +215,10 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dq_acc);
   a.sfmg = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_sfmg);
+  if (fabwd::split_heads(a)) {
+    a.dk_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dk_acc);
+    a.dv_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dv_acc);
+  }
 
   if (fabwd::launch_preprocess(a, true, stream) != 0) return FA_ERR_RUNTIME;
   if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;

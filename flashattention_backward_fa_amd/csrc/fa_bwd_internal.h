@@ -11,7 +11,8 @@ namespace fabwd {
 // sequence and one key/value head (4 wavefronts x 32 keys); query rows stream
 // through LDS Q_TILE at a time.
 constexpr int KV_TILE = 128;
-constexpr int Q_TILE = 64;
+constexpr int Q_TILE = 64;      // query rows per step of the 4-wavefront kernel
+constexpr int Q_TILE_2G = 32;   // query rows per step and group of the 8-wavefront kernel
 
 // Everything a launch needs, plain old data, passed by value to the kernels.
 struct KernelArgs {
@@ -25,6 +26,8 @@ struct KernelArgs {
   const int32_t* cu_kv;  // TND only (device)
   float* dq_acc;         // fp32, q's layout
   float* sfmg;           // fp32, lse's layout
+  float* dk_acc;         // fp32, k's layout (only when query heads are split)
+  float* dv_acc;         // fp32, v's layout (only when query heads are split)
   void* dq;
   void* dk;
   void* dv;
@@ -48,11 +51,19 @@ struct KernelArgs {
   int32_t win_left;      // -1 = unbounded
   int32_t win_right;     // -1 = unbounded
   int32_t has_mask;      // any bound present
+
+  int32_t variant;        // main kernel: 0 = 4 wavefronts, 1 = 8 wavefronts in two query groups
+  int32_t heads_per_job;  // query heads of a GQA group handled by one workgroup (G or 1)
 };
+
+// True when dK/dV of one key/value head are summed over several workgroups
+// (through the fp32 dk_acc / dv_acc workspace) instead of in registers.
+inline bool split_heads(const KernelArgs& a) { return a.heads_per_job < a.G; }
 
 // Launchers (fa_bwd_kernels.hip).  Each returns 0 or a hipError_t value.
 int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream);
 int launch_main(const KernelArgs& a, void* stream);
+bool main_v2_instantiated(int D, int Dv);
 int launch_dq_finalize(const KernelArgs& a, void* stream);
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream);
 bool main_instantiated(int D, int Dv);

@@ -73,7 +73,7 @@ __device__ __forceinline__ bf16x8 join(shortx4 lo, shortx4 hi) {
 // with one 16-byte load of each tensor.
 template <int DV>
 __global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t rows, int zero_dq,
-                                                          int64_t dq_elems) {
+                                                          int64_t dq_elems, int64_t dk_elems, int64_t dv_elems) {
   constexpr int LPR = DV / 8;             // lanes per row
   constexpr int RPB = 256 / LPR;          // rows per block
   const int tid = threadIdx.x;
@@ -102,11 +102,18 @@ __global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t r
     }
     a.sfmg[o] = s;
   }
-  if (zero_dq) {
-    floatx4* p = reinterpret_cast<floatx4*>(a.dq_acc);
-    const int64_t n4 = dq_elems / 4;
+  if (zero_dq) {  // clear the fp32 accumulators (dQ, and dK/dV when heads are split)
     const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n4; i += (int64_t)gridDim.x * 256) p[i] = z;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t first = (int64_t)blockIdx.x * 256 + tid;
+    floatx4* p = reinterpret_cast<floatx4*>(a.dq_acc);
+    for (int64_t i = first; i < dq_elems / 4; i += stride) p[i] = z;
+    if (dk_elems) {
+      p = reinterpret_cast<floatx4*>(a.dk_acc);
+      for (int64_t i = first; i < dk_elems / 4; i += stride) p[i] = z;
+      p = reinterpret_cast<floatx4*>(a.dv_acc);
+      for (int64_t i = first; i < dv_elems / 4; i += stride) p[i] = z;
+    }
   }
 }
 
@@ -380,11 +387,348 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- main, 8 wavefronts
+
+// One workgroup = 8 wavefronts = two query groups of 4 wavefronts sharing one
+// 128-key tile of K and V in LDS.  Wavefront (group, w) owns keys 32w..32w+31 of
+// the tile for its group's work; the groups take alternate 32-row query blocks
+// (over the query heads of the job), so every SIMD runs two wavefronts that
+// interleave their MFMA, exp and LDS work.  The next block of each group is
+// prefetched into registers while the current one is computed.  When the loop
+// ends the second group's dK/dV partials are added into the first group's
+// through LDS.  Jobs are (key tile, query-head slot, sequence, key/value head),
+// the key tile slowest, so long causal tiles are dispatched first and the
+// query heads of one key/value head sit on the same XCD (blockIdx mod 8) when
+// N2 is a multiple of 8.
+template <int HD, int HDV>
+__global__ __launch_bounds__(512, 1) void bwd_main_v2_kernel(KernelArgs a) {
+  constexpr int BC = KV_TILE;
+  constexpr int BR = Q_TILE_2G;
+  constexpr int KP = HD + 8;
+  constexpr int VP = HDV + 8;
+  constexpr int SP = BR + 8;
+  constexpr int NKQ = HD / 16;
+  constexpr int NKV = HDV / 16;
+  constexpr int NBK = HD / 32;
+  constexpr int NBV = HDV / 32;
+  constexpr int NQC = BR * HD / 8 / 256;    // 16-byte Q chunks per thread and block
+  constexpr int NYC = BR * HDV / 8 / 256;   // 16-byte dY chunks per thread and block
+  static_assert(NQC * 256 * 8 == BR * HD && NYC * 256 * 8 == BR * HDV, "tile split");
+
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BC * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BC * VP];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BR * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Ys[2][BR * VP];
+  __shared__ __attribute__((aligned(16))) bf16 St[2][BC * SP];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BR];
+  __shared__ __attribute__((aligned(16))) float sfm_s[2][BR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qg = wave >> 2;       // query group
+  const int kw = wave & 3;        // key slice of the tile
+  const int gt = tid & 255;       // thread index within the group
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- job
+  const int hpj = a.heads_per_job;
+  const int HJ = a.G / hpj;
+  int r = blockIdx.x;
+  const int n2 = r % a.N2; r /= a.N2;
+  const int b = r % a.B; r /= a.B;
+  const int gslot = r % HJ;
+  const int tile = r / HJ;
+
+  int s1, s2;
+  int64_t qbase, kbase, vbase, obase, lbase;
+  if (a.varlen) {
+    const int q0 = a.cu_q[b], k0 = a.cu_kv[b];
+    s1 = a.cu_q[b + 1] - q0;
+    s2 = a.cu_kv[b + 1] - k0;
+    qbase = (int64_t)q0 * a.q_ss;
+    obase = (int64_t)q0 * a.o_ss;
+    kbase = (int64_t)k0 * a.k_ss;
+    vbase = (int64_t)k0 * a.v_ss;
+    lbase = q0;
+  } else {
+    s1 = a.S1;
+    s2 = a.S2;
+    qbase = (int64_t)b * a.q_sb;
+    obase = (int64_t)b * a.o_sb;
+    kbase = (int64_t)b * a.k_sb;
+    vbase = (int64_t)b * a.v_sb;
+    lbase = (int64_t)b * a.l_sb;
+  }
+  const int j0 = tile * BC;
+  if (j0 >= s2) return;
+  const int j1 = min(j0 + BC, s2);
+  const int off = s2 - s1;
+  const int wl = a.win_left, wr = a.win_right;
+
+  // ---- K and V tiles -> LDS
+  {
+    const bf16* Kg = static_cast<const bf16*>(a.k) + kbase + (int64_t)n2 * a.k_sn;
+    const bf16* Vg = static_cast<const bf16*>(a.v) + vbase + (int64_t)n2 * a.v_sn;
+    for (int c = tid; c < BC * (HD / 8); c += 512) {
+      const int rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+      bf16x8 val = {};
+      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Kg + (int64_t)(j0 + rr) * a.k_ss + cc);
+      *reinterpret_cast<bf16x8*>(&Ks[rr * KP + cc]) = val;
+    }
+    for (int c = tid; c < BC * (HDV / 8); c += 512) {
+      const int rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+      bf16x8 val = {};
+      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)(j0 + rr) * a.v_ss + cc);
+      *reinterpret_cast<bf16x8*>(&Vs[rr * VP + cc]) = val;
+    }
+  }
+
+  // ---- query blocks that see a key of [j0, j1), for each head of the job
+  int i_lo = 0, i_hi = s1;
+  if (wr >= 0) i_lo = max(0, j0 - off - wr);
+  if (wl >= 0) i_hi = min(s1, j1 - off + wl);
+  const int blk_lo = i_lo / BR;
+  const int nblk = i_hi > i_lo ? (i_hi + BR - 1) / BR - blk_lo : 0;
+  const int T = hpj * nblk;
+  const int g0 = gslot * hpj;
+
+  // prefetch registers of the group's next item
+  bf16x8 pq[NQC], py[NYC];
+  float pl = __builtin_inff(), pf = 0.f;
+  auto fetch = [&](int t) {
+    if (t < T) {
+      const int n1 = n2 * a.G + g0 + t / nblk;
+      const int i0 = (blk_lo + t % nblk) * BR;
+      const bf16* Qg = static_cast<const bf16*>(a.q) + qbase + (int64_t)n1 * a.q_sn;
+      const bf16* Yg = static_cast<const bf16*>(a.dout) + obase + (int64_t)n1 * a.o_sn;
+#pragma unroll
+      for (int u = 0; u < NQC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+        bf16x8 val = {};
+        if (i0 + rr < s1) val = *reinterpret_cast<const bf16x8*>(Qg + (int64_t)(i0 + rr) * a.q_ss + cc);
+        pq[u] = val;
+      }
+#pragma unroll
+      for (int u = 0; u < NYC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+        bf16x8 val = {};
+        if (i0 + rr < s1) val = *reinterpret_cast<const bf16x8*>(Yg + (int64_t)(i0 + rr) * a.o_ss + cc);
+        py[u] = val;
+      }
+      if (gt < BR) {
+        const int i = i0 + gt;
+        pl = __builtin_inff();
+        pf = 0.f;
+        if (i < s1) {
+          const float l = a.lse[lbase + (int64_t)n1 * a.l_sn + i];
+          pl = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;  // empty row -> P = 0
+          pf = a.sfmg[lbase + (int64_t)n1 * a.l_sn + i];
+        }
+      }
+    }
+  };
+  fetch(qg);
+
+  floatx16 dKr[NBK], dVr[NBV];
+#pragma unroll
+  for (int i = 0; i < NBK; ++i) dKr[i] = floatx16{};
+#pragma unroll
+  for (int i = 0; i < NBV; ++i) dVr[i] = floatx16{};
+
+  const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
+  const int tr_r8 = 8 * hi + ((lane & 15) >> 2);
+  const int krow = kw * 32 + l32;  // this lane's key within the tile
+  const int jk = j0 + krow;
+  bf16* Qg_s = Qs[qg];
+  bf16* Yg_s = Ys[qg];
+  bf16* St_s = St[qg];
+
+  const int iters = (T + 1) / 2;
+  for (int it = 0; it < iters; ++it) {
+    const int t = 2 * it + qg;
+    const bool valid = t < T;
+    int n1 = 0, i0 = 0;
+    if (valid) {
+      n1 = n2 * a.G + g0 + t / nblk;
+      i0 = (blk_lo + t % nblk) * BR;
+#pragma unroll
+      for (int u = 0; u < NQC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&Qg_s[rr * KP + cc]) = pq[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NYC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&Yg_s[rr * VP + cc]) = py[u];
+      }
+      if (gt < BR) {
+        lse_s[qg][gt] = pl;
+        sfm_s[qg][gt] = pf;
+      }
+    }
+    fetch(t + 2);
+    __syncthreads();
+
+    if (valid) {
+      // S = Q K^T and dP = dY V^T for this wavefront's 32 keys (B operands from LDS)
+      floatx16 sacc = {}, pacc = {};
+#pragma unroll
+      for (int kk = 0; kk < NKQ; ++kk) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[krow * KP + 16 * kk + 8 * hi]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qg_s[l32 * KP + 16 * kk + 8 * hi]);
+        sacc = mfma32(qa, kb, sacc);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vs[krow * VP + 16 * kk + 8 * hi]);
+        const bf16x8 ya = *reinterpret_cast<const bf16x8*>(&Yg_s[l32 * VP + 16 * kk + 8 * hi]);
+        pacc = mfma32(ya, vb, pacc);
+      }
+      const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
+                        (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
+      bf16x8 pa[2], da[2];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ib = r4 * 8 + hi * 4;
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[qg][ib]);
+        const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][ib]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rg = r4 * 4 + e;
+          float p = __builtin_amdgcn_exp2f(sacc[rg] * a.scale_log2 - l4[e]);
+          if (!full) {
+            const int i = i0 + ib + e;
+            const bool vis = (i < s1) && (jk < s2) && (wl < 0 || jk >= i + off - wl) && (wr < 0 || jk <= i + off + wr);
+            p = vis ? p : 0.f;
+          }
+          const float ds = p * (pacc[rg] - f4[e]);
+          pa[rg >> 3][rg & 7] = (bf16)p;
+          da[rg >> 3][rg & 7] = (bf16)ds;
+        }
+      }
+      // dV += P^T dY, dK += dS^T Q (B operands by transposing LDS reads)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) {
+          const bf16* p0 = &Yg_s[(16 * kc + tr_r4) * VP + nb * 32 + tr_c];
+          dVr[nb] = mfma32(pa[kc], join(lds_tr(p0), lds_tr(p0 + 8 * VP)), dVr[nb]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) {
+          const bf16* p0 = &Qg_s[(16 * kc + tr_r4) * KP + nb * 32 + tr_c];
+          dKr[nb] = mfma32(da[kc], join(lds_tr(p0), lds_tr(p0 + 8 * KP)), dKr[nb]);
+        }
+      }
+      // dS^T -> LDS (whole-vector bit casts only)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const uintx4 u = __builtin_bit_cast(uintx4, da[kc]);
+        bf16* row = &St_s[krow * SP + kc * 16 + hi * 4];
+        *reinterpret_cast<uintx2*>(row) = uintx2{u[0], u[1]};
+        *reinterpret_cast<uintx2*>(row + 8) = uintx2{u[2], u[3]};
+      }
+    }
+    __syncthreads();
+
+    if (valid) {
+      // dQ(rows i0..i0+31) += dS K: wavefront kw takes head-dim blocks kw, kw+4, ...
+      float* dQa = a.dq_acc + qbase + (int64_t)n1 * a.q_sn;
+#pragma unroll
+      for (int nd = kw; nd < NBK; nd += 4) {
+        floatx16 acc = {};
+#pragma unroll
+        for (int kc = 0; kc < BC / 16; ++kc) {
+          const bf16* pa0 = &St_s[(16 * kc + tr_r8) * SP + tr_c];
+          const bf16* pb0 = &Ks[(16 * kc + tr_r8) * KP + nd * 32 + tr_c];
+          acc = mfma32(join(lds_tr(pa0), lds_tr(pa0 + 4 * SP)), join(lds_tr(pb0), lds_tr(pb0 + 4 * KP)), acc);
+        }
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+          const int i = i0 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+          if (i < s1) unsafeAtomicAdd(dQa + (int64_t)i * a.q_ss + nd * 32 + l32, acc[rg]);
+        }
+      }
+    }
+  }
+
+  // ---- add the second group's dK/dV into the first group's, 32 columns at a time
+  float* red = reinterpret_cast<float*>(Ks);  // K/V tiles are no longer read
+#pragma unroll
+  for (int nb = 0; nb < NBK; ++nb) {
+    __syncthreads();
+    if (qg == 1) {
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) red[(kw * 16 + rg) * 64 + lane] = dKr[nb][rg];
+    }
+    __syncthreads();
+    if (qg == 0) {
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) dKr[nb][rg] += red[(kw * 16 + rg) * 64 + lane];
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NBV; ++nb) {
+    __syncthreads();
+    if (qg == 1) {
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) red[(kw * 16 + rg) * 64 + lane] = dVr[nb][rg];
+    }
+    __syncthreads();
+    if (qg == 0) {
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) dVr[nb][rg] += red[(kw * 16 + rg) * 64 + lane];
+    }
+  }
+  const bool split = a.heads_per_job < a.G;  // other workgroups share this key/value head
+  if (qg != 0 || (T == 0 && split)) return;
+
+  // ---- output: bf16 directly, or fp32 adds when other workgroups share the key/value head
+#pragma unroll
+  for (int rg = 0; rg < 16; ++rg) {
+    const int j = j0 + kw * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+    if (j >= s2) continue;
+    if (split) {
+      float* dKa = a.dk_acc + kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
+      float* dVa = a.dv_acc + vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) unsafeAtomicAdd(dKa + nb * 32 + l32, dKr[nb][rg] * a.scale);
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) unsafeAtomicAdd(dVa + nb * 32 + l32, dVr[nb][rg]);
+    } else {
+      bf16* dKg = static_cast<bf16*>(a.dk) + kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
+      bf16* dVg = static_cast<bf16*>(a.dv) + vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) dKg[nb * 32 + l32] = (bf16)(dKr[nb][rg] * a.scale);
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) dVg[nb * 32 + l32] = (bf16)dVr[nb][rg];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 namespace {
+// Launch and return the status of this launch only (hipLaunchKernel's own
+// return value), never a stale error left in the runtime by another call.
+template <typename T> struct same_type { using type = T; };
+template <typename... KArgs>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, typename same_type<KArgs>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+}
+
 int64_t q_elems(const KernelArgs& a) {
   return a.varlen ? a.T1 * a.N1 * a.D : (int64_t)a.B * a.S1 * a.N1 * a.D;
+}
+int64_t k_elems(const KernelArgs& a) {
+  return a.varlen ? a.T2 * a.N2 * a.D : (int64_t)a.B * a.S2 * a.N2 * a.D;
+}
+int64_t v_elems(const KernelArgs& a) {
+  return a.varlen ? a.T2 * a.N2 * a.Dv : (int64_t)a.B * a.S2 * a.N2 * a.Dv;
 }
 int64_t out_rows(const KernelArgs& a) {
   return a.varlen ? a.T1 * a.N1 : (int64_t)a.B * a.S1 * a.N1;
@@ -399,43 +743,62 @@ int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream) {
   if (blocks <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t dqe = zero_dq_acc ? q_elems(a) : 0;
-  if (a.Dv == 128)
-    hipLaunchKernelGGL(preprocess_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a, rows, zero_dq_acc ? 1 : 0, dqe);
-  else if (a.Dv == 64)
-    hipLaunchKernelGGL(preprocess_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, rows, zero_dq_acc ? 1 : 0, dqe);
-  else
-    return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  const int64_t dke = zero_dq_acc && split_heads(a) ? k_elems(a) : 0;
+  const int64_t dve = zero_dq_acc && split_heads(a) ? v_elems(a) : 0;
+  const dim3 grid((unsigned)blocks), block(256);
+  const int z = zero_dq_acc ? 1 : 0;
+  if (a.Dv == 128) return launch(preprocess_kernel<128>, grid, block, s, a, rows, z, dqe, dke, dve);
+  if (a.Dv == 64) return launch(preprocess_kernel<64>, grid, block, s, a, rows, z, dqe, dke, dve);
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_dq_finalize(const KernelArgs& a, void* stream) {
-  const int64_t n8 = q_elems(a) / 8;
-  int64_t blocks = (n8 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks <= 0) return 0;
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     a.dq_acc, static_cast<bf16*>(a.dq), n8, a.scale);
-  return (int)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto one = [&](const float* acc, void* out, int64_t elems, float scale) -> int {
+    const int64_t n8 = elems / 8;
+    int64_t blocks = (n8 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks <= 0) return 0;
+    return launch(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), s, acc, static_cast<bf16*>(out), n8, scale);
+  };
+  int e = one(a.dq_acc, a.dq, q_elems(a), a.scale);
+  if (e == 0 && split_heads(a)) e = one(a.dk_acc, a.dk, k_elems(a), 1.f);
+  if (e == 0 && split_heads(a)) e = one(a.dv_acc, a.dv, v_elems(a), 1.f);
+  return e;
 }
 
 bool main_instantiated(int D, int Dv) {
   return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128)) || (D == 192 && (Dv == 64 || Dv == 128));
 }
 
+bool main_v2_instantiated(int D, int Dv) {
+  return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128));
+}
+
 int launch_main(const KernelArgs& a, void* stream) {
   const int64_t tiles = (a.S2 + KV_TILE - 1) / KV_TILE;
+  if (a.variant == 1) {
+    const int64_t blocks = tiles * (a.G / a.heads_per_job) * a.B * a.N2;
+    if (blocks <= 0) return 0;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)blocks), block(512);
+    if (a.D == 64 && a.Dv == 64) return launch(bwd_main_v2_kernel<64, 64>, grid, block, s, a);
+    if (a.D == 128 && a.Dv == 64) return launch(bwd_main_v2_kernel<128, 64>, grid, block, s, a);
+    if (a.D == 128 && a.Dv == 128) return launch(bwd_main_v2_kernel<128, 128>, grid, block, s, a);
+    return (int)hipErrorInvalidValue;
+  }
   const int64_t blocks = tiles * a.N2 * a.B;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)blocks), block(256);
-  if (a.D == 64 && a.Dv == 64) hipLaunchKernelGGL((bwd_main_kernel<64, 64>), grid, block, 0, s, a);
-  else if (a.D == 128 && a.Dv == 64) hipLaunchKernelGGL((bwd_main_kernel<128, 64>), grid, block, 0, s, a);
-  else if (a.D == 128 && a.Dv == 128) hipLaunchKernelGGL((bwd_main_kernel<128, 128>), grid, block, 0, s, a);
-  else if (a.D == 192 && a.Dv == 64) hipLaunchKernelGGL((bwd_main_kernel<192, 64>), grid, block, 0, s, a);
-  else if (a.D == 192 && a.Dv == 128) hipLaunchKernelGGL((bwd_main_kernel<192, 128>), grid, block, 0, s, a);
-  else return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  if (a.D == 64 && a.Dv == 64) return launch(bwd_main_kernel<64, 64>, grid, block, s, a);
+  else if (a.D == 128 && a.Dv == 64) return launch(bwd_main_kernel<128, 64>, grid, block, s, a);
+  else if (a.D == 128 && a.Dv == 128) return launch(bwd_main_kernel<128, 128>, grid, block, s, a);
+  else if (a.D == 192 && a.Dv == 64) return launch(bwd_main_kernel<192, 64>, grid, block, s, a);
+  else if (a.D == 192 && a.Dv == 128) return launch(bwd_main_kernel<192, 128>, grid, block, s, a);
+  return (int)hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- timing hook

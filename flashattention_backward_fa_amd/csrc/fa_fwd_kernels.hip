@@ -219,6 +219,15 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
 
 }  // namespace
 
+// Launch and return the status of this launch only (hipLaunchKernel's own
+// return value), never a stale error left in the runtime by another call.
+template <typename T> struct same_type { using type = T; };
+template <typename... KArgs>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, typename same_type<KArgs>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+}
+
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream) {
   const int64_t tiles = (a.S1 + FQ - 1) / FQ;
   const int64_t blocks = tiles * a.N1 * a.B;
@@ -227,13 +236,12 @@ int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   bf16* o = static_cast<bf16*>(out);
   const dim3 grid((unsigned)blocks), block(256);
-  if (a.D == 64 && a.Dv == 64) hipLaunchKernelGGL((fwd_kernel<64, 64>), grid, block, 0, s, a, o, lse);
-  else if (a.D == 128 && a.Dv == 64) hipLaunchKernelGGL((fwd_kernel<128, 64>), grid, block, 0, s, a, o, lse);
-  else if (a.D == 128 && a.Dv == 128) hipLaunchKernelGGL((fwd_kernel<128, 128>), grid, block, 0, s, a, o, lse);
-  else if (a.D == 192 && a.Dv == 64) hipLaunchKernelGGL((fwd_kernel<192, 64>), grid, block, 0, s, a, o, lse);
-  else if (a.D == 192 && a.Dv == 128) hipLaunchKernelGGL((fwd_kernel<192, 128>), grid, block, 0, s, a, o, lse);
-  else return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  if (a.D == 64 && a.Dv == 64) return launch(fwd_kernel<64, 64>, grid, block, s, a, o, lse);
+  else if (a.D == 128 && a.Dv == 64) return launch(fwd_kernel<128, 64>, grid, block, s, a, o, lse);
+  else if (a.D == 128 && a.Dv == 128) return launch(fwd_kernel<128, 128>, grid, block, s, a, o, lse);
+  else if (a.D == 192 && a.Dv == 64) return launch(fwd_kernel<192, 64>, grid, block, s, a, o, lse);
+  else if (a.D == 192 && a.Dv == 128) return launch(fwd_kernel<192, 128>, grid, block, s, a, o, lse);
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace fabwd

@@ -92,6 +92,13 @@ def load_library(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m flashattention_backward_fa_amd.build`")
+    # PyTorch ships its own HIP runtime.  Import it first so that this
+    # library binds to that same runtime: with two runtimes in one process,
+    # device pointers allocated by torch are invalid for our launches.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the library itself needs no torch
+        pass
     lib = ctypes.CDLL(path)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.fa_bwd_create.argtypes = [ctypes.POINTER(FaBwdDesc), ctypes.POINTER(vp), ctypes.POINTER(sz)]

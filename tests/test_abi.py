@@ -59,11 +59,17 @@ def create(lib, **kw):
 
 
 def test_valid_problem_and_workspace_size(lib):
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # GQA (N1=8, N2=2): fp32 dQ accumulator, sfmg, and fp32 dK/dV accumulators
+    # (query heads of a group are split over workgroups)
     st, ws = create(lib)
     assert st == fb.FA_OK
-    q_elems = 2 * 128 * 8 * 128
-    lse = 2 * 8 * 128
-    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    q_elems, lse, k_elems = 2 * 128 * 8 * 128, 2 * 8 * 128, 2 * 128 * 2 * 128
+    assert ws == rnd(q_elems * 4) + rnd(lse * 4) + 2 * rnd(k_elems * 4)
+    # MHA: dK/dV complete inside a workgroup, no dK/dV accumulators
+    st, ws = create(lib, N1=2, N2=2)
+    assert st == fb.FA_OK
+    q_elems, lse = 2 * 128 * 2 * 128, 2 * 2 * 128
     assert ws == rnd(q_elems * 4) + rnd(lse * 4)
 
 

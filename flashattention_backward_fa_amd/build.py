@@ -58,14 +58,17 @@ def build(verbose=False):
     api_o = os.path.join(BUILDDIR, "fa_bwd_api.o")
     ker_o = os.path.join(BUILDDIR, "fa_bwd_kernels.o")
     fwd_o = os.path.join(BUILDDIR, "fa_fwd_kernels.o")
+    det_o = os.path.join(BUILDDIR, "fa_bwd_det_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
           "-c", os.path.join(CSRC, "fa_bwd_api.cpp"), "-o", api_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_kernels.hip"),
           "-o", ker_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_fwd_kernels.hip"),
           "-o", fwd_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_det_kernels.hip"),
+          "-o", det_o], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o, det_o], verbose)
     os.replace(tmp, LIB)
     return LIB
 

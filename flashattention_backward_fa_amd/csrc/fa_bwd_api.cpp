@@ -91,8 +91,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
 
   // valid on the page, not built here
   if (d.dtype == FA_DTYPE_FP16) return FA_ERR_UNSUPPORTED;
-  if (d.flags & FA_FLAG_DETERMINISTIC) return FA_ERR_UNSUPPORTED;
-  if (!fabwd::main_instantiated(d.D, d.Dv)) return FA_ERR_UNSUPPORTED;
+  if (!fabwd::main_instantiated(d.D, d.Dv) || !fabwd::det_instantiated(d.D, d.Dv)) return FA_ERR_UNSUPPORTED;
 
   KernelArgs& a = p.args;
   std::memset(&a, 0, sizeof(a));
@@ -134,28 +133,64 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   else { a.win_left = d.win_left; a.win_right = d.win_right; }
   a.has_mask = (a.win_left >= 0 || a.win_right >= 0) ? 1 : 0;
 
-  // Main kernel choice: the 8-wavefront kernel where its register budget
-  // allows (D <= 128); there a GQA group's query heads go to separate
-  // workgroups (better balance of causal work) and dK/dV are summed in fp32.
-  a.variant = fabwd::main_v2_instantiated(d.D, d.Dv) ? 1 : 0;
-  a.heads_per_job = (a.variant == 1) ? 1 : a.G;
-  if (const char* e = std::getenv("FA_BWD_VARIANT")) {  // tuning override: 0 or 1
-    if (e[0] == '0') { a.variant = 0; a.heads_per_job = a.G; }
+  // Kernel choice.  Default: the atomic-free pair (dK/dV kernel over key
+  // tiles, dQ kernel over query tiles); dQ is then bitwise repeatable.
+  // FA_BWD_VARIANT=0/1 selects the fp32-atomic dQ kernels instead (tuning).
+  const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
+  const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
+  a.variant = 2;
+  if (const char* e = std::getenv("FA_BWD_VARIANT")) {
+    if (e[0] == '0') a.variant = 0;
+    if (e[0] == '1' && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
+  }
+  if (d.flags & FA_FLAG_DETERMINISTIC) a.variant = 2;
+  a.heads_per_job = a.G;
+  a.q_splits = 1;
+  a.n_partials = 1;
+  a.k_part_stride = k_elems;
+  a.v_part_stride = v_elems;
+  if (a.variant == 1 && a.G > 1) a.heads_per_job = 1;
+  if (a.variant == 2) {
+    // Enough jobs to balance causal work over the CUs: split the query heads
+    // of a GQA group, then the query range of a key tile, until there are at
+    // least 2 jobs per CU of an MI355X (256 CUs); each split adds an fp32
+    // partial sum per key that a reduce kernel adds up.
+    const int64_t bc = 4 * fabwd::det_keys_per_wave(d.D);
+    const int64_t tiles = (S2 + bc - 1) / bc;
+    const int64_t target = 2 * 256;
+    while (tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.N2 < target) {
+      if (a.heads_per_job > 1 && a.heads_per_job % 2 == 0) a.heads_per_job /= 2;
+      else if (a.q_splits < 4) a.q_splits *= 2;
+      else break;
+    }
+    if (const char* e = std::getenv("FA_BWD_SPLIT")) {  // tuning override "heads_per_job,q_splits"
+      int h = 0, q = 0;
+      if (std::sscanf(e, "%d,%d", &h, &q) == 2 && h >= 1 && a.G % h == 0 && q >= 1 && q <= 64) {
+        a.heads_per_job = h;
+        a.q_splits = q;
+      }
+    }
+    a.n_partials = (a.G / a.heads_per_job) * a.q_splits;
   }
 
   p.q_elems = tnd ? d.T1 * N1 * D : (int64_t)d.B * S1 * N1 * D;
   p.lse_elems = tnd ? N1 * d.T1 : (int64_t)d.B * N1 * S1;
-  const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
-  const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
+  p.off_sfmg = 0;
   p.off_dq_acc = 0;
-  p.off_sfmg = align_up((size_t)p.q_elems * sizeof(float));
-  p.off_dk_acc = p.off_sfmg + align_up((size_t)p.lse_elems * sizeof(float));
-  p.off_dv_acc = p.off_dk_acc;
-  p.ws_bytes = p.off_dk_acc;
-  if (fabwd::split_heads(a)) {
-    p.off_dv_acc = p.off_dk_acc + align_up((size_t)k_elems * sizeof(float));
-    p.ws_bytes = p.off_dv_acc + align_up((size_t)v_elems * sizeof(float));
+  size_t cur = align_up((size_t)p.lse_elems * sizeof(float));
+  if (a.variant != 2) {
+    p.off_dq_acc = cur;
+    cur += align_up((size_t)p.q_elems * sizeof(float));
   }
+  p.off_dk_acc = p.off_dv_acc = cur;
+  if (fabwd::split_heads(a) || (a.variant == 2 && a.n_partials > 1)) {
+    const size_t parts = a.variant == 2 ? (size_t)a.n_partials : 1;
+    p.off_dk_acc = cur;
+    cur += align_up(parts * (size_t)k_elems * sizeof(float));
+    p.off_dv_acc = cur;
+    cur += align_up(parts * (size_t)v_elems * sizeof(float));
+  }
+  p.ws_bytes = cur;
   p.desc = d;
   p.desc.S1 = (int32_t)S1;
   p.desc.S2 = (int32_t)S2;
@@ -191,10 +226,10 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
     const KernelArgs& a = p->args;
     std::fprintf(stderr,
                  "[fa_bwd] plan layout=%d B=%d N1=%d N2=%d S1=%d S2=%d D=%d Dv=%d T1=%lld T2=%lld "
-                 "scale=%g window=(%d,%d) kv_tile=%d variant=%d heads_per_job=%d workspace=%zu B\n",
+                 "scale=%g window=(%d,%d) variant=%d heads_per_job=%d q_splits=%d partials=%d workspace=%zu B\n",
                  p->desc.layout, a.B, a.N1, a.N2, a.S1, a.S2, a.D, a.Dv, (long long)a.T1,
-                 (long long)a.T2, (double)a.scale, a.win_left, a.win_right, fabwd::KV_TILE,
-                 a.variant, a.heads_per_job, p->ws_bytes);
+                 (long long)a.T2, (double)a.scale, a.win_left, a.win_right, a.variant,
+                 a.heads_per_job, a.q_splits, a.n_partials, p->ws_bytes);
   }
   return FA_OK;
 }
@@ -213,13 +248,22 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out = attn_out; a.lse = softmax_lse;
   a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dq_acc);
-  a.sfmg = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_sfmg);
-  if (fabwd::split_heads(a)) {
-    a.dk_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dk_acc);
-    a.dv_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->off_dv_acc);
-  }
+  char* ws = static_cast<char*>(workspace);
+  a.sfmg = reinterpret_cast<float*>(ws + plan->off_sfmg);
+  if (a.variant != 2) a.dq_acc = reinterpret_cast<float*>(ws + plan->off_dq_acc);
+  a.dk_acc = reinterpret_cast<float*>(ws + plan->off_dk_acc);
+  a.dv_acc = reinterpret_cast<float*>(ws + plan->off_dv_acc);
 
+  if (a.variant == 2) {
+    // sfmg -> dK/dV kernel -> dQ kernel -> partial-sum reduce (when split)
+    if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_dq(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
+    return FA_OK;
+  }
   if (fabwd::launch_preprocess(a, true, stream) != 0) return FA_ERR_RUNTIME;
   if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
   if (fabwd::launch_main(a, stream) != 0) return FA_ERR_RUNTIME;

@@ -1,0 +1,701 @@
+// gfx950 (MI355X) FlashAttention backward, atomic-free path: one kernel for
+// dK/dV (key tiles in parallel) and one for dQ (query tiles in parallel).
+//
+// Formulas: page "CANN ops-transformer FlashAttnGrad 算子详解", section 一
+// (P = exp(scale*QK^T - softmax_lse), dV = P^T dY, dP = dY V^T,
+// sfmg = rowsum(dY (.) Y), dS = P (.) (dP - sfmg), dQ = scale*dS K,
+// dK = scale*dS^T Q).  The page's own kernel reduces dQ across key tiles with
+// atomic adds into an fp32 workspace (section 五 5.2).  On MI355X fp32
+// atomics reach about 1.35 TB/s against about 7.5 TB/s for plain stores, so
+// here dQ gets its own query-tile-parallel pass that recomputes S and dP
+// (two extra GEMMs) and writes every dQ element once; results are bitwise
+// repeatable.
+//
+// dK/dV kernel: one workgroup = 4 wavefronts owning KPW keys each (KPW = 64:
+// a 256-key tile).  K and V stay in LDS; 32-row query blocks stream through
+// LDS (the next one is prefetched into registers).  S = Q K^T and dP = dY V^T
+// use query rows as M and keys as N of v_mfma_f32_32x32x16_bf16, so each lane
+// holds one key and 16 query rows: exactly the A-operand layout of the
+// key-major products dV += P^T dY and dK += dS^T Q, whose B operands (dY and
+// Q read down their columns) come from ds_read_b64_tr_b16.  A job is (key
+// tile, query-head slot, query-range split, sequence, key/value head).  When
+// a key tile is split over several jobs (GQA heads, or query ranges for
+// balance) each job stores fp32 partial sums and a reduce kernel adds them;
+// otherwise the job writes bf16 dK/dV directly.
+//
+// dQ kernel: one workgroup = 4 wavefronts owning 32 query rows each.  Q and
+// dY fragments stay in VGPRs; 64-key blocks of K and V stream through LDS.
+// S^T = K Q^T and dP^T = V dY^T put keys on M and query rows on N, so each lane
+// owns one query row (its lse and sfmg are lane-local) and 16 keys; dS packed
+// to bf16 is then the A operand of dQ += dS K as it stands, with K read down
+// its columns through ds_read_b64_tr_b16.
+
+#include <hip/hip_runtime.h>
+
+#include "fa_bwd_internal.h"
+
+namespace fabwd {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Transposing LDS read (see fa_bwd_kernels.hip): lane i of a 16-lane group,
+// pointing at row r0 + i/4, column c0 + 4*(i%4) of a row-major bf16 tile,
+// receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ shortx4 lds_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(p));
+}
+__device__ __forceinline__ bf16x8 join(shortx4 lo, shortx4 hi) {
+  shortx8 s = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, s);
+}
+
+// LDS tile layout.  Tiles are stored without padding; the 16-byte chunk
+// (8 bf16) holding element (r, c) is permuted within its row by an XOR with a
+// function of r, chosen so that both access patterns of the kernels are free
+// of bank conflicts on gfx950 (measured: 16-byte row reads ~200 B/clk/CU and
+// transposing 8-byte reads ~130 B/clk/CU, against ~59 B/clk/CU for the
+// transposing reads on a 272-byte padded pitch):
+//  * 16 consecutive rows, same chunk (the A/B fragments of row-major reads);
+//  * 4 consecutive rows x 64 bytes (one transposing read of 32 lanes).
+// A 128-column block uses f(r) = 4*(r%4) + (r/4)%4 over its 16 chunks, a
+// 64-column block (128-byte rows, two per bank cycle) uses
+// g(r) = 4*((r/2)%2) + (r/4)%4 over its 8 chunks; 192 columns are a
+// 128-column block followed by a 64-column block.
+template <int COLS, int ROWS>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (COLS == 128) {
+    return r * 128 + ((((c >> 3) ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3) | (c & 7));
+  } else if constexpr (COLS == 64) {
+    return r * 64 + ((((c >> 3) ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))) << 3) | (c & 7));
+  } else {
+    static_assert(COLS == 192, "tile width");
+    return c < 128 ? swz<128, ROWS>(r, c) : ROWS * 128 + swz<64, ROWS>(r, c - 128);
+  }
+}
+
+struct SeqBounds {
+  int s1, s2;
+  int64_t qbase, kbase, vbase, obase, lbase;
+};
+
+__device__ __forceinline__ SeqBounds seq_bounds(const KernelArgs& a, int b) {
+  SeqBounds r;
+  if (a.varlen) {
+    const int q0 = a.cu_q[b], k0 = a.cu_kv[b];
+    r.s1 = a.cu_q[b + 1] - q0;
+    r.s2 = a.cu_kv[b + 1] - k0;
+    r.qbase = (int64_t)q0 * a.q_ss;
+    r.obase = (int64_t)q0 * a.o_ss;
+    r.kbase = (int64_t)k0 * a.k_ss;
+    r.vbase = (int64_t)k0 * a.v_ss;
+    r.lbase = q0;
+  } else {
+    r.s1 = a.S1;
+    r.s2 = a.S2;
+    r.qbase = (int64_t)b * a.q_sb;
+    r.obase = (int64_t)b * a.o_sb;
+    r.kbase = (int64_t)b * a.k_sb;
+    r.vbase = (int64_t)b * a.v_sb;
+    r.lbase = (int64_t)b * a.l_sb;
+  }
+  return r;
+}
+
+// Per-lane byte addresses of a swizzled tile block of width W (128 or 64
+// columns), computed once: a 16-byte row read of (row l32, column 16*kk+8*hi)
+// is at a_base ^ (kk*32); a transposing read of rows 16*kc + 8*s + tr_r4,
+// columns nb*32 + tr_c is at (t_base[s] ^ (nb*64)) + kc*16*W*2.  Both equal
+// the swz() offsets (the XOR acts on bits that the other terms leave clear).
+template <int W>
+struct SwzBlock {
+  int a_base;
+  int t_base[2];
+  __device__ __forceinline__ void init(int blk_byte_off, int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int f = (W == 128) ? (((l32 & 3) << 2) | ((l32 >> 2) & 3)) : ((((l32 >> 1) & 1) << 2) | ((l32 >> 2) & 3));
+    a_base = (blk_byte_off + l32 * W * 2 + 16 * (hi ^ (f & 1))) | ((f >> 1) << 5);
+    const int q = (W == 128) ? ((lane & 15) >> 2) : ((lane >> 3) & 1);
+    const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      t_base[s] = (blk_byte_off + tr_r4 * W * 2 + 8 * (lane & 1) + s * 8 * W * 2 + 16 * (cl ^ ((2 * s + hi) & 3))) | (q << 6);
+  }
+};
+
+// Addressing of a swizzled tile of COLS (64, 128 or 192) columns and ROWS rows.
+template <int COLS, int ROWS>
+struct SwzTile {
+  static constexpr int W0 = COLS == 64 ? 64 : 128;
+  SwzBlock<W0> b0;
+  SwzBlock<64> b1;  // second block of a 192-column tile
+  __device__ __forceinline__ void init(int lane) {
+    b0.init(0, lane);
+    if constexpr (COLS == 192) b1.init(ROWS * 128 * 2, lane);
+  }
+  // byte offset of the 16-byte row read for k-step kk (columns 16*kk + 8*hi)
+  __device__ __forceinline__ int row_read(int kk) const {
+    if constexpr (COLS == 192) return kk < 8 ? (b0.a_base ^ (kk * 32)) : (b1.a_base ^ ((kk - 8) * 32));
+    else return b0.a_base ^ (kk * 32);
+  }
+  // byte offset of the transposing read for row chunk kc, half s, column block nb
+  __device__ __forceinline__ int tr_read(int kc, int s, int nb) const {
+    if constexpr (COLS == 192) {
+      return nb < 4 ? ((b0.t_base[s] ^ (nb * 64)) + kc * 16 * 128 * 2) : ((b1.t_base[s] ^ ((nb - 4) * 64)) + kc * 16 * 64 * 2);
+    } else {
+      return (b0.t_base[s] ^ (nb * 64)) + kc * 16 * W0 * 2;
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_row16(const bf16* base, int byte_off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ __forceinline__ shortx4 lds_tr_at(const bf16* base, int byte_off) {
+  return lds_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+
+// ------------------------------------------------------------------ dK / dV
+
+// QG query groups of 4 wavefronts share one tile of 4*KPW keys; wavefront w of
+// each group owns keys w*KPW .. w*KPW+KPW-1 of the tile.  The groups take
+// alternate 32-row query blocks; each group double-buffers its Q/dY tile so a
+// step needs one barrier.  K/V tiles use a padded pitch (16-byte row reads
+// only); Q/dY tiles are swizzled (row reads and transposing reads).
+template <int HD, int HDV, int KPW, int QG>
+__global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
+  constexpr int NT = 256 * QG;        // threads
+  constexpr int BC = 4 * KPW;         // keys per workgroup
+  constexpr int NKB = KPW / 32;       // 32-key blocks per wavefront
+  constexpr int BR = 32;              // query rows per step and group
+  constexpr int KP = HD + 8;          // padded pitches of the K and V tiles
+  constexpr int VP = HDV + 8;
+  constexpr int NKQ = HD / 16;
+  constexpr int NKV = HDV / 16;
+  constexpr int NBK = HD / 32;
+  constexpr int NBV = HDV / 32;
+  constexpr int NQC = BR * HD / 8 / 256;   // 16-byte Q chunks per thread of a group
+  constexpr int NYC = BR * HDV / 8 / 256;
+  static_assert(NQC * 256 * 8 == BR * HD && NYC * 256 * 8 == BR * HDV, "tile split");
+
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BC * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BC * VP];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[QG][2][BR * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Ys[QG][2][BR * HDV];
+  __shared__ __attribute__((aligned(16))) float lse_s[QG][2][BR];
+  __shared__ __attribute__((aligned(16))) float sfm_s[QG][2][BR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qg = wave >> 2;      // query group
+  const int kw = wave & 3;       // key slice
+  const int gt = tid & 255;      // thread within the group
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // job = ((((tile * HJ + hslot) * QS + qs) * B + b) * N2 + n2)
+  const int hpj = a.heads_per_job;
+  const int HJ = a.G / hpj;
+  const int QS = a.q_splits;
+  int r = blockIdx.x;
+  const int n2 = r % a.N2; r /= a.N2;
+  const int b = r % a.B; r /= a.B;
+  const int qs = r % QS; r /= QS;
+  const int hslot = r % HJ;
+  const int tile = r / HJ;
+  const int part = hslot * QS + qs;
+
+  const SeqBounds sb = seq_bounds(a, b);
+  const int s1 = sb.s1, s2 = sb.s2;
+  const int j0 = tile * BC;
+  if (j0 >= s2) return;
+  const int j1 = min(j0 + BC, s2);
+  const int off = s2 - s1;
+  const int wl = a.win_left, wr = a.win_right;
+
+  {
+    const bf16* Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
+    const bf16* Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn;
+    for (int c = tid; c < BC * (HD / 8); c += NT) {
+      const int rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+      bf16x8 val = {};
+      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Kg + (int64_t)(j0 + rr) * a.k_ss + cc);
+      *reinterpret_cast<bf16x8*>(&Ks[rr * KP + cc]) = val;
+    }
+    for (int c = tid; c < BC * (HDV / 8); c += NT) {
+      const int rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+      bf16x8 val = {};
+      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)(j0 + rr) * a.v_ss + cc);
+      *reinterpret_cast<bf16x8*>(&Vs[rr * VP + cc]) = val;
+    }
+  }
+
+  // query blocks that see a key of [j0, j1); this job takes split qs of them
+  int i_lo = 0, i_hi = s1;
+  if (wr >= 0) i_lo = max(0, j0 - off - wr);
+  if (wl >= 0) i_hi = min(s1, j1 - off + wl);
+  const int blk0 = i_lo / BR;
+  const int nblk_all = i_hi > i_lo ? (i_hi + BR - 1) / BR - blk0 : 0;
+  const int bs_lo = blk0 + (int)((int64_t)nblk_all * qs / QS);
+  const int bs_hi = blk0 + (int)((int64_t)nblk_all * (qs + 1) / QS);
+  const int nblk = bs_hi - bs_lo;
+  const int T = hpj * nblk;
+  const int g0 = hslot * hpj;
+
+  bf16x8 pq[NQC], py[NYC];
+  float pl = __builtin_inff(), pf = 0.f;
+  auto fetch = [&](int t) {
+    if (t < T) {
+      const int n1 = n2 * a.G + g0 + t / nblk;
+      const int i0 = (bs_lo + t % nblk) * BR;
+      const bf16* Qg = static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn;
+      const bf16* Yg = static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn;
+#pragma unroll
+      for (int u = 0; u < NQC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+        bf16x8 val = {};
+        if (i0 + rr < s1) val = *reinterpret_cast<const bf16x8*>(Qg + (int64_t)(i0 + rr) * a.q_ss + cc);
+        pq[u] = val;
+      }
+#pragma unroll
+      for (int u = 0; u < NYC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+        bf16x8 val = {};
+        if (i0 + rr < s1) val = *reinterpret_cast<const bf16x8*>(Yg + (int64_t)(i0 + rr) * a.o_ss + cc);
+        py[u] = val;
+      }
+      if (gt < BR) {
+        const int i = i0 + gt;
+        pl = __builtin_inff();
+        pf = 0.f;
+        if (i < s1) {
+          const float l = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + i];
+          pl = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;  // empty row -> P = 0
+          pf = a.sfmg[sb.lbase + (int64_t)n1 * a.l_sn + i];
+        }
+      }
+    }
+  };
+  fetch(qg);
+
+  floatx16 dKr[NKB][NBK], dVr[NKB][NBV];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) dKr[kb][i] = floatx16{};
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) dVr[kb][i] = floatx16{};
+  }
+
+  SwzTile<HD, BR> qadr;
+  SwzTile<HDV, BR> yadr;
+  qadr.init(lane);
+  yadr.init(lane);
+  const int kw0 = kw * KPW;  // first key of this wavefront within the tile
+
+  const int iters = (T + QG - 1) / QG;
+  for (int it = 0; it < iters; ++it) {
+    const int t = it * QG + qg;
+    const bool valid = t < T;
+    const int buf = it & 1;
+    const bf16* Qb = Qs[qg][buf];
+    const bf16* Yb = Ys[qg][buf];
+    int i0 = 0;
+    if (valid) {
+      i0 = (bs_lo + t % nblk) * BR;
+#pragma unroll
+      for (int u = 0; u < NQC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&Qs[qg][buf][swz<HD, BR>(rr, cc)]) = pq[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NYC; ++u) {
+        const int c = gt + 256 * u, rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&Ys[qg][buf][swz<HDV, BR>(rr, cc)]) = py[u];
+      }
+      if (gt < BR) {
+        lse_s[qg][buf][gt] = pl;
+        sfm_s[qg][buf][gt] = pf;
+      }
+    }
+    fetch(t + QG);
+    __syncthreads();
+    if (!valid) continue;
+
+    // S = Q K^T and dP = dY V^T for this wavefront's KPW keys
+    floatx16 sacc[NKB], pacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = floatx16{};
+      pacc[kb] = floatx16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKQ; ++kk) {
+      const bf16x8 qa = lds_row16(Qb, qadr.row_read(kk));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&Ks[(kw0 + kb * 32 + l32) * KP + 16 * kk + 8 * hi]);
+        sacc[kb] = mfma32(qa, kv, sacc[kb]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKV; ++kk) {
+      const bf16x8 ya = lds_row16(Yb, yadr.row_read(kk));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(&Vs[(kw0 + kb * 32 + l32) * VP + 16 * kk + 8 * hi]);
+        pacc[kb] = mfma32(ya, vv, pacc[kb]);
+      }
+    }
+
+    // P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), packed as bf16 A operands
+    const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
+                      (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
+    bf16x8 pa[NKB][2], da[NKB][2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int ib = r4 * 8 + hi * 4;
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[qg][buf][ib]);
+      const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][buf][ib]);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int jk = j0 + kw0 + kb * 32 + l32;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rg = r4 * 4 + e;
+          float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+          if (!full) {
+            const int i = i0 + ib + e;
+            const bool vis = (i < s1) && (jk < s2) && (wl < 0 || jk >= i + off - wl) && (wr < 0 || jk <= i + off + wr);
+            p = vis ? p : 0.f;
+          }
+          const float ds = p * (pacc[kb][rg] - f4[e]);
+          pa[kb][rg >> 3][rg & 7] = (bf16)p;
+          da[kb][rg >> 3][rg & 7] = (bf16)ds;
+        }
+      }
+    }
+
+    // dV += P^T dY, dK += dS^T Q; one transposing read serves all key blocks
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) {
+        const bf16x8 yb = join(lds_tr_at(Yb, yadr.tr_read(kc, 0, nb)), lds_tr_at(Yb, yadr.tr_read(kc, 1, nb)));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) dVr[kb][nb] = mfma32(pa[kb][kc], yb, dVr[kb][nb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        const bf16x8 qb = join(lds_tr_at(Qb, qadr.tr_read(kc, 0, nb)), lds_tr_at(Qb, qadr.tr_read(kc, 1, nb)));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32(da[kb][kc], qb, dKr[kb][nb]);
+      }
+    }
+  }
+
+  // ---- add the other groups' dK/dV into group 0, 32 columns at a time
+  if constexpr (QG > 1) {
+    float* red = reinterpret_cast<float*>(Ks);  // K/V tiles are no longer read
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int nb = 0; nb < NBK + NBV; ++nb) {
+        __syncthreads();
+        if (qg != 0) {
+#pragma unroll
+          for (int rg = 0; rg < 16; ++rg)
+            red[(((qg - 1) * 4 + kw) * 16 + rg) * 64 + lane] = nb < NBK ? dKr[kb][nb][rg] : dVr[kb][nb - NBK][rg];
+        }
+        __syncthreads();
+        if (qg == 0) {
+#pragma unroll
+          for (int g = 1; g < QG; ++g) {
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+              const float x = red[(((g - 1) * 4 + kw) * 16 + rg) * 64 + lane];
+              if (nb < NBK) dKr[kb][nb][rg] += x; else dVr[kb][nb - NBK][rg] += x;
+            }
+          }
+        }
+      }
+    }
+    if (qg != 0) return;
+  }
+
+  // ---- output: bf16 when this job alone covers the key tile, else fp32 partials
+  const bool partial = a.n_partials > 1;
+  const int64_t kpart = (int64_t)part * a.k_part_stride;
+  const int64_t vpart = (int64_t)part * a.v_part_stride;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int rg = 0; rg < 16; ++rg) {
+      const int j = j0 + kw0 + kb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+      if (j >= s2) continue;
+      const int64_t ko = sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
+      const int64_t vo = sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
+      if (partial) {
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) a.dk_acc[kpart + ko + nb * 32 + l32] = dKr[kb][nb][rg] * a.scale;
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) a.dv_acc[vpart + vo + nb * 32 + l32] = dVr[kb][nb][rg];
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) static_cast<bf16*>(a.dk)[ko + nb * 32 + l32] = (bf16)(dKr[kb][nb][rg] * a.scale);
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) static_cast<bf16*>(a.dv)[vo + nb * 32 + l32] = (bf16)dVr[kb][nb][rg];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+
+constexpr int DQ_BQ = 128;  // query rows per workgroup (4 wavefronts x 32)
+constexpr int DQ_BK = 64;   // keys per step
+
+template <int HD, int HDV>
+__global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a) {
+  constexpr int NKQ = HD / 16;
+  constexpr int NKV = HDV / 16;
+  constexpr int NBK = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[DQ_BK * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[DQ_BK * HDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  // job -> (query tile, query head, sequence); the query tile varies slowest
+  // and counts down, so the causal tiles with the most keys start first
+  const int per_tile = a.N1 * a.B;
+  const int ntiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
+  const int tile = ntiles - 1 - (int)(blockIdx.x / per_tile);
+  const int rem = blockIdx.x % per_tile;
+  const int n1 = rem % a.N1;
+  const int b = rem / a.N1;
+  const int n2 = n1 / a.G;
+
+  const SeqBounds sb = seq_bounds(a, b);
+  const int s1 = sb.s1, s2 = sb.s2;
+  const int i0 = tile * DQ_BQ;
+  if (i0 >= s1) return;
+  const int off = s2 - s1;
+  const int wl = a.win_left, wr = a.win_right;
+  const int iq = i0 + wave * 32 + l32;  // this lane's query row
+
+  const bf16* __restrict__ Qg = static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn;
+  const bf16* __restrict__ Yg = static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn;
+  const bf16* __restrict__ Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
+  const bf16* __restrict__ Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn;
+
+  bf16x8 qf[NKQ], yf[NKV];  // B operands: query row iq, dims 16*kk + 8*hi + 0..7
+#pragma unroll
+  for (int kk = 0; kk < NKQ; ++kk) {
+    bf16x8 val = {};
+    if (iq < s1) val = *reinterpret_cast<const bf16x8*>(Qg + (int64_t)iq * a.q_ss + 16 * kk + 8 * hi);
+    qf[kk] = val;
+  }
+#pragma unroll
+  for (int kk = 0; kk < NKV; ++kk) {
+    bf16x8 val = {};
+    if (iq < s1) val = *reinterpret_cast<const bf16x8*>(Yg + (int64_t)iq * a.o_ss + 16 * kk + 8 * hi);
+    yf[kk] = val;
+  }
+  float l2 = __builtin_inff(), sf = 0.f;
+  if (iq < s1) {
+    const float l = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + iq];
+    l2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
+    sf = a.sfmg[sb.lbase + (int64_t)n1 * a.l_sn + iq];
+  }
+
+  const int i_last = min(i0 + DQ_BQ, s1) - 1;
+  int j_lo = 0, j_hi = s2;
+  if (wl >= 0) j_lo = max(0, i0 + off - wl);
+  if (wr >= 0) j_hi = min(s2, i_last + off + wr + 1);
+
+  const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
+
+  floatx16 dq[NBK];
+#pragma unroll
+  for (int nb = 0; nb < NBK; ++nb) dq[nb] = floatx16{};
+
+  for (int j0 = (j_lo / DQ_BK) * DQ_BK; j0 < j_hi; j0 += DQ_BK) {
+    __syncthreads();
+    for (int c = tid; c < DQ_BK * (HD / 8); c += 256) {
+      const int rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+      bf16x8 val = {};
+      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Kg + (int64_t)(j0 + rr) * a.k_ss + cc);
+      *reinterpret_cast<bf16x8*>(&Ks[swz<HD, DQ_BK>(rr, cc)]) = val;
+    }
+    for (int c = tid; c < DQ_BK * (HDV / 8); c += 256) {
+      const int rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
+      bf16x8 val = {};
+      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)(j0 + rr) * a.v_ss + cc);
+      *reinterpret_cast<bf16x8*>(&Vs[swz<HDV, DQ_BK>(rr, cc)]) = val;
+    }
+    __syncthreads();
+
+    // S^T and dP^T for 64 keys (2 blocks of 32) x this wavefront's 32 rows
+    floatx16 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = floatx16{};
+      dp[mb] = floatx16{};
+#pragma unroll
+      for (int kk = 0; kk < NKQ; ++kk) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[swz<HD, DQ_BK>(mb * 32 + l32, 16 * kk + 8 * hi)]);
+        s[mb] = mfma32(ka, qf[kk], s[mb]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[swz<HDV, DQ_BK>(mb * 32 + l32, 16 * kk + 8 * hi)]);
+        dp[mb] = mfma32(va, yf[kk], dp[mb]);
+      }
+    }
+    const bool full = (i0 + DQ_BQ <= s1) && (j0 + DQ_BK <= s2) &&
+                      (wr < 0 || j0 + DQ_BK - 1 <= i0 + off + wr) &&
+                      (wl < 0 || j0 >= i0 + DQ_BQ - 1 + off - wl);
+    bf16x8 da[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) {
+        float p = __builtin_amdgcn_exp2f(s[mb][rg] * a.scale_log2 - l2);
+        if (!full) {
+          const int j = j0 + mb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+          const bool vis = (iq < s1) && (j < s2) && (wl < 0 || j >= iq + off - wl) && (wr < 0 || j <= iq + off + wr);
+          p = vis ? p : 0.f;
+        }
+        da[mb * 2 + (rg >> 3)][rg & 7] = (bf16)(p * (dp[mb][rg] - sf));
+      }
+    }
+    // dQ += dS K over 4 chunks of 16 keys
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        const bf16x8 kb = join(lds_tr(&Ks[swz<HD, DQ_BK>(16 * kc + tr_r4, nb * 32 + tr_c)]),
+                               lds_tr(&Ks[swz<HD, DQ_BK>(16 * kc + 8 + tr_r4, nb * 32 + tr_c)]));
+        dq[nb] = mfma32(da[kc], kb, dq[nb]);
+      }
+    }
+  }
+
+  // dq = bf16(scale * acc): lane holds head-dim column nb*32 + l32 of 16 rows
+  bf16* __restrict__ dQg = static_cast<bf16*>(a.dq) + sb.qbase + (int64_t)n1 * a.q_sn;
+#pragma unroll
+  for (int rg = 0; rg < 16; ++rg) {
+    const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+    if (i < s1) {
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = (bf16)(dq[nb][rg] * a.scale);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ partial sums
+
+// dk = bf16(sum over parts), dv likewise; 8 elements per thread.
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ part, int64_t part_stride,
+                                                           int nparts, bf16* __restrict__ out, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    floatx4 s0 = reinterpret_cast<const floatx4*>(part)[2 * i];
+    floatx4 s1 = reinterpret_cast<const floatx4*>(part)[2 * i + 1];
+    for (int p = 1; p < nparts; ++p) {
+      const float* q = part + (int64_t)p * part_stride;
+      s0 += reinterpret_cast<const floatx4*>(q)[2 * i];
+      s1 += reinterpret_cast<const floatx4*>(q)[2 * i + 1];
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = (bf16)s0[e];
+      o[e + 4] = (bf16)s1[e];
+    }
+    reinterpret_cast<bf16x8*>(out)[i] = o;
+  }
+}
+
+template <typename T> struct same_type { using type = T; };
+template <typename... KArgs>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, typename same_type<KArgs>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+}
+
+}  // namespace
+
+bool det_instantiated(int D, int Dv) {
+  return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128)) || (D == 192 && (Dv == 64 || Dv == 128));
+}
+
+// (keys per wavefront, query groups) of the dK/dV kernel for a head dim:
+// D <= 128: 32 keys x 2 groups (8 wavefronts, two per SIMD, 128-key tiles);
+// D = 192: 32 keys x 1 group (the accumulators need more registers).
+int det_keys_per_wave(int D) { (void)D; return 32; }
+static int det_query_groups(int D) { return D <= 128 ? 2 : 1; }
+
+int launch_dkdv(const KernelArgs& a, void* stream) {
+  const int kpw = det_keys_per_wave(a.D);
+  const int qg = det_query_groups(a.D);
+  const int64_t tiles = (a.S2 + 4 * kpw - 1) / (4 * kpw);
+  const int64_t blocks = tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.N2;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks), block(256 * qg);
+  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 2>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 2>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 2>, grid, block, s, a);
+  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 1>, grid, block, s, a);
+  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 1>, grid, block, s, a);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_dq(const KernelArgs& a, void* stream) {
+  const int64_t tiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
+  const int64_t blocks = tiles * a.N1 * a.B;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (a.D == 64 && a.Dv == 64) return launch(dq_kernel<64, 64>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(dq_kernel<128, 64>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(dq_kernel<128, 128>, grid, block, s, a);
+  if (a.D == 192 && a.Dv == 64) return launch(dq_kernel<192, 64>, grid, block, s, a);
+  if (a.D == 192 && a.Dv == 128) return launch(dq_kernel<192, 128>, grid, block, s, a);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_reduce_parts(const KernelArgs& a, void* stream) {
+  if (a.n_partials <= 1) return 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto one = [&](const float* part, int64_t stride, void* out, int64_t elems) -> int {
+    const int64_t n8 = elems / 8;
+    int64_t blocks = (n8 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks <= 0) return 0;
+    return launch(reduce_parts_kernel, dim3((unsigned)blocks), dim3(256), s, part, stride, a.n_partials,
+                  static_cast<bf16*>(out), n8);
+  };
+  int e = one(a.dk_acc, a.k_part_stride, a.dk, a.k_part_stride);
+  if (e == 0) e = one(a.dv_acc, a.v_part_stride, a.dv, a.v_part_stride);
+  return e;
+}
+
+}  // namespace fabwd

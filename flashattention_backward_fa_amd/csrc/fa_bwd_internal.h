@@ -52,18 +52,30 @@ struct KernelArgs {
   int32_t win_right;     // -1 = unbounded
   int32_t has_mask;      // any bound present
 
-  int32_t variant;        // main kernel: 0 = 4 wavefronts, 1 = 8 wavefronts in two query groups
-  int32_t heads_per_job;  // query heads of a GQA group handled by one workgroup (G or 1)
+  int32_t variant;        // 0 = 4-wavefront atomic kernel, 1 = 8-wavefront atomic kernel,
+                          // 2 = atomic-free pair (dK/dV kernel + dQ kernel)
+  int32_t heads_per_job;  // query heads of a GQA group handled by one workgroup
+  int32_t q_splits;       // query-range splits of one key tile (atomic-free pair only)
+  int32_t n_partials;     // fp32 dK/dV partial sums per key tile (atomic-free pair only)
+  int64_t k_part_stride;  // elements between dK partials (= elements of k)
+  int64_t v_part_stride;  // elements between dV partials (= elements of v)
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups
 // (through the fp32 dk_acc / dv_acc workspace) instead of in registers.
-inline bool split_heads(const KernelArgs& a) { return a.heads_per_job < a.G; }
+inline bool split_heads(const KernelArgs& a) { return a.variant != 2 && a.heads_per_job < a.G; }
 
 // Launchers (fa_bwd_kernels.hip).  Each returns 0 or a hipError_t value.
 int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream);
 int launch_main(const KernelArgs& a, void* stream);
 bool main_v2_instantiated(int D, int Dv);
+
+// Atomic-free pair (fa_bwd_det_kernels.hip).
+bool det_instantiated(int D, int Dv);
+int det_keys_per_wave(int D);
+int launch_dkdv(const KernelArgs& a, void* stream);
+int launch_dq(const KernelArgs& a, void* stream);
+int launch_reduce_parts(const KernelArgs& a, void* stream);
 int launch_dq_finalize(const KernelArgs& a, void* stream);
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream);
 bool main_instantiated(int D, int Dv);

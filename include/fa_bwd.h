@@ -77,7 +77,7 @@ enum { FA_LAYOUT_BSND = 0, FA_LAYOUT_BNSD = 1, FA_LAYOUT_TND = 2 };
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 };
 
 /* flags */
-#define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable dQ (not built: FA_ERR_UNSUPPORTED) */
+#define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable results; the default path already is */
 
 typedef struct fa_bwd_plan_s* fa_bwd_plan; /* opaque, host memory only */
 
@@ -100,7 +100,7 @@ typedef struct fa_bwd_desc {
   float softmax_scale;   /* 0 selects 1/sqrt(D) (section 一, scale rule)         */
   int32_t mask_mode;     /* FA_MASK_*                                             */
   int32_t win_left, win_right; /* window bounds, -1 = unbounded                  */
-  uint32_t flags;        /* FA_FLAG_* ; 0 for the default (fp32 atomic dQ)       */
+  uint32_t flags;        /* FA_FLAG_*                                             */
 } fa_bwd_desc;
 
 /* Validate `desc` (all rules of section 四 4.6 that this library enforces) and

@@ -60,17 +60,17 @@ def create(lib, **kw):
 
 def test_valid_problem_and_workspace_size(lib):
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # GQA (N1=8, N2=2): fp32 dQ accumulator, sfmg, and fp32 dK/dV accumulators
-    # (query heads of a group are split over workgroups)
+    # Enough key tiles x heads for every CU: sfmg only (dQ is written once by
+    # its own kernel, dK/dV by the key-tile kernel).
+    st, ws = create(lib, B=64, N1=8, N2=8, S1=256, S2=256)
+    assert st == fb.FA_OK
+    assert ws == rnd(64 * 8 * 256 * 4)
+    # A small GQA problem is split over query heads (4) and query ranges (4):
+    # 16 fp32 partial sums of dK and of dV per key.
     st, ws = create(lib)
     assert st == fb.FA_OK
-    q_elems, lse, k_elems = 2 * 128 * 8 * 128, 2 * 8 * 128, 2 * 128 * 2 * 128
-    assert ws == rnd(q_elems * 4) + rnd(lse * 4) + 2 * rnd(k_elems * 4)
-    # MHA: dK/dV complete inside a workgroup, no dK/dV accumulators
-    st, ws = create(lib, N1=2, N2=2)
-    assert st == fb.FA_OK
-    q_elems, lse = 2 * 128 * 2 * 128, 2 * 2 * 128
-    assert ws == rnd(q_elems * 4) + rnd(lse * 4)
+    lse, k_elems = 2 * 8 * 128, 2 * 128 * 2 * 128
+    assert ws == rnd(lse * 4) + 2 * rnd(16 * k_elems * 4)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -91,7 +91,6 @@ def test_valid_problem_and_workspace_size(lib):
     (dict(softmax_scale=float("nan")), fb.FA_ERR_PARAM_INVALID),
     (dict(dtype=1), fb.FA_ERR_UNSUPPORTED),          # fp16 is on the page, not built
     (dict(D=96, Dv=96), fb.FA_ERR_UNSUPPORTED),      # head dim not instantiated
-    (dict(flags=fb.FLAG_DETERMINISTIC), fb.FA_ERR_UNSUPPORTED),
 ])
 def test_create_rejects(lib, kw, code):
     assert create(lib, **kw)[0] == code
@@ -101,6 +100,7 @@ def test_create_rejects(lib, kw, code):
     dict(mask_mode=1), dict(mask_mode=1, win_left=1024, win_right=0), dict(mask_mode=2, win_left=3, win_right=7),
     dict(mask_mode="causal"), dict(mask_mode=fb.MaskMode.WINDOW, win_left=-1, win_right=-1),
     dict(D=192, Dv=128), dict(D=64, Dv=64), dict(N1=32, N2=8), dict(softmax_scale=0.25),
+    dict(flags=fb.FLAG_DETERMINISTIC),
 ])
 def test_create_accepts(lib, kw):
     assert create(lib, **kw)[0] == fb.FA_OK

@@ -152,6 +152,11 @@ struct SwzTile {
     if constexpr (COLS == 192) return kk < 8 ? (b0.a_base ^ (kk * 32)) : (b1.a_base ^ ((kk - 8) * 32));
     else return b0.a_base ^ (kk * 32);
   }
+  // the same for rows r0 + l32 (r0 a multiple of 16)
+  __device__ __forceinline__ int row_read_at(int kk, int r0) const {
+    if constexpr (COLS == 192) return kk < 8 ? (b0.a_base ^ (kk * 32)) + r0 * 256 : (b1.a_base ^ ((kk - 8) * 32)) + r0 * 128;
+    else return (b0.a_base ^ (kk * 32)) + r0 * W0 * 2;
+  }
   // byte offset of the transposing read for row chunk kc, half s, column block nb
   __device__ __forceinline__ int tr_read(int kc, int s, int nb) const {
     if constexpr (COLS == 192) {
@@ -167,6 +172,65 @@ __device__ __forceinline__ bf16x8 lds_row16(const bf16* base, int byte_off) {
 }
 __device__ __forceinline__ shortx4 lds_tr_at(const bf16* base, int byte_off) {
   return lds_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+
+// Asynchronous copy of rows [0, ROWS) of a COLS-wide bf16 tile from global
+// memory (row r at g + min(r, nvalid-1)*ld; rows past the end repeat the last
+// valid row, which the masks then ignore) into a swizzled LDS tile with
+// global_load_lds_dwordx4: each instruction fills 1 KB of LDS, lane t writing
+// bytes 16t..16t+15, so each lane loads the logical chunk that the swizzle
+// puts in its slot.  The NW wavefronts of the workgroup share the
+// instructions.  Completion: s_waitcnt vmcnt(0) then a barrier.
+template <int W>
+__device__ __forceinline__ int swz_f(int r) {
+  return (W == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+template <int W, int ROWS, int NW>
+__device__ __forceinline__ void async_block_load(bf16* lds_blk, const bf16* g, int col0, int64_t ld, int nvalid,
+                                                 int wave, int lane) {
+  constexpr int RPI = 1024 / (W * 2);  // rows per instruction
+  constexpr int CPR = W / 8;           // chunks per row
+  constexpr int NI = ROWS / RPI;
+#pragma unroll
+  for (int u = wave; u < NI; u += NW) {
+    const int row = u * RPI + lane / CPR;
+    const int logical = (lane % CPR) ^ swz_f<W>(row);
+    const int rs = min(row, nvalid - 1);
+    const bf16* src = g + (int64_t)rs * ld + col0 + logical * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_blk + u * 512), 16, 0, 0);
+  }
+}
+
+template <int COLS, int ROWS, int NW>
+__device__ __forceinline__ void async_tile_load(bf16* lds_tile, const bf16* g, int64_t ld, int nvalid, int wave,
+                                                int lane) {
+  if constexpr (COLS == 192) {
+    async_block_load<128, ROWS, NW>(lds_tile, g, 0, ld, nvalid, wave, lane);
+    async_block_load<64, ROWS, NW>(lds_tile + ROWS * 128, g, 128, ld, nvalid, wave, lane);
+  } else {
+    async_block_load<COLS, ROWS, NW>(lds_tile, g, 0, ld, nvalid, wave, lane);
+  }
+}
+
+// The same into a padded tile (row pitch COLS + 8 elements, 16-byte row reads
+// only): ROWS*(COLS/8 + 1) 16-byte slots, a multiple of 64 for ROWS % 64 == 0;
+// a lane whose slot is the pad loads a valid dummy chunk.
+template <int COLS, int ROWS, int NW>
+__device__ __forceinline__ void async_padded_load(bf16* lds_tile, const bf16* g, int64_t ld, int nvalid, int wave,
+                                                  int lane) {
+  constexpr int PC = COLS / 8 + 1;  // 16-byte slots per padded row
+  constexpr int NI = ROWS * PC / 64;
+  static_assert(NI * 64 == ROWS * PC, "whole instructions");
+#pragma unroll
+  for (int u = wave; u < NI; u += NW) {
+    const int slot = u * 64 + lane;
+    const int row = slot / PC;
+    const int ch = slot % PC;
+    const int rs = min(row, nvalid - 1);
+    const bf16* src = g + (int64_t)rs * ld + (ch < COLS / 8 ? ch * 8 : 0);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_tile + u * 512), 16, 0, 0);
+  }
 }
 
 // ------------------------------------------------------------------ dK / dV
@@ -188,9 +252,6 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   constexpr int NKV = HDV / 16;
   constexpr int NBK = HD / 32;
   constexpr int NBV = HDV / 32;
-  constexpr int NQC = BR * HD / 8 / 256;   // 16-byte Q chunks per thread of a group
-  constexpr int NYC = BR * HDV / 8 / 256;
-  static_assert(NQC * 256 * 8 == BR * HD && NYC * 256 * 8 == BR * HDV, "tile split");
 
   __shared__ __attribute__((aligned(16))) bf16 Ks[BC * KP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[BC * VP];
@@ -228,21 +289,11 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int off = s2 - s1;
   const int wl = a.win_left, wr = a.win_right;
 
-  {
-    const bf16* Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
-    const bf16* Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn;
-    for (int c = tid; c < BC * (HD / 8); c += NT) {
-      const int rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-      bf16x8 val = {};
-      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Kg + (int64_t)(j0 + rr) * a.k_ss + cc);
-      *reinterpret_cast<bf16x8*>(&Ks[rr * KP + cc]) = val;
-    }
-    for (int c = tid; c < BC * (HDV / 8); c += NT) {
-      const int rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
-      bf16x8 val = {};
-      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)(j0 + rr) * a.v_ss + cc);
-      *reinterpret_cast<bf16x8*>(&Vs[rr * VP + cc]) = val;
-    }
+  {  // K and V tiles, asynchronously (rows past the sequence end repeat its last key)
+    const bf16* Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j0 * a.k_ss;
+    const bf16* Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j0 * a.v_ss;
+    async_padded_load<HD, BC, 4 * QG>(Ks, Kg, a.k_ss, s2 - j0, wave, lane);
+    async_padded_load<HDV, BC, 4 * QG>(Vs, Vg, a.v_ss, s2 - j0, wave, lane);
   }
 
   // query blocks that see a key of [j0, j1); this job takes split qs of them
@@ -257,28 +308,17 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int T = hpj * nblk;
   const int g0 = hslot * hpj;
 
-  bf16x8 pq[NQC], py[NYC];
+  // Q/dY tiles of item t of this group go straight to LDS (async); lse and
+  // sfmg of its rows go through registers
   float pl = __builtin_inff(), pf = 0.f;
-  auto fetch = [&](int t) {
+  auto fetch = [&](int t, int buf) {
     if (t < T) {
       const int n1 = n2 * a.G + g0 + t / nblk;
       const int i0 = (bs_lo + t % nblk) * BR;
-      const bf16* Qg = static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn;
-      const bf16* Yg = static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn;
-#pragma unroll
-      for (int u = 0; u < NQC; ++u) {
-        const int c = gt + 256 * u, rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-        bf16x8 val = {};
-        if (i0 + rr < s1) val = *reinterpret_cast<const bf16x8*>(Qg + (int64_t)(i0 + rr) * a.q_ss + cc);
-        pq[u] = val;
-      }
-#pragma unroll
-      for (int u = 0; u < NYC; ++u) {
-        const int c = gt + 256 * u, rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
-        bf16x8 val = {};
-        if (i0 + rr < s1) val = *reinterpret_cast<const bf16x8*>(Yg + (int64_t)(i0 + rr) * a.o_ss + cc);
-        py[u] = val;
-      }
+      const bf16* Qg = static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn + (int64_t)i0 * a.q_ss;
+      const bf16* Yg = static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i0 * a.o_ss;
+      async_tile_load<HD, BR, 4>(Qs[qg][buf], Qg, a.q_ss, s1 - i0, kw, lane);
+      async_tile_load<HDV, BR, 4>(Ys[qg][buf], Yg, a.o_ss, s1 - i0, kw, lane);
       if (gt < BR) {
         const int i = i0 + gt;
         pl = __builtin_inff();
@@ -291,7 +331,7 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
       }
     }
   };
-  fetch(qg);
+  fetch(qg, 0);
 
   floatx16 dKr[NKB][NBK], dVr[NKB][NBV];
 #pragma unroll
@@ -318,23 +358,14 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
     int i0 = 0;
     if (valid) {
       i0 = (bs_lo + t % nblk) * BR;
-#pragma unroll
-      for (int u = 0; u < NQC; ++u) {
-        const int c = gt + 256 * u, rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&Qs[qg][buf][swz<HD, BR>(rr, cc)]) = pq[u];
-      }
-#pragma unroll
-      for (int u = 0; u < NYC; ++u) {
-        const int c = gt + 256 * u, rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&Ys[qg][buf][swz<HDV, BR>(rr, cc)]) = py[u];
-      }
       if (gt < BR) {
         lse_s[qg][buf][gt] = pl;
         sfm_s[qg][buf][gt] = pf;
       }
     }
-    fetch(t + QG);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's async copies landed
+    __syncthreads();                                    // ... and everyone else's
+    fetch(t + QG, buf ^ 1);
     if (!valid) continue;
 
     // S = Q K^T and dP = dY V^T for this wavefront's KPW keys
@@ -475,8 +506,8 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   constexpr int NKQ = HD / 16;
   constexpr int NKV = HDV / 16;
   constexpr int NBK = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[DQ_BK * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[DQ_BK * HDV];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][DQ_BK * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][DQ_BK * HDV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   // job -> (query tile, query head, sequence); the query tile varies slowest
@@ -502,6 +533,19 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   const bf16* __restrict__ Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
   const bf16* __restrict__ Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn;
 
+  // keys that any row of [i0, i0 + DQ_BQ) can see
+  const int i_last = min(i0 + DQ_BQ, s1) - 1;
+  int j_lo = 0, j_hi = s2;
+  if (wl >= 0) j_lo = max(0, i0 + off - wl);
+  if (wr >= 0) j_hi = min(s2, i_last + off + wr + 1);
+  const int jb0 = (j_lo / DQ_BK) * DQ_BK;
+  const int nsteps = j_hi > j_lo ? (j_hi - jb0 + DQ_BK - 1) / DQ_BK : 0;
+
+  if (nsteps > 0) {
+    async_tile_load<HD, DQ_BK, 4>(Ks[0], Kg + (int64_t)jb0 * a.k_ss, a.k_ss, s2 - jb0, wave, lane);
+    async_tile_load<HDV, DQ_BK, 4>(Vs[0], Vg + (int64_t)jb0 * a.v_ss, a.v_ss, s2 - jb0, wave, lane);
+  }
+
   bf16x8 qf[NKQ], yf[NKV];  // B operands: query row iq, dims 16*kk + 8*hi + 0..7
 #pragma unroll
   for (int kk = 0; kk < NKQ; ++kk) {
@@ -522,33 +566,27 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     sf = a.sfmg[sb.lbase + (int64_t)n1 * a.l_sn + iq];
   }
 
-  const int i_last = min(i0 + DQ_BQ, s1) - 1;
-  int j_lo = 0, j_hi = s2;
-  if (wl >= 0) j_lo = max(0, i0 + off - wl);
-  if (wr >= 0) j_hi = min(s2, i_last + off + wr + 1);
-
-  const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
+  SwzTile<HD, DQ_BK> kadr;
+  SwzTile<HDV, DQ_BK> vadr;
+  kadr.init(lane);
+  vadr.init(lane);
 
   floatx16 dq[NBK];
 #pragma unroll
   for (int nb = 0; nb < NBK; ++nb) dq[nb] = floatx16{};
 
-  for (int j0 = (j_lo / DQ_BK) * DQ_BK; j0 < j_hi; j0 += DQ_BK) {
+  for (int st = 0; st < nsteps; ++st) {
+    const int j0 = jb0 + st * DQ_BK;
+    const int buf = st & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int c = tid; c < DQ_BK * (HD / 8); c += 256) {
-      const int rr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-      bf16x8 val = {};
-      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Kg + (int64_t)(j0 + rr) * a.k_ss + cc);
-      *reinterpret_cast<bf16x8*>(&Ks[swz<HD, DQ_BK>(rr, cc)]) = val;
+    if (st + 1 < nsteps) {  // next block into the other buffer while this one is used
+      const int jn = j0 + DQ_BK;
+      async_tile_load<HD, DQ_BK, 4>(Ks[buf ^ 1], Kg + (int64_t)jn * a.k_ss, a.k_ss, s2 - jn, wave, lane);
+      async_tile_load<HDV, DQ_BK, 4>(Vs[buf ^ 1], Vg + (int64_t)jn * a.v_ss, a.v_ss, s2 - jn, wave, lane);
     }
-    for (int c = tid; c < DQ_BK * (HDV / 8); c += 256) {
-      const int rr = c / (HDV / 8), cc = (c % (HDV / 8)) * 8;
-      bf16x8 val = {};
-      if (j0 + rr < s2) val = *reinterpret_cast<const bf16x8*>(Vg + (int64_t)(j0 + rr) * a.v_ss + cc);
-      *reinterpret_cast<bf16x8*>(&Vs[swz<HDV, DQ_BK>(rr, cc)]) = val;
-    }
-    __syncthreads();
+    const bf16* Kb = Ks[buf];
+    const bf16* Vb = Vs[buf];
 
     // S^T and dP^T for 64 keys (2 blocks of 32) x this wavefront's 32 rows
     floatx16 s[2], dp[2];
@@ -557,15 +595,11 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
       s[mb] = floatx16{};
       dp[mb] = floatx16{};
 #pragma unroll
-      for (int kk = 0; kk < NKQ; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[swz<HD, DQ_BK>(mb * 32 + l32, 16 * kk + 8 * hi)]);
-        s[mb] = mfma32(ka, qf[kk], s[mb]);
-      }
+      for (int kk = 0; kk < NKQ; ++kk)
+        s[mb] = mfma32(lds_row16(Kb, kadr.row_read_at(kk, mb * 32)), qf[kk], s[mb]);
 #pragma unroll
-      for (int kk = 0; kk < NKV; ++kk) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[swz<HDV, DQ_BK>(mb * 32 + l32, 16 * kk + 8 * hi)]);
-        dp[mb] = mfma32(va, yf[kk], dp[mb]);
-      }
+      for (int kk = 0; kk < NKV; ++kk)
+        dp[mb] = mfma32(lds_row16(Vb, vadr.row_read_at(kk, mb * 32)), yf[kk], dp[mb]);
     }
     const bool full = (i0 + DQ_BQ <= s1) && (j0 + DQ_BK <= s2) &&
                       (wr < 0 || j0 + DQ_BK - 1 <= i0 + off + wr) &&
@@ -589,8 +623,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
-        const bf16x8 kb = join(lds_tr(&Ks[swz<HD, DQ_BK>(16 * kc + tr_r4, nb * 32 + tr_c)]),
-                               lds_tr(&Ks[swz<HD, DQ_BK>(16 * kc + 8 + tr_r4, nb * 32 + tr_c)]));
+        const bf16x8 kb = join(lds_tr_at(Kb, kadr.tr_read(kc, 0, nb)), lds_tr_at(Kb, kadr.tr_read(kc, 1, nb)));
         dq[nb] = mfma32(da[kc], kb, dq[nb]);
       }
     }

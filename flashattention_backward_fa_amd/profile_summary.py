@@ -1,0 +1,85 @@
+"""Summaries of rocprofv3 CSV output for profiles/ (measurement tooling).
+
+    python -m flashattention_backward_fa_amd.profile_summary traffic \
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
+        --kernels dkdv_kernel,dq_kernel --workload gqa_causal --out FILE
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernels are scaled
+by what the same counters read for a plain device copy of known size (bench.py
+--copy-calibration: 256 MiB read and written per launch) and written out with
+the hash of the kernel source they were taken from; bench.py reports the
+traffic only while that hash matches the current source.
+"""
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc", "fa_bwd_det_kernels.hip")
+COPY_BYTES = 256 << 20
+
+
+def _rows(d):
+    path = os.path.join(d, "run_counter_collection.csv")
+    return list(csv.DictReader(open(path)))
+
+
+def _per_dispatch(d, counter, match):
+    vals = {}
+    for r in _rows(d):
+        if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+            vals.setdefault(int(r["Dispatch_Id"]), 0.0)
+            vals[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def traffic(args):
+    names = args.kernels.split(",")
+    cf = statistics.median(_per_dispatch(args.copy_fetch, "FETCH_SIZE", lambda n: "copyBuffer" in n))
+    cw = statistics.median(_per_dispatch(args.copy_write, "WRITE_SIZE", lambda n: "copyBuffer" in n))
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    lines = []
+    total = 0.0
+    for n in names:
+        f = statistics.median(_per_dispatch(args.fetch, "FETCH_SIZE", lambda k, n=n: n in k))
+        w = statistics.median(_per_dispatch(args.write, "WRITE_SIZE", lambda k, n=n: n in k))
+        fb, wb = f * 1024.0 * f_scale, w * 1024.0 * w_scale
+        total += fb + wb
+        lines.append(f"# {n}: FETCH_SIZE {f:.0f} KiB -> {fb / 2**20:.1f} MiB, WRITE_SIZE {w:.0f} KiB -> {wb / 2**20:.1f} MiB")
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    out = [
+        f"# HBM traffic per launch of {'+'.join(names)}, workload {args.workload}",
+        f"# command: {args.command}",
+        f"# calibration: copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE {cf:.0f} KiB (scale {f_scale:.3f}),",
+        f"#   WRITE_SIZE {cw:.0f} KiB (scale {w_scale:.3f})",
+        *lines,
+        f"kernel_source_sha256_16: {src_hash}",
+        f"hbm_bytes_per_launch: {total:.0f}",
+    ]
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernels", "--workload"):
+        t.add_argument(k, required=True)
+    t.add_argument("--out")
+    t.add_argument("--command", default="(see profiles/README.md)")
+    args = ap.parse_args()
+    if args.cmd == "traffic":
+        traffic(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -394,30 +394,59 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
       }
     }
 
-    // P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), packed as bf16 A operands
+    // P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), packed as bf16 A operands.
+    // A tile that every (row, key) pair sees takes the unmasked path; otherwise
+    // row i is kept iff it lies in [vis_lo, vis_hi] of the lane's key (one
+    // unsigned compare per element, no branches).
     const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
                       (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
     bf16x8 pa[NKB][2], da[NKB][2];
+    if (full) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int ib = r4 * 8 + hi * 4;
-      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[qg][buf][ib]);
-      const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][buf][ib]);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ib = r4 * 8 + hi * 4;
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[qg][buf][ib]);
+        const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][buf][ib]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rg = r4 * 4 + e;
+            const float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+            pa[kb][rg >> 3][rg & 7] = (bf16)p;
+            da[kb][rg >> 3][rg & 7] = (bf16)(p * (pacc[kb][rg] - f4[e]));
+          }
+        }
+      }
+    } else {
+      unsigned vlo[NKB], vspan[NKB];  // visible rows of this lane's key, relative to i0
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int jk = j0 + kw0 + kb * 32 + l32;
+        int lo = (wr >= 0) ? jk - off - wr : 0;
+        int hi_r = (wl >= 0) ? jk - off + wl : s1 - 1;
+        lo = max(lo, 0);
+        hi_r = min(hi_r, s1 - 1);
+        if (jk >= s2) hi_r = lo - 1;
+        vlo[kb] = (unsigned)(lo - i0);
+        vspan[kb] = (unsigned)(hi_r - lo);  // huge when empty: nothing passes
+        if (hi_r < lo) { vlo[kb] = 0x7fffffffu; vspan[kb] = 0; }
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rg = r4 * 4 + e;
-          float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
-          if (!full) {
-            const int i = i0 + ib + e;
-            const bool vis = (i < s1) && (jk < s2) && (wl < 0 || jk >= i + off - wl) && (wr < 0 || jk <= i + off + wr);
-            p = vis ? p : 0.f;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ib = r4 * 8 + hi * 4;
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[qg][buf][ib]);
+        const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][buf][ib]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rg = r4 * 4 + e;
+            float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+            p = ((unsigned)(ib + e) - vlo[kb] <= vspan[kb]) ? p : 0.f;
+            pa[kb][rg >> 3][rg & 7] = (bf16)p;
+            da[kb][rg >> 3][rg & 7] = (bf16)(p * (pacc[kb][rg] - f4[e]));
           }
-          const float ds = p * (pacc[kb][rg] - f4[e]);
-          pa[kb][rg >> 3][rg & 7] = (bf16)p;
-          da[kb][rg >> 3][rg & 7] = (bf16)ds;
         }
       }
     }
@@ -588,43 +617,53 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     const bf16* Kb = Ks[buf];
     const bf16* Vb = Vs[buf];
 
-    // S^T and dP^T for 64 keys (2 blocks of 32) x this wavefront's 32 rows
-    floatx16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = floatx16{};
-      dp[mb] = floatx16{};
-#pragma unroll
-      for (int kk = 0; kk < NKQ; ++kk)
-        s[mb] = mfma32(lds_row16(Kb, kadr.row_read_at(kk, mb * 32)), qf[kk], s[mb]);
-#pragma unroll
-      for (int kk = 0; kk < NKV; ++kk)
-        dp[mb] = mfma32(lds_row16(Vb, vadr.row_read_at(kk, mb * 32)), yf[kk], dp[mb]);
-    }
     const bool full = (i0 + DQ_BQ <= s1) && (j0 + DQ_BK <= s2) &&
                       (wr < 0 || j0 + DQ_BK - 1 <= i0 + off + wr) &&
                       (wl < 0 || j0 >= i0 + DQ_BQ - 1 + off - wl);
-    bf16x8 da[4];
+    // keys visible to this lane's row, relative to j0 (used on partial tiles):
+    // one unsigned compare per element
+    unsigned klo = 0, kspan = 0xffffffffu;
+    if (!full) {
+      int lo = (wl >= 0) ? iq + off - wl : 0;
+      int hi_k = (wr >= 0) ? iq + off + wr : s2 - 1;
+      lo = max(lo, 0);
+      hi_k = min(hi_k, s2 - 1);
+      klo = (unsigned)(lo - j0);
+      kspan = (unsigned)(hi_k - lo);
+      if (iq >= s1 || hi_k < lo) { klo = 0x7fffffffu; kspan = 0; }
+    }
+    // two halves of 32 keys: S^T, dP^T, dS, then dQ += dS K for that half
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      floatx16 s = {}, dp = {};
 #pragma unroll
-      for (int rg = 0; rg < 16; ++rg) {
-        float p = __builtin_amdgcn_exp2f(s[mb][rg] * a.scale_log2 - l2);
-        if (!full) {
-          const int j = j0 + mb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
-          const bool vis = (iq < s1) && (j < s2) && (wl < 0 || j >= iq + off - wl) && (wr < 0 || j <= iq + off + wr);
-          p = vis ? p : 0.f;
+      for (int kk = 0; kk < NKQ; ++kk) s = mfma32(lds_row16(Kb, kadr.row_read_at(kk, mb * 32)), qf[kk], s);
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) dp = mfma32(lds_row16(Vb, vadr.row_read_at(kk, mb * 32)), yf[kk], dp);
+      bf16x8 da[2];
+      if (full) {
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+          const float p = __builtin_amdgcn_exp2f(s[rg] * a.scale_log2 - l2);
+          da[rg >> 3][rg & 7] = (bf16)(p * (dp[rg] - sf));
         }
-        da[mb * 2 + (rg >> 3)][rg & 7] = (bf16)(p * (dp[mb][rg] - sf));
+      } else {
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+          const int jj = mb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+          float p = __builtin_amdgcn_exp2f(s[rg] * a.scale_log2 - l2);
+          p = ((unsigned)jj - klo <= kspan) ? p : 0.f;
+          da[rg >> 3][rg & 7] = (bf16)(p * (dp[rg] - sf));
+        }
       }
-    }
-    // dQ += dS K over 4 chunks of 16 keys
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+      for (int c = 0; c < 2; ++c) {
+        const int kc = mb * 2 + c;
 #pragma unroll
-      for (int nb = 0; nb < NBK; ++nb) {
-        const bf16x8 kb = join(lds_tr_at(Kb, kadr.tr_read(kc, 0, nb)), lds_tr_at(Kb, kadr.tr_read(kc, 1, nb)));
-        dq[nb] = mfma32(da[kc], kb, dq[nb]);
+        for (int nb = 0; nb < NBK; ++nb) {
+          const bf16x8 kb = join(lds_tr_at(Kb, kadr.tr_read(kc, 0, nb)), lds_tr_at(Kb, kadr.tr_read(kc, 1, nb)));
+          dq[nb] = mfma32(da[c], kb, dq[nb]);
+        }
       }
     }
   }

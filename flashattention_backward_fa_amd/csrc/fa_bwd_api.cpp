@@ -125,6 +125,12 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
       a.l_sb = 0; a.l_sn = d.T1;
       break;
   }
+  // The kernels address a tile of up to 128 rows by 32-bit byte offsets from
+  // its first row: the distance between consecutive rows of q, k, v, dout
+  // must stay below 2^23 elements.
+  constexpr int64_t kMaxRowStride = int64_t(1) << 23;
+  if (a.q_ss >= kMaxRowStride || a.k_ss >= kMaxRowStride || a.v_ss >= kMaxRowStride || a.o_ss >= kMaxRowStride)
+    return FA_ERR_SHAPE;
   const double scale = d.softmax_scale != 0.0f ? (double)d.softmax_scale : 1.0 / std::sqrt((double)d.D);
   a.scale = (float)scale;
   a.scale_log2 = (float)(scale * 1.4426950408889634);

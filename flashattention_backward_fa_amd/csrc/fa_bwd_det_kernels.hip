@@ -115,25 +115,38 @@ __device__ __forceinline__ SeqBounds seq_bounds(const KernelArgs& a, int b) {
   return r;
 }
 
-// Per-lane byte addresses of a swizzled tile block of width W (128 or 64
-// columns), computed once: a 16-byte row read of (row l32, column 16*kk+8*hi)
-// is at a_base ^ (kk*32); a transposing read of rows 16*kc + 8*s + tr_r4,
-// columns nb*32 + tr_c is at (t_base[s] ^ (nb*64)) + kc*16*W*2.  Both equal
-// the swz() offsets (the XOR acts on bits that the other terms leave clear).
+// LDS addressing.  LDS addresses are 32-bit byte offsets; reads go through
+// them directly, so that per-lane parts are computed once and the rest (tile
+// buffer, k-step) lands in the instructions' immediate offsets.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t) reinterpret_cast<uintptr_t>((LDS_AS const void*)p);
+}
+__device__ __forceinline__ bf16x8 lds_load16(uint32_t addr) { return *(LDS_AS const bf16x8*)(uintptr_t)addr; }
+__device__ __forceinline__ shortx4 lds_load_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(uintptr_t)addr);
+}
+
+// Per-lane LDS byte addresses of a swizzled tile block of width W (128 or 64
+// columns) starting at LDS address blk (a multiple of 512), computed once: a
+// 16-byte row read of (row l32, column 16*kk+8*hi) is at a_base ^ (kk*32); a
+// transposing read of rows 16*kc + 8*s + tr_r4, columns nb*32 + tr_c is at
+// (t_base[s] ^ (nb*64)) + kc*16*W*2.  Both equal blk + the swz() offsets (the
+// XOR acts on bits 5..7 that the other terms leave clear or, for blk, do not
+// carry into).
 template <int W>
 struct SwzBlock {
-  int a_base;
-  int t_base[2];
-  __device__ __forceinline__ void init(int blk_byte_off, int lane) {
+  uint32_t a_base;
+  uint32_t t_base[2];
+  __device__ __forceinline__ void init(uint32_t blk, int lane) {
     const int l32 = lane & 31, hi = lane >> 5;
     const int f = (W == 128) ? (((l32 & 3) << 2) | ((l32 >> 2) & 3)) : ((((l32 >> 1) & 1) << 2) | ((l32 >> 2) & 3));
-    a_base = (blk_byte_off + l32 * W * 2 + 16 * (hi ^ (f & 1))) | ((f >> 1) << 5);
+    a_base = (blk + l32 * W * 2 + 16 * (hi ^ (f & 1))) | ((f >> 1) << 5);
     const int q = (W == 128) ? ((lane & 15) >> 2) : ((lane >> 3) & 1);
     const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
     const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      t_base[s] = (blk_byte_off + tr_r4 * W * 2 + 8 * (lane & 1) + s * 8 * W * 2 + 16 * (cl ^ ((2 * s + hi) & 3))) | (q << 6);
+      t_base[s] = (blk + tr_r4 * W * 2 + 8 * (lane & 1) + s * 8 * W * 2 + 16 * (cl ^ ((2 * s + hi) & 3))) | (q << 6);
   }
 };
 
@@ -143,93 +156,147 @@ struct SwzTile {
   static constexpr int W0 = COLS == 64 ? 64 : 128;
   SwzBlock<W0> b0;
   SwzBlock<64> b1;  // second block of a 192-column tile
-  __device__ __forceinline__ void init(int lane) {
-    b0.init(0, lane);
-    if constexpr (COLS == 192) b1.init(ROWS * 128 * 2, lane);
+  __device__ __forceinline__ void init(uint32_t tile, int lane) {
+    b0.init(tile, lane);
+    if constexpr (COLS == 192) b1.init(tile + ROWS * 128 * 2, lane);
   }
-  // byte offset of the 16-byte row read for k-step kk (columns 16*kk + 8*hi)
-  __device__ __forceinline__ int row_read(int kk) const {
-    if constexpr (COLS == 192) return kk < 8 ? (b0.a_base ^ (kk * 32)) : (b1.a_base ^ ((kk - 8) * 32));
-    else return b0.a_base ^ (kk * 32);
+  // LDS address of the 16-byte row read for k-step kk (columns 16*kk + 8*hi)
+  // of the tile copy boff bytes further on (boff a multiple of 512)
+  __device__ __forceinline__ uint32_t row_read(int kk, uint32_t boff = 0) const {
+    if constexpr (COLS == 192) return kk < 8 ? ((b0.a_base + boff) ^ (kk * 32)) : ((b1.a_base + boff) ^ ((kk - 8) * 32));
+    else return (b0.a_base + boff) ^ (kk * 32);
   }
   // the same for rows r0 + l32 (r0 a multiple of 16)
-  __device__ __forceinline__ int row_read_at(int kk, int r0) const {
-    if constexpr (COLS == 192) return kk < 8 ? (b0.a_base ^ (kk * 32)) + r0 * 256 : (b1.a_base ^ ((kk - 8) * 32)) + r0 * 128;
-    else return (b0.a_base ^ (kk * 32)) + r0 * W0 * 2;
+  __device__ __forceinline__ uint32_t row_read_at(int kk, int r0, uint32_t boff = 0) const {
+    if constexpr (COLS == 192) return kk < 8 ? row_read(kk, boff) + r0 * 256 : row_read(kk, boff) + r0 * 128;
+    else return row_read(kk, boff) + r0 * W0 * 2;
   }
-  // byte offset of the transposing read for row chunk kc, half s, column block nb
-  __device__ __forceinline__ int tr_read(int kc, int s, int nb) const {
+  // LDS address of the transposing read for row chunk kc, half s, column block nb
+  __device__ __forceinline__ uint32_t tr_read(int kc, int s, int nb, uint32_t boff = 0) const {
     if constexpr (COLS == 192) {
-      return nb < 4 ? ((b0.t_base[s] ^ (nb * 64)) + kc * 16 * 128 * 2) : ((b1.t_base[s] ^ ((nb - 4) * 64)) + kc * 16 * 64 * 2);
+      return nb < 4 ? (((b0.t_base[s] + boff) ^ (nb * 64)) + kc * 16 * 128 * 2)
+                    : (((b1.t_base[s] + boff) ^ ((nb - 4) * 64)) + kc * 16 * 64 * 2);
     } else {
-      return (b0.t_base[s] ^ (nb * 64)) + kc * 16 * W0 * 2;
+      return ((b0.t_base[s] + boff) ^ (nb * 64)) + kc * 16 * W0 * 2;
     }
   }
 };
 
-__device__ __forceinline__ bf16x8 lds_row16(const bf16* base, int byte_off) {
-  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
-}
-__device__ __forceinline__ shortx4 lds_tr_at(const bf16* base, int byte_off) {
-  return lds_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off));
+// Workgroup barrier for LDS-only hand-offs: waits for this wavefront's own LDS
+// operations, then s_barrier.  Unlike __syncthreads it does not drain
+// outstanding global loads (the compiler's release fence would), so a
+// prefetch issued before it stays in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(0) as the compiler's own instruction (gfx9 encoding: vmcnt
+// 0, expcnt 7, lgkmcnt 15), so that its wait insertion knows that every
+// earlier global load has completed and adds no wait of its own later.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
 }
 
-// Asynchronous copy of rows [0, ROWS) of a COLS-wide bf16 tile from global
-// memory (row r at g + min(r, nvalid-1)*ld; rows past the end repeat the last
-// valid row, which the masks then ignore) into a swizzled LDS tile with
-// global_load_lds_dwordx4: each instruction fills 1 KB of LDS, lane t writing
-// bytes 16t..16t+15, so each lane loads the logical chunk that the swizzle
-// puts in its slot.  The NW wavefronts of the workgroup share the
-// instructions.  Completion: s_waitcnt vmcnt(0) then a barrier.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
+// One global_load_lds_dwordx4: lane t copies the 16 bytes at base + voff (base
+// the same in all lanes, voff the lane's byte offset) to LDS byte lds + 16t
+// (lds the same in all lanes).
+// Issued as inline assembly so that the compiler's wait insertion does not see
+// a pending LDS write: it would otherwise wait for every such copy before each
+// later LDS read, whichever buffer the read targets, and a prefetch into the
+// other half of a double buffer would stall the reads of the current half.
+// Completion is therefore always awaited explicitly: s_waitcnt vmcnt(0), then
+// a barrier.  M0 is set here and used by nothing else in these kernels.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
+               "s"(m0)
+               : "memory");
+}
+
+// Asynchronous copy of rows [0, ROWS) of a W-column block (columns col0 ..
+// col0+W-1 of the source rows) into a swizzled LDS block: each instruction
+// fills 1 KB of LDS, lane t writing bytes 16t..16t+15, so each lane loads the
+// logical chunk that the swizzle puts in its slot.  Source row r is at
+// g + r*ldb bytes; rows at or past nvalid repeat row nvalid-1 (the masks
+// ignore them).  The NW wavefronts of a group share the NI instructions; the
+// lane offsets of full tiles are kept from init().
 template <int W>
 __device__ __forceinline__ int swz_f(int r) {
   return (W == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 template <int W, int ROWS, int NW>
-__device__ __forceinline__ void async_block_load(bf16* lds_blk, const bf16* g, int col0, int64_t ld, int nvalid,
-                                                 int wave, int lane) {
-  constexpr int RPI = 1024 / (W * 2);  // rows per instruction
-  constexpr int CPR = W / 8;           // chunks per row
-  constexpr int NI = ROWS / RPI;
-#pragma unroll
-  for (int u = wave; u < NI; u += NW) {
+struct BlockCopy {
+  static constexpr int RPI = 1024 / (W * 2);  // rows per instruction
+  static constexpr int CPR = W / 8;           // chunks per row
+  static constexpr int NI = ROWS / RPI;
+  static_assert(NI % NW == 0, "whole instructions per wavefront");
+  static constexpr int PER = NI / NW;
+  // Instruction wave + x*NW covers rows x*NW*RPI further down than
+  // instruction wave, a multiple of the swizzle's 16-row period: for full
+  // tiles one lane offset serves all x, the rest goes to the scalar base.
+  static_assert((NW * RPI) % 16 == 0, "swizzle period");
+  uint32_t voff;
+  __device__ __forceinline__ static uint32_t lane_off(int u, int lane, int ldb, int col0, int nvalid) {
     const int row = u * RPI + lane / CPR;
-    const int logical = (lane % CPR) ^ swz_f<W>(row);
-    const int rs = min(row, nvalid - 1);
-    const bf16* src = g + (int64_t)rs * ld + col0 + logical * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_blk + u * 512), 16, 0, 0);
+    const int chunk = (lane % CPR) ^ swz_f<W>(row);
+    return (uint32_t)(min(row, nvalid - 1) * ldb + col0 * 2 + chunk * 16);
   }
-}
+  __device__ __forceinline__ void init(int wave, int lane, int ldb, int col0) {
+    voff = lane_off(wave, lane, ldb, col0, ROWS);
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_blk, const void* g, int ldb, int col0, int nvalid, int wave,
+                                        int lane) const {
+    const char* gb = static_cast<const char*>(g);
+    if (nvalid >= ROWS) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) dma16(gb + (int64_t)x * NW * RPI * ldb, voff, lds_blk + (wave + x * NW) * 1024);
+    } else {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int u = wave + x * NW;
+        dma16(gb, lane_off(u, lane, ldb, col0, nvalid), lds_blk + u * 1024);
+      }
+    }
+  }
+};
 
+// A swizzled tile of COLS (64, 128 or 192 = 128 + 64) columns.
 template <int COLS, int ROWS, int NW>
-__device__ __forceinline__ void async_tile_load(bf16* lds_tile, const bf16* g, int64_t ld, int nvalid, int wave,
-                                                int lane) {
-  if constexpr (COLS == 192) {
-    async_block_load<128, ROWS, NW>(lds_tile, g, 0, ld, nvalid, wave, lane);
-    async_block_load<64, ROWS, NW>(lds_tile + ROWS * 128, g, 128, ld, nvalid, wave, lane);
-  } else {
-    async_block_load<COLS, ROWS, NW>(lds_tile, g, 0, ld, nvalid, wave, lane);
+struct TileCopy {
+  BlockCopy<COLS == 64 ? 64 : 128, ROWS, NW> c0;
+  BlockCopy<64, ROWS, NW> c1;  // second block of a 192-column tile
+  int ldb;
+  __device__ __forceinline__ void init(int wave, int lane, int ld_bytes) {
+    ldb = ld_bytes;
+    c0.init(wave, lane, ldb, 0);
+    if constexpr (COLS == 192) c1.init(wave, lane, ldb, 128);
   }
-}
+  __device__ __forceinline__ void issue(uint32_t lds_tile, const void* g, int nvalid, int wave, int lane) const {
+    c0.issue(lds_tile, g, ldb, 0, nvalid, wave, lane);
+    if constexpr (COLS == 192) c1.issue(lds_tile + ROWS * 128 * 2, g, ldb, 128, nvalid, wave, lane);
+  }
+};
 
 // The same into a padded tile (row pitch COLS + 8 elements, 16-byte row reads
 // only): ROWS*(COLS/8 + 1) 16-byte slots, a multiple of 64 for ROWS % 64 == 0;
 // a lane whose slot is the pad loads a valid dummy chunk.
 template <int COLS, int ROWS, int NW>
-__device__ __forceinline__ void async_padded_load(bf16* lds_tile, const bf16* g, int64_t ld, int nvalid, int wave,
-                                                  int lane) {
+__device__ __forceinline__ void padded_copy(uint32_t lds_tile, const void* g, int ldb, int nvalid, int wave, int lane) {
   constexpr int PC = COLS / 8 + 1;  // 16-byte slots per padded row
   constexpr int NI = ROWS * PC / 64;
   static_assert(NI * 64 == ROWS * PC, "whole instructions");
-#pragma unroll
   for (int u = wave; u < NI; u += NW) {
     const int slot = u * 64 + lane;
     const int row = slot / PC;
     const int ch = slot % PC;
-    const int rs = min(row, nvalid - 1);
-    const bf16* src = g + (int64_t)rs * ld + (ch < COLS / 8 ? ch * 8 : 0);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_tile + u * 512), 16, 0, 0);
+    dma16(g, (uint32_t)(min(row, nvalid - 1) * ldb + (ch < COLS / 8 ? ch * 16 : 0)), lds_tile + u * 1024);
   }
 }
 
@@ -242,7 +309,6 @@ __device__ __forceinline__ void async_padded_load(bf16* lds_tile, const bf16* g,
 // only); Q/dY tiles are swizzled (row reads and transposing reads).
 template <int HD, int HDV, int KPW, int QG>
 __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
-  constexpr int NT = 256 * QG;        // threads
   constexpr int BC = 4 * KPW;         // keys per workgroup
   constexpr int NKB = KPW / 32;       // 32-key blocks per wavefront
   constexpr int BR = 32;              // query rows per step and group
@@ -252,20 +318,21 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   constexpr int NKV = HDV / 16;
   constexpr int NBK = HD / 32;
   constexpr int NBV = HDV / 32;
+  constexpr int QTB = BR * HD * 2;    // bytes of one Q / dY tile buffer
+  constexpr int YTB = BR * HDV * 2;
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BC * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BC * VP];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[QG][2][BR * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Ys[QG][2][BR * HDV];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[BC * KP];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[BC * VP];
+  __shared__ __attribute__((aligned(1024))) bf16 Qs[QG][2][BR * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Ys[QG][2][BR * HDV];
   __shared__ __attribute__((aligned(16))) float lse_s[QG][2][BR];
   __shared__ __attribute__((aligned(16))) float sfm_s[QG][2][BR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave >> 2;      // query group
   const int kw = wave & 3;       // key slice
-  const int gt = tid & 255;      // thread within the group
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -289,12 +356,11 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int off = s2 - s1;
   const int wl = a.win_left, wr = a.win_right;
 
-  {  // K and V tiles, asynchronously (rows past the sequence end repeat its last key)
-    const bf16* Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j0 * a.k_ss;
-    const bf16* Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j0 * a.v_ss;
-    async_padded_load<HD, BC, 4 * QG>(Ks, Kg, a.k_ss, s2 - j0, wave, lane);
-    async_padded_load<HDV, BC, 4 * QG>(Vs, Vg, a.v_ss, s2 - j0, wave, lane);
-  }
+  // K and V tiles, asynchronously (rows past the sequence end repeat its last key)
+  padded_copy<HD, BC, 4 * QG>(lds_addr(Ks), static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j0 * a.k_ss,
+                              (int)a.k_ss * 2, s2 - j0, wave, lane);
+  padded_copy<HDV, BC, 4 * QG>(lds_addr(Vs), static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j0 * a.v_ss,
+                               (int)a.v_ss * 2, s2 - j0, wave, lane);
 
   // query blocks that see a key of [j0, j1); this job takes split qs of them
   int i_lo = 0, i_hi = s1;
@@ -305,33 +371,50 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int bs_lo = blk0 + (int)((int64_t)nblk_all * qs / QS);
   const int bs_hi = blk0 + (int)((int64_t)nblk_all * (qs + 1) / QS);
   const int nblk = bs_hi - bs_lo;
-  const int T = hpj * nblk;
+  const int T = hpj * nblk;  // items: (query head, query block) pairs
   const int g0 = hslot * hpj;
 
-  // Q/dY tiles of item t of this group go straight to LDS (async); lse and
-  // sfmg of its rows go through registers
-  float pl = __builtin_inff(), pf = 0.f;
-  auto fetch = [&](int t, int buf) {
+  // Item t = it*QG + qg of this group is query head g0 + t / nblk, block
+  // bs_lo + t % nblk; a cursor walks it without divisions.
+  struct Cursor { int h, blk; };
+  auto step_cursor = [&](Cursor& c, int n) {
+    c.blk += n;
+    while (c.blk >= nblk) { c.blk -= nblk; ++c.h; }
+  };
+
+  // Q/dY tiles of an item go straight to LDS (async); lse and sfmg of its rows
+  // go through registers of wavefront kw = 0, raw and loaded first, so that
+  // nothing waits for them before the tile itself is awaited.
+  TileCopy<HD, BR, 4> qcp;
+  TileCopy<HDV, BR, 4> ycp;
+  const uint32_t q_lds = lds_addr(Qs) + qg * 2 * QTB;  // this group's Q / dY buffers
+  const uint32_t y_lds = lds_addr(Ys) + qg * 2 * YTB;
+  qcp.init(kw, lane, (int)a.q_ss * 2);
+  ycp.init(kw, lane, (int)a.o_ss * 2);
+  float pl = 0.f, pf = 0.f;
+  auto fetch = [&](const Cursor& c, int t, int buf) {
     if (t < T) {
-      const int n1 = n2 * a.G + g0 + t / nblk;
-      const int i0 = (bs_lo + t % nblk) * BR;
-      const bf16* Qg = static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn + (int64_t)i0 * a.q_ss;
-      const bf16* Yg = static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i0 * a.o_ss;
-      async_tile_load<HD, BR, 4>(Qs[qg][buf], Qg, a.q_ss, s1 - i0, kw, lane);
-      async_tile_load<HDV, BR, 4>(Ys[qg][buf], Yg, a.o_ss, s1 - i0, kw, lane);
-      if (gt < BR) {
-        const int i = i0 + gt;
-        pl = __builtin_inff();
-        pf = 0.f;
-        if (i < s1) {
-          const float l = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + i];
-          pl = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;  // empty row -> P = 0
-          pf = a.sfmg[sb.lbase + (int64_t)n1 * a.l_sn + i];
-        }
+      const int n1 = n2 * a.G + g0 + c.h;
+      const int i0 = (bs_lo + c.blk) * BR;
+      if (kw == 0) {
+        const int64_t lrow = sb.lbase + (int64_t)n1 * a.l_sn + min(i0 + l32, s1 - 1);
+        pl = a.lse[lrow];
+        pf = a.sfmg[lrow];
       }
+      qcp.issue(q_lds + buf * QTB, static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn + (int64_t)i0 * a.q_ss,
+                s1 - i0, kw, lane);
+      ycp.issue(y_lds + buf * YTB, static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i0 * a.o_ss,
+                s1 - i0, kw, lane);
     }
   };
-  fetch(qg, 0);
+  // lse in base 2 for the rows of the block at i0; a row past the end or an
+  // empty row (lse = -inf) gets +inf, so that its P is 0
+  auto put_row_stats = [&](int i0, int buf) {
+    if (kw == 0 && lane < BR) {
+      lse_s[qg][buf][lane] = (i0 + lane >= s1 || pl == -__builtin_inff()) ? __builtin_inff() : pl * kLog2e;
+      sfm_s[qg][buf][lane] = pf;
+    }
+  };
 
   floatx16 dKr[NKB][NBK], dVr[NKB][NBV];
 #pragma unroll
@@ -344,32 +427,15 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
 
   SwzTile<HD, BR> qadr;
   SwzTile<HDV, BR> yadr;
-  qadr.init(lane);
-  yadr.init(lane);
+  qadr.init(q_lds, lane);
+  yadr.init(y_lds, lane);
   const int kw0 = kw * KPW;  // first key of this wavefront within the tile
+  const uint32_t k_lane = lds_addr(Ks) + ((kw0 + l32) * KP + 8 * hi) * 2;
+  const uint32_t v_lane = lds_addr(Vs) + ((kw0 + l32) * VP + 8 * hi) * 2;
 
-  const int iters = (T + QG - 1) / QG;
-  for (int it = 0; it < iters; ++it) {
-    const int t = it * QG + qg;
-    const bool valid = t < T;
-    const int buf = it & 1;
-    const bf16* Qb = Qs[qg][buf];
-    const bf16* Yb = Ys[qg][buf];
-    int i0 = 0;
-    if (valid) {
-      i0 = (bs_lo + t % nblk) * BR;
-      if (gt < BR) {
-        lse_s[qg][buf][gt] = pl;
-        sfm_s[qg][buf][gt] = pf;
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's async copies landed
-    __syncthreads();                                    // ... and everyone else's
-    fetch(t + QG, buf ^ 1);
-    if (!valid) continue;
-
-    // S = Q K^T and dP = dY V^T for this wavefront's KPW keys
-    floatx16 sacc[NKB], pacc[NKB];
+  floatx16 sacc[NKB], pacc[NKB];
+  // S = Q K^T and dP = dY V^T for this wavefront's KPW keys
+  auto phase_a = [&](int buf) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       sacc[kb] = floatx16{};
@@ -377,23 +443,19 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
     }
 #pragma unroll
     for (int kk = 0; kk < NKQ; ++kk) {
-      const bf16x8 qa = lds_row16(Qb, qadr.row_read(kk));
+      const bf16x8 qa = lds_load16(qadr.row_read(kk, buf * QTB));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&Ks[(kw0 + kb * 32 + l32) * KP + 16 * kk + 8 * hi]);
-        sacc[kb] = mfma32(qa, kv, sacc[kb]);
-      }
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32(qa, lds_load16(k_lane + (kb * 32 * KP + 16 * kk) * 2), sacc[kb]);
     }
 #pragma unroll
     for (int kk = 0; kk < NKV; ++kk) {
-      const bf16x8 ya = lds_row16(Yb, yadr.row_read(kk));
+      const bf16x8 ya = lds_load16(yadr.row_read(kk, buf * YTB));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(&Vs[(kw0 + kb * 32 + l32) * VP + 16 * kk + 8 * hi]);
-        pacc[kb] = mfma32(ya, vv, pacc[kb]);
-      }
+      for (int kb = 0; kb < NKB; ++kb) pacc[kb] = mfma32(ya, lds_load16(v_lane + (kb * 32 * VP + 16 * kk) * 2), pacc[kb]);
     }
-
+  };
+  // P, dS (masked when the tile is partial), then dV += P^T dY and dK += dS^T Q
+  auto phase_b = [&](int buf, int i0) {
     // P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), packed as bf16 A operands.
     // A tile that every (row, key) pair sees takes the unmasked path; otherwise
     // row i is kept iff it lies in [vis_lo, vis_hi] of the lane's key (one
@@ -456,18 +518,45 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
       for (int nb = 0; nb < NBV; ++nb) {
-        const bf16x8 yb = join(lds_tr_at(Yb, yadr.tr_read(kc, 0, nb)), lds_tr_at(Yb, yadr.tr_read(kc, 1, nb)));
+        const bf16x8 yb = join(lds_load_tr(yadr.tr_read(kc, 0, nb, buf * YTB)), lds_load_tr(yadr.tr_read(kc, 1, nb, buf * YTB)));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) dVr[kb][nb] = mfma32(pa[kb][kc], yb, dVr[kb][nb]);
       }
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
-        const bf16x8 qb = join(lds_tr_at(Qb, qadr.tr_read(kc, 0, nb)), lds_tr_at(Qb, qadr.tr_read(kc, 1, nb)));
+        const bf16x8 qb = join(lds_load_tr(qadr.tr_read(kc, 0, nb, buf * QTB)), lds_load_tr(qadr.tr_read(kc, 1, nb, buf * QTB)));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32(da[kb][kc], qb, dKr[kb][nb]);
       }
     }
+  };
+
+  // Step it: wait for item t's tile (buffer buf), prefetch item t + QG into
+  // the other buffer, compute item t.
+  const int iters = (T + QG - 1) / QG;
+  Cursor cc{0, qg}, cf{0, qg};  // item t being computed, item being fetched
+  if (nblk > 0) {
+    step_cursor(cc, 0);
+    step_cursor(cf, 0);
   }
+  fetch(cf, qg, 0);
+  if (nblk > 0) step_cursor(cf, QG);
+  auto step = [&](int it, int buf) {
+    const int t = it * QG + qg;
+    const int i0 = (bs_lo + cc.blk) * BR;
+    if (t < T) put_row_stats(i0, buf);
+    wait_vmem();    // this wavefront's copies of item t landed
+    lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
+    fetch(cf, t + QG, buf ^ 1);
+    step_cursor(cf, QG);
+    if (t < T) {
+      phase_a(buf);
+      phase_b(buf, i0);
+    }
+    step_cursor(cc, QG);
+  };
+  for (int it = 0; it < iters; ++it) step(it, it & 1);
+  wait_vmem();  // no copy may still be landing when LDS is reused below
 
   // ---- add the other groups' dK/dV into group 0, 32 columns at a time
   if constexpr (QG > 1) {
@@ -535,10 +624,13 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   constexpr int NKQ = HD / 16;
   constexpr int NKV = HDV / 16;
   constexpr int NBK = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][DQ_BK * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][DQ_BK * HDV];
+  constexpr int KTB = DQ_BK * HD * 2;  // bytes of one K / V tile buffer
+  constexpr int VTB = DQ_BK * HDV * 2;
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][DQ_BK * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][DQ_BK * HDV];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // job -> (query tile, query head, sequence); the query tile varies slowest
   // and counts down, so the causal tiles with the most keys start first
   const int per_tile = a.N1 * a.B;
@@ -570,10 +662,16 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   const int jb0 = (j_lo / DQ_BK) * DQ_BK;
   const int nsteps = j_hi > j_lo ? (j_hi - jb0 + DQ_BK - 1) / DQ_BK : 0;
 
-  if (nsteps > 0) {
-    async_tile_load<HD, DQ_BK, 4>(Ks[0], Kg + (int64_t)jb0 * a.k_ss, a.k_ss, s2 - jb0, wave, lane);
-    async_tile_load<HDV, DQ_BK, 4>(Vs[0], Vg + (int64_t)jb0 * a.v_ss, a.v_ss, s2 - jb0, wave, lane);
-  }
+  // K/V blocks go straight to LDS (async), double-buffered
+  TileCopy<HD, DQ_BK, 4> kcp;
+  TileCopy<HDV, DQ_BK, 4> vcp;
+  kcp.init(wave, lane, (int)a.k_ss * 2);
+  vcp.init(wave, lane, (int)a.v_ss * 2);
+  auto fetch = [&](int jb, int buf) {
+    kcp.issue(lds_addr(Ks) + buf * KTB, Kg + (int64_t)jb * a.k_ss, s2 - jb, wave, lane);
+    vcp.issue(lds_addr(Vs) + buf * VTB, Vg + (int64_t)jb * a.v_ss, s2 - jb, wave, lane);
+  };
+  if (nsteps > 0) fetch(jb0, 0);
 
   bf16x8 qf[NKQ], yf[NKV];  // B operands: query row iq, dims 16*kk + 8*hi + 0..7
 #pragma unroll
@@ -597,25 +695,20 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
 
   SwzTile<HD, DQ_BK> kadr;
   SwzTile<HDV, DQ_BK> vadr;
-  kadr.init(lane);
-  vadr.init(lane);
+  kadr.init(lds_addr(Ks), lane);
+  vadr.init(lds_addr(Vs), lane);
 
   floatx16 dq[NBK];
 #pragma unroll
   for (int nb = 0; nb < NBK; ++nb) dq[nb] = floatx16{};
 
-  for (int st = 0; st < nsteps; ++st) {
+  // Step st: wait for key block st (buffer buf), prefetch block st + 1 into the
+  // other buffer, compute.
+  auto step = [&](int st, int buf) {
     const int j0 = jb0 + st * DQ_BK;
-    const int buf = st & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (st + 1 < nsteps) {  // next block into the other buffer while this one is used
-      const int jn = j0 + DQ_BK;
-      async_tile_load<HD, DQ_BK, 4>(Ks[buf ^ 1], Kg + (int64_t)jn * a.k_ss, a.k_ss, s2 - jn, wave, lane);
-      async_tile_load<HDV, DQ_BK, 4>(Vs[buf ^ 1], Vg + (int64_t)jn * a.v_ss, a.v_ss, s2 - jn, wave, lane);
-    }
-    const bf16* Kb = Ks[buf];
-    const bf16* Vb = Vs[buf];
+    wait_vmem();    // this wavefront's copies of block st landed
+    lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
+    if (st + 1 < nsteps) fetch(j0 + DQ_BK, buf ^ 1);
 
     const bool full = (i0 + DQ_BQ <= s1) && (j0 + DQ_BK <= s2) &&
                       (wr < 0 || j0 + DQ_BK - 1 <= i0 + off + wr) &&
@@ -637,9 +730,9 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     for (int mb = 0; mb < 2; ++mb) {
       floatx16 s = {}, dp = {};
 #pragma unroll
-      for (int kk = 0; kk < NKQ; ++kk) s = mfma32(lds_row16(Kb, kadr.row_read_at(kk, mb * 32)), qf[kk], s);
+      for (int kk = 0; kk < NKQ; ++kk) s = mfma32(lds_load16(kadr.row_read_at(kk, mb * 32, buf * KTB)), qf[kk], s);
 #pragma unroll
-      for (int kk = 0; kk < NKV; ++kk) dp = mfma32(lds_row16(Vb, vadr.row_read_at(kk, mb * 32)), yf[kk], dp);
+      for (int kk = 0; kk < NKV; ++kk) dp = mfma32(lds_load16(vadr.row_read_at(kk, mb * 32, buf * VTB)), yf[kk], dp);
       bf16x8 da[2];
       if (full) {
 #pragma unroll
@@ -661,12 +754,14 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
         const int kc = mb * 2 + c;
 #pragma unroll
         for (int nb = 0; nb < NBK; ++nb) {
-          const bf16x8 kb = join(lds_tr_at(Kb, kadr.tr_read(kc, 0, nb)), lds_tr_at(Kb, kadr.tr_read(kc, 1, nb)));
+          const bf16x8 kb = join(lds_load_tr(kadr.tr_read(kc, 0, nb, buf * KTB)),
+                                 lds_load_tr(kadr.tr_read(kc, 1, nb, buf * KTB)));
           dq[nb] = mfma32(da[c], kb, dq[nb]);
         }
       }
     }
-  }
+  };
+  for (int st = 0; st < nsteps; ++st) step(st, st & 1);
 
   // dq = bf16(scale * acc): lane holds head-dim column nb*32 + l32 of 16 rows
   bf16* __restrict__ dQg = static_cast<bf16*>(a.dq) + sb.qbase + (int64_t)n1 * a.q_sn;

@@ -48,7 +48,8 @@ enum {
   FA_ERR_PARAM_INVALID = 2, /* unknown dtype / layout / mask_mode / flag, bad
                                abi_version, non-finite softmax_scale          */
   FA_ERR_SHAPE = 3,         /* a shape constraint of section 四 4.6 is broken,
-                               or cu_seqlens are inconsistent                  */
+                               cu_seqlens are inconsistent, or a row stride
+                               (N*D elements in BSND/TND) reaches 2^23         */
   FA_ERR_UNSUPPORTED = 4,   /* valid on the page but not built here (fp16,
                                head dims outside the built set, flags)         */
   FA_ERR_WORKSPACE = 5,     /* workspace pointer NULL or smaller than needed   */

@@ -378,6 +378,7 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   // bs_lo + t % nblk; a cursor walks it without divisions.
   struct Cursor { int h, blk; };
   auto step_cursor = [&](Cursor& c, int n) {
+    if (nblk == 0) return;  // no items at all (the loop below would not end)
     c.blk += n;
     while (c.blk >= nblk) { c.blk -= nblk; ++c.h; }
   };
@@ -535,12 +536,10 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   // the other buffer, compute item t.
   const int iters = (T + QG - 1) / QG;
   Cursor cc{0, qg}, cf{0, qg};  // item t being computed, item being fetched
-  if (nblk > 0) {
-    step_cursor(cc, 0);
-    step_cursor(cf, 0);
-  }
+  step_cursor(cc, 0);
+  step_cursor(cf, 0);
   fetch(cf, qg, 0);
-  if (nblk > 0) step_cursor(cf, QG);
+  step_cursor(cf, QG);
   auto step = [&](int it, int buf) {
     const int t = it * QG + qg;
     const int i0 = (bs_lo + cc.blk) * BR;

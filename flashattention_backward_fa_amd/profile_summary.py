@@ -4,6 +4,13 @@
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --kernels dkdv_kernel,dq_kernel --workload gqa_causal --out FILE
 
+    python -m flashattention_backward_fa_amd.profile_summary trace \
+        --stats DIR --workload gqa_causal --out FILE [--bench-json FILE]
+
+trace: the per-kernel table of a --kernel-trace --stats run (calls, average,
+min and max duration, share of GPU time), with the kernel source hash and,
+when given, the bench.py JSON line of the same build.
+
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernels are scaled
 by what the same counters read for a plain device copy of known size (bench.py
 --copy-calibration: 256 MiB read and written per launch) and written out with
@@ -68,6 +75,33 @@ def traffic(args):
     sys.stdout.write(text)
 
 
+def _short(name):
+    name = name.replace("fabwd::(anonymous namespace)::", "").replace("fabwd::", "")
+    return name[:64]
+
+
+def trace(args):
+    rows = list(csv.DictReader(open(os.path.join(args.stats, "run_kernel_stats.csv"))))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    out = [
+        f"# rocprofv3 kernel-trace summary, workload {args.workload}",
+        f"# command: {args.command}",
+        "# columns: kernel | calls | average us | min us | max us | share of GPU time",
+    ]
+    for r in rows:
+        out.append(f"{_short(r['Name']):64s} | {int(r['Calls']):4d} | {float(r['AverageNs']) / 1e3:9.1f} | "
+                   f"{float(r['MinNs']) / 1e3:9.1f} | {float(r['MaxNs']) / 1e3:9.1f} | {float(r['Percentage']):5.1f}%")
+    out.append(f"kernel_source_sha256_16: {src_hash}")
+    if args.bench_json:
+        out.append("bench.py line of this build: " + open(args.bench_json).read().strip().splitlines()[-1])
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -76,9 +110,17 @@ def main():
         t.add_argument(k, required=True)
     t.add_argument("--out")
     t.add_argument("--command", default="(see profiles/README.md)")
+    tr = sub.add_parser("trace")
+    tr.add_argument("--stats", required=True)
+    tr.add_argument("--workload", required=True)
+    tr.add_argument("--bench-json")
+    tr.add_argument("--out")
+    tr.add_argument("--command", default="(see profiles/README.md)")
     args = ap.parse_args()
     if args.cmd == "traffic":
         traffic(args)
+    else:
+        trace(args)
 
 
 if __name__ == "__main__":

@@ -1,10 +1,11 @@
 """Build libfa_bwd.so in-tree for gfx950.
 
 The host planner (csrc/fa_bwd_api.cpp) is plain C++ built with g++; the
-kernels (csrc/fa_bwd_kernels.hip: backward; csrc/fa_fwd_kernels.hip: the
-forward that produces attn_out and softmax_lse) are built with hipcc for
-gfx950 only; the objects are linked into
-flashattention_backward_fa_amd/lib/libfa_bwd.so.
+kernels (csrc/fa_bwd_det_kernels.hip: the default dK/dV and dQ kernels;
+csrc/fa_bwd_kernels.hip: preprocess and the atomic variants;
+csrc/fa_fwd_kernels.hip: the forward that produces attn_out and
+softmax_lse) are built with hipcc for gfx950 only; the objects are linked
+into flashattention_backward_fa_amd/lib/libfa_bwd.so.
 
 Usage: python -m flashattention_backward_fa_amd.build
 """
@@ -30,6 +31,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# The default kernels are scheduled with LLVM's iterative ILP strategy:
+# measured on MI355X it shortens the dK/dV kernel by 6-10 % and the D = 192
+# dQ kernel by 20 % against the default occupancy-driven scheduler.
+DET_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 
 
 def _hipcc():
@@ -65,8 +70,8 @@ def build(verbose=False):
           "-o", ker_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_fwd_kernels.hip"),
           "-o", fwd_o], verbose)
-    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_det_kernels.hip"),
-          "-o", det_o], verbose)
+    _run([hipcc, *HIP_FLAGS, *DET_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+          os.path.join(CSRC, "fa_bwd_det_kernels.hip"), "-o", det_o], verbose)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o, det_o], verbose)
     os.replace(tmp, LIB)

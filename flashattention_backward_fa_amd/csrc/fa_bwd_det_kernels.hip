@@ -238,25 +238,30 @@ struct BlockCopy {
   static constexpr int NI = ROWS / RPI;
   static_assert(NI % NW == 0, "whole instructions per wavefront");
   static constexpr int PER = NI / NW;
-  // Instruction wave + x*NW covers rows x*NW*RPI further down than
-  // instruction wave, a multiple of the swizzle's 16-row period: for full
-  // tiles one lane offset serves all x, the rest goes to the scalar base.
-  static_assert((NW * RPI) % 16 == 0, "swizzle period");
-  uint32_t voff;
+  // Instruction wave + x*NW covers rows x*STEP further down than instruction
+  // wave.  The swizzle repeats every 16 rows, so for full tiles the lane
+  // offsets of x and x + Q (Q*STEP a multiple of 16) differ by a uniform row
+  // shift that goes to the scalar base: Q lane offsets serve all x.
+  static constexpr int STEP = NW * RPI;
+  static constexpr int Q = STEP % 16 == 0 ? 1 : 16 / STEP;
+  static_assert(Q * STEP % 16 == 0, "swizzle period");
+  uint32_t voff[Q];
   __device__ __forceinline__ static uint32_t lane_off(int u, int lane, int ldb, int col0, int nvalid) {
     const int row = u * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ swz_f<W>(row);
     return (uint32_t)(min(row, nvalid - 1) * ldb + col0 * 2 + chunk * 16);
   }
   __device__ __forceinline__ void init(int wave, int lane, int ldb, int col0) {
-    voff = lane_off(wave, lane, ldb, col0, ROWS);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) voff[q] = lane_off(wave + q * NW, lane, ldb, col0, ROWS);
   }
   __device__ __forceinline__ void issue(uint32_t lds_blk, const void* g, int ldb, int col0, int nvalid, int wave,
                                         int lane) const {
     const char* gb = static_cast<const char*>(g);
     if (nvalid >= ROWS) {
 #pragma unroll
-      for (int x = 0; x < PER; ++x) dma16(gb + (int64_t)x * NW * RPI * ldb, voff, lds_blk + (wave + x * NW) * 1024);
+      for (int x = 0; x < PER; ++x)
+        dma16(gb + (int64_t)(x / Q) * Q * STEP * ldb, voff[x % Q], lds_blk + (wave + x * NW) * 1024);
     } else {
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
@@ -302,14 +307,16 @@ __device__ __forceinline__ void padded_copy(uint32_t lds_tile, const void* g, in
 
 // ------------------------------------------------------------------ dK / dV
 
-// QG query groups of 4 wavefronts share one tile of 4*KPW keys; wavefront w of
-// each group owns keys w*KPW .. w*KPW+KPW-1 of the tile.  The groups take
+// QG query groups of NWG wavefronts share one tile of NWG*KPW keys; wavefront
+// w of each group owns keys w*KPW .. w*KPW+KPW-1 of the tile.  The groups take
 // alternate 32-row query blocks; each group double-buffers its Q/dY tile so a
 // step needs one barrier.  K/V tiles use a padded pitch (16-byte row reads
 // only); Q/dY tiles are swizzled (row reads and transposing reads).
-template <int HD, int HDV, int KPW, int QG>
-__global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
-  constexpr int BC = 4 * KPW;         // keys per workgroup
+// Instantiated with NWG = 4, KPW = 32: 8 wavefronts in two query groups (two
+// per SIMD) at D <= 128, 4 wavefronts in one group at D = 192.
+template <int HD, int HDV, int KPW, int NWG, int QG>
+__global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
+  constexpr int BC = NWG * KPW;       // keys per workgroup
   constexpr int NKB = KPW / 32;       // 32-key blocks per wavefront
   constexpr int BR = 32;              // query rows per step and group
   constexpr int KP = HD + 8;          // padded pitches of the K and V tiles
@@ -331,8 +338,8 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wave >> 2;      // query group
-  const int kw = wave & 3;       // key slice
+  const int qg = wave / NWG;     // query group
+  const int kw = wave % NWG;     // key slice
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -357,9 +364,9 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int wl = a.win_left, wr = a.win_right;
 
   // K and V tiles, asynchronously (rows past the sequence end repeat its last key)
-  padded_copy<HD, BC, 4 * QG>(lds_addr(Ks), static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j0 * a.k_ss,
-                              (int)a.k_ss * 2, s2 - j0, wave, lane);
-  padded_copy<HDV, BC, 4 * QG>(lds_addr(Vs), static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j0 * a.v_ss,
+  padded_copy<HD, BC, NWG * QG>(lds_addr(Ks), static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j0 * a.k_ss,
+                                (int)a.k_ss * 2, s2 - j0, wave, lane);
+  padded_copy<HDV, BC, NWG * QG>(lds_addr(Vs), static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j0 * a.v_ss,
                                (int)a.v_ss * 2, s2 - j0, wave, lane);
 
   // query blocks that see a key of [j0, j1); this job takes split qs of them
@@ -386,8 +393,8 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   // Q/dY tiles of an item go straight to LDS (async); lse and sfmg of its rows
   // go through registers of wavefront kw = 0, raw and loaded first, so that
   // nothing waits for them before the tile itself is awaited.
-  TileCopy<HD, BR, 4> qcp;
-  TileCopy<HDV, BR, 4> ycp;
+  TileCopy<HD, BR, NWG> qcp;
+  TileCopy<HDV, BR, NWG> ycp;
   const uint32_t q_lds = lds_addr(Qs) + qg * 2 * QTB;  // this group's Q / dY buffers
   const uint32_t y_lds = lds_addr(Ys) + qg * 2 * YTB;
   qcp.init(kw, lane, (int)a.q_ss * 2);
@@ -543,12 +550,12 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
   auto step = [&](int it, int buf) {
     const int t = it * QG + qg;
     const int i0 = (bs_lo + cc.blk) * BR;
-    if (t < T) put_row_stats(i0, buf);
+    if (QG == 1 || t < T) put_row_stats(i0, buf);  // with one group every step has an item
     wait_vmem();    // this wavefront's copies of item t landed
     lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
     fetch(cf, t + QG, buf ^ 1);
     step_cursor(cf, QG);
-    if (t < T) {
+    if (QG == 1 || t < T) {
       phase_a(buf);
       phase_b(buf, i0);
     }
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
         if (qg != 0) {
 #pragma unroll
           for (int rg = 0; rg < 16; ++rg)
-            red[(((qg - 1) * 4 + kw) * 16 + rg) * 64 + lane] = nb < NBK ? dKr[kb][nb][rg] : dVr[kb][nb - NBK][rg];
+            red[(((qg - 1) * NWG + kw) * 16 + rg) * 64 + lane] = nb < NBK ? dKr[kb][nb][rg] : dVr[kb][nb - NBK][rg];
         }
         __syncthreads();
         if (qg == 0) {
@@ -576,7 +583,7 @@ __global__ __launch_bounds__(256 * QG, 1) void dkdv_kernel(KernelArgs a) {
           for (int g = 1; g < QG; ++g) {
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg) {
-              const float x = red[(((g - 1) * 4 + kw) * 16 + rg) * 64 + lane];
+              const float x = red[(((g - 1) * NWG + kw) * 16 + rg) * 64 + lane];
               if (nb < NBK) dKr[kb][nb][rg] += x; else dVr[kb][nb - NBK][rg] += x;
             }
           }
@@ -810,26 +817,22 @@ bool det_instantiated(int D, int Dv) {
   return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128)) || (D == 192 && (Dv == 64 || Dv == 128));
 }
 
-// (keys per wavefront, query groups) of the dK/dV kernel for a head dim:
-// D <= 128: 32 keys x 2 groups (8 wavefronts, two per SIMD, 128-key tiles);
-// D = 192: 32 keys x 1 group (the accumulators need more registers).
+// Keys per tile of the dK/dV kernel divided by 4 (every shape uses 128-key
+// tiles: 8 wavefronts x 32 keys in two query groups, 4 x 32 at D = 192).
 int det_keys_per_wave(int D) { (void)D; return 32; }
-static int det_query_groups(int D) { return D <= 128 ? 2 : 1; }
 
 int launch_dkdv(const KernelArgs& a, void* stream) {
-  const int kpw = det_keys_per_wave(a.D);
-  const int qg = det_query_groups(a.D);
-  const int64_t tiles = (a.S2 + 4 * kpw - 1) / (4 * kpw);
+  const int64_t tiles = (a.S2 + 127) / 128;  // 128-key tiles in every shape
   const int64_t blocks = tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.N2;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)blocks), block(256 * qg);
-  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 2>, grid, block, s, a);
-  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 2>, grid, block, s, a);
-  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 2>, grid, block, s, a);
-  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 1>, grid, block, s, a);
-  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 1>, grid, block, s, a);
+  const dim3 grid((unsigned)blocks);
+  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 4, 2>, grid, dim3(512), s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 4, 2>, grid, dim3(512), s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 4, 2>, grid, dim3(512), s, a);
+  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 4, 1>, grid, dim3(256), s, a);
+  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 4, 1>, grid, dim3(256), s, a);
   return (int)hipErrorInvalidValue;
 }
 

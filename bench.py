@@ -2,23 +2,27 @@
 """Benchmark of the FlashAttention backward on one MI355X.
 
 One step = one fa_bwd_run over one batch of the workload: the sfmg
-preprocess, the main kernel (S/P recompute, dP, dS, dV, dK, dQ) and the dQ
-finalize, with every input already resident in HBM.  attn_out and
-softmax_lse come from the library's own GPU forward (fa_fwd_run), made once
-before timing.  The default workload is the GQA causal one (B=1, N1=32, N2=8,
-S=4096, D=Dv=128, BSND).
+preprocess, the dK/dV kernel (S/P recompute, dP, dS, dV, dK over key tiles),
+the dQ kernel (S/P/dP/dS recompute and dQ over query tiles) and the fp32
+partial-sum reduce when the plan splits a key tile, with every input already
+resident in HBM.  attn_out and softmax_lse come from the library's own GPU
+forward (fa_fwd_run), made once before timing.  The default workload is the
+GQA causal one (B=1, N1=32, N2=8, S=4096, D=Dv=128, BSND).
 
 Prints one JSON line: whole-step throughput in TFLOP/s under the standard
 FLOP count (2*(3D+2Dv) per visible (query, key) pair per query head; causal
-with S1 = S2 counted as exactly half of S1*S2), the main kernel's roofline
-entry from HIP events recorded around it inside the timed region, and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+with S1 = S2 counted as exactly half of S1*S2); the roofline entry of the
+MFMA-bound kernel pair from HIP events the library records around it inside
+the timed region; the preprocess kernel's HBM bandwidth (its own timed
+launches); and the fp64 CPU oracle timed on a bounded sample of the same
+workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload gqa_causal]
                     [--no-cpu-baseline] [--copy-calibration]
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -217,6 +221,26 @@ def main():
     plan.profile_enable(0)
     main_avg = sum(main_ms) / max(len(main_ms), 1)
 
+    # preprocess alone (sfmg = rowsum(dY * Y)): HBM-bound, timed over its own
+    # launches on the same stream; algorithmic bytes = dY and Y read once
+    # (2 B each per element) plus 4 B of sfmg written per query row
+    rows = cfg["N1"] * (int(sum(cfg["lengths"])) if cfg["layout"] == "TND" else cfg["B"] * cfg["S1"])
+    pre_bytes = rows * (2 * 2 * cfg["Dv"] + 4)
+    sf = torch.empty(rows, dtype=torch.float32, device=dev)
+    pre_iters = max(args.steps, 1)
+    for _ in range(2):
+        plan.sfmg(fb._ptr(dout), fb._ptr(attn_out), fb._ptr(cu_q), fb._ptr(sf), ctypes.c_void_p(stream.cuda_stream))
+    p0 = torch.cuda.Event(enable_timing=True)
+    p1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    p0.record(stream)
+    for _ in range(pre_iters):
+        plan.sfmg(fb._ptr(dout), fb._ptr(attn_out), fb._ptr(cu_q), fb._ptr(sf), ctypes.c_void_p(stream.cuda_stream))
+    p1.record(stream)
+    torch.cuda.synchronize()
+    pre_ms = p0.elapsed_time(p1) / pre_iters
+    pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
+
     flops = algorithmic_flops(cfg)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (main_avg * 1e-3) / 1e12
@@ -247,6 +271,11 @@ def main():
             "bound": "mfma", "kernel": MAIN_KERNELS, "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic, "avg_launch_ms": round(main_avg, 5), "launches_timed": len(main_ms),
+        },
+        "preprocess": {
+            "bound": "hbm", "kernel": "preprocess_kernel (sfmg)", "achieved": round(pre_gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": pre_bytes, "avg_launch_ms": round(pre_ms, 5),
         },
         "cpu_baseline": None,
     }

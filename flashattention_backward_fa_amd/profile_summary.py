@@ -7,9 +7,19 @@
     python -m flashattention_backward_fa_amd.profile_summary trace \
         --stats DIR --workload gqa_causal --out FILE [--bench-json FILE]
 
+    python -m flashattention_backward_fa_amd.profile_summary mfma \
+        --pmc DIR --kernels dkdv_kernel,dq_kernel --workload gqa_causal --out FILE
+
 trace: the per-kernel table of a --kernel-trace --stats run (calls, average,
 min and max duration, share of GPU time), with the kernel source hash and,
 when given, the bench.py JSON line of the same build.
+
+mfma: MFMA-pipe utilisation per kernel from a --pmc GRBM_GUI_ACTIVE
+SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA run.  SQ_VALU_MFMA_BUSY_CYCLES is the
+sum over all 1024 SIMDs (it equals 32 cycles per v_mfma_f32_32x32x16_bf16
+counted by SQ_INSTS_MFMA); GRBM_GUI_ACTIVE is the sum over the 8 XCDs, so a
+kernel's elapsed shader cycles are GRBM_GUI_ACTIVE / 8 (divided by the
+dispatch's duration this gives the shader clock, also reported).
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernels are scaled
 by what the same counters read for a plain device copy of known size (bench.py
@@ -28,6 +38,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc", "fa_bwd_det_kernels.hip")
 COPY_BYTES = 256 << 20
+XCDS = 8        # MI355X: 8 XCDs of 32 CUs
+SIMDS = 1024    # 256 CUs x 4 SIMDs
 
 
 def _rows(d):
@@ -102,6 +114,39 @@ def trace(args):
     sys.stdout.write(text)
 
 
+def mfma(args):
+    names = args.kernels.split(",")
+    rows = _rows(args.pmc)
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    out = [f"# MFMA-pipe utilisation per kernel, workload {args.workload}", f"# command: {args.command}",
+           "# columns: kernel | MFMA instructions | MFMA busy cycles (all SIMDs) | elapsed cycles | "
+           "utilisation | clock GHz"]
+    tot_busy = tot_el = 0.0
+    for n in names:
+        match = lambda k, n=n: n in k  # noqa: E731
+        busy = statistics.median(_per_dispatch(args.pmc, "SQ_VALU_MFMA_BUSY_CYCLES", match))
+        gui = statistics.median(_per_dispatch(args.pmc, "GRBM_GUI_ACTIVE", match))
+        insts = statistics.median(_per_dispatch(args.pmc, "SQ_INSTS_MFMA", match))
+        durs = {}
+        for r in rows:
+            if match(r["Kernel_Name"]):
+                durs[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        dur_ns = statistics.median(durs.values())
+        elapsed = gui / XCDS
+        util = busy / (elapsed * SIMDS)
+        tot_busy += busy
+        tot_el += elapsed
+        out.append(f"{n:16s} | {insts:12.0f} | {busy:14.0f} | {elapsed:11.0f} | {100 * util:5.1f} % | "
+                   f"{elapsed / dur_ns:4.2f}")
+    out.append(f"pair_mfma_utilisation: {100 * tot_busy / (tot_el * SIMDS):.1f} %")
+    out.append(f"kernel_source_sha256_16: {src_hash}")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -116,11 +161,18 @@ def main():
     tr.add_argument("--bench-json")
     tr.add_argument("--out")
     tr.add_argument("--command", default="(see profiles/README.md)")
+    m = sub.add_parser("mfma")
+    for k in ("--pmc", "--kernels", "--workload"):
+        m.add_argument(k, required=True)
+    m.add_argument("--out")
+    m.add_argument("--command", default="(see profiles/README.md)")
     args = ap.parse_args()
     if args.cmd == "traffic":
         traffic(args)
-    else:
+    elif args.cmd == "trace":
         trace(args)
+    else:
+        mfma(args)
 
 
 if __name__ == "__main__":

@@ -18,7 +18,10 @@ launches); and the fp64 CPU oracle timed on a bounded sample of the same
 workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload gqa_causal]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-configs] [--copy-calibration]
+
+The line also carries `configs`: the same step, pair and preprocess figures
+for every benchmark configuration (10 timed steps each).
 """
 
 import argparse
@@ -158,30 +161,15 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
-    ap.add_argument("--copy-calibration", action="store_true")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the kernel shards over "
-              "KV-head groups with no exchange, see the design notes)", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
+def measure(name, steps, warmup):
+    """Time `steps` backward steps of a workload (after `warmup` untimed ones)
+    on the current stream: whole-step time from events around the loop, the
+    dK/dV + dQ pair from the library's events, and the preprocess kernel over
+    its own launches.  Returns times in ms and the preprocess bytes."""
     import torch
     from flashattention_backward_fa_amd import fa_bwd as fb
     from flashattention_backward_fa_amd import workloads as W
 
-    name = args.workload or W.BENCH_WORKLOAD
     cfg = W.CONFIGS[name]
     dev = torch.device("cuda", 0)
     x = W.make_inputs(cfg)
@@ -204,20 +192,20 @@ def main():
     def step():
         fb.flash_attn_grad(q, k, v, dout, attn_out, lse, cu_q, cu_kv, workspace=ws, out=(dq, dk, dv), **kw)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    plan.profile_enable(max(args.steps, 1))
+    plan.profile_enable(max(steps, 1))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     t1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / max(args.steps, 1)
-    main_ms = plan.profile_read(args.steps)
+    ms_per_step = t0.elapsed_time(t1) / max(steps, 1)
+    main_ms = plan.profile_read(steps)
     plan.profile_enable(0)
     main_avg = sum(main_ms) / max(len(main_ms), 1)
 
@@ -227,18 +215,49 @@ def main():
     rows = cfg["N1"] * (int(sum(cfg["lengths"])) if cfg["layout"] == "TND" else cfg["B"] * cfg["S1"])
     pre_bytes = rows * (2 * 2 * cfg["Dv"] + 4)
     sf = torch.empty(rows, dtype=torch.float32, device=dev)
-    pre_iters = max(args.steps, 1)
+    sargs = (fb._ptr(dout), fb._ptr(attn_out), fb._ptr(cu_q), fb._ptr(sf), ctypes.c_void_p(stream.cuda_stream))
+    pre_iters = max(steps, 1)
     for _ in range(2):
-        plan.sfmg(fb._ptr(dout), fb._ptr(attn_out), fb._ptr(cu_q), fb._ptr(sf), ctypes.c_void_p(stream.cuda_stream))
+        plan.sfmg(*sargs)
     p0 = torch.cuda.Event(enable_timing=True)
     p1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     p0.record(stream)
     for _ in range(pre_iters):
-        plan.sfmg(fb._ptr(dout), fb._ptr(attn_out), fb._ptr(cu_q), fb._ptr(sf), ctypes.c_void_p(stream.cuda_stream))
+        plan.sfmg(*sargs)
     p1.record(stream)
     torch.cuda.synchronize()
     pre_ms = p0.elapsed_time(p1) / pre_iters
+    return dict(ms_per_step=ms_per_step, pair_ms=main_avg, pair_launches=len(main_ms), pre_ms=pre_ms,
+                pre_bytes=pre_bytes)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration summary")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the kernel shards over "
+              "KV-head groups with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from flashattention_backward_fa_amd import workloads as W
+
+    name = args.workload or W.BENCH_WORKLOAD
+    cfg = W.CONFIGS[name]
+    m = measure(name, args.steps, args.warmup)
+    ms_per_step, main_avg, pre_ms, pre_bytes = m["ms_per_step"], m["pair_ms"], m["pre_ms"], m["pre_bytes"]
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
 
     flops = algorithmic_flops(cfg)
@@ -270,15 +289,39 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": MAIN_KERNELS, "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic, "avg_launch_ms": round(main_avg, 5), "launches_timed": len(main_ms),
+            "traffic": traffic, "avg_launch_ms": round(main_avg, 5), "launches_timed": m["pair_launches"],
         },
         "preprocess": {
             "bound": "hbm", "kernel": "preprocess_kernel (sfmg)", "achieved": round(pre_gbs, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4),
             "bytes_per_launch": pre_bytes, "avg_launch_ms": round(pre_ms, 5),
         },
+        "configs": None,
         "cpu_baseline": None,
     }
+    if not args.no_configs:
+        # every benchmark configuration at the same settings (10 timed steps
+        # each): whole step, the dK/dV + dQ pair and the preprocess bandwidth
+        import torch
+
+        rows = {}
+        for other in W.CONFIGS:
+            if other == name:
+                r = m
+            else:
+                torch.cuda.empty_cache()
+                r = measure(other, 10, 2)
+            f = algorithmic_flops(W.CONFIGS[other])
+            rows[other] = {
+                "ms_per_step": round(r["ms_per_step"], 4),
+                "tflops": round(f / (r["ms_per_step"] * 1e-3) / 1e12, 1),
+                "pct_of_peak": round(100 * f / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "pair_ms": round(r["pair_ms"], 4),
+                "pair_tflops": round(f / (r["pair_ms"] * 1e-3) / 1e12, 1),
+                "preprocess_gbs": round(r["pre_bytes"] / (r["pre_ms"] * 1e-3) / 1e9, 1),
+                "algorithmic_gflop": round(f / 1e9, 3),
+            }
+        line["configs"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads, name)
     print(json.dumps(line), flush=True)

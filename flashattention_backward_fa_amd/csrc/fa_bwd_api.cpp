@@ -57,7 +57,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   if (d.layout < FA_LAYOUT_BSND || d.layout > FA_LAYOUT_TND) return FA_ERR_PARAM_INVALID;
   if (d.mask_mode < FA_MASK_NONE || d.mask_mode > FA_MASK_WINDOW) return FA_ERR_PARAM_INVALID;
   if (!std::isfinite(d.softmax_scale)) return FA_ERR_PARAM_INVALID;
-  if (d.flags & ~FA_FLAG_DETERMINISTIC) return FA_ERR_PARAM_INVALID;
+  if (d.flags & ~(FA_FLAG_DETERMINISTIC | FA_FLAG_FP32_OUT)) return FA_ERR_PARAM_INVALID;
 
   // section 四 4.6: positive sizes, 0 < B < 65536, N1 % N2 == 0, 0 < Dv <= D <= 192
   if (d.B <= 0 || d.B >= 65536) return FA_ERR_SHAPE;
@@ -150,6 +150,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     if (e[0] == '1' && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
   }
   if (d.flags & FA_FLAG_DETERMINISTIC) a.variant = 2;
+  if (d.flags & FA_FLAG_FP32_OUT) a.variant = 3;  // fp32 debugging form: sfmg + two VALU kernels
   a.heads_per_job = a.G;
   a.q_splits = 1;
   a.n_partials = 1;
@@ -184,7 +185,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   p.off_sfmg = 0;
   p.off_dq_acc = 0;
   size_t cur = align_up((size_t)p.lse_elems * sizeof(float));
-  if (a.variant != 2) {
+  if (a.variant < 2) {
     p.off_dq_acc = cur;
     cur += align_up((size_t)p.q_elems * sizeof(float));
   }
@@ -256,10 +257,17 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   a.dq = dq; a.dk = dk; a.dv = dv;
   char* ws = static_cast<char*>(workspace);
   a.sfmg = reinterpret_cast<float*>(ws + plan->off_sfmg);
-  if (a.variant != 2) a.dq_acc = reinterpret_cast<float*>(ws + plan->off_dq_acc);
+  if (a.variant < 2) a.dq_acc = reinterpret_cast<float*>(ws + plan->off_dq_acc);
   a.dk_acc = reinterpret_cast<float*>(ws + plan->off_dk_acc);
   a.dv_acc = reinterpret_cast<float*>(ws + plan->off_dv_acc);
 
+  if (a.variant == 3) {
+    if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_f32_debug(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    return FA_OK;
+  }
   if (a.variant == 2) {
     // sfmg -> dK/dV kernel -> dQ kernel -> partial-sum reduce (when split)
     if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;

@@ -53,7 +53,8 @@ struct KernelArgs {
   int32_t has_mask;      // any bound present
 
   int32_t variant;        // 0 = 4-wavefront atomic kernel, 1 = 8-wavefront atomic kernel,
-                          // 2 = atomic-free pair (dK/dV kernel + dQ kernel)
+                          // 2 = atomic-free pair (dK/dV kernel + dQ kernel),
+                          // 3 = fp32 debugging form (fp32 outputs)
   int32_t heads_per_job;  // query heads of a GQA group handled by one workgroup
   int32_t q_splits;       // query-range splits of one key tile (atomic-free pair only)
   int32_t n_partials;     // fp32 dK/dV partial sums per key tile (atomic-free pair only)
@@ -63,7 +64,7 @@ struct KernelArgs {
 
 // True when dK/dV of one key/value head are summed over several workgroups
 // (through the fp32 dk_acc / dv_acc workspace) instead of in registers.
-inline bool split_heads(const KernelArgs& a) { return a.variant != 2 && a.heads_per_job < a.G; }
+inline bool split_heads(const KernelArgs& a) { return a.variant < 2 && a.heads_per_job < a.G; }
 
 // Launchers (fa_bwd_kernels.hip).  Each returns 0 or a hipError_t value.
 int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream);
@@ -78,6 +79,9 @@ int launch_dq(const KernelArgs& a, void* stream);
 int launch_reduce_parts(const KernelArgs& a, void* stream);
 int launch_dq_finalize(const KernelArgs& a, void* stream);
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream);
+
+// fp32 debugging form (fa_bwd_f32_kernels.hip): dK/dV and dQ, fp32 outputs.
+int launch_f32_debug(const KernelArgs& a, void* stream);
 bool main_instantiated(int D, int Dv);
 
 // Ring of HIP event pairs bracketing the main kernel (timing hook).

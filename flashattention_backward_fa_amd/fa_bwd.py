@@ -31,6 +31,7 @@ FA_ERR_RUNTIME = 6
 
 LAYOUTS = {"BSND": 0, "BNSD": 1, "TND": 2}
 FLAG_DETERMINISTIC = 0x1
+FLAG_FP32_OUT = 0x2
 
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_profile_enable",
             "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version")
@@ -232,10 +233,10 @@ def _check(name, t, dtype, device):
 
 def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0,
              mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1,
-             deterministic=False, host_cu_seqlens=None):
+             deterministic=False, host_cu_seqlens=None, fp32_out=False):
     """Create (or reuse) the plan for these shapes and attributes."""
     sh = _shapes(q, k, v, layout)
-    flags = FLAG_DETERMINISTIC if deterministic else 0
+    flags = (FLAG_DETERMINISTIC if deterministic else 0) | (FLAG_FP32_OUT if fp32_out else 0)
     mm = mask_mode_value(mask_mode)
     if layout == "TND":
         if cu_seqlens_q is None or cu_seqlens_kv is None:
@@ -271,13 +272,16 @@ def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, soft
 
 def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None,
                     softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
-                    max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None):
+                    max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None,
+                    fp32_out=False):
     """dq, dk, dv of attention (bf16) on the current HIP stream.
 
     q, k, v, dout, attn_out: bf16 CUDA(HIP) tensors in `layout`; softmax_lse:
     float32, (B, N1, S1) or (N1, T1); cu_seqlens_*: int32 device tensors for
     TND only.  Non-contiguous inputs are made contiguous first.  `workspace`
     (uint8 tensor) and `out` ((dq, dk, dv)) may be passed to avoid allocation.
+    fp32_out=True selects the fp32 debugging form (float32 outputs, P and dS
+    kept in fp32; slow).
     """
     import torch
 
@@ -295,11 +299,16 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
     if dout.shape != attn_out.shape:
         raise ValueError("dout and attn_out must have the same shape")
     plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
-                    max_seqlen_q, max_seqlen_kv, deterministic)
+                    max_seqlen_q, max_seqlen_kv, deterministic, fp32_out=fp32_out)
+    odt = torch.float32 if fp32_out else torch.bfloat16
     if out is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dq, dk, dv = (torch.empty(t.shape, dtype=odt, device=dev) for t in (q, k, v))
     else:
         dq, dk, dv = out
+        for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            _check(name, t, odt, dev)
+            if t.shape != ref.shape or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(ref.shape)}")
     if workspace is None or workspace.numel() < plan.workspace_bytes:
         workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)

@@ -79,6 +79,12 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 };
 
 /* flags */
 #define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable results; the default path already is */
+/* fp32 debugging form (not on the page; it checks the arithmetic of section 一
+ * at fp32 accuracy): dq, dk, dv are float32 arrays with the shapes and layouts
+ * of q, k, v; P and dS are kept in fp32 and every product is an fp32 FMA, so
+ * the only bf16 roundings are those of the inputs.  Slow (VALU, untuned);
+ * deterministic.  Overrides FA_FLAG_DETERMINISTIC's kernel choice. */
+#define FA_FLAG_FP32_OUT 0x2u
 
 typedef struct fa_bwd_plan_s* fa_bwd_plan; /* opaque, host memory only */
 

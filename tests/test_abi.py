@@ -71,6 +71,10 @@ def test_valid_problem_and_workspace_size(lib):
     assert st == fb.FA_OK
     lse, k_elems = 2 * 8 * 128, 2 * 128 * 2 * 128
     assert ws == rnd(lse * 4) + 2 * rnd(16 * k_elems * 4)
+    # the fp32 debugging form needs sfmg only
+    st, ws = create(lib, flags=fb.FLAG_FP32_OUT)
+    assert st == fb.FA_OK
+    assert ws == rnd(lse * 4)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -100,7 +104,8 @@ def test_create_rejects(lib, kw, code):
     dict(mask_mode=1), dict(mask_mode=1, win_left=1024, win_right=0), dict(mask_mode=2, win_left=3, win_right=7),
     dict(mask_mode="causal"), dict(mask_mode=fb.MaskMode.WINDOW, win_left=-1, win_right=-1),
     dict(D=192, Dv=128), dict(D=64, Dv=64), dict(N1=32, N2=8), dict(softmax_scale=0.25),
-    dict(flags=fb.FLAG_DETERMINISTIC),
+    dict(flags=fb.FLAG_DETERMINISTIC), dict(flags=fb.FLAG_FP32_OUT),
+    dict(flags=fb.FLAG_FP32_OUT | fb.FLAG_DETERMINISTIC, D=192, Dv=128),
 ])
 def test_create_accepts(lib, kw):
     assert create(lib, **kw)[0] == fb.FA_OK

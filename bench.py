@@ -26,7 +26,6 @@ for every benchmark configuration (10 timed steps each).
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -79,8 +78,8 @@ def algorithmic_flops(cfg):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    from flashattention_backward_fa_amd.profile_summary import kernel_code_hash
+    return kernel_code_hash(KERNEL_SRC)
 
 
 def committed_traffic(workload):
@@ -95,7 +94,7 @@ def committed_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_code_sha256_16") != kernel_source_hash():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

@@ -11,15 +11,17 @@
 // (two extra GEMMs) and writes every dQ element once; results are bitwise
 // repeatable.
 //
-// dK/dV kernel: one workgroup = 4 wavefronts owning KPW keys each (KPW = 64:
-// a 256-key tile).  K and V stay in LDS; 32-row query blocks stream through
-// LDS (the next one is prefetched into registers).  S = Q K^T and dP = dY V^T
-// use query rows as M and keys as N of v_mfma_f32_32x32x16_bf16, so each lane
-// holds one key and 16 query rows: exactly the A-operand layout of the
-// key-major products dV += P^T dY and dK += dS^T Q, whose B operands (dY and
-// Q read down their columns) come from ds_read_b64_tr_b16.  A job is (key
-// tile, query-head slot, query-range split, sequence, key/value head).  When
-// a key tile is split over several jobs (GQA heads, or query ranges for
+// dK/dV kernel: one workgroup owns a 128-key tile of one (sequence, key/value
+// head): 4 wavefronts of 32 keys in each of QG query groups (QG = 2 at
+// D <= 128, two wavefronts per SIMD; QG = 1 at D = 192).  K and V stay in LDS;
+// the groups take alternate 32-row query blocks, whose Q and dY tiles are
+// copied global -> LDS one block ahead (double-buffered).  S = Q K^T and
+// dP = dY V^T use query rows as M and keys as N of v_mfma_f32_32x32x16_bf16,
+// so each lane holds one key and 16 query rows: exactly the A-operand layout
+// of the key-major products dV += P^T dY and dK += dS^T Q, whose B operands
+// (dY and Q read down their columns) come from ds_read_b64_tr_b16.  A job is
+// (key tile, query-head slot, query-range split, sequence, key/value head).
+// When a key tile is split over several jobs (GQA heads, or query ranges for
 // balance) each job stores fp32 partial sums and a reduce kernel adds them;
 // otherwise the job writes bf16 dK/dV directly.
 //

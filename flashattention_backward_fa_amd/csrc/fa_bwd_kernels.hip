@@ -1,4 +1,7 @@
-// gfx950 (MI355X) kernels of the FlashAttention backward.
+// gfx950 (MI355X) kernels of the FlashAttention backward: the sfmg
+// preprocess used by every path, and the two fp32-atomic forms of the main
+// kernel (selected with FA_BWD_VARIANT=0/1; the default path is the
+// atomic-free pair of fa_bwd_det_kernels.hip).
 //
 // Formulas: page "CANN ops-transformer FlashAttnGrad 算子详解", section 一
 // (P = exp(scale*QK^T - softmax_lse), dV = P^T dY, dP = dY V^T,

@@ -32,6 +32,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 import sys
 
@@ -40,6 +41,17 @@ KERNEL_SRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc", "fa_bw
 COPY_BYTES = 256 << 20
 XCDS = 8        # MI355X: 8 XCDs of 32 CUs
 SIMDS = 1024    # 256 CUs x 4 SIMDs
+
+
+def kernel_code_hash(path=KERNEL_SRC):
+    """sha256 (16 hex digits) of the kernel source with comments and blank
+    lines removed: a summary stays valid across comment-only edits and goes
+    stale on any change to the code."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
 def _rows(d):
@@ -70,14 +82,14 @@ def traffic(args):
         fb, wb = f * 1024.0 * f_scale, w * 1024.0 * w_scale
         total += fb + wb
         lines.append(f"# {n}: FETCH_SIZE {f:.0f} KiB -> {fb / 2**20:.1f} MiB, WRITE_SIZE {w:.0f} KiB -> {wb / 2**20:.1f} MiB")
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = kernel_code_hash()
     out = [
         f"# HBM traffic per launch of {'+'.join(names)}, workload {args.workload}",
         f"# command: {args.command}",
         f"# calibration: copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE {cf:.0f} KiB (scale {f_scale:.3f}),",
         f"#   WRITE_SIZE {cw:.0f} KiB (scale {w_scale:.3f})",
         *lines,
-        f"kernel_source_sha256_16: {src_hash}",
+        f"kernel_code_sha256_16: {src_hash}",
         f"hbm_bytes_per_launch: {total:.0f}",
     ]
     text = "\n".join(out) + "\n"
@@ -95,7 +107,7 @@ def _short(name):
 def trace(args):
     rows = list(csv.DictReader(open(os.path.join(args.stats, "run_kernel_stats.csv"))))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = kernel_code_hash()
     out = [
         f"# rocprofv3 kernel-trace summary, workload {args.workload}",
         f"# command: {args.command}",
@@ -104,7 +116,7 @@ def trace(args):
     for r in rows:
         out.append(f"{_short(r['Name']):64s} | {int(r['Calls']):4d} | {float(r['AverageNs']) / 1e3:9.1f} | "
                    f"{float(r['MinNs']) / 1e3:9.1f} | {float(r['MaxNs']) / 1e3:9.1f} | {float(r['Percentage']):5.1f}%")
-    out.append(f"kernel_source_sha256_16: {src_hash}")
+    out.append(f"kernel_code_sha256_16: {src_hash}")
     if args.bench_json:
         out.append("bench.py line of this build: " + open(args.bench_json).read().strip().splitlines()[-1])
     text = "\n".join(out) + "\n"
@@ -117,7 +129,7 @@ def trace(args):
 def mfma(args):
     names = args.kernels.split(",")
     rows = _rows(args.pmc)
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = kernel_code_hash()
     out = [f"# MFMA-pipe utilisation per kernel, workload {args.workload}", f"# command: {args.command}",
            "# columns: kernel | MFMA instructions | MFMA busy cycles (all SIMDs) | elapsed cycles | "
            "utilisation | clock GHz"]
@@ -139,7 +151,7 @@ def mfma(args):
         out.append(f"{n:16s} | {insts:12.0f} | {busy:14.0f} | {elapsed:11.0f} | {100 * util:5.1f} % | "
                    f"{elapsed / dur_ns:4.2f}")
     out.append(f"pair_mfma_utilisation: {100 * tot_busy / (tot_el * SIMDS):.1f} %")
-    out.append(f"kernel_source_sha256_16: {src_hash}")
+    out.append(f"kernel_code_sha256_16: {src_hash}")
     text = "\n".join(out) + "\n"
     if args.out:
         with open(args.out, "w") as fh:

@@ -14,8 +14,10 @@ FLOP count (2*(3D+2Dv) per visible (query, key) pair per query head; causal
 with S1 = S2 counted as exactly half of S1*S2); the roofline entry of the
 MFMA-bound kernel pair from HIP events the library records around it inside
 the timed region; the preprocess kernel's HBM bandwidth (its own timed
-launches); and the fp64 CPU oracle timed on a bounded sample of the same
-workload.
+launches); the fp64 CPU oracle timed on a bounded sample of the same
+workload; and `accuracy`: the library's gradients on that sample (made from
+the oracle forward's stored Y and lse) against the oracle's, every element,
+so that the speed figure comes with its parity error.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload gqa_causal]
                     [--no-cpu-baseline] [--no-configs] [--copy-calibration]
@@ -104,7 +106,9 @@ def committed_traffic(workload):
 
 def cpu_baseline(cfg, max_heads, name=""):
     """The fp64 oracle's backward, untuned, on the first KV-head groups of
-    the workload (its forward is run first, untimed, to make Y and lse)."""
+    the workload (its forward is run first, untimed, to make Y and lse).
+    Returns the baseline entry and the sample (inputs, oracle Y/lse and the
+    oracle's gradients) for the accuracy leg."""
     import numpy as np
     import oracle
     from flashattention_backward_fa_amd import workloads as W
@@ -119,30 +123,78 @@ def cpu_baseline(cfg, max_heads, name=""):
     sub = dict(cfg, N1=groups * G, N2=groups)
     x = W.make_inputs(cfg)
     lay = cfg["layout"]
-    # head slice of the full workload's tensors
+    # head slice of the full workload's tensors (the head axis is 2 in BSND,
+    # 1 in BNSD and TND)
     if lay == "BSND":
-        sl = lambda t, n: t[:, :, :n]  # noqa: E731
-    elif lay == "BNSD":
-        sl = lambda t, n: t[:, :n]  # noqa: E731
+        sl = lambda t, n: t[:, :, :n].contiguous()  # noqa: E731
     else:
-        sl = lambda t, n: t[:, :n]  # noqa: E731
-    q = sl(x["q"], sub["N1"]).double().numpy()
-    k = sl(x["k"], sub["N2"]).double().numpy()
-    v = sl(x["v"], sub["N2"]).double().numpy()
-    dy = sl(x["dout"], sub["N1"]).double().numpy()
+        sl = lambda t, n: t[:, :n].contiguous()  # noqa: E731
+    tq, tk, tv, tdy = sl(x["q"], sub["N1"]), sl(x["k"], sub["N2"]), sl(x["v"], sub["N2"]), sl(x["dout"], sub["N1"])
+    q, k, v, dy = (t.double().numpy() for t in (tq, tk, tv, tdy))
     args = (lay, x["cu_q"], x["cu_kv"], cfg["softmax_scale"], cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
     Y, lse = oracle.forward(q, k, v, *args)
     Yst, lst = oracle.store(Y, lse)
     t0 = time.perf_counter()
-    oracle.backward(q, k, v, dy, Yst, lst, *args)
+    ref = oracle.backward(q, k, v, dy, Yst, lst, *args)
     dt = time.perf_counter() - t0
     flops = algorithmic_flops(sub)
-    return {
+    entry = {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
         "sample": (f"{sub['N1']} of {cfg['N1']} query heads ({groups} KV-head group(s)) of the {name} workload, "
                    f"full sequence; oracle backward (dense fp64 NumPy, masked work not skipped) took {dt:.2f} s; "
                    f"value = algorithmic FLOP of the sample / time"),
     }
+    sample = dict(cfg=sub, x=x, t=(tq, tk, tv, tdy), Yst=Yst, lst=lst, ref=ref)
+    return entry, sample
+
+
+def _errors(got, ref):
+    """Relative Frobenius error and max |err| / max |ref| of one tensor."""
+    import numpy as np
+
+    err = got - ref
+    nref = float(np.linalg.norm(ref))
+    mref = float(np.abs(ref).max()) if ref.size else 0.0
+    rel = float(np.linalg.norm(err)) / nref if nref > 0 else (0.0 if not np.any(err) else math.inf)
+    mx = float(np.abs(err).max()) / mref if mref > 0 else (0.0 if not np.any(err) else math.inf)
+    return rel, mx
+
+
+def accuracy(sample, name):
+    """Parity error beside the speed figure: the library's backward (same
+    entry point and plan as the timed step) on the CPU-baseline sample's
+    inputs, with the oracle forward's stored Y and lse as attn_out and
+    softmax_lse, compared element by element with the oracle's dq, dk, dv."""
+    import numpy as np
+    import torch
+    from flashattention_backward_fa_amd import fa_bwd as fb
+
+    cfg, x = sample["cfg"], sample["x"]
+    dev = torch.device("cuda", 0)
+    q, k, v, dout = (t.to(dev) for t in sample["t"])
+    attn_out = torch.from_numpy(np.ascontiguousarray(sample["Yst"])).to(torch.bfloat16).to(dev)
+    lse = torch.from_numpy(np.ascontiguousarray(sample["lst"], dtype=np.float32)).to(dev)
+    cu_q = cu_kv = None
+    mq = mk = -1
+    if cfg["layout"] == "TND":
+        cu_q = torch.from_numpy(x["cu_q"]).to(dev)
+        cu_kv = torch.from_numpy(x["cu_kv"]).to(dev)
+        mq, mk = int(np.diff(x["cu_q"]).max()), int(np.diff(x["cu_kv"]).max())
+    dq, dk, dv = fb.flash_attn_grad(q, k, v, dout, attn_out, lse, cu_q, cu_kv, softmax_scale=cfg["softmax_scale"],
+                                    mask_mode=cfg["mask_mode"], win_left=cfg["win_left"],
+                                    win_right=cfg["win_right"], max_seqlen_q=mq, max_seqlen_kv=mk,
+                                    layout=cfg["layout"])
+    torch.cuda.synchronize()
+    out = {"reference": "fp64 oracle (oracle.backward) on the CPU-baseline sample, every element",
+           "tolerance": {"rel_fro": 1e-2, "max_abs_ratio": 2e-2}}
+    ok = True
+    for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), sample["ref"]):
+        rel, mx = _errors(got.cpu().double().numpy(), ref)
+        out[nm] = {"rel_fro": float(f"{rel:.4g}"), "max_abs_ratio": float(f"{mx:.4g}")}
+        ok = ok and rel <= 1e-2 and mx <= 2e-2
+    out["within_tolerance"] = bool(ok)
+    out["sample"] = f"{cfg['N1']} query heads of the {name} workload"
+    return out
 
 
 def copy_calibration():
@@ -237,7 +289,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (cpu_baseline and accuracy)")
     ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration summary")
@@ -297,6 +349,7 @@ def main():
         },
         "configs": None,
         "cpu_baseline": None,
+        "accuracy": None,
     }
     if not args.no_configs:
         # every benchmark configuration at the same settings (10 timed steps
@@ -322,7 +375,8 @@ def main():
             }
         line["configs"] = rows
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads, name)
+        line["cpu_baseline"], sample = cpu_baseline(cfg, args.cpu_heads, name)
+        line["accuracy"] = accuracy(sample, name)
     print(json.dumps(line), flush=True)
 
 

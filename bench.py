@@ -42,7 +42,6 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # The MFMA-bound part of a step is the dK/dV kernel followed by the dQ kernel;
 # the library records HIP events around that pair on the launch stream.
-KERNEL_SRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc", "fa_bwd_det_kernels.hip")
 MAIN_KERNELS = "dkdv_kernel+dq_kernel"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -81,7 +80,7 @@ def algorithmic_flops(cfg):
 
 def kernel_source_hash():
     from flashattention_backward_fa_amd.profile_summary import kernel_code_hash
-    return kernel_code_hash(KERNEL_SRC)
+    return kernel_code_hash()
 
 
 def committed_traffic(workload):

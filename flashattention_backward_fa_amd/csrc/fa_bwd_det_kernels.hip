@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fa_bwd_internal.h"
+#include "fa_bwd_schedule.h"
 
 namespace fabwd {
 namespace {
@@ -372,14 +373,10 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
                                (int)a.v_ss * 2, s2 - j0, wave, lane);
 
   // query blocks that see a key of [j0, j1); this job takes split qs of them
-  int i_lo = 0, i_hi = s1;
-  if (wr >= 0) i_lo = max(0, j0 - off - wr);
-  if (wl >= 0) i_hi = min(s1, j1 - off + wl);
-  const int blk0 = i_lo / BR;
-  const int nblk_all = i_hi > i_lo ? (i_hi + BR - 1) / BR - blk0 : 0;
-  const int bs_lo = blk0 + (int)((int64_t)nblk_all * qs / QS);
-  const int bs_hi = blk0 + (int)((int64_t)nblk_all * (qs + 1) / QS);
-  const int nblk = bs_hi - bs_lo;
+  const fa_sched::Span blks =
+      fa_sched::split_part(fa_sched::blocks_covering(fa_sched::rows_seeing(s1, j0, j1, off, wl, wr), BR), qs, QS);
+  const int bs_lo = blks.lo;
+  const int nblk = blks.hi - blks.lo;
   const int T = hpj * nblk;  // items: (query head, query block) pairs
   const int g0 = hslot * hpj;
 
@@ -470,8 +467,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     // A tile that every (row, key) pair sees takes the unmasked path; otherwise
     // row i is kept iff it lies in [vis_lo, vis_hi] of the lane's key (one
     // unsigned compare per element, no branches).
-    const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
-                      (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
+    const bool full = fa_sched::tile_full(i0, BR, j0, BC, s1, s2, off, wl, wr);
     bf16x8 pa[NKB][2], da[NKB][2];
     if (full) {
 #pragma unroll
@@ -491,19 +487,10 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
         }
       }
     } else {
-      unsigned vlo[NKB], vspan[NKB];  // visible rows of this lane's key, relative to i0
+      fa_sched::Window vis[NKB];  // visible rows of this lane's key, relative to i0
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int jk = j0 + kw0 + kb * 32 + l32;
-        int lo = (wr >= 0) ? jk - off - wr : 0;
-        int hi_r = (wl >= 0) ? jk - off + wl : s1 - 1;
-        lo = max(lo, 0);
-        hi_r = min(hi_r, s1 - 1);
-        if (jk >= s2) hi_r = lo - 1;
-        vlo[kb] = (unsigned)(lo - i0);
-        vspan[kb] = (unsigned)(hi_r - lo);  // huge when empty: nothing passes
-        if (hi_r < lo) { vlo[kb] = 0x7fffffffu; vspan[kb] = 0; }
-      }
+      for (int kb = 0; kb < NKB; ++kb)
+        vis[kb] = fa_sched::window(fa_sched::rows_of_key(j0 + kw0 + kb * 32 + l32, s1, s2, off, wl, wr), i0);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int ib = r4 * 8 + hi * 4;
@@ -515,7 +502,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int rg = r4 * 4 + e;
             float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
-            p = ((unsigned)(ib + e) - vlo[kb] <= vspan[kb]) ? p : 0.f;
+            p = fa_sched::in_window(vis[kb], ib + e) ? p : 0.f;
             pa[kb][rg >> 3][rg & 7] = (bf16)p;
             da[kb][rg >> 3][rg & 7] = (bf16)(p * (pacc[kb][rg] - f4[e]));
           }
@@ -663,12 +650,10 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   const bf16* __restrict__ Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn;
 
   // keys that any row of [i0, i0 + DQ_BQ) can see
-  const int i_last = min(i0 + DQ_BQ, s1) - 1;
-  int j_lo = 0, j_hi = s2;
-  if (wl >= 0) j_lo = max(0, i0 + off - wl);
-  if (wr >= 0) j_hi = min(s2, i_last + off + wr + 1);
-  const int jb0 = (j_lo / DQ_BK) * DQ_BK;
-  const int nsteps = j_hi > j_lo ? (j_hi - jb0 + DQ_BK - 1) / DQ_BK : 0;
+  const fa_sched::Span kblk =
+      fa_sched::blocks_covering(fa_sched::keys_seen(s2, i0, min(i0 + DQ_BQ, s1), off, wl, wr), DQ_BK);
+  const int jb0 = kblk.lo * DQ_BK;
+  const int nsteps = kblk.hi - kblk.lo;
 
   // K/V blocks go straight to LDS (async), double-buffered
   TileCopy<HD, DQ_BK, 4> kcp;
@@ -718,21 +703,11 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
     if (st + 1 < nsteps) fetch(j0 + DQ_BK, buf ^ 1);
 
-    const bool full = (i0 + DQ_BQ <= s1) && (j0 + DQ_BK <= s2) &&
-                      (wr < 0 || j0 + DQ_BK - 1 <= i0 + off + wr) &&
-                      (wl < 0 || j0 >= i0 + DQ_BQ - 1 + off - wl);
+    const bool full = fa_sched::tile_full(i0, DQ_BQ, j0, DQ_BK, s1, s2, off, wl, wr);
     // keys visible to this lane's row, relative to j0 (used on partial tiles):
     // one unsigned compare per element
-    unsigned klo = 0, kspan = 0xffffffffu;
-    if (!full) {
-      int lo = (wl >= 0) ? iq + off - wl : 0;
-      int hi_k = (wr >= 0) ? iq + off + wr : s2 - 1;
-      lo = max(lo, 0);
-      hi_k = min(hi_k, s2 - 1);
-      klo = (unsigned)(lo - j0);
-      kspan = (unsigned)(hi_k - lo);
-      if (iq >= s1 || hi_k < lo) { klo = 0x7fffffffu; kspan = 0; }
-    }
+    fa_sched::Window kvis{0u, 0xffffffffu};
+    if (!full) kvis = fa_sched::window(fa_sched::keys_of_row(iq, s1, s2, off, wl, wr), j0);
     // two halves of 32 keys: S^T, dP^T, dS, then dQ += dS K for that half
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -753,7 +728,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
         for (int rg = 0; rg < 16; ++rg) {
           const int jj = mb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
           float p = __builtin_amdgcn_exp2f(s[rg] * a.scale_log2 - l2);
-          p = ((unsigned)jj - klo <= kspan) ? p : 0.f;
+          p = fa_sched::in_window(kvis, jj) ? p : 0.f;
           da[rg >> 3][rg & 7] = (bf16)(p * (dp[rg] - sf));
         }
       }

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fa_bwd_internal.h"
+#include "fa_bwd_schedule.h"
 
 namespace fabwd {
 namespace {
@@ -57,10 +58,6 @@ __device__ Seq seq_of(const KernelArgs& a, int b) {
   return r;
 }
 
-// key j visible to query row i (bottom-right aligned window bounds, -1 = open)
-__device__ __forceinline__ bool visible(const KernelArgs& a, int i, int j, int off) {
-  return (a.win_left < 0 || j >= i + off - a.win_left) && (a.win_right < 0 || j <= i + off + a.win_right);
-}
 
 __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   __shared__ float Ks[F32_BK][F32_MAXD + 1];   // +1: conflict-free column walks
@@ -92,10 +89,9 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   }
 
   // rows that can see a key of the tile
-  const int j1 = min(j0 + F32_BK, sq.s2) - 1;
-  int i_lo = 0, i_hi = sq.s1;
-  if (a.win_right >= 0) i_lo = max(0, j0 - off - a.win_right);
-  if (a.win_left >= 0) i_hi = min(sq.s1, j1 - off + a.win_left + 1);
+  const fa_sched::Span rows =
+      fa_sched::rows_seeing(sq.s1, j0, min(j0 + F32_BK, sq.s2), off, a.win_left, a.win_right);
+  const int i_lo = rows.lo, i_hi = rows.hi;
 
   const int pr = t / F32_BK, pj = t % F32_BK;   // pair role: row pr of the chunk, key pj
   const int ak = t / 8, sl = t % 8;             // accumulation role: key ak, columns sl, sl+8, ...
@@ -126,7 +122,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
       {
         const int i = c0 + pr, j = j0 + pj;
         float p = 0.f, ds = 0.f;
-        if (i < i_hi && j < sq.s2 && visible(a, i, j, off) && lse_s[pr] != -__builtin_inff()) {
+        if (i < i_hi && fa_sched::visible(i, j, sq.s1, sq.s2, off, a.win_left, a.win_right) &&
+            lse_s[pr] != -__builtin_inff()) {
           float s = 0.f, dp = 0.f;
           for (int d = 0; d < D; ++d) s = fmaf(Qr[pr][d], Ks[pj][d], s);
           for (int d = 0; d < Dv; ++d) dp = fmaf(Yr[pr][d], Vs[pj][d], dp);
@@ -198,10 +195,9 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
   }
 
   // keys that a row of the tile can see
-  const int i1 = min(i0 + F32_BQ, sq.s1) - 1;
-  int j_lo = 0, j_hi = sq.s2;
-  if (a.win_left >= 0) j_lo = max(0, i0 + off - a.win_left);
-  if (a.win_right >= 0) j_hi = min(sq.s2, i1 + off + a.win_right + 1);
+  const fa_sched::Span keys =
+      fa_sched::keys_seen(sq.s2, i0, min(i0 + F32_BQ, sq.s1), off, a.win_left, a.win_right);
+  const int j_lo = keys.lo, j_hi = keys.hi;
 
   const int pr = t / F32_CH, pc = t % F32_CH;   // pair role: row pr, key pc of the chunk
   const int ar = t / 8, sl = t % 8;             // accumulation role: row ar, columns sl, sl+8, ...
@@ -221,7 +217,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
     {
       const int i = i0 + pr, j = c0 + pc;
       float ds = 0.f;
-      if (i < sq.s1 && j < j_hi && visible(a, i, j, off) && lse_s[pr] != -__builtin_inff()) {
+      if (j < j_hi && fa_sched::visible(i, j, sq.s1, sq.s2, off, a.win_left, a.win_right) &&
+          lse_s[pr] != -__builtin_inff()) {
         float s = 0.f, dp = 0.f;
         for (int d = 0; d < D; ++d) s = fmaf(Qs[pr][d], Kc[pc][d], s);
         for (int d = 0; d < Dv; ++d) dp = fmaf(Ys[pr][d], Vc[pc][d], dp);

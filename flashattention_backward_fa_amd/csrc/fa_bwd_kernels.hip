@@ -37,6 +37,7 @@
 #include <new>
 
 #include "fa_bwd_internal.h"
+#include "fa_bwd_schedule.h"
 
 namespace fabwd {
 
@@ -235,9 +236,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
   const int tr_r8 = 8 * hi + ((lane & 15) >> 2);             // row pattern of contiguous chunks
 
   // query rows that see at least one key of [j0, j1)
-  int i_lo = 0, i_hi = s1;
-  if (wr >= 0) i_lo = max(0, j0 - off - wr);
-  if (wl >= 0) i_hi = min(s1, j1 - off + wl);
+  const fa_sched::Span qblk = fa_sched::blocks_covering(fa_sched::rows_seeing(s1, j0, j1, off, wl, wr), BR);
 
   for (int g = 0; g < a.G; ++g) {
     const int n1 = n2 * a.G + g;
@@ -247,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
     const float* __restrict__ Lg = a.lse + lbase + (int64_t)n1 * a.l_sn;
     const float* __restrict__ Fg = a.sfmg + lbase + (int64_t)n1 * a.l_sn;
 
-    for (int i0 = (i_lo / BR) * BR; i0 < i_hi; i0 += BR) {
+    for (int i0 = qblk.lo * BR; i0 < qblk.hi * BR; i0 += BR) {
       // ---- stage Q, dY, lse, sfmg of rows [i0, i0 + BR) in LDS
       for (int c = tid; c < BR * (HD / 8); c += 256) {
         const int r = c / (HD / 8), cc = (c % (HD / 8)) * 8;
@@ -294,9 +293,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
       }
 
       // ---- P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), both packed as bf16
-      const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) &&
-                        (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
-                        (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
+      const bool full = fa_sched::tile_full(i0, BR, j0, BC, s1, s2, off, wl, wr);
       const int jk = j0 + kw;
       bf16x8 pa[2 * NMB], da[2 * NMB];
 #pragma unroll
@@ -312,8 +309,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KernelArgs a) {
             float p = __builtin_amdgcn_exp2f(sacc[mb][r] * a.scale_log2 - l4[e]);
             if (!full) {
               const int i = i0 + ib + e;
-              const bool vis = (i < s1) && (jk < s2) && (wl < 0 || jk >= i + off - wl) &&
-                               (wr < 0 || jk <= i + off + wr);
+              const bool vis = fa_sched::visible(i, jk, s1, s2, off, wl, wr);
               p = vis ? p : 0.f;
             }
             const float ds = p * (pacc[mb][r] - f4[e]);
@@ -489,11 +485,9 @@ __global__ __launch_bounds__(512, 1) void bwd_main_v2_kernel(KernelArgs a) {
   }
 
   // ---- query blocks that see a key of [j0, j1), for each head of the job
-  int i_lo = 0, i_hi = s1;
-  if (wr >= 0) i_lo = max(0, j0 - off - wr);
-  if (wl >= 0) i_hi = min(s1, j1 - off + wl);
-  const int blk_lo = i_lo / BR;
-  const int nblk = i_hi > i_lo ? (i_hi + BR - 1) / BR - blk_lo : 0;
+  const fa_sched::Span qblk = fa_sched::blocks_covering(fa_sched::rows_seeing(s1, j0, j1, off, wl, wr), BR);
+  const int blk_lo = qblk.lo;
+  const int nblk = qblk.hi - qblk.lo;
   const int T = hpj * nblk;
   const int g0 = gslot * hpj;
 
@@ -590,8 +584,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_v2_kernel(KernelArgs a) {
         const bf16x8 ya = *reinterpret_cast<const bf16x8*>(&Yg_s[l32 * VP + 16 * kk + 8 * hi]);
         pacc = mfma32(ya, vb, pacc);
       }
-      const bool full = (i0 + BR <= s1) && (j0 + BC <= s2) && (wr < 0 || j0 + BC - 1 <= i0 + off + wr) &&
-                        (wl < 0 || j0 >= i0 + BR - 1 + off - wl);
+      const bool full = fa_sched::tile_full(i0, BR, j0, BC, s1, s2, off, wl, wr);
       bf16x8 pa[2], da[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -604,7 +597,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_v2_kernel(KernelArgs a) {
           float p = __builtin_amdgcn_exp2f(sacc[rg] * a.scale_log2 - l4[e]);
           if (!full) {
             const int i = i0 + ib + e;
-            const bool vis = (i < s1) && (jk < s2) && (wl < 0 || jk >= i + off - wl) && (wr < 0 || jk <= i + off + wr);
+            const bool vis = fa_sched::visible(i, jk, s1, s2, off, wl, wr);
             p = vis ? p : 0.f;
           }
           const float ds = p * (pacc[rg] - f4[e]);

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fa_bwd_internal.h"
+#include "fa_bwd_schedule.h"
 
 namespace fabwd {
 namespace {
@@ -103,10 +104,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
   }
 
   // keys that any row of [i0, i0 + FQ) can see
-  const int i_last = min(i0 + FQ, s1) - 1;
-  int j_lo = 0, j_hi = s2;
-  if (wl >= 0) j_lo = max(0, i0 + off - wl);
-  if (wr >= 0) j_hi = min(s2, i_last + off + wr + 1);
+  const fa_sched::Span kblk =
+      fa_sched::blocks_covering(fa_sched::keys_seen(s2, i0, min(i0 + FQ, s1), off, wl, wr), FK);
 
   const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
@@ -116,7 +115,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
   for (int nb = 0; nb < NB; ++nb) o[nb] = floatx16{};
   float m = -__builtin_inff(), l = 0.f;
 
-  for (int j0 = (j_lo / FK) * FK; j0 < j_hi; j0 += FK) {
+  for (int j0 = kblk.lo * FK; j0 < kblk.hi * FK; j0 += FK) {
     __syncthreads();
     for (int c = tid; c < FK * (HD / 8); c += 256) {
       const int r = c / (HD / 8), cc = (c % (HD / 8)) * 8;
@@ -144,9 +143,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
       }
     }
     // scores in log2 units, masked to -inf
-    const bool full = (i0 + FQ <= s1) && (j0 + FK <= s2) &&
-                      (wr < 0 || j0 + FK - 1 <= i0 + off + wr) &&
-                      (wl < 0 || j0 >= i0 + FQ - 1 + off - wl);
+    const bool full = fa_sched::tile_full(i0, FQ, j0, FK, s1, s2, off, wl, wr);
     float mx = -__builtin_inff();
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -155,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
         float x = s[mb][r] * a.scale_log2;
         if (!full) {
           const int j = j0 + mb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          const bool vis = (iq < s1) && (j < s2) && (wl < 0 || j >= iq + off - wl) && (wr < 0 || j <= iq + off + wr);
+          const bool vis = fa_sched::visible(iq, j, s1, s2, off, wl, wr);
           x = vis ? x : -__builtin_inff();
         }
         s[mb][r] = x;

@@ -37,21 +37,26 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc", "fa_bwd_det_kernels.hip")
+CSRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc")
+# the sources the timed dK/dV and dQ kernels are compiled from
+KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_det_kernels.hip", "fa_bwd_schedule.h",
+                                                    "fa_bwd_internal.h"))
 COPY_BYTES = 256 << 20
 XCDS = 8        # MI355X: 8 XCDs of 32 CUs
 SIMDS = 1024    # 256 CUs x 4 SIMDs
 
 
-def kernel_code_hash(path=KERNEL_SRC):
-    """sha256 (16 hex digits) of the kernel source with comments and blank
+def kernel_code_hash(paths=KERNEL_SRCS):
+    """sha256 (16 hex digits) of the kernel sources with comments and blank
     lines removed: a summary stays valid across comment-only edits and goes
     stale on any change to the code."""
-    text = open(path, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-    code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
+    parts = []
+    for path in paths:
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        parts.append("\n".join(ln for ln in lines if ln.strip()))
+    return hashlib.sha256("\n\f\n".join(parts).encode("utf-8")).hexdigest()[:16]
 
 
 def _rows(d):

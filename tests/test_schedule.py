@@ -1,0 +1,205 @@
+"""Brute-force check of the kernels' tile schedule (host logic, no GPU).
+
+Every kernel skips work through the ranges of csrc/fa_bwd_schedule.h: the
+query blocks a key tile visits (and their split over jobs), the key blocks a
+query tile visits, the full-tile test that drops the element mask, and the
+per-row / per-key windows applied inside partial tiles.  A host-compiled shim
+over that header is checked here against the oracle's mask
+(oracle.allowed_matrix, pinned by the oracle tests) on every tile pair of many
+shapes: bands of page "CANN ops-transformer FlashAttnGrad 算子详解", section
+四 4.3 (none, causal with and without a left bound, two-sided windows), with
+s1 < s2, s1 = s2 and s1 > s2 and lengths that are and are not tile multiples.
+A visited block with no visible pair is wasted work; a skipped block with one is
+a wrong gradient; both fail here."""
+
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SHIM = os.path.join(ROOT, "tests", "schedule", "sched_shim.cpp")
+
+
+@pytest.fixture(scope="module")
+def sched(tmp_path_factory):
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    so = str(tmp_path_factory.mktemp("sched") / "libsched.so")
+    subprocess.run([cxx, "-std=c++17", "-O1", "-Wall", "-Werror", "-shared", "-fPIC", SHIM, "-o", so], check=True)
+    lib = ctypes.CDLL(so)
+    i32 = ctypes.c_int
+    out2 = ctypes.POINTER(ctypes.c_int)
+    lib.sched_visible.argtypes = [i32] * 6
+    lib.sched_key_tile_blocks.argtypes = [i32] * 9 + [out2]
+    lib.sched_rows_seeing.argtypes = [i32] * 6 + [out2]
+    lib.sched_query_tile_blocks.argtypes = [i32] * 7 + [out2]
+    lib.sched_keys_seen.argtypes = [i32] * 6 + [out2]
+    lib.sched_tile_full.argtypes = [i32] * 8
+    lib.sched_window_mask.argtypes = [i32] * 8 + [ctypes.POINTER(ctypes.c_ubyte)]
+    return lib
+
+
+def _pair(fn, *args):
+    buf = (ctypes.c_int * 2)()
+    fn(*args, buf)
+    return buf[0], buf[1]
+
+
+def _span_of(mask):
+    """[first, last + 1) of the True entries of a 1-D mask (asserting they are
+    contiguous), or None when there are none."""
+    idx = np.flatnonzero(mask)
+    if idx.size == 0:
+        return None
+    assert idx[-1] - idx[0] + 1 == idx.size, "band visibility is contiguous"
+    return int(idx[0]), int(idx[-1]) + 1
+
+
+def _bands():
+    # (mask_mode, win_left, win_right) as a caller passes them
+    return [(0, -1, -1), (1, -1, -1), (1, 0, -1), (1, 1, -1), (1, 37, -1), (1, 64, -1), (2, 0, 0), (2, 5, 3),
+            (2, -1, 0), (2, 0, -1), (2, -1, 11), (2, 37, 11), (2, 128, 1), (2, 1, 128), (2, 1000, 1000)]
+
+
+LENGTHS = [(1, 1), (1, 300), (300, 1), (31, 31), (32, 32), (33, 65), (64, 64), (100, 260), (128, 128),
+           (129, 129), (200, 333), (257, 130), (260, 100), (300, 300)]
+
+
+def _cases():
+    for s1, s2 in LENGTHS:
+        for mode, wl, wr in _bands():
+            yield s1, s2, mode, wl, wr
+
+
+def test_visible_matches_oracle_mask(sched):
+    for s1, s2, mode, wl, wr in _cases():
+        L, R = oracle.mask_bounds(mode, wl, wr)
+        ok = oracle.allowed_matrix(s1, s2, L, R)
+        for i in sorted({0, s1 // 2, s1 - 1}):
+            for j in range(-1, s2 + 2):
+                want = bool(0 <= j < s2 and ok[i, j])
+                assert bool(sched.sched_visible(i, j, s1, s2, L, R)) == want, (s1, s2, L, R, i, j)
+        assert not sched.sched_visible(s1, 0, s1, s2, L, R)
+        assert not sched.sched_visible(-1, 0, s1, s2, L, R)
+
+
+@pytest.mark.parametrize("br,bc", [(32, 128), (64, 64), (128, 128), (128, 32)])
+def test_key_tile_query_blocks(sched, br, bc):
+    """dK/dV side: for each key tile, the query blocks visited are exactly the
+    blocks holding a row that sees a key of the tile, and every split of them
+    over 1..4 jobs partitions that range in order."""
+    for s1, s2, mode, wl, wr in _cases():
+        L, R = oracle.mask_bounds(mode, wl, wr)
+        ok = oracle.allowed_matrix(s1, s2, L, R)
+        nblk_q = -(-s1 // br)
+        for j0 in range(0, s2, bc):
+            j1 = min(j0 + bc, s2)
+            rows = ok[:, j0:j1].any(axis=1)
+            want_rows = _span_of(rows)
+            lo, hi = _pair(sched.sched_rows_seeing, s1, s2, j0, j1, L, R)
+            if want_rows is None:
+                assert hi <= lo, (s1, s2, L, R, j0)
+            else:
+                assert (lo, hi) == want_rows, (s1, s2, L, R, j0)
+            blk_has = np.array([rows[b * br:(b + 1) * br].any() for b in range(nblk_q)], dtype=bool)
+            want_blk = _span_of(blk_has)
+            b_lo, b_hi = _pair(sched.sched_key_tile_blocks, s1, s2, j0, bc, br, 0, 1, L, R)
+            if want_blk is None:
+                assert b_hi <= b_lo
+            else:
+                assert (b_lo, b_hi) == want_blk, (s1, s2, L, R, j0, br, bc)
+            for parts in (2, 3, 4):
+                cur = b_lo
+                for p in range(parts):
+                    p_lo, p_hi = _pair(sched.sched_key_tile_blocks, s1, s2, j0, bc, br, p, parts, L, R)
+                    assert p_lo == cur and p_hi >= p_lo
+                    cur = p_hi
+                assert cur == max(b_hi, b_lo)
+
+
+@pytest.mark.parametrize("bq,bk", [(128, 64), (64, 64), (32, 32), (128, 128)])
+def test_query_tile_key_blocks(sched, bq, bk):
+    """dQ and forward side: for each query tile, the key blocks visited are
+    exactly the blocks holding a key that a row of the tile sees."""
+    for s1, s2, mode, wl, wr in _cases():
+        L, R = oracle.mask_bounds(mode, wl, wr)
+        ok = oracle.allowed_matrix(s1, s2, L, R)
+        nblk_k = -(-s2 // bk)
+        for i0 in range(0, s1, bq):
+            i1 = min(i0 + bq, s1)
+            keys = ok[i0:i1].any(axis=0)
+            lo, hi = _pair(sched.sched_keys_seen, s1, s2, i0, i1, L, R)
+            want = _span_of(keys)
+            if want is None:
+                assert hi <= lo, (s1, s2, L, R, i0)
+            else:
+                assert (lo, hi) == want, (s1, s2, L, R, i0)
+            blk_has = np.array([keys[b * bk:(b + 1) * bk].any() for b in range(nblk_k)], dtype=bool)
+            b_lo, b_hi = _pair(sched.sched_query_tile_blocks, s1, s2, i0, bq, bk, L, R)
+            want_blk = _span_of(blk_has)
+            if want_blk is None:
+                assert b_hi <= b_lo
+            else:
+                assert (b_lo, b_hi) == want_blk, (s1, s2, L, R, i0, bq, bk)
+
+
+@pytest.mark.parametrize("bi,bj", [(32, 128), (128, 64), (64, 64), (128, 128)])
+def test_tile_full_is_exact(sched, bi, bj):
+    """A tile takes the unmasked path iff it lies inside the sequence and every
+    pair in it is visible."""
+    for s1, s2, mode, wl, wr in _cases():
+        L, R = oracle.mask_bounds(mode, wl, wr)
+        ok = oracle.allowed_matrix(s1, s2, L, R)
+        for i0 in range(0, s1, bi):
+            for j0 in range(0, s2, bj):
+                inside = i0 + bi <= s1 and j0 + bj <= s2
+                want = inside and bool(ok[i0:i0 + bi, j0:j0 + bj].all())
+                got = bool(sched.sched_tile_full(i0, bi, j0, bj, s1, s2, L, R))
+                assert got == want, (s1, s2, L, R, i0, j0, bi, bj)
+
+
+def test_element_windows_match_mask(sched):
+    """Inside a partial tile each row keeps the keys of its window and each key
+    the rows of its window; rows and keys past the ends keep nothing."""
+    n = 128
+    buf = (ctypes.c_ubyte * n)()
+    for s1, s2, mode, wl, wr in _cases():
+        L, R = oracle.mask_bounds(mode, wl, wr)
+        ok = oracle.allowed_matrix(s1, s2, L, R)
+        for i in sorted({0, 1, s1 // 3, s1 - 1, s1, s1 + 5}):
+            for j0 in range(0, s2 + 1, 64):
+                sched.sched_window_mask(1, i, j0, n, s1, s2, L, R, buf)
+                got = np.frombuffer(buf, dtype=np.uint8).astype(bool)
+                want = np.zeros(n, dtype=bool)
+                if i < s1:
+                    seg = ok[i, j0:j0 + n]
+                    want[:seg.size] = seg
+                assert np.array_equal(got, want), (s1, s2, L, R, i, j0)
+        for j in sorted({0, 1, s2 // 3, s2 - 1, s2, s2 + 5}):
+            for i0 in range(0, s1 + 1, 32):
+                sched.sched_window_mask(0, j, i0, n, s1, s2, L, R, buf)
+                got = np.frombuffer(buf, dtype=np.uint8).astype(bool)
+                want = np.zeros(n, dtype=bool)
+                if j < s2:
+                    seg = ok[i0:i0 + n, j]
+                    want[:seg.size] = seg
+                assert np.array_equal(got, want), (s1, s2, L, R, j, i0)
+
+
+def test_check_fails_on_a_planted_off_by_one(sched):
+    """The brute force is sharp: shifting the oracle's band by one key (a
+    plausible off-by-one in either side) is caught by the same comparison."""
+    s1 = s2 = 130
+    L, R = 37, 0
+    ok = oracle.allowed_matrix(s1, s2, L, R)
+    shifted = oracle.allowed_matrix(s1, s2, L + 1, R)
+    lo, hi = _pair(sched.sched_rows_seeing, s1, s2, 0, 1, L, R)
+    assert (lo, hi) == _span_of(ok[:, 0:1].any(axis=1))
+    assert (lo, hi) != _span_of(shifted[:, 0:1].any(axis=1))

@@ -1,11 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the FlashAttention backward on one MI355X.
 
-One step = one fa_bwd_run over one batch of the workload: the sfmg
-preprocess, the dK/dV kernel (S/P recompute, dP, dS, dV, dK over key tiles),
-the dQ kernel (S/P/dP/dS recompute and dQ over query tiles) and the fp32
-partial-sum reduce when the plan splits a key tile, with every input already
-resident in HBM.  attn_out and softmax_lse come from the library's own GPU
+One step = one fa_bwd_run over one batch of the workload: the dQ kernel
+(S/P/dP/dS recompute and dQ over query tiles; it also forms sfmg =
+rowsum(dY * Y) for its rows), the dK/dV kernel (S/P recompute, dP, dS, dV, dK
+over key tiles) and the fp32 partial-sum reduce when the plan splits a key
+tile, with every input already resident in HBM.  attn_out and softmax_lse come from the library's own GPU
 forward (fa_fwd_run), made once before timing.  The default workload is the
 GQA causal one (B=1, N1=32, N2=8, S=4096, D=Dv=128, BSND).
 
@@ -13,8 +13,8 @@ Prints one JSON line: whole-step throughput in TFLOP/s under the standard
 FLOP count (2*(3D+2Dv) per visible (query, key) pair per query head; causal
 with S1 = S2 counted as exactly half of S1*S2); the roofline entry of the
 MFMA-bound kernel pair from HIP events the library records around it inside
-the timed region; the preprocess kernel's HBM bandwidth (its own timed
-launches); the fp64 CPU oracle timed on a bounded sample of the same
+the timed region; the standalone sfmg preprocess kernel's HBM bandwidth
+(its own timed launches; the default step forms sfmg inside the dQ kernel); the fp64 CPU oracle timed on a bounded sample of the same
 workload; and `accuracy`: the library's gradients on that sample (made from
 the oracle forward's stored Y and lse) against the oracle's, every element,
 so that the speed figure comes with its parity error.
@@ -345,6 +345,7 @@ def main():
             "bound": "hbm", "kernel": "preprocess_kernel (sfmg)", "achieved": round(pre_gbs, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4),
             "bytes_per_launch": pre_bytes, "avg_launch_ms": round(pre_ms, 5),
+            "note": "standalone fa_bwd_sfmg entry point; the default step forms sfmg inside dq_kernel",
         },
         "configs": None,
         "cpu_baseline": None,

@@ -269,11 +269,11 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
     return FA_OK;
   }
   if (a.variant == 2) {
-    // sfmg -> dK/dV kernel -> dQ kernel -> partial-sum reduce (when split)
-    if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
+    // dQ kernel (which also forms sfmg) -> dK/dV kernel (which reads it) ->
+    // partial-sum reduce (when a key tile is split over jobs)
     if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
-    if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_dq(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
     return FA_OK;

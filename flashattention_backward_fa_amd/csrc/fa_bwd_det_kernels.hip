@@ -679,12 +679,25 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     if (iq < s1) val = *reinterpret_cast<const bf16x8*>(Yg + (int64_t)iq * a.o_ss + 16 * kk + 8 * hi);
     yf[kk] = val;
   }
+  // sfmg = rowsum(dY * Y) of this lane's row: the dY fragments above times Y
+  // read in the same layout (lanes l and l ^ 32 hold the two halves of the
+  // row's columns), in fp32; written out for the dK/dV kernel, which runs next
+  const int64_t lrow = sb.lbase + (int64_t)n1 * a.l_sn + iq;
   float l2 = __builtin_inff(), sf = 0.f;
   if (iq < s1) {
-    const float l = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + iq];
+    const bf16* __restrict__ Og =
+        static_cast<const bf16*>(a.out) + sb.obase + (int64_t)n1 * a.o_sn + (int64_t)iq * a.o_ss;
+#pragma unroll
+    for (int kk = 0; kk < NKV; ++kk) {
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(Og + 16 * kk + 8 * hi);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sf += (float)yf[kk][e] * (float)y[e];
+    }
+    const float l = a.lse[lrow];
     l2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
-    sf = a.sfmg[sb.lbase + (int64_t)n1 * a.l_sn + iq];
   }
+  sf += __shfl_xor(sf, 32);
+  if (iq < s1 && hi == 0) a.sfmg[lrow] = sf;
 
   SwzTile<HD, DQ_BK> kadr;
   SwzTile<HDV, DQ_BK> vadr;
@@ -760,14 +773,25 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
 
 // ------------------------------------------------------------------ partial sums
 
-// dk = bf16(sum over parts), dv likewise; 8 elements per thread.
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ part, int64_t part_stride,
-                                                           int nparts, bf16* __restrict__ out, int64_t n8) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+// dk = bf16(sum over parts) and dv likewise in one launch: blocks below
+// `kblocks` take dK, the rest dV; 8 elements per thread, parts added in index
+// order (so the result is repeatable).
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ kpart, int64_t k_stride,
+                                                           bf16* __restrict__ kout, const float* __restrict__ vpart,
+                                                           int64_t v_stride, bf16* __restrict__ vout, int nparts,
+                                                           int kblocks) {
+  const bool is_k = (int)blockIdx.x < kblocks;
+  const float* __restrict__ part = is_k ? kpart : vpart;
+  const int64_t stride = is_k ? k_stride : v_stride;
+  bf16* __restrict__ out = is_k ? kout : vout;
+  const int64_t n8 = stride / 8;
+  const int64_t nblk = is_k ? kblocks : (int64_t)gridDim.x - kblocks;
+  const int64_t blk = is_k ? blockIdx.x : blockIdx.x - kblocks;
+  for (int64_t i = blk * 256 + threadIdx.x; i < n8; i += nblk * 256) {
     floatx4 s0 = reinterpret_cast<const floatx4*>(part)[2 * i];
     floatx4 s1 = reinterpret_cast<const floatx4*>(part)[2 * i + 1];
     for (int p = 1; p < nparts; ++p) {
-      const float* q = part + (int64_t)p * part_stride;
+      const float* q = part + (int64_t)p * stride;
       s0 += reinterpret_cast<const floatx4*>(q)[2 * i];
       s1 += reinterpret_cast<const floatx4*>(q)[2 * i + 1];
     }
@@ -831,17 +855,15 @@ int launch_dq(const KernelArgs& a, void* stream) {
 int launch_reduce_parts(const KernelArgs& a, void* stream) {
   if (a.n_partials <= 1) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto one = [&](const float* part, int64_t stride, void* out, int64_t elems) -> int {
-    const int64_t n8 = elems / 8;
-    int64_t blocks = (n8 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    if (blocks <= 0) return 0;
-    return launch(reduce_parts_kernel, dim3((unsigned)blocks), dim3(256), s, part, stride, a.n_partials,
-                  static_cast<bf16*>(out), n8);
+  auto blocks = [](int64_t elems) -> int64_t {
+    const int64_t b = (elems / 8 + 255) / 256;
+    return b > 4096 ? 4096 : b;
   };
-  int e = one(a.dk_acc, a.k_part_stride, a.dk, a.k_part_stride);
-  if (e == 0) e = one(a.dv_acc, a.v_part_stride, a.dv, a.v_part_stride);
-  return e;
+  const int64_t kb = blocks(a.k_part_stride), vb = blocks(a.v_part_stride);
+  if (kb <= 0 || vb <= 0) return 0;
+  return launch(reduce_parts_kernel, dim3((unsigned)(kb + vb)), dim3(256), s, (const float*)a.dk_acc, a.k_part_stride,
+                static_cast<bf16*>(a.dk), (const float*)a.dv_acc, a.v_part_stride, static_cast<bf16*>(a.dv),
+                a.n_partials, (int)kb);
 }
 
 }  // namespace fabwd

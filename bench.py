@@ -19,8 +19,12 @@ workload; and `accuracy`: the library's gradients on that sample (made from
 the oracle forward's stored Y and lse) against the oracle's, every element,
 so that the speed figure comes with its parity error.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload gqa_causal]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--settle 0.5] [--workload gqa_causal]
                     [--no-cpu-baseline] [--no-configs] [--copy-calibration]
+
+Before the warmup steps, untimed steps run for --settle seconds: the shader
+clock ramps up over the first tens of milliseconds of load and drops again
+while the host builds inputs, so a short warmup alone times a cold clock.
 
 The line also carries `configs`: the same step, pair and preprocess figures
 for every benchmark configuration (10 timed steps each).
@@ -211,11 +215,14 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
-def measure(name, steps, warmup):
-    """Time `steps` backward steps of a workload (after `warmup` untimed ones)
-    on the current stream: whole-step time from events around the loop, the
-    dK/dV + dQ pair from the library's events, and the preprocess kernel over
-    its own launches.  Returns times in ms and the preprocess bytes."""
+def measure(name, steps, warmup, settle_s=0.0):
+    """Time `steps` backward steps of a workload on the current stream, after
+    untimed steps for at least `settle_s` seconds (the shader clock ramps up
+    over the first tens of milliseconds of load, and drops again while the host
+    builds the next workload's inputs) and then `warmup` untimed ones:
+    whole-step time from events around the loop, the dK/dV + dQ pair from the
+    library's events, and the preprocess kernel over its own launches.
+    Returns times in ms, the preprocess bytes and the settle step count."""
     import torch
     from flashattention_backward_fa_amd import fa_bwd as fb
     from flashattention_backward_fa_amd import workloads as W
@@ -242,6 +249,13 @@ def measure(name, steps, warmup):
     def step():
         fb.flash_attn_grad(q, k, v, dout, attn_out, lse, cu_q, cu_kv, workspace=ws, out=(dq, dk, dv), **kw)
 
+    settle_steps = 0
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 8
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -279,7 +293,7 @@ def measure(name, steps, warmup):
     torch.cuda.synchronize()
     pre_ms = p0.elapsed_time(p1) / pre_iters
     return dict(ms_per_step=ms_per_step, pair_ms=main_avg, pair_launches=len(main_ms), pre_ms=pre_ms,
-                pre_bytes=pre_bytes)
+                pre_bytes=pre_bytes, settle_steps=settle_steps)
 
 
 def main():
@@ -287,6 +301,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (clock ramp-up)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (cpu_baseline and accuracy)")
     ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
@@ -306,7 +322,7 @@ def main():
 
     name = args.workload or W.BENCH_WORKLOAD
     cfg = W.CONFIGS[name]
-    m = measure(name, args.steps, args.warmup)
+    m = measure(name, args.steps, args.warmup, args.settle)
     ms_per_step, main_avg, pre_ms, pre_bytes = m["ms_per_step"], m["pair_ms"], m["pre_ms"], m["pre_bytes"]
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
 
@@ -322,6 +338,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "settle": {"seconds": args.settle, "untimed_steps": m["settle_steps"],
+                   "why": "untimed steps before the warmup so that the timed steps run at the steady-state clock"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -362,7 +380,7 @@ def main():
                 r = m
             else:
                 torch.cuda.empty_cache()
-                r = measure(other, 10, 2)
+                r = measure(other, 10, 2, args.settle)
             f = algorithmic_flops(W.CONFIGS[other])
             rows[other] = {
                 "ms_per_step": round(r["ms_per_step"], 4),

@@ -442,12 +442,16 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
 
   floatx16 sacc[NKB], pacc[NKB];
   // S = Q K^T and dP = dY V^T for this wavefront's KPW keys
+  // Each run of MFMAs raises the wavefront's issue priority, so that on a SIMD
+  // shared by two wavefronts the one with matrix work issues first and the
+  // other's exp / LDS work fills the MFMA pipe's shadow.
   auto phase_a = [&](int buf) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       sacc[kb] = floatx16{};
       pacc[kb] = floatx16{};
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < NKQ; ++kk) {
       const bf16x8 qa = lds_load16(qadr.row_read(kk, buf * QTB));
@@ -460,6 +464,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) pacc[kb] = mfma32(ya, lds_load16(v_lane + (kb * 32 * VP + 16 * kk) * 2), pacc[kb]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // P, dS (masked when the tile is partial), then dV += P^T dY and dK += dS^T Q
   auto phase_b = [&](int buf, int i0) {
@@ -511,6 +516,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     }
 
     // dV += P^T dY, dK += dS^T Q; one transposing read serves all key blocks
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
@@ -526,6 +532,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
         for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32(da[kb][kc], qb, dKr[kb][nb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Step it: wait for item t's tile (buffer buf), prefetch item t + QG into
@@ -721,14 +728,17 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     // one unsigned compare per element
     fa_sched::Window kvis{0u, 0xffffffffu};
     if (!full) kvis = fa_sched::window(fa_sched::keys_of_row(iq, s1, s2, off, wl, wr), j0);
-    // two halves of 32 keys: S^T, dP^T, dS, then dQ += dS K for that half
+    // two halves of 32 keys: S^T, dP^T, dS, then dQ += dS K for that half;
+    // the MFMA runs raise the wavefront's issue priority as in the dK/dV kernel
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       floatx16 s = {}, dp = {};
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < NKQ; ++kk) s = mfma32(lds_load16(kadr.row_read_at(kk, mb * 32, buf * KTB)), qf[kk], s);
 #pragma unroll
       for (int kk = 0; kk < NKV; ++kk) dp = mfma32(lds_load16(vadr.row_read_at(kk, mb * 32, buf * VTB)), yf[kk], dp);
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 da[2];
       if (full) {
 #pragma unroll
@@ -745,6 +755,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
           da[rg >> 3][rg & 7] = (bf16)(p * (dp[rg] - sf));
         }
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int kc = mb * 2 + c;
@@ -755,6 +766,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
           dq[nb] = mfma32(da[c], kb, dq[nb]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
   for (int st = 0; st < nsteps; ++st) step(st, st & 1);

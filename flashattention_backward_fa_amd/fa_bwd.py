@@ -161,42 +161,44 @@ class Plan:
         st = lib.fa_bwd_create(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(ws))
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_create")
+        self._lib = lib  # the handle belongs to this library instance
         self.handle = h
         self.workspace_bytes = ws.value
         self.layout = desc.layout
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and _lib is not None:
-            _lib.fa_bwd_destroy(h)
+        lib = getattr(self, "_lib", None)
+        if h is not None and lib is not None:
+            lib.fa_bwd_destroy(h)
             self.handle = None
 
     def run(self, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv, workspace, workspace_bytes, stream):
-        st = load_library().fa_bwd_run(self.handle, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv,
+        st = self._lib.fa_bwd_run(self.handle, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv,
                                        workspace, workspace_bytes, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_run")
 
     def forward(self, q, k, v, cu_q, cu_kv, attn_out, lse, stream):
-        st = load_library().fa_fwd_run(self.handle, q, k, v, cu_q, cu_kv, attn_out, lse, stream)
+        st = self._lib.fa_fwd_run(self.handle, q, k, v, cu_q, cu_kv, attn_out, lse, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_fwd_run")
 
     def profile_enable(self, slots):
-        st = load_library().fa_bwd_profile_enable(self.handle, int(slots))
+        st = self._lib.fa_bwd_profile_enable(self.handle, int(slots))
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_profile_enable")
 
     def profile_read(self, cap):
         buf = (ctypes.c_float * max(int(cap), 1))()
         n = ctypes.c_int()
-        st = load_library().fa_bwd_profile_read(self.handle, buf, int(cap), ctypes.byref(n))
+        st = self._lib.fa_bwd_profile_read(self.handle, buf, int(cap), ctypes.byref(n))
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_profile_read")
         return [buf[i] for i in range(n.value)]
 
     def sfmg(self, dout, attn_out, cu_q, out, stream):
-        st = load_library().fa_bwd_sfmg(self.handle, dout, attn_out, cu_q, out, stream)
+        st = self._lib.fa_bwd_sfmg(self.handle, dout, attn_out, cu_q, out, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_sfmg")
 

@@ -89,8 +89,6 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     if (S1 <= 0 || S2 <= 0) return FA_ERR_SHAPE;
   }
 
-  // valid on the page, not built here
-  if (d.dtype == FA_DTYPE_FP16) return FA_ERR_UNSUPPORTED;
   if (!fabwd::main_instantiated(d.D, d.Dv) || !fabwd::det_instantiated(d.D, d.Dv)) return FA_ERR_UNSUPPORTED;
 
   KernelArgs& a = p.args;
@@ -99,6 +97,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   a.S1 = (int32_t)S1; a.S2 = (int32_t)S2;
   a.D = d.D; a.Dv = d.Dv;
   a.varlen = tnd ? 1 : 0;
+  a.f16 = d.dtype == FA_DTYPE_FP16 ? 1 : 0;
   a.layout = d.layout;
   a.T1 = tnd ? d.T1 : 0; a.T2 = tnd ? d.T2 : 0;
   const int64_t N1 = d.N1, N2 = d.N2, D = d.D, Dv = d.Dv;
@@ -141,11 +140,12 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
 
   // Kernel choice.  Default: the atomic-free pair (dK/dV kernel over key
   // tiles, dQ kernel over query tiles); dQ is then bitwise repeatable.
-  // FA_BWD_VARIANT=0/1 selects the fp32-atomic dQ kernels instead (tuning).
+  // FA_BWD_VARIANT=0/1 selects the fp32-atomic dQ kernels instead (tuning,
+  // bf16 only).
   const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
   const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
   a.variant = 2;
-  if (const char* e = std::getenv("FA_BWD_VARIANT")) {
+  if (const char* e = std::getenv("FA_BWD_VARIANT"); e && !a.f16) {
     if (e[0] == '0') a.variant = 0;
     if (e[0] == '1' && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
   }

@@ -52,8 +52,21 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Elements are 16-bit: bf16, or IEEE fp16 when F16, held in the same storage
+// type; only the MFMA and the conversions to and from fp32 differ.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+template <bool F16>
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ bf16 to_elem(float x) {  // round to nearest even
+  if constexpr (F16) return __builtin_bit_cast(bf16, (_Float16)x);
+  else return (bf16)x;
 }
 // Transposing LDS read (see fa_bwd_kernels.hip): lane i of a 16-lane group,
 // pointing at row r0 + i/4, column c0 + 4*(i%4) of a row-major bf16 tile,
@@ -317,7 +330,7 @@ __device__ __forceinline__ void padded_copy(uint32_t lds_tile, const void* g, in
 // only); Q/dY tiles are swizzled (row reads and transposing reads).
 // Instantiated with NWG = 4, KPW = 32: 8 wavefronts in two query groups (two
 // per SIMD) at D <= 128, 4 wavefronts in one group at D = 192.
-template <int HD, int HDV, int KPW, int NWG, int QG>
+template <int HD, int HDV, int KPW, int NWG, int QG, bool F16>
 __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   constexpr int BC = NWG * KPW;       // keys per workgroup
   constexpr int NKB = KPW / 32;       // 32-key blocks per wavefront
@@ -456,13 +469,13 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     for (int kk = 0; kk < NKQ; ++kk) {
       const bf16x8 qa = lds_load16(qadr.row_read(kk, buf * QTB));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32(qa, lds_load16(k_lane + (kb * 32 * KP + 16 * kk) * 2), sacc[kb]);
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32<F16>(qa, lds_load16(k_lane + (kb * 32 * KP + 16 * kk) * 2), sacc[kb]);
     }
 #pragma unroll
     for (int kk = 0; kk < NKV; ++kk) {
       const bf16x8 ya = lds_load16(yadr.row_read(kk, buf * YTB));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) pacc[kb] = mfma32(ya, lds_load16(v_lane + (kb * 32 * VP + 16 * kk) * 2), pacc[kb]);
+      for (int kb = 0; kb < NKB; ++kb) pacc[kb] = mfma32<F16>(ya, lds_load16(v_lane + (kb * 32 * VP + 16 * kk) * 2), pacc[kb]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -486,8 +499,8 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int rg = r4 * 4 + e;
             const float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
-            pa[kb][rg >> 3][rg & 7] = (bf16)p;
-            da[kb][rg >> 3][rg & 7] = (bf16)(p * (pacc[kb][rg] - f4[e]));
+            pa[kb][rg >> 3][rg & 7] = to_elem<F16>(p);
+            da[kb][rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[kb][rg] - f4[e]));
           }
         }
       }
@@ -508,8 +521,8 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
             const int rg = r4 * 4 + e;
             float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
             p = fa_sched::in_window(vis[kb], ib + e) ? p : 0.f;
-            pa[kb][rg >> 3][rg & 7] = (bf16)p;
-            da[kb][rg >> 3][rg & 7] = (bf16)(p * (pacc[kb][rg] - f4[e]));
+            pa[kb][rg >> 3][rg & 7] = to_elem<F16>(p);
+            da[kb][rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[kb][rg] - f4[e]));
           }
         }
       }
@@ -523,13 +536,13 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
       for (int nb = 0; nb < NBV; ++nb) {
         const bf16x8 yb = join(lds_load_tr(yadr.tr_read(kc, 0, nb, buf * YTB)), lds_load_tr(yadr.tr_read(kc, 1, nb, buf * YTB)));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) dVr[kb][nb] = mfma32(pa[kb][kc], yb, dVr[kb][nb]);
+        for (int kb = 0; kb < NKB; ++kb) dVr[kb][nb] = mfma32<F16>(pa[kb][kc], yb, dVr[kb][nb]);
       }
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
         const bf16x8 qb = join(lds_load_tr(qadr.tr_read(kc, 0, nb, buf * QTB)), lds_load_tr(qadr.tr_read(kc, 1, nb, buf * QTB)));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32(da[kb][kc], qb, dKr[kb][nb]);
+        for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32<F16>(da[kb][kc], qb, dKr[kb][nb]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -608,9 +621,9 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
         for (int nb = 0; nb < NBV; ++nb) a.dv_acc[vpart + vo + nb * 32 + l32] = dVr[kb][nb][rg];
       } else {
 #pragma unroll
-        for (int nb = 0; nb < NBK; ++nb) static_cast<bf16*>(a.dk)[ko + nb * 32 + l32] = (bf16)(dKr[kb][nb][rg] * a.scale);
+        for (int nb = 0; nb < NBK; ++nb) static_cast<bf16*>(a.dk)[ko + nb * 32 + l32] = to_elem<F16>(dKr[kb][nb][rg] * a.scale);
 #pragma unroll
-        for (int nb = 0; nb < NBV; ++nb) static_cast<bf16*>(a.dv)[vo + nb * 32 + l32] = (bf16)dVr[kb][nb][rg];
+        for (int nb = 0; nb < NBV; ++nb) static_cast<bf16*>(a.dv)[vo + nb * 32 + l32] = to_elem<F16>(dVr[kb][nb][rg]);
       }
     }
   }
@@ -621,7 +634,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
 constexpr int DQ_BQ = 128;  // query rows per workgroup (4 wavefronts x 32)
 constexpr int DQ_BK = 64;   // keys per step
 
-template <int HD, int HDV>
+template <int HD, int HDV, bool F16>
 __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a) {
   constexpr int NKQ = HD / 16;
   constexpr int NKV = HDV / 16;
@@ -697,8 +710,14 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
 #pragma unroll
     for (int kk = 0; kk < NKV; ++kk) {
       const bf16x8 y = *reinterpret_cast<const bf16x8*>(Og + 16 * kk + 8 * hi);
+      if constexpr (F16) {  // reinterpret whole vectors (element-wise casts of bf16 lanes miscompile)
+        const halfx8 gh = __builtin_bit_cast(halfx8, yf[kk]), yh = __builtin_bit_cast(halfx8, y);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sf += (float)yf[kk][e] * (float)y[e];
+        for (int e = 0; e < 8; ++e) sf += (float)gh[e] * (float)yh[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf += (float)yf[kk][e] * (float)y[e];
+      }
     }
     const float l = a.lse[lrow];
     l2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
@@ -735,16 +754,16 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
       floatx16 s = {}, dp = {};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kk = 0; kk < NKQ; ++kk) s = mfma32(lds_load16(kadr.row_read_at(kk, mb * 32, buf * KTB)), qf[kk], s);
+      for (int kk = 0; kk < NKQ; ++kk) s = mfma32<F16>(lds_load16(kadr.row_read_at(kk, mb * 32, buf * KTB)), qf[kk], s);
 #pragma unroll
-      for (int kk = 0; kk < NKV; ++kk) dp = mfma32(lds_load16(vadr.row_read_at(kk, mb * 32, buf * VTB)), yf[kk], dp);
+      for (int kk = 0; kk < NKV; ++kk) dp = mfma32<F16>(lds_load16(vadr.row_read_at(kk, mb * 32, buf * VTB)), yf[kk], dp);
       __builtin_amdgcn_s_setprio(0);
       bf16x8 da[2];
       if (full) {
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg) {
           const float p = __builtin_amdgcn_exp2f(s[rg] * a.scale_log2 - l2);
-          da[rg >> 3][rg & 7] = (bf16)(p * (dp[rg] - sf));
+          da[rg >> 3][rg & 7] = to_elem<F16>(p * (dp[rg] - sf));
         }
       } else {
 #pragma unroll
@@ -752,7 +771,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
           const int jj = mb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
           float p = __builtin_amdgcn_exp2f(s[rg] * a.scale_log2 - l2);
           p = fa_sched::in_window(kvis, jj) ? p : 0.f;
-          da[rg >> 3][rg & 7] = (bf16)(p * (dp[rg] - sf));
+          da[rg >> 3][rg & 7] = to_elem<F16>(p * (dp[rg] - sf));
         }
       }
       __builtin_amdgcn_s_setprio(1);
@@ -763,7 +782,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
         for (int nb = 0; nb < NBK; ++nb) {
           const bf16x8 kb = join(lds_load_tr(kadr.tr_read(kc, 0, nb, buf * KTB)),
                                  lds_load_tr(kadr.tr_read(kc, 1, nb, buf * KTB)));
-          dq[nb] = mfma32(da[c], kb, dq[nb]);
+          dq[nb] = mfma32<F16>(da[c], kb, dq[nb]);
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -778,7 +797,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
     const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
     if (i < s1) {
 #pragma unroll
-      for (int nb = 0; nb < NBK; ++nb) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = (bf16)(dq[nb][rg] * a.scale);
+      for (int nb = 0; nb < NBK; ++nb) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
     }
   }
 }
@@ -788,6 +807,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
 // dk = bf16(sum over parts) and dv likewise in one launch: blocks below
 // `kblocks` take dK, the rest dV; 8 elements per thread, parts added in index
 // order (so the result is repeatable).
+template <bool F16>
 __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ kpart, int64_t k_stride,
                                                            bf16* __restrict__ kout, const float* __restrict__ vpart,
                                                            int64_t v_stride, bf16* __restrict__ vout, int nparts,
@@ -810,8 +830,8 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restri
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o[e] = (bf16)s0[e];
-      o[e + 4] = (bf16)s1[e];
+      o[e] = to_elem<F16>(s0[e]);
+      o[e + 4] = to_elem<F16>(s1[e]);
     }
     reinterpret_cast<bf16x8*>(out)[i] = o;
   }
@@ -834,6 +854,31 @@ bool det_instantiated(int D, int Dv) {
 // tiles: 8 wavefronts x 32 keys in two query groups, 4 x 32 at D = 192).
 int det_keys_per_wave(int D) { (void)D; return 32; }
 
+namespace {
+
+template <bool F16>
+int launch_dkdv_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
+  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 4, 2, F16>, grid, dim3(512), s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 4, 2, F16>, grid, dim3(512), s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 4, 2, F16>, grid, dim3(512), s, a);
+  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 4, 1, F16>, grid, dim3(256), s, a);
+  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 4, 1, F16>, grid, dim3(256), s, a);
+  return (int)hipErrorInvalidValue;
+}
+
+template <bool F16>
+int launch_dq_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (a.D == 64 && a.Dv == 64) return launch(dq_kernel<64, 64, F16>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(dq_kernel<128, 64, F16>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(dq_kernel<128, 128, F16>, grid, block, s, a);
+  if (a.D == 192 && a.Dv == 64) return launch(dq_kernel<192, 64, F16>, grid, block, s, a);
+  if (a.D == 192 && a.Dv == 128) return launch(dq_kernel<192, 128, F16>, grid, block, s, a);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
 int launch_dkdv(const KernelArgs& a, void* stream) {
   const int64_t tiles = (a.S2 + 127) / 128;  // 128-key tiles in every shape
   const int64_t blocks = tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.N2;
@@ -841,12 +886,7 @@ int launch_dkdv(const KernelArgs& a, void* stream) {
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)blocks);
-  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 4, 2>, grid, dim3(512), s, a);
-  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 4, 2>, grid, dim3(512), s, a);
-  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 4, 2>, grid, dim3(512), s, a);
-  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 4, 1>, grid, dim3(256), s, a);
-  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 4, 1>, grid, dim3(256), s, a);
-  return (int)hipErrorInvalidValue;
+  return a.f16 ? launch_dkdv_t<true>(a, grid, s) : launch_dkdv_t<false>(a, grid, s);
 }
 
 int launch_dq(const KernelArgs& a, void* stream) {
@@ -855,13 +895,8 @@ int launch_dq(const KernelArgs& a, void* stream) {
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)blocks), block(256);
-  if (a.D == 64 && a.Dv == 64) return launch(dq_kernel<64, 64>, grid, block, s, a);
-  if (a.D == 128 && a.Dv == 64) return launch(dq_kernel<128, 64>, grid, block, s, a);
-  if (a.D == 128 && a.Dv == 128) return launch(dq_kernel<128, 128>, grid, block, s, a);
-  if (a.D == 192 && a.Dv == 64) return launch(dq_kernel<192, 64>, grid, block, s, a);
-  if (a.D == 192 && a.Dv == 128) return launch(dq_kernel<192, 128>, grid, block, s, a);
-  return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+  return a.f16 ? launch_dq_t<true>(a, grid, s) : launch_dq_t<false>(a, grid, s);
 }
 
 int launch_reduce_parts(const KernelArgs& a, void* stream) {
@@ -873,9 +908,9 @@ int launch_reduce_parts(const KernelArgs& a, void* stream) {
   };
   const int64_t kb = blocks(a.k_part_stride), vb = blocks(a.v_part_stride);
   if (kb <= 0 || vb <= 0) return 0;
-  return launch(reduce_parts_kernel, dim3((unsigned)(kb + vb)), dim3(256), s, (const float*)a.dk_acc, a.k_part_stride,
-                static_cast<bf16*>(a.dk), (const float*)a.dv_acc, a.v_part_stride, static_cast<bf16*>(a.dv),
-                a.n_partials, (int)kb);
+  return launch(a.f16 ? reduce_parts_kernel<true> : reduce_parts_kernel<false>, dim3((unsigned)(kb + vb)), dim3(256), s,
+                (const float*)a.dk_acc, a.k_part_stride, static_cast<bf16*>(a.dk), (const float*)a.dv_acc,
+                a.v_part_stride, static_cast<bf16*>(a.dv), a.n_partials, (int)kb);
 }
 
 }  // namespace fabwd

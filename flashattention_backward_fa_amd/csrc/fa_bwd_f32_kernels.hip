@@ -25,6 +25,13 @@ namespace {
 
 typedef __bf16 bf16;
 
+// Inputs are bf16, or IEEE fp16 when F16 (same 16-bit storage).
+template <bool F16>
+__device__ __forceinline__ float from_elem(bf16 v) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, v);
+  else return (float)v;
+}
+
 constexpr int F32_BK = 32;   // keys per dK/dV workgroup
 constexpr int F32_BQ = 32;   // query rows per dQ workgroup
 constexpr int F32_CH = 8;    // rows (dK/dV) or keys (dQ) per LDS chunk
@@ -59,6 +66,7 @@ __device__ Seq seq_of(const KernelArgs& a, int b) {
 }
 
 
+template <bool F16>
 __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   __shared__ float Ks[F32_BK][F32_MAXD + 1];   // +1: conflict-free column walks
   __shared__ float Vs[F32_BK][F32_MAXD + 1];
@@ -84,8 +92,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   for (int e = t; e < F32_BK * F32_MAXD; e += 256) {
     const int jj = e / F32_MAXD, d = e % F32_MAXD;
     const int j = j0 + jj;
-    Ks[jj][d] = (j < sq.s2 && d < D) ? (float)K[(int64_t)j * a.k_ss + d] : 0.f;
-    Vs[jj][d] = (j < sq.s2 && d < Dv) ? (float)V[(int64_t)j * a.v_ss + d] : 0.f;
+    Ks[jj][d] = (j < sq.s2 && d < D) ? from_elem<F16>(K[(int64_t)j * a.k_ss + d]) : 0.f;
+    Vs[jj][d] = (j < sq.s2 && d < Dv) ? from_elem<F16>(V[(int64_t)j * a.v_ss + d]) : 0.f;
   }
 
   // rows that can see a key of the tile
@@ -110,8 +118,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
       for (int e = t; e < F32_CH * F32_MAXD; e += 256) {
         const int rr = e / F32_MAXD, d = e % F32_MAXD;
         const int i = c0 + rr;
-        Qr[rr][d] = (i < i_hi && d < D) ? (float)Q[(int64_t)i * a.q_ss + d] : 0.f;
-        Yr[rr][d] = (i < i_hi && d < Dv) ? (float)Y[(int64_t)i * a.o_ss + d] : 0.f;
+        Qr[rr][d] = (i < i_hi && d < D) ? from_elem<F16>(Q[(int64_t)i * a.q_ss + d]) : 0.f;
+        Yr[rr][d] = (i < i_hi && d < Dv) ? from_elem<F16>(Y[(int64_t)i * a.o_ss + d]) : 0.f;
       }
       if (t < F32_CH) {
         const int i = c0 + t;
@@ -158,6 +166,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   }
 }
 
+template <bool F16>
 __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
   __shared__ float Qs[F32_BQ][F32_MAXD + 1];
   __shared__ float Ys[F32_BQ][F32_MAXD + 1];
@@ -185,8 +194,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
   for (int e = t; e < F32_BQ * F32_MAXD; e += 256) {
     const int rr = e / F32_MAXD, d = e % F32_MAXD;
     const int i = i0 + rr;
-    Qs[rr][d] = (i < sq.s1 && d < D) ? (float)Q[(int64_t)i * a.q_ss + d] : 0.f;
-    Ys[rr][d] = (i < sq.s1 && d < Dv) ? (float)Y[(int64_t)i * a.o_ss + d] : 0.f;
+    Qs[rr][d] = (i < sq.s1 && d < D) ? from_elem<F16>(Q[(int64_t)i * a.q_ss + d]) : 0.f;
+    Ys[rr][d] = (i < sq.s1 && d < Dv) ? from_elem<F16>(Y[(int64_t)i * a.o_ss + d]) : 0.f;
   }
   if (t < F32_BQ) {
     const int i = i0 + t;
@@ -210,8 +219,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
     for (int e = t; e < F32_CH * F32_MAXD; e += 256) {
       const int cc = e / F32_MAXD, d = e % F32_MAXD;
       const int j = c0 + cc;
-      Kc[cc][d] = (j < j_hi && d < D) ? (float)K[(int64_t)j * a.k_ss + d] : 0.f;
-      Vc[cc][d] = (j < j_hi && d < Dv) ? (float)V[(int64_t)j * a.v_ss + d] : 0.f;
+      Kc[cc][d] = (j < j_hi && d < D) ? from_elem<F16>(K[(int64_t)j * a.k_ss + d]) : 0.f;
+      Vc[cc][d] = (j < j_hi && d < Dv) ? from_elem<F16>(V[(int64_t)j * a.v_ss + d]) : 0.f;
     }
     __syncthreads();
     {
@@ -259,14 +268,14 @@ int launch_f32_debug(const KernelArgs& a, void* stream) {
   KernelArgs args = a;
   if (kb > 0) {
     void* argv[] = {&args};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(dkdv_f32_kernel), dim3((unsigned)kb),
-                                         dim3(256), argv, 0, s);
+    const void* k = reinterpret_cast<const void*>(a.f16 ? dkdv_f32_kernel<true> : dkdv_f32_kernel<false>);
+    const hipError_t e = hipLaunchKernel(k, dim3((unsigned)kb), dim3(256), argv, 0, s);
     if (e != hipSuccess) return (int)e;
   }
   if (qb > 0) {
     void* argv[] = {&args};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(dq_f32_kernel), dim3((unsigned)qb),
-                                         dim3(256), argv, 0, s);
+    const void* k = reinterpret_cast<const void*>(a.f16 ? dq_f32_kernel<true> : dq_f32_kernel<false>);
+    const hipError_t e = hipLaunchKernel(k, dim3((unsigned)qb), dim3(256), argv, 0, s);
     if (e != hipSuccess) return (int)e;
   }
   return 0;

@@ -37,6 +37,7 @@ struct KernelArgs {
   int32_t D, Dv;
   int64_t T1, T2;
   int32_t varlen;        // 1 for TND
+  int32_t f16;           // 1: elements are IEEE fp16, 0: bf16 (same 16-bit storage)
   int32_t layout;        // FA_LAYOUT_* of include/fa_bwd.h
 
   // element strides: batch (dense layouts), sequence row, head

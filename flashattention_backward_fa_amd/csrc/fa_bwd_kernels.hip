@@ -75,7 +75,7 @@ __device__ __forceinline__ bf16x8 join(shortx4 lo, shortx4 hi) {
 
 // One row = Dv contiguous bf16 of dout / attn_out.  DV/8 lanes per row, each
 // with one 16-byte load of each tensor.
-template <int DV>
+template <int DV, bool F16>
 __global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t rows, int zero_dq,
                                                           int64_t dq_elems, int64_t dk_elems, int64_t dv_elems) {
   constexpr int LPR = DV / 8;             // lanes per row
@@ -87,8 +87,16 @@ __global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t r
   if (row < rows) {
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + row * DV + part * 8);
     const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + row * DV + part * 8);
+    if constexpr (F16) {  // fp16 in the same storage: reinterpret whole vectors (element-wise casts of
+                          // bf16 lanes miscompile)
+      typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+      const halfx8 yh = __builtin_bit_cast(halfx8, y), gh = __builtin_bit_cast(halfx8, g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)g[e] * (float)y[e];
+      for (int e = 0; e < 8; ++e) s += (float)gh[e] * (float)yh[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (float)g[e] * (float)y[e];
+    }
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
@@ -743,8 +751,12 @@ int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream) {
   const int64_t dve = zero_dq_acc && split_heads(a) ? v_elems(a) : 0;
   const dim3 grid((unsigned)blocks), block(256);
   const int z = zero_dq_acc ? 1 : 0;
-  if (a.Dv == 128) return launch(preprocess_kernel<128>, grid, block, s, a, rows, z, dqe, dke, dve);
-  if (a.Dv == 64) return launch(preprocess_kernel<64>, grid, block, s, a, rows, z, dqe, dke, dve);
+  if (a.Dv == 128)
+    return launch(a.f16 ? preprocess_kernel<128, true> : preprocess_kernel<128, false>, grid, block, s, a, rows, z, dqe,
+                  dke, dve);
+  if (a.Dv == 64)
+    return launch(a.f16 ? preprocess_kernel<64, true> : preprocess_kernel<64, false>, grid, block, s, a, rows, z, dqe,
+                  dke, dve);
   return (int)hipErrorInvalidValue;
 }
 

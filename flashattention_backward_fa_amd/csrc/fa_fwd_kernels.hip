@@ -36,8 +36,20 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Elements are bf16, or IEEE fp16 when F16 (same 16-bit storage).
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+template <bool F16>
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ bf16 to_elem(float x) {  // round to nearest even
+  if constexpr (F16) return __builtin_bit_cast(bf16, (_Float16)x);
+  else return (bf16)x;
 }
 __device__ __forceinline__ shortx4 lds_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(p));
@@ -50,7 +62,7 @@ __device__ __forceinline__ bf16x8 join(shortx4 lo, shortx4 hi) {
 constexpr int FQ = 128;  // query rows per workgroup
 constexpr int FK = 64;   // keys per step
 
-template <int HD, int HDV>
+template <int HD, int HDV, bool F16>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restrict__ out, float* __restrict__ lse) {
   constexpr int KP = HD + 8;
   constexpr int VP = HDV + 8;
@@ -139,7 +151,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
 #pragma unroll
       for (int kk = 0; kk < NKQ; ++kk) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[(mb * 32 + l32) * KP + 16 * kk + 8 * hi]);
-        s[mb] = mfma32(ka, qf[kk], s[mb]);
+        s[mb] = mfma32<F16>(ka, qf[kk], s[mb]);
       }
     }
     // scores in log2 units, masked to -inf
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(s[mb][r] - m_use);
         rs += p;
-        pb[mb * 2 + (r >> 3)][r & 7] = (bf16)p;
+        pb[mb * 2 + (r >> 3)][r & 7] = to_elem<F16>(p);
       }
     }
     rs += __shfl_xor(rs, 32);
@@ -189,7 +201,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
       for (int nb = 0; nb < NB; ++nb) {
         const bf16* p0 = &Vs[(16 * kc + tr_r4) * VP + nb * 32 + tr_c];
         const bf16x8 va = join(lds_tr(p0), lds_tr(p0 + 8 * VP));
-        o[nb] = mfma32(va, pb[kc], o[nb]);
+        o[nb] = mfma32<F16>(va, pb[kc], o[nb]);
       }
     }
   }
@@ -203,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[nb][r4 * 4 + e] * inv);
+        for (int e = 0; e < 4; ++e) w[e] = to_elem<F16>(o[nb][r4 * 4 + e] * inv);
         *reinterpret_cast<bf16x4*>(Og + nb * 32 + r4 * 8 + hi * 4) = w;
       }
     }
@@ -225,6 +237,19 @@ int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, typen
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
 }
 
+namespace {
+template <bool F16>
+int launch_forward_t(const KernelArgs& a, dim3 grid, hipStream_t s, bf16* o, float* lse) {
+  const dim3 block(256);
+  if (a.D == 64 && a.Dv == 64) return launch(fwd_kernel<64, 64, F16>, grid, block, s, a, o, lse);
+  if (a.D == 128 && a.Dv == 64) return launch(fwd_kernel<128, 64, F16>, grid, block, s, a, o, lse);
+  if (a.D == 128 && a.Dv == 128) return launch(fwd_kernel<128, 128, F16>, grid, block, s, a, o, lse);
+  if (a.D == 192 && a.Dv == 64) return launch(fwd_kernel<192, 64, F16>, grid, block, s, a, o, lse);
+  if (a.D == 192 && a.Dv == 128) return launch(fwd_kernel<192, 128, F16>, grid, block, s, a, o, lse);
+  return (int)hipErrorInvalidValue;
+}
+}  // namespace
+
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream) {
   const int64_t tiles = (a.S1 + FQ - 1) / FQ;
   const int64_t blocks = tiles * a.N1 * a.B;
@@ -232,13 +257,8 @@ int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream) {
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   bf16* o = static_cast<bf16*>(out);
-  const dim3 grid((unsigned)blocks), block(256);
-  if (a.D == 64 && a.Dv == 64) return launch(fwd_kernel<64, 64>, grid, block, s, a, o, lse);
-  else if (a.D == 128 && a.Dv == 64) return launch(fwd_kernel<128, 64>, grid, block, s, a, o, lse);
-  else if (a.D == 128 && a.Dv == 128) return launch(fwd_kernel<128, 128>, grid, block, s, a, o, lse);
-  else if (a.D == 192 && a.Dv == 64) return launch(fwd_kernel<192, 64>, grid, block, s, a, o, lse);
-  else if (a.D == 192 && a.Dv == 128) return launch(fwd_kernel<192, 128>, grid, block, s, a, o, lse);
-  return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+  return a.f16 ? launch_forward_t<true>(a, grid, s, o, lse) : launch_forward_t<false>(a, grid, s, o, lse);
 }
 
 }  // namespace fabwd

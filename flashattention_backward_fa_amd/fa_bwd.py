@@ -32,6 +32,8 @@ FA_ERR_RUNTIME = 6
 LAYOUTS = {"BSND": 0, "BNSD": 1, "TND": 2}
 FLAG_DETERMINISTIC = 0x1
 FLAG_FP32_OUT = 0x2
+DTYPE_BF16 = 0
+DTYPE_FP16 = 1
 
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_profile_enable",
             "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version")
@@ -226,6 +228,16 @@ def _shapes(q, k, v, layout):
     return dict(B=B, N1=N1, N2=N2, S1=S1, S2=S2, D=D, Dv=v.shape[-1])
 
 
+def _dtype_code(t):
+    """FA_DTYPE_* of a tensor's element type (bf16 or fp16)."""
+    import torch
+
+    codes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}
+    if t.dtype not in codes:
+        raise TypeError(f"elements must be bfloat16 or float16, got {t.dtype}")
+    return codes[t.dtype]
+
+
 def _check(name, t, dtype, device):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -236,8 +248,9 @@ def _check(name, t, dtype, device):
 def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0,
              mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1,
              deterministic=False, host_cu_seqlens=None, fp32_out=False):
-    """Create (or reuse) the plan for these shapes and attributes."""
+    """Create (or reuse) the plan for these shapes, element type and attributes."""
     sh = _shapes(q, k, v, layout)
+    dt = _dtype_code(q)
     flags = (FLAG_DETERMINISTIC if deterministic else 0) | (FLAG_FP32_OUT if fp32_out else 0)
     mm = mask_mode_value(mask_mode)
     if layout == "TND":
@@ -253,21 +266,21 @@ def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, soft
             hk = [int(x) for x in cu_seqlens_kv.cpu().tolist()]
         key = ("TND", B, sh["N1"], sh["N2"], sh["D"], sh["Dv"], sh["T1"], sh["T2"], max_seqlen_q,
                max_seqlen_kv, tuple(hq) if hq else None, tuple(hk) if hk else None, float(softmax_scale),
-               mm, win_left, win_right, flags)
+               mm, win_left, win_right, flags, dt)
         if key not in _plans:
             aq = (ctypes.c_int32 * len(hq))(*hq) if hq else None
             ak = (ctypes.c_int32 * len(hk))(*hk) if hk else None
             d = make_desc("TND", B, sh["N1"], sh["N2"], max_seqlen_q, max_seqlen_kv, sh["D"], sh["Dv"],
-                          sh["T1"], sh["T2"], softmax_scale, mm, win_left, win_right, flags, aq, ak)
+                          sh["T1"], sh["T2"], softmax_scale, mm, win_left, win_right, flags, aq, ak, dtype=dt)
             _plans[key] = Plan(d)
         return _plans[key]
     if cu_seqlens_q is not None or cu_seqlens_kv is not None:
         raise ValueError("cu_seqlens are only accepted with the TND layout")
     key = (layout, sh["B"], sh["N1"], sh["N2"], sh["S1"], sh["S2"], sh["D"], sh["Dv"], float(softmax_scale), mm,
-           win_left, win_right, flags)
+           win_left, win_right, flags, dt)
     if key not in _plans:
         d = make_desc(layout, sh["B"], sh["N1"], sh["N2"], sh["S1"], sh["S2"], sh["D"], sh["Dv"], 0, 0,
-                      softmax_scale, mm, win_left, win_right, flags)
+                      softmax_scale, mm, win_left, win_right, flags, dtype=dt)
         _plans[key] = Plan(d)
     return _plans[key]
 
@@ -276,9 +289,11 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
                     softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
                     max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None,
                     fp32_out=False):
-    """dq, dk, dv of attention (bf16) on the current HIP stream.
+    """dq, dk, dv of attention on the current HIP stream, in the inputs' element
+    type (bf16 or fp16).
 
-    q, k, v, dout, attn_out: bf16 CUDA(HIP) tensors in `layout`; softmax_lse:
+    q, k, v, dout, attn_out: bf16 or fp16 CUDA(HIP) tensors of one type in
+    `layout`; softmax_lse:
     float32, (B, N1, S1) or (N1, T1); cu_seqlens_*: int32 device tensors for
     TND only.  Non-contiguous inputs are made contiguous first.  `workspace`
     (uint8 tensor) and `out` ((dq, dk, dv)) may be passed to avoid allocation.
@@ -290,8 +305,9 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
     dev = q.device
+    _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("attn_out", attn_out)):
-        _check(name, t, torch.bfloat16, dev)
+        _check(name, t, q.dtype, dev)
     _check("softmax_lse", softmax_lse, torch.float32, dev)
     q, k, v, dout, attn_out, softmax_lse = (t.contiguous() for t in (q, k, v, dout, attn_out, softmax_lse))
     if cu_seqlens_q is not None:
@@ -302,7 +318,7 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
         raise ValueError("dout and attn_out must have the same shape")
     plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
                     max_seqlen_q, max_seqlen_kv, deterministic, fp32_out=fp32_out)
-    odt = torch.float32 if fp32_out else torch.bfloat16
+    odt = torch.float32 if fp32_out else q.dtype
     if out is None:
         dq, dk, dv = (torch.empty(t.shape, dtype=odt, device=dev) for t in (q, k, v))
     else:
@@ -321,20 +337,22 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
 
 def flash_attn(q, k, v, cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0, mask_mode=0, win_left=-1,
                win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1, layout="BSND"):
-    """Forward (attn_out bf16, softmax_lse float32) with the same conventions
-    as flash_attn_grad; its outputs are what flash_attn_grad expects."""
+    """Forward (attn_out in the inputs' element type, softmax_lse float32) with
+    the same conventions as flash_attn_grad; its outputs are what
+    flash_attn_grad expects."""
     import torch
 
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
     dev = q.device
+    _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(name, t, torch.bfloat16, dev)
+        _check(name, t, q.dtype, dev)
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
                     max_seqlen_q, max_seqlen_kv)
     sh = _shapes(q, k, v, layout)
-    out = torch.empty(tuple(q.shape[:-1]) + (sh["Dv"],), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(tuple(q.shape[:-1]) + (sh["Dv"],), dtype=q.dtype, device=dev)
     if layout == "TND":
         lse = torch.empty((sh["N1"], sh["T1"]), dtype=torch.float32, device=dev)
     else:
@@ -352,7 +370,7 @@ def sfmg(dout, attn_out, layout="BSND", cu_seqlens_q=None, N2=None, max_seqlen_q
     # a plan needs key shapes; use a self-attention stand-in with N2 = N1 / 1
     if layout == "TND":
         T1, N1, Dv = dout.shape
-        q = torch.empty((T1, N1, Dv), dtype=torch.bfloat16, device="meta")
+        q = torch.empty((T1, N1, Dv), dtype=dout.dtype, device="meta")
         plan = get_plan(q, q, q, "TND", cu_seqlens_q, cu_seqlens_q, max_seqlen_q=max_seqlen_q,
                         max_seqlen_kv=max_seqlen_q)
         res = torch.empty((N1, T1), dtype=torch.float32, device=dout.device)
@@ -361,7 +379,7 @@ def sfmg(dout, attn_out, layout="BSND", cu_seqlens_q=None, N2=None, max_seqlen_q
             B, S1, N1, Dv = dout.shape
         else:
             B, N1, S1, Dv = dout.shape
-        q = torch.empty(tuple(dout.shape), dtype=torch.bfloat16, device="meta")
+        q = torch.empty(tuple(dout.shape), dtype=dout.dtype, device="meta")
         plan = get_plan(q, q, q, layout)
         res = torch.empty((B, N1, S1), dtype=torch.float32, device=dout.device)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dout.device).cuda_stream)

@@ -1,12 +1,14 @@
 """Seeded synthetic inputs for the five benchmark/parity workloads.
 
-This module only draws random numbers and rounds them to bfloat16; it holds
+This module only draws random numbers and rounds them to bfloat16 (or, on
+request, IEEE fp16); it holds
 none of the backward's arithmetic, so both the fp64 oracle (tests) and the
 HIP path (tests, bench) take their inputs from here.
 
 Recipe: numpy.random.default_rng(seed), draws in the order q, k, v, dout, each
 standard normal float32 in the layout's logical shape, dout multiplied by
-`dy_std`, then rounded to bfloat16 (round to nearest even, via torch).  The
+`dy_std`, then rounded to bfloat16 (round to nearest even, via torch; fp16
+likewise when a caller asks for it).  The
 forward output attn_out and softmax_lse are NOT made here: tests take them
 from the oracle's forward, the benchmark from the library's own forward.
 """
@@ -57,18 +59,20 @@ def shapes(cfg):
     return (B, N1, S1, D), (B, N2, S2, D), (B, N2, S2, Dv), (B, N1, S1, Dv)
 
 
-def make_inputs(cfg, seed=None):
-    """q, k, v, dout as CPU torch.bfloat16 tensors, plus cu_seqlens (numpy
-    int32, TND only, else None)."""
+def make_inputs(cfg, seed=None, dtype=None):
+    """q, k, v, dout as CPU torch tensors of `dtype` (default torch.bfloat16;
+    torch.float16 for the fp16 path), plus cu_seqlens (numpy int32, TND only,
+    else None)."""
     import torch
 
+    dtype = torch.bfloat16 if dtype is None else dtype
     rng = np.random.default_rng(seed_of(cfg) if seed is None else seed)
     out = {}
     for name, shp in zip(("q", "k", "v", "dout"), shapes(cfg)):
         x = rng.standard_normal(shp, dtype=np.float32)
         if name == "dout":
             x *= np.float32(cfg["dy_std"])
-        out[name] = torch.from_numpy(x).to(torch.bfloat16)
+        out[name] = torch.from_numpy(x).to(dtype)
     if cfg["layout"] == "TND":
         cu = cu_seqlens(cfg["lengths"])
         out["cu_q"], out["cu_kv"] = cu, cu.copy()
@@ -88,10 +92,11 @@ def custom(layout="BSND", B=1, N1=2, N2=2, S1=128, S2=128, D=64, Dv=64, mask_mod
     return c
 
 
-def make_inputs_custom(cfg, seed):
+def make_inputs_custom(cfg, seed, dtype=None):
     """Like make_inputs, but TND may have different query and key lengths."""
     import torch
 
+    dtype = torch.bfloat16 if dtype is None else dtype
     rng = np.random.default_rng(seed)
     L, N1, N2, D, Dv = cfg["layout"], cfg["N1"], cfg["N2"], cfg["D"], cfg["Dv"]
     if L == "TND":
@@ -104,7 +109,7 @@ def make_inputs_custom(cfg, seed):
         x = rng.standard_normal(s, dtype=np.float32)
         if name == "dout":
             x *= np.float32(cfg["dy_std"])
-        out[name] = torch.from_numpy(x).to(torch.bfloat16)
+        out[name] = torch.from_numpy(x).to(dtype)
     if L == "TND":
         out["cu_q"], out["cu_kv"] = cu_seqlens(cfg["lengths"]), cu_seqlens(cfg["lengths_kv"])
     else:

@@ -22,7 +22,9 @@
  *  - All tensors are dense, row-major, contiguous, in device memory, owned by
  *    the caller.  Inputs are only read.  dq, dk, dv are fully overwritten
  *    (rows that receive no gradient are written as zeros).
- *  - bf16 is the only element type built (the page also lists fp16).
+ *  - Element types (section 五 5.4 registers both): bf16 and IEEE fp16.  q, k,
+ *    v, dout, attn_out and dq, dk, dv share the plan's type; softmax_lse and
+ *    the workspace are float32.
  *  - Return value: FA_OK (0) or one of the FA_ERR_* codes below; nothing
  *    is thrown across the ABI and nothing is printed unless FA_BWD_LOG=1.
  *  - Plans hold host memory only; a plan may be used by one stream at a time.
@@ -50,12 +52,13 @@ enum {
   FA_ERR_SHAPE = 3,         /* a shape constraint of section 四 4.6 is broken,
                                cu_seqlens are inconsistent, or a row stride
                                (N*D elements in BSND/TND) reaches 2^23         */
-  FA_ERR_UNSUPPORTED = 4,   /* valid on the page but not built here (fp16,
-                               head dims outside the built set, flags)         */
+  FA_ERR_UNSUPPORTED = 4,   /* valid on the page but not built here (head dims
+                               outside the built set, flags)                   */
   FA_ERR_WORKSPACE = 5,     /* workspace pointer NULL or smaller than needed   */
   FA_ERR_RUNTIME = 6        /* a HIP call or kernel launch failed              */
 };
 
+/* element types of the page's two binaries (section 五 5.4) */
 enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
 
 /* Layouts of section 四 4.6; q, k, v, dout, attn_out, dq, dk, dv share one.
@@ -82,7 +85,7 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 };
 /* fp32 debugging form (not on the page; it checks the arithmetic of section 一
  * at fp32 accuracy): dq, dk, dv are float32 arrays with the shapes and layouts
  * of q, k, v; P and dS are kept in fp32 and every product is an fp32 FMA, so
- * the only bf16 roundings are those of the inputs.  Slow (VALU, untuned);
+ * the only 16-bit roundings are those of the inputs.  Slow (VALU, untuned);
  * deterministic.  Overrides FA_FLAG_DETERMINISTIC's kernel choice. */
 #define FA_FLAG_FP32_OUT 0x2u
 
@@ -91,7 +94,7 @@ typedef struct fa_bwd_plan_s* fa_bwd_plan; /* opaque, host memory only */
 /* Problem description (the page's attributes and shapes, section 四 4.2/4.6). */
 typedef struct fa_bwd_desc {
   int32_t abi_version;   /* FA_BWD_ABI_VERSION                                    */
-  int32_t dtype;         /* FA_DTYPE_BF16                                          */
+  int32_t dtype;         /* FA_DTYPE_BF16 or FA_DTYPE_FP16                         */
   int32_t layout;        /* FA_LAYOUT_*                                            */
   int32_t B;             /* batch (BSND/BNSD) or number of sequences (TND); 0 < B < 65536 */
   int32_t N1, N2;        /* query heads, key/value heads; N1 % N2 == 0           */
@@ -119,13 +122,15 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
 
 /* Enqueue the backward on `stream` (a hipStream_t; NULL = the null stream).
  * Asynchronous: no allocation, no host synchronisation.
- *   q, k, v, dout, attn_out : bf16 in the plan's layout (see above)
+ *   q, k, v, dout, attn_out : the plan's element type (bf16 or fp16), in the
+ *                             plan's layout (see above)
  *   softmax_lse             : float32, [B, N1, S1] or [N1, T1]; -inf marks a
  *                             query row with no visible key (its dq row is 0)
  *   cu_seqlens_q/kv         : device int32 [B+1] prefix sums; required for TND
  *                             (cu[0] = 0, non-decreasing, cu[B] = T), NULL
  *                             otherwise (section 四 4.6)
- *   dq, dk, dv              : bf16 outputs, shapes of q, k, v
+ *   dq, dk, dv              : outputs of the plan's element type, shapes of
+ *                             q, k, v
  *   workspace               : device memory of at least *workspace_bytes from
  *                             fa_bwd_create, exclusively owned by this call
  *                             until it completes on `stream`
@@ -149,9 +154,10 @@ int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
 
 /* Attention forward producing the two tensors the backward consumes
  * (section 一, S = scale*Q K^T, P = exp(S - softmax_lse), Y = P V, with
- * softmax_lse the natural-log row log-sum-exp): writes bf16 attn_out (q's
- * layout with Dv) and float32 softmax_lse ([B, N1, S1] or [N1, T1]) for the
- * plan's problem, masks and layout.  A query row with no visible key gets
+ * softmax_lse the natural-log row log-sum-exp): writes attn_out (the plan's
+ * element type, q's layout with Dv) and float32 softmax_lse ([B, N1, S1] or
+ * [N1, T1]) for the plan's problem, masks and layout.  A query row with no
+ * visible key gets
  * attn_out = 0 and softmax_lse = -inf.  Same pointer rules and errors as
  * fa_bwd_run; needs no workspace. */
 int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,

@@ -15,7 +15,7 @@ in float64 with NumPy.
 from .attention import (  # noqa: F401
     MASK_NONE, MASK_CAUSAL, MASK_WINDOW,
     resolve_scale, mask_bounds, allowed_matrix,
-    bf16_round, split_heads, merge_heads,
+    bf16_round, f16_round, split_heads, merge_heads,
     head_forward, head_backward,
     forward, store, sfmg, backward, backward_rows,
 )

@@ -88,6 +88,22 @@ def bf16_round(x):
     return np.round(x / quantum) * quantum
 
 
+def f16_round(x):
+    """Round float64 values to the nearest IEEE binary16 (fp16) value (ties to
+    even), returned as float64.  binary16 keeps 11 significant bits, normal
+    numbers down to 2**-14 and a fixed spacing of 2**-24 below; its largest
+    finite value is 65504, and magnitudes from 65520 up round to infinity."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    e = np.maximum(e, -13)
+    quantum = np.ldexp(1.0, e - 11)
+    r = np.round(x / quantum) * quantum
+    return np.where(np.abs(r) > 65504.0, np.copysign(np.inf, x), r)
+
+
+ROUND = {"bf16": bf16_round, "fp16": f16_round}
+
+
 # ---------------------------------------------------------------- layouts
 
 def _seq_bounds(layout, B, S, cu):
@@ -231,10 +247,10 @@ def forward(q, k, v, layout="BSND", cu_q=None, cu_kv=None, softmax_scale=0.0,
     return merge_heads(Ys, layout, yshape), _merge_lse(lses, layout, _lse_shape(q, layout))
 
 
-def store(Y, lse):
-    """What a forward hands to the backward: Y rounded to bfloat16 (kept as
-    float64 values) and lse rounded to float32."""
-    return bf16_round(Y), np.asarray(lse, dtype=np.float64).astype(np.float32)
+def store(Y, lse, dtype="bf16"):
+    """What a forward hands to the backward: Y rounded to the element type
+    ("bf16" or "fp16", kept as float64 values) and lse rounded to float32."""
+    return ROUND[dtype](Y), np.asarray(lse, dtype=np.float64).astype(np.float32)
 
 
 def sfmg(dY, Y, layout="BSND", cu_q=None):

@@ -23,12 +23,13 @@ def f64(t):
     return t.double().numpy()
 
 
-def oracle_inputs(cfg, x):
-    """Stored-mode Y (bf16 values) and lse (fp32) from the oracle forward."""
+def oracle_inputs(cfg, x, dtype="bf16"):
+    """Stored-mode Y (values of the element type) and lse (fp32) from the
+    oracle forward."""
     q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
     Y, lse = oracle.forward(q, k, v, cfg["layout"], x["cu_q"], x["cu_kv"], cfg["softmax_scale"],
                             cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
-    return oracle.store(Y, lse)
+    return oracle.store(Y, lse, dtype)
 
 
 def oracle_backward(cfg, x, Yst, lst):
@@ -50,7 +51,7 @@ def gpu_backward(cfg, x, Yst, lst, **extra):
 
     dev = torch.device("cuda", 0)
     t = {k: x[k].to(dev) for k in ("q", "k", "v", "dout")}
-    attn_out = torch.from_numpy(np.ascontiguousarray(Yst)).to(torch.bfloat16).to(dev)
+    attn_out = torch.from_numpy(np.ascontiguousarray(Yst)).to(x["q"].dtype).to(dev)
     lse = torch.from_numpy(np.ascontiguousarray(lst, dtype=np.float32)).to(dev)
     cu_q = cu_kv = None
     if cfg["layout"] == "TND":
@@ -111,8 +112,9 @@ def assert_all_close(triples):
     assert not bad, "; ".join(bad)
 
 
-def case_inputs(cfg, seed=0):
-    """Named workloads use their own seed; edge cases use 1000 + seed."""
+def case_inputs(cfg, seed=0, dtype=None):
+    """Named workloads use their own seed; edge cases use 1000 + seed.
+    dtype: torch element type of q, k, v, dout (default bfloat16)."""
     if cfg.get("index", 0) == 0:
-        return W.make_inputs_custom(cfg, 1000 + seed)
-    return W.make_inputs(cfg)
+        return W.make_inputs_custom(cfg, 1000 + seed, dtype=dtype)
+    return W.make_inputs(cfg, dtype=dtype)

@@ -75,6 +75,9 @@ def test_valid_problem_and_workspace_size(lib):
     st, ws = create(lib, flags=fb.FLAG_FP32_OUT)
     assert st == fb.FA_OK
     assert ws == rnd(lse * 4)
+    # fp16 elements (the page's second binary) plan exactly like bf16
+    assert create(lib, dtype=fb.DTYPE_FP16) == create(lib, dtype=fb.DTYPE_BF16)
+    assert create(lib, dtype=fb.DTYPE_FP16, flags=fb.FLAG_FP32_OUT)[0] == fb.FA_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -93,7 +96,6 @@ def test_valid_problem_and_workspace_size(lib):
     (dict(dtype=2), fb.FA_ERR_PARAM_INVALID),
     (dict(flags=0x10), fb.FA_ERR_PARAM_INVALID),
     (dict(softmax_scale=float("nan")), fb.FA_ERR_PARAM_INVALID),
-    (dict(dtype=1), fb.FA_ERR_UNSUPPORTED),          # fp16 is on the page, not built
     (dict(D=96, Dv=96), fb.FA_ERR_UNSUPPORTED),      # head dim not instantiated
 ])
 def test_create_rejects(lib, kw, code):
@@ -195,3 +197,17 @@ def test_default_scale_is_reported_in_plan(lib):
     # scale 0 -> 1/sqrt(D) is a host decision; a plan must accept it
     assert create(lib, softmax_scale=0.0, D=192, Dv=128)[0] == fb.FA_OK
     assert math.isclose(1 / math.sqrt(192), 0.07216878364870322)
+
+
+def test_binding_rejects_mixed_or_unknown_element_types():
+    """q, k, v, dout and attn_out share one element type, bf16 or fp16; the
+    binding checks this before any library call."""
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 8, 2, 64), dtype=torch.float16)
+    kb = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 2, 8), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        fb.flash_attn_grad(q, kb, q, q, q, lse)
+    q32 = q.float()
+    with pytest.raises(TypeError):
+        fb.flash_attn_grad(q32, q32, q32, q32, q32, lse)

@@ -70,6 +70,37 @@ def test_bf16_round_ties_to_even():
     assert list(vals) == [1.0, 1 + 2**-6, 1.0, 3.0]
 
 
+def test_f16_round_matches_numpy_half_cast():
+    """IEEE binary16 rounding against numpy's float64 -> float16 conversion
+    (round to nearest even), normal, subnormal and overflowing magnitudes."""
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(20000),
+        rng.standard_normal(2000) * 1e-6,      # subnormal range (below 2**-14)
+        rng.standard_normal(2000) * 3e4,       # up to and past the largest finite value
+        np.array([0.0, -0.0, 1.0, 65504.0, 65519.0, 65520.0, -65520.0, 2.0**-24, 2.0**-25, 2.0**-14]),
+    ])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.f16_round(x), ref)
+
+
+def test_f16_round_ties_and_limits():
+    """Values fixed by the binary16 format: 11 significant bits, ties to even,
+    largest finite 65504, spacing 2**-24 below 2**-14."""
+    vals = oracle.f16_round(np.array([1 + 2**-11, 1 + 3 * 2**-11, 65504.0, 65519.0, 65520.0, -65520.0,
+                                      2.0**-24, 2.0**-25, 3 * 2.0**-25, 2.0**-14 + 2.0**-25]))
+    assert list(vals[:4]) == [1.0, 1 + 2**-9, 65504.0, 65504.0]
+    assert vals[4] == np.inf and vals[5] == -np.inf
+    assert list(vals[6:]) == [2.0**-24, 0.0, 2.0**-23, 2.0**-14]
+
+
+def test_store_rounds_to_the_element_type():
+    Y = np.array([[1 + 2**-9, 1 + 2**-12]])
+    assert list(oracle.store(Y, np.zeros(1), "bf16")[0][0]) == [1.0, 1.0]
+    assert list(oracle.store(Y, np.zeros(1), "fp16")[0][0]) == [1 + 2**-9, 1.0]
+
+
 # ------------------------------------------------------------------ masks
 
 @pytest.mark.parametrize("s1,s2", [(6, 6), (4, 9), (9, 4), (1, 1)])

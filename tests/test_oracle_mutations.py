@@ -1,7 +1,8 @@
 """The oracle's pins must catch plausible mistakes.  Each case plants one
 mistake in a private copy of the oracle's source (CPU only) and checks that at
 least one independent pin (finite differences of the forward, PyTorch fp64
-autograd, NumPy tril/triu, GQA-by-repeat) rejects it."""
+autograd, NumPy tril/triu, GQA-by-repeat, the library's bf16 / fp16 casts)
+rejects it."""
 
 import math
 import os
@@ -23,6 +24,10 @@ MUTATIONS = {
     "mask_off_by_one": ("ok &= j <= i + off + right", "ok &= j < i + off + right"),
     "mask_top_left": ("off = s2 - s1\n    i = np.arange(s1)[:, None]", "off = 0\n    i = np.arange(s1)[:, None]"),
     "scale_rule": ("else 1.0 / math.sqrt(D)", "else 1.0 / D"),
+    "bf16_bits": ("quantum = np.ldexp(1.0, e - 8)", "quantum = np.ldexp(1.0, e - 7)"),
+    "f16_bits": ("quantum = np.ldexp(1.0, e - 11)", "quantum = np.ldexp(1.0, e - 10)"),
+    "f16_subnormal_spacing": ("e = np.maximum(e, -13)", "e = np.maximum(e, -14)"),
+    "f16_no_overflow": ("np.abs(r) > 65504.0", "np.abs(r) > np.inf"),
 }
 
 
@@ -95,15 +100,30 @@ def library_pin_fails(mod):
     return not np.allclose(Y[0], out.detach().numpy(), rtol=0, atol=1e-12)
 
 
-def test_unmutated_oracle_passes_both_pins():
+def rounding_pin_fails(mod):
+    """The stored-mode roundings against the library casts: torch's float ->
+    bfloat16 and numpy's float64 -> float16 (both round to nearest even)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000), rng.standard_normal(500) * 1e-6, rng.standard_normal(500) * 3e4])
+    ref16 = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    if not np.array_equal(mod.bf16_round(x.astype(np.float32).astype(np.float64)), ref16):
+        return True
+    with np.errstate(over="ignore"):
+        refh = x.astype(np.float16).astype(np.float64)
+    return not np.array_equal(mod.f16_round(x), refh)
+
+
+def test_unmutated_oracle_passes_every_pin():
     src = open(SRC, encoding="utf-8").read()
     mod = types.ModuleType("oracle_plain")
     exec(compile(src, "<plain>", "exec"), mod.__dict__)
     assert not fd_pin_fails(mod)
     assert not library_pin_fails(mod)
+    assert not rounding_pin_fails(mod)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name):
     mod = load_mutant(name)
-    assert library_pin_fails(mod) or fd_pin_fails(mod), f"pins missed mutation {name}"
+    assert library_pin_fails(mod) or fd_pin_fails(mod) or rounding_pin_fails(mod), f"pins missed mutation {name}"

@@ -20,7 +20,7 @@ the oracle forward's stored Y and lse) against the oracle's, every element,
 so that the speed figure comes with its parity error.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--settle 0.5] [--workload gqa_causal]
-                    [--no-cpu-baseline] [--no-configs] [--copy-calibration]
+                    [--dtype bf16|fp16] [--no-cpu-baseline] [--no-configs] [--copy-calibration]
 
 Before the warmup steps, untimed steps run for --settle seconds: the shader
 clock ramps up over the first tens of milliseconds of load and drops again
@@ -107,7 +107,7 @@ def committed_traffic(workload):
         return None
 
 
-def cpu_baseline(cfg, max_heads, name=""):
+def cpu_baseline(cfg, max_heads, name="", dtype="bf16"):
     """The fp64 oracle's backward, untuned, on the first KV-head groups of
     the workload (its forward is run first, untimed, to make Y and lse).
     Returns the baseline entry and the sample (inputs, oracle Y/lse and the
@@ -124,7 +124,9 @@ def cpu_baseline(cfg, max_heads, name=""):
     G = cfg["N1"] // cfg["N2"]
     groups = max(1, min(cfg["N2"], max_heads // G))
     sub = dict(cfg, N1=groups * G, N2=groups)
-    x = W.make_inputs(cfg)
+    import torch
+
+    x = W.make_inputs(cfg, dtype=torch.float16 if dtype == "fp16" else torch.bfloat16)
     lay = cfg["layout"]
     # head slice of the full workload's tensors (the head axis is 2 in BSND,
     # 1 in BNSD and TND)
@@ -136,7 +138,7 @@ def cpu_baseline(cfg, max_heads, name=""):
     q, k, v, dy = (t.double().numpy() for t in (tq, tk, tv, tdy))
     args = (lay, x["cu_q"], x["cu_kv"], cfg["softmax_scale"], cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
     Y, lse = oracle.forward(q, k, v, *args)
-    Yst, lst = oracle.store(Y, lse)
+    Yst, lst = oracle.store(Y, lse, dtype)
     t0 = time.perf_counter()
     ref = oracle.backward(q, k, v, dy, Yst, lst, *args)
     dt = time.perf_counter() - t0
@@ -175,7 +177,7 @@ def accuracy(sample, name):
     cfg, x = sample["cfg"], sample["x"]
     dev = torch.device("cuda", 0)
     q, k, v, dout = (t.to(dev) for t in sample["t"])
-    attn_out = torch.from_numpy(np.ascontiguousarray(sample["Yst"])).to(torch.bfloat16).to(dev)
+    attn_out = torch.from_numpy(np.ascontiguousarray(sample["Yst"])).to(q.dtype).to(dev)
     lse = torch.from_numpy(np.ascontiguousarray(sample["lst"], dtype=np.float32)).to(dev)
     cu_q = cu_kv = None
     mq = mk = -1
@@ -188,13 +190,15 @@ def accuracy(sample, name):
                                     win_right=cfg["win_right"], max_seqlen_q=mq, max_seqlen_kv=mk,
                                     layout=cfg["layout"])
     torch.cuda.synchronize()
+    # the parity tests' bounds: bf16, and 2^3 tighter for fp16 (3 more significant bits)
+    tol_rel, tol_max = (1.25e-3, 2.5e-3) if q.dtype == torch.float16 else (1e-2, 2e-2)
     out = {"reference": "fp64 oracle (oracle.backward) on the CPU-baseline sample, every element",
-           "tolerance": {"rel_fro": 1e-2, "max_abs_ratio": 2e-2}}
+           "tolerance": {"rel_fro": tol_rel, "max_abs_ratio": tol_max}}
     ok = True
     for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), sample["ref"]):
         rel, mx = _errors(got.cpu().double().numpy(), ref)
         out[nm] = {"rel_fro": float(f"{rel:.4g}"), "max_abs_ratio": float(f"{mx:.4g}")}
-        ok = ok and rel <= 1e-2 and mx <= 2e-2
+        ok = ok and rel <= tol_rel and mx <= tol_max
     out["within_tolerance"] = bool(ok)
     out["sample"] = f"{cfg['N1']} query heads of the {name} workload"
     return out
@@ -215,7 +219,7 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
-def measure(name, steps, warmup, settle_s=0.0):
+def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     """Time `steps` backward steps of a workload on the current stream, after
     untimed steps for at least `settle_s` seconds (the shader clock ramps up
     over the first tens of milliseconds of load, and drops again while the host
@@ -229,7 +233,7 @@ def measure(name, steps, warmup, settle_s=0.0):
 
     cfg = W.CONFIGS[name]
     dev = torch.device("cuda", 0)
-    x = W.make_inputs(cfg)
+    x = W.make_inputs(cfg, dtype=torch.float16 if dtype == "fp16" else torch.bfloat16)
     q, k, v, dout = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
     cu_q = cu_kv = None
     mq = mk = -1
@@ -304,6 +308,8 @@ def main():
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp-up)")
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
+                    help="element type of q, k, v, dout, attn_out and the gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (cpu_baseline and accuracy)")
     ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -322,7 +328,7 @@ def main():
 
     name = args.workload or W.BENCH_WORKLOAD
     cfg = W.CONFIGS[name]
-    m = measure(name, args.steps, args.warmup, args.settle)
+    m = measure(name, args.steps, args.warmup, args.settle, args.dtype)
     ms_per_step, main_avg, pre_ms, pre_bytes = m["ms_per_step"], m["pair_ms"], m["pre_ms"], m["pre_bytes"]
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
 
@@ -343,7 +349,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
@@ -380,7 +386,7 @@ def main():
                 r = m
             else:
                 torch.cuda.empty_cache()
-                r = measure(other, 10, 2, args.settle)
+                r = measure(other, 10, 2, args.settle, args.dtype)
             f = algorithmic_flops(W.CONFIGS[other])
             rows[other] = {
                 "ms_per_step": round(r["ms_per_step"], 4),
@@ -393,7 +399,7 @@ def main():
             }
         line["configs"] = rows
     if not args.no_cpu_baseline:
-        line["cpu_baseline"], sample = cpu_baseline(cfg, args.cpu_heads, name)
+        line["cpu_baseline"], sample = cpu_baseline(cfg, args.cpu_heads, name, args.dtype)
         line["accuracy"] = accuracy(sample, name)
     print(json.dumps(line), flush=True)
 

@@ -243,17 +243,20 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
 
 int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, const void* dout,
                const void* attn_out, const float* softmax_lse, const int32_t* cu_seqlens_q,
-               const int32_t* cu_seqlens_kv, void* dq, void* dk, void* dv, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               const int32_t* cu_seqlens_kv, const int32_t* seqused_q, const int32_t* seqused_kv, void* dq,
+               void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || !q || !k || !v || !dout || !attn_out || !softmax_lse || !dq || !dk || !dv)
     return FA_ERR_NULLPTR;
   int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
   if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < plan->ws_bytes) return FA_ERR_WORKSPACE;
+  // the tuning-only atomic kernels do not read seqused
+  if ((seqused_q || seqused_kv) && plan->args.variant < 2) return FA_ERR_UNSUPPORTED;
 
   KernelArgs a = plan->args;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out = attn_out; a.lse = softmax_lse;
   a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
+  a.seqused_q = seqused_q; a.seqused_kv = seqused_kv;
   a.dq = dq; a.dk = dk; a.dv = dv;
   char* ws = static_cast<char*>(workspace);
   a.sfmg = reinterpret_cast<float*>(ws + plan->off_sfmg);
@@ -287,13 +290,15 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
 }
 
 int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-               const int32_t* cu_seqlens_kv, void* attn_out, float* softmax_lse, void* stream) {
+               const int32_t* cu_seqlens_kv, const int32_t* seqused_q, const int32_t* seqused_kv, void* attn_out,
+               float* softmax_lse, void* stream) {
   if (!plan || !q || !k || !v || !attn_out || !softmax_lse) return FA_ERR_NULLPTR;
   int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
   if (st != FA_OK) return st;
   KernelArgs a = plan->args;
   a.q = q; a.k = k; a.v = v;
   a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
+  a.seqused_q = seqused_q; a.seqused_kv = seqused_kv;
   if (fabwd::launch_forward(a, attn_out, softmax_lse, stream) != 0) return FA_ERR_RUNTIME;
   return FA_OK;
 }

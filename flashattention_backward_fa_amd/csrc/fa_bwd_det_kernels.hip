@@ -103,8 +103,10 @@ __device__ __forceinline__ int swz(int r, int c) {
   }
 }
 
+// s1, s2: rows / keys that take part; s1a, s2a: rows / keys the sequence
+// holds (they differ only when seqused_q / seqused_kv are given).
 struct SeqBounds {
-  int s1, s2;
+  int s1, s2, s1a, s2a;
   int64_t qbase, kbase, vbase, obase, lbase;
 };
 
@@ -128,6 +130,10 @@ __device__ __forceinline__ SeqBounds seq_bounds(const KernelArgs& a, int b) {
     r.vbase = (int64_t)b * a.v_sb;
     r.lbase = (int64_t)b * a.l_sb;
   }
+  r.s1a = r.s1;
+  r.s2a = r.s2;
+  if (a.seqused_q) r.s1 = fa_sched::used_len(r.s1a, a.seqused_q[b]);
+  if (a.seqused_kv) r.s2 = fa_sched::used_len(r.s2a, a.seqused_kv[b]);
   return r;
 }
 
@@ -374,20 +380,24 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   const SeqBounds sb = seq_bounds(a, b);
   const int s1 = sb.s1, s2 = sb.s2;
   const int j0 = tile * BC;
-  if (j0 >= s2) return;
+  if (j0 >= sb.s2a) return;
+  // a tile past the used keys (seqused_kv) computes nothing and writes zeros
+  const bool live = j0 < s2;
   const int j1 = min(j0 + BC, s2);
   const int off = s2 - s1;
   const int wl = a.win_left, wr = a.win_right;
 
   // K and V tiles, asynchronously (rows past the sequence end repeat its last key)
+  const int kvalid = (live ? s2 : sb.s2a) - j0;
   padded_copy<HD, BC, NWG * QG>(lds_addr(Ks), static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j0 * a.k_ss,
-                                (int)a.k_ss * 2, s2 - j0, wave, lane);
+                                (int)a.k_ss * 2, kvalid, wave, lane);
   padded_copy<HDV, BC, NWG * QG>(lds_addr(Vs), static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j0 * a.v_ss,
-                               (int)a.v_ss * 2, s2 - j0, wave, lane);
+                               (int)a.v_ss * 2, kvalid, wave, lane);
 
   // query blocks that see a key of [j0, j1); this job takes split qs of them
   const fa_sched::Span blks =
-      fa_sched::split_part(fa_sched::blocks_covering(fa_sched::rows_seeing(s1, j0, j1, off, wl, wr), BR), qs, QS);
+      live ? fa_sched::split_part(fa_sched::blocks_covering(fa_sched::rows_seeing(s1, j0, j1, off, wl, wr), BR), qs, QS)
+           : fa_sched::Span{0, 0};
   const int bs_lo = blks.lo;
   const int nblk = blks.hi - blks.lo;
   const int T = hpj * nblk;  // items: (query head, query block) pairs
@@ -611,7 +621,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
 #pragma unroll
     for (int rg = 0; rg < 16; ++rg) {
       const int j = j0 + kw0 + kb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
-      if (j >= s2) continue;
+      if (j >= sb.s2a) continue;  // keys past the used ones hold zeros
       const int64_t ko = sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
       const int64_t vo = sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
       if (partial) {
@@ -659,7 +669,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   const SeqBounds sb = seq_bounds(a, b);
   const int s1 = sb.s1, s2 = sb.s2;
   const int i0 = tile * DQ_BQ;
-  if (i0 >= s1) return;
+  if (i0 >= sb.s1a) return;  // a tile past the used rows (seqused_q) writes zeros
   const int off = s2 - s1;
   const int wl = a.win_left, wr = a.win_right;
   const int iq = i0 + wave * 32 + l32;  // this lane's query row
@@ -670,8 +680,9 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   const bf16* __restrict__ Vg = static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn;
 
   // keys that any row of [i0, i0 + DQ_BQ) can see
-  const fa_sched::Span kblk =
-      fa_sched::blocks_covering(fa_sched::keys_seen(s2, i0, min(i0 + DQ_BQ, s1), off, wl, wr), DQ_BK);
+  const fa_sched::Span kblk = i0 < s1 ? fa_sched::blocks_covering(
+                                             fa_sched::keys_seen(s2, i0, min(i0 + DQ_BQ, s1), off, wl, wr), DQ_BK)
+                                       : fa_sched::Span{0, 0};
   const int jb0 = kblk.lo * DQ_BK;
   const int nsteps = kblk.hi - kblk.lo;
 
@@ -795,7 +806,7 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
 #pragma unroll
   for (int rg = 0; rg < 16; ++rg) {
     const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
-    if (i < s1) {
+    if (i < sb.s1a) {  // rows past the used ones hold zeros
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
     }

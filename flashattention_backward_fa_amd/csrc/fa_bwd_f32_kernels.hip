@@ -37,8 +37,10 @@ constexpr int F32_BQ = 32;   // query rows per dQ workgroup
 constexpr int F32_CH = 8;    // rows (dK/dV) or keys (dQ) per LDS chunk
 constexpr int F32_MAXD = 192;
 
+// s1, s2: rows / keys that take part (seqused_q / seqused_kv when given);
+// s1a, s2a: rows / keys the sequence holds.
 struct Seq {
-  int s1, s2;
+  int s1, s2, s1a, s2a;
   int64_t qbase, kbase, vbase, obase, lbase;
 };
 
@@ -62,6 +64,10 @@ __device__ Seq seq_of(const KernelArgs& a, int b) {
     r.vbase = (int64_t)b * a.v_sb;
     r.lbase = (int64_t)b * a.l_sb;
   }
+  r.s1a = r.s1;
+  r.s2a = r.s2;
+  if (a.seqused_q) r.s1 = fa_sched::used_len(r.s1a, a.seqused_q[b]);
+  if (a.seqused_kv) r.s2 = fa_sched::used_len(r.s2a, a.seqused_kv[b]);
   return r;
 }
 
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   const int tile = r / a.B;
   const Seq sq = seq_of(a, b);
   const int j0 = tile * F32_BK;
-  if (j0 >= sq.s2) return;
+  if (j0 >= sq.s2a) return;  // keys past the used ones get zeros below
   const int off = sq.s2 - sq.s1;
 
   const bf16* K = static_cast<const bf16*>(a.k) + sq.kbase + (int64_t)n2 * a.k_sn;
@@ -97,8 +103,9 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
   }
 
   // rows that can see a key of the tile
-  const fa_sched::Span rows =
-      fa_sched::rows_seeing(sq.s1, j0, min(j0 + F32_BK, sq.s2), off, a.win_left, a.win_right);
+  const fa_sched::Span rows = j0 < sq.s2 ? fa_sched::rows_seeing(sq.s1, j0, min(j0 + F32_BK, sq.s2), off,
+                                                                  a.win_left, a.win_right)
+                                         : fa_sched::Span{0, 0};
   const int i_lo = rows.lo, i_hi = rows.hi;
 
   const int pr = t / F32_BK, pj = t % F32_BK;   // pair role: row pr of the chunk, key pj
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(KernelArgs a) {
     }
   }
   const int j = j0 + ak;
-  if (j < sq.s2) {
+  if (j < sq.s2a) {
     float* dK = static_cast<float*>(a.dk) + sq.kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
     float* dV = static_cast<float*>(a.dv) + sq.vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
 #pragma unroll
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
   const int n2 = n1 / a.G;
   const Seq sq = seq_of(a, b);
   const int i0 = tile * F32_BQ;
-  if (i0 >= sq.s1) return;
+  if (i0 >= sq.s1a) return;  // rows past the used ones get zeros below
   const int off = sq.s2 - sq.s1;
 
   const bf16* Q = static_cast<const bf16*>(a.q) + sq.qbase + (int64_t)n1 * a.q_sn;
@@ -204,8 +211,9 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
   }
 
   // keys that a row of the tile can see
-  const fa_sched::Span keys =
-      fa_sched::keys_seen(sq.s2, i0, min(i0 + F32_BQ, sq.s1), off, a.win_left, a.win_right);
+  const fa_sched::Span keys = i0 < sq.s1 ? fa_sched::keys_seen(sq.s2, i0, min(i0 + F32_BQ, sq.s1), off,
+                                                                a.win_left, a.win_right)
+                                         : fa_sched::Span{0, 0};
   const int j_lo = keys.lo, j_hi = keys.hi;
 
   const int pr = t / F32_CH, pc = t % F32_CH;   // pair role: row pr, key pc of the chunk
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(KernelArgs a) {
     }
   }
   const int i = i0 + ar;
-  if (i < sq.s1) {
+  if (i < sq.s1a) {
     float* dQ = static_cast<float*>(a.dq) + sq.qbase + (int64_t)n1 * a.q_sn + (int64_t)i * a.q_ss;
 #pragma unroll
     for (int m = 0; m < F32_MAXD / 8; ++m) {

@@ -24,6 +24,8 @@ struct KernelArgs {
   const float* lse;
   const int32_t* cu_q;   // TND only (device)
   const int32_t* cu_kv;  // TND only (device)
+  const int32_t* seqused_q;   // optional (device, [B]): rows of each sequence that take part
+  const int32_t* seqused_kv;  // optional (device, [B]): keys of each sequence that take part
   float* dq_acc;         // fp32, q's layout
   float* sfmg;           // fp32, lse's layout
   float* dk_acc;         // fp32, k's layout (only when query heads are split)

@@ -55,6 +55,12 @@ constexpr Span rows_of_key(int j, int s1, int s2, int off, int left, int right) 
   return j < s2 ? rows_seeing(s1, j, j + 1, off, left, right) : Span{0, 0};
 }
 
+// Rows of a sequence that take part: the first `used` of its `alloc` rows when a
+// per-sequence used length is given (seqused_q / seqused_kv), clamped to
+// [0, alloc]; the rest are padding that nothing attends and whose gradients are
+// zero.
+constexpr int used_len(int alloc, int used) { return used < 0 ? 0 : (used < alloc ? used : alloc); }
+
 // Blocks of `bs` indices that cover r: block indices [lo, hi) (empty when r is).
 constexpr Span blocks_covering(Span r, int bs) {
   return r.hi > r.lo ? Span{r.lo / bs, (r.hi + bs - 1) / bs} : Span{r.lo / bs, r.lo / bs};

@@ -97,8 +97,13 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
     kbase = (int64_t)b * a.k_sb; vbase = (int64_t)b * a.v_sb;
     lbase = (int64_t)b * a.l_sb;
   }
+  // rows / keys that take part (seqused_q / seqused_kv); rows past them
+  // (s1 <= row < s1a) get attn_out = 0 and softmax_lse = -inf
+  const int s1a = s1;
+  if (a.seqused_q) s1 = fa_sched::used_len(s1a, a.seqused_q[b]);
+  if (a.seqused_kv) s2 = fa_sched::used_len(s2, a.seqused_kv[b]);
   const int i0 = tile * FQ;
-  if (i0 >= s1) return;
+  if (i0 >= s1a) return;
   const int off = s2 - s1;
   const int wl = a.win_left, wr = a.win_right;
   const int iq = i0 + wave * 32 + l32;  // this lane's query row
@@ -117,7 +122,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
 
   // keys that any row of [i0, i0 + FQ) can see
   const fa_sched::Span kblk =
-      fa_sched::blocks_covering(fa_sched::keys_seen(s2, i0, min(i0 + FQ, s1), off, wl, wr), FK);
+      i0 < s1 ? fa_sched::blocks_covering(fa_sched::keys_seen(s2, i0, min(i0 + FQ, s1), off, wl, wr), FK)
+              : fa_sched::Span{0, 0};
 
   const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int tr_r4 = 4 * hi + ((lane & 15) >> 2);
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(KernelArgs a, bf16* __restr
     }
   }
 
-  if (iq < s1) {
+  if (iq < s1a) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     bf16* __restrict__ Og = out + obase + (int64_t)n1 * a.o_sn + (int64_t)iq * a.o_ss;
 #pragma unroll

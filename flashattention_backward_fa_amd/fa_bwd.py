@@ -19,7 +19,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libfa_bwd.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 FA_OK = 0
 FA_ERR_NULLPTR = 1
@@ -106,11 +106,11 @@ def load_library(path=LIB_PATH):
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.fa_bwd_create.argtypes = [ctypes.POINTER(FaBwdDesc), ctypes.POINTER(vp), ctypes.POINTER(sz)]
     lib.fa_bwd_create.restype = ctypes.c_int
-    lib.fa_bwd_run.argtypes = [vp] * 9 + [vp] * 3 + [vp, sz, vp]
+    lib.fa_bwd_run.argtypes = [vp] * 11 + [vp] * 3 + [vp, sz, vp]
     lib.fa_bwd_run.restype = ctypes.c_int
     lib.fa_bwd_sfmg.argtypes = [vp] * 6
     lib.fa_bwd_sfmg.restype = ctypes.c_int
-    lib.fa_fwd_run.argtypes = [vp] * 9
+    lib.fa_fwd_run.argtypes = [vp] * 11
     lib.fa_fwd_run.restype = ctypes.c_int
     lib.fa_bwd_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.fa_bwd_profile_enable.restype = ctypes.c_int
@@ -175,14 +175,15 @@ class Plan:
             lib.fa_bwd_destroy(h)
             self.handle = None
 
-    def run(self, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv, workspace, workspace_bytes, stream):
-        st = self._lib.fa_bwd_run(self.handle, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv,
-                                       workspace, workspace_bytes, stream)
+    def run(self, q, k, v, dout, attn_out, lse, cu_q, cu_kv, dq, dk, dv, workspace, workspace_bytes, stream,
+            seqused_q=None, seqused_kv=None):
+        st = self._lib.fa_bwd_run(self.handle, q, k, v, dout, attn_out, lse, cu_q, cu_kv, seqused_q, seqused_kv,
+                                  dq, dk, dv, workspace, workspace_bytes, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_run")
 
-    def forward(self, q, k, v, cu_q, cu_kv, attn_out, lse, stream):
-        st = self._lib.fa_fwd_run(self.handle, q, k, v, cu_q, cu_kv, attn_out, lse, stream)
+    def forward(self, q, k, v, cu_q, cu_kv, attn_out, lse, stream, seqused_q=None, seqused_kv=None):
+        st = self._lib.fa_fwd_run(self.handle, q, k, v, cu_q, cu_kv, seqused_q, seqused_kv, attn_out, lse, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_fwd_run")
 
@@ -238,6 +239,16 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
+def _seqused(t, device):
+    """Validate an optional seqused tensor (int32 on the inputs' device)."""
+    import torch
+
+    if t is None:
+        return None
+    _check("seqused", t, torch.int32, device)
+    return t.contiguous()
+
+
 def _check(name, t, dtype, device):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -288,7 +299,7 @@ def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, soft
 def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None,
                     softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
                     max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None,
-                    fp32_out=False):
+                    fp32_out=False, seqused_q=None, seqused_kv=None):
     """dq, dk, dv of attention on the current HIP stream, in the inputs' element
     type (bf16 or fp16).
 
@@ -298,7 +309,9 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
     TND only.  Non-contiguous inputs are made contiguous first.  `workspace`
     (uint8 tensor) and `out` ((dq, dk, dv)) may be passed to avoid allocation.
     fp32_out=True selects the fp32 debugging form (float32 outputs, P and dS
-    kept in fp32; slow).
+    kept in fp32; slow).  seqused_q / seqused_kv: optional int32 device
+    tensors [B]; only the first seqused[b] rows / keys of sequence b take part
+    and the gradients of the rest are zero.
     """
     import torch
 
@@ -316,6 +329,7 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
         cu_seqlens_q, cu_seqlens_kv = cu_seqlens_q.contiguous(), cu_seqlens_kv.contiguous()
     if dout.shape != attn_out.shape:
         raise ValueError("dout and attn_out must have the same shape")
+    seqused_q, seqused_kv = _seqused(seqused_q, dev), _seqused(seqused_kv, dev)
     plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
                     max_seqlen_q, max_seqlen_kv, deterministic, fp32_out=fp32_out)
     odt = torch.float32 if fp32_out else q.dtype
@@ -331,12 +345,13 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
         workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     plan.run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(attn_out), _ptr(softmax_lse), _ptr(cu_seqlens_q),
-             _ptr(cu_seqlens_kv), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stream)
+             _ptr(cu_seqlens_kv), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stream,
+             _ptr(seqused_q), _ptr(seqused_kv))
     return dq, dk, dv
 
 
 def flash_attn(q, k, v, cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0, mask_mode=0, win_left=-1,
-               win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1, layout="BSND"):
+               win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1, layout="BSND", seqused_q=None, seqused_kv=None):
     """Forward (attn_out in the inputs' element type, softmax_lse float32) with
     the same conventions as flash_attn_grad; its outputs are what
     flash_attn_grad expects."""
@@ -358,7 +373,8 @@ def flash_attn(q, k, v, cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0
     else:
         lse = torch.empty((sh["B"], sh["N1"], sh["S1"]), dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    plan.forward(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out), _ptr(lse), stream)
+    plan.forward(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out), _ptr(lse), stream,
+                 _ptr(_seqused(seqused_q, dev)), _ptr(_seqused(seqused_kv, dev)))
     return out, lse
 
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 1
+#define FA_BWD_ABI_VERSION 2
 
 /* Status codes.  The classes mirror the aclnn error families that page
  * "aclnnFusedFloydAttentionGrad" lists (null pointer 161001, invalid
@@ -129,6 +129,16 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
  *   cu_seqlens_q/kv         : device int32 [B+1] prefix sums; required for TND
  *                             (cu[0] = 0, non-decreasing, cu[B] = T), NULL
  *                             otherwise (section 四 4.6)
+ *   seqused_q/kv            : optional device int32 [B] (the page's seqused_q /
+ *                             seqused_kv inputs, section 二 2.1; it names them
+ *                             only): of sequence b only the first seqused[b]
+ *                             query rows / keys take part (values clamped to
+ *                             [0, the sequence's length]); masks align on those
+ *                             used lengths; the rest is padding that nothing
+ *                             attends and whose dq / dk / dv rows are written
+ *                             as zeros.  NULL: every row takes part.  Any layout.
+ *                             Not available with the tuning-only atomic kernels
+ *                             (FA_ERR_UNSUPPORTED).
  *   dq, dk, dv              : outputs of the plan's element type, shapes of
  *                             q, k, v
  *   workspace               : device memory of at least *workspace_bytes from
@@ -142,6 +152,7 @@ int fa_bwd_run(fa_bwd_plan plan,
                const void* q, const void* k, const void* v,
                const void* dout, const void* attn_out, const float* softmax_lse,
                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+               const int32_t* seqused_q, const int32_t* seqused_kv,
                void* dq, void* dk, void* dv,
                void* workspace, size_t workspace_bytes, void* stream);
 
@@ -158,10 +169,11 @@ int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
  * element type, q's layout with Dv) and float32 softmax_lse ([B, N1, S1] or
  * [N1, T1]) for the plan's problem, masks and layout.  A query row with no
  * visible key gets
- * attn_out = 0 and softmax_lse = -inf.  Same pointer rules and errors as
- * fa_bwd_run; needs no workspace. */
+ * attn_out = 0 and softmax_lse = -inf, and so does a row past seqused_q.
+ * Same pointer rules and errors as fa_bwd_run; needs no workspace. */
 int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,
                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+               const int32_t* seqused_q, const int32_t* seqused_kv,
                void* attn_out, float* softmax_lse, void* stream);
 
 /* Timing hook.  With slots > 0, every later fa_bwd_run records one pair of

@@ -225,21 +225,33 @@ def _lse_shape(q, layout):
     return (q.shape[0], q.shape[1], q.shape[2])
 
 
+def used_lengths(b, s1, s2, seqused_q=None, seqused_kv=None):
+    """Rows and keys of sequence b that take part (reading: the page only names
+    seqused_q / seqused_kv; the first seqused[b] rows of a sequence take part,
+    clamped to [0, its length], and the rest are padding)."""
+    u1 = s1 if seqused_q is None else min(max(int(seqused_q[b]), 0), s1)
+    u2 = s2 if seqused_kv is None else min(max(int(seqused_kv[b]), 0), s2)
+    return u1, u2
+
+
 def forward(q, k, v, layout="BSND", cu_q=None, cu_kv=None, softmax_scale=0.0,
-            mask_mode=0, win_left=-1, win_right=-1):
-    """Y (layout of q with Dv) and lse (float64) for the whole problem."""
+            mask_mode=0, win_left=-1, win_right=-1, seqused_q=None, seqused_kv=None):
+    """Y (layout of q with Dv) and lse (float64) for the whole problem.  Rows
+    past seqused_q get Y = 0 and lse = -inf; keys past seqused_kv are not
+    attended; the diagonal aligns on the used lengths."""
     qs, ks, N1, N2, G = _problem(q, k, layout, cu_q, cu_kv)
     vs = split_heads(v, layout, cu_kv)
     scale = resolve_scale(softmax_scale, qs[0].shape[2])
     left, right = mask_bounds(mask_mode, win_left, win_right)
     Ys, lses = [], []
-    for qb, kb, vb in zip(qs, ks, vs):
+    for b, (qb, kb, vb) in enumerate(zip(qs, ks, vs)):
         s1, s2 = qb.shape[1], kb.shape[1]
-        ok = allowed_matrix(s1, s2, left, right)
+        u1, u2 = used_lengths(b, s1, s2, seqused_q, seqused_kv)
+        ok = allowed_matrix(u1, u2, left, right)
         Yb = np.zeros((N1, s1, vb.shape[2]))
-        lb = np.zeros((N1, s1))
+        lb = np.full((N1, s1), -np.inf)
         for n1 in range(N1):
-            Yb[n1], lb[n1] = head_forward(qb[n1], kb[n1 // G], vb[n1 // G], scale, ok)
+            Yb[n1, :u1], lb[n1, :u1] = head_forward(qb[n1, :u1], kb[n1 // G, :u2], vb[n1 // G, :u2], scale, ok)
         Ys.append(Yb)
         lses.append(lb)
     qa = np.asarray(q)
@@ -262,9 +274,12 @@ def sfmg(dY, Y, layout="BSND", cu_q=None):
 
 
 def backward(q, k, v, dY, Y, lse, layout="BSND", cu_q=None, cu_kv=None,
-             softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1):
+             softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, seqused_q=None,
+             seqused_kv=None):
     """dq, dk, dv (float64, shapes of q, k, v).  dK/dV of key/value head n2
-    sum the contributions of its G query heads."""
+    sum the contributions of its G query heads.  With seqused_q / seqused_kv
+    only the used rows and keys take part (see used_lengths); the gradients of
+    the rest are zero."""
     qs, ks, N1, N2, G = _problem(q, k, layout, cu_q, cu_kv)
     vs = split_heads(v, layout, cu_kv)
     dYs = split_heads(dY, layout, cu_q)
@@ -273,18 +288,20 @@ def backward(q, k, v, dY, Y, lse, layout="BSND", cu_q=None, cu_kv=None,
     scale = resolve_scale(softmax_scale, qs[0].shape[2])
     left, right = mask_bounds(mask_mode, win_left, win_right)
     dqs, dks, dvs = [], [], []
-    for qb, kb, vb, dyb, yb, lb in zip(qs, ks, vs, dYs, Yst, lses):
+    for b, (qb, kb, vb, dyb, yb, lb) in enumerate(zip(qs, ks, vs, dYs, Yst, lses)):
         s1, s2 = qb.shape[1], kb.shape[1]
-        ok = allowed_matrix(s1, s2, left, right)
+        u1, u2 = used_lengths(b, s1, s2, seqused_q, seqused_kv)
+        ok = allowed_matrix(u1, u2, left, right)
         dqb = np.zeros_like(qb)
         dkb = np.zeros_like(kb)
         dvb = np.zeros_like(vb)
         for n1 in range(N1):
             n2 = n1 // G
-            r = head_backward(qb[n1], kb[n2], vb[n2], dyb[n1], yb[n1], lb[n1], scale, ok)
-            dqb[n1] = r["dq"]
-            dkb[n2] += r["dk"]
-            dvb[n2] += r["dv"]
+            r = head_backward(qb[n1, :u1], kb[n2, :u2], vb[n2, :u2], dyb[n1, :u1], yb[n1, :u1], lb[n1, :u1],
+                              scale, ok)
+            dqb[n1, :u1] = r["dq"]
+            dkb[n2, :u2] += r["dk"]
+            dvb[n2, :u2] += r["dv"]
         dqs.append(dqb)
         dks.append(dkb)
         dvs.append(dvb)

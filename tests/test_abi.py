@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.fa_bwd_abi_version() == 1
+    assert lib.fa_bwd_abi_version() == fb.ABI_VERSION == 2
     for st in range(0, 7):
         assert len(fb.strerror(st)) > 0
     assert fb.strerror(99) == "unknown status"
@@ -172,16 +172,22 @@ def test_tnd_decreasing_cu_rejected(lib):
 def test_run_checks_before_any_device_call(lib):
     plan = fb.Plan(fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64))
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every check below fails first
-    args = [fake] * 6 + [None, None] + [fake] * 3
+    # q k v dout attn_out lse | cu_q cu_kv | seqused_q seqused_kv | dq dk dv
+    args = [fake] * 6 + [None, None] + [None, None] + [fake] * 3
     st = lib.fa_bwd_run(plan.handle, *args, None, plan.workspace_bytes, None)
     assert st == fb.FA_ERR_WORKSPACE
     st = lib.fa_bwd_run(plan.handle, *args, fake, plan.workspace_bytes - 1, None)
     assert st == fb.FA_ERR_WORKSPACE
-    st = lib.fa_bwd_run(plan.handle, *([fake] * 6), fake, fake, *([fake] * 3), fake, plan.workspace_bytes, None)
+    st = lib.fa_bwd_run(plan.handle, *([fake] * 6), fake, fake, None, None, *([fake] * 3), fake,
+                        plan.workspace_bytes, None)
     assert st == fb.FA_ERR_SHAPE   # cu_seqlens given for a dense layout
     st = lib.fa_bwd_run(plan.handle, None, *args[1:], fake, plan.workspace_bytes, None)
     assert st == fb.FA_ERR_NULLPTR
     assert lib.fa_bwd_run(None, *args, fake, plan.workspace_bytes, None) == fb.FA_ERR_NULLPTR
+    st = lib.fa_fwd_run(plan.handle, fake, fake, fake, fake, None, None, None, fake, fake, None)
+    assert st == fb.FA_ERR_SHAPE   # cu_seqlens given for a dense layout
+    st = lib.fa_fwd_run(plan.handle, None, fake, fake, None, None, None, None, fake, fake, None)
+    assert st == fb.FA_ERR_NULLPTR
     assert lib.fa_bwd_sfmg(plan.handle, None, fake, None, fake, None) == fb.FA_ERR_NULLPTR
 
 

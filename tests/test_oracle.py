@@ -392,6 +392,83 @@ def test_tnd_equals_per_sequence_dense():
     assert not np.any(dk[5:7]) and not np.any(dv[5:7])
 
 
+# ------------------------------------------------------------------ seqused (reading)
+
+def test_seqused_at_full_length_changes_nothing():
+    rng = np.random.default_rng(21)
+    p = problem(rng, "BSND", B=2, N1=4, N2=2, S1=5, S2=7)
+    akw = dict(mask_mode=1, softmax_scale=0.6)
+    Y, lse = fwd(p, **akw)
+    g = bwd(p, Y, lse, **akw)
+    used = dict(seqused_q=np.array([5, 5]), seqused_kv=np.array([7, 9]))  # 9 is clamped to 7
+    Yu, lu = fwd(p, **akw, **used)
+    gu = bwd(p, Y, lse, **akw, **used)
+    assert np.array_equal(Y, Yu) and np.array_equal(lse, lu)
+    for a, b in zip(g, gu):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("layout", ["BSND", "BNSD", "TND"])
+def test_seqused_equals_the_truncated_problem(layout):
+    """Used rows of each sequence behave as a problem of the used lengths
+    (masks aligned on them); padding rows have Y = 0, lse = -inf and zero
+    gradients.  Checked against the unpadded problem, sequence by sequence."""
+    rng = np.random.default_rng(22)
+    B, S1, S2 = 3, 8, 9
+    if layout == "TND":
+        lens_q, lens_kv = [8, 3, 6], [9, 5, 9]
+        p = problem(rng, "TND", N1=4, N2=2, D=4, Dv=3, lens_q=lens_q, lens_kv=lens_kv)
+    else:
+        lens_q, lens_kv = [S1] * B, [S2] * B
+        p = problem(rng, layout, B=B, N1=4, N2=2, S1=S1, S2=S2, D=4, Dv=3)
+    uq, ukv = np.array([5, 0, 20]), np.array([6, 3, 2])
+    akw = dict(mask_mode=2, win_left=3, win_right=1, softmax_scale=0.55)
+    Y, lse = fwd(p, **akw, seqused_q=uq, seqused_kv=ukv)
+    dq, dk, dv = bwd(p, Y, lse, **akw, seqused_q=uq, seqused_kv=ukv)
+    parts = [oracle.split_heads(t, layout, c) for t, c in
+             ((p["q"], p["cu_q"]), (p["k"], p["cu_kv"]), (p["v"], p["cu_kv"]), (p["dY"], p["cu_q"]),
+              (Y, p["cu_q"]), (dq, p["cu_q"]), (dk, p["cu_kv"]), (dv, p["cu_kv"]))]
+    lses = oracle.attention._split_lse(lse, layout, p["cu_q"])
+    for b in range(B):
+        u1, u2 = min(uq[b], lens_q[b]), min(ukv[b], lens_kv[b])
+        qb, kb, vb, dyb, yb, dqb, dkb, dvb = (x[b] for x in parts)
+        assert not np.any(yb[:, u1:]) and np.all(lses[b][:, u1:] == -np.inf)
+        assert not np.any(dqb[:, u1:]) and not np.any(dkb[:, u2:]) and not np.any(dvb[:, u2:])
+        t = dict(q=qb[None, :, :u1], k=kb[None, :, :u2], v=vb[None, :, :u2], dY=dyb[None, :, :u1],
+                 layout="BNSD", cu_q=None, cu_kv=None)
+        if u1 == 0:
+            assert not np.any(dkb) and not np.any(dvb)
+            continue
+        Yt, lt = fwd(t, **akw)
+        assert np.allclose(Yt[0], yb[:, :u1], atol=1e-13)
+        assert np.allclose(lt[0], lses[b][:, :u1], atol=1e-13)
+        gq, gk, gv = bwd(t, Yt, lt, **akw)
+        assert np.allclose(gq[0], dqb[:, :u1], atol=1e-12)
+        assert np.allclose(gk[0], dkb[:, :u2], atol=1e-12)
+        assert np.allclose(gv[0], dvb[:, :u2], atol=1e-12)
+
+
+def test_seqused_backward_matches_finite_differences():
+    """With seqused the backward is still the gradient of the forward, padding
+    entries included (their gradient is zero because they do not enter Y)."""
+    rng = np.random.default_rng(23)
+    p = problem(rng, "BSND", B=2, N1=2, N2=1, S1=4, S2=5, D=3, Dv=2)
+    kw = dict(mask_mode=1, softmax_scale=0.7, seqused_q=np.array([3, 4]), seqused_kv=np.array([2, 5]))
+    Y, lse = fwd(p, **kw)
+    g = bwd(p, Y, lse, **kw)
+    h = 1e-6
+    for gi, name in enumerate(("q", "k", "v")):
+        x = p[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            for sgn in (1, -1):
+                pp = dict(p)
+                pp[name] = x.copy()
+                pp[name][idx] += sgn * h
+                fd[idx] += sgn * float((fwd(pp, **kw)[0] * p["dY"]).sum()) / (2 * h)
+        assert np.abs(g[gi] - fd).max() <= 1e-6 * max(np.abs(fd).max(), 1e-3)
+
+
 def test_wide_window_equals_causal_and_open_window_equals_dense():
     rng = np.random.default_rng(14)
     p = problem(rng, "BSND", B=1, N1=2, N2=2, S1=8, S2=8, D=4, Dv=4)

@@ -1,8 +1,8 @@
 """The oracle's pins must catch plausible mistakes.  Each case plants one
 mistake in a private copy of the oracle's source (CPU only) and checks that at
 least one independent pin (finite differences of the forward, PyTorch fp64
-autograd, NumPy tril/triu, GQA-by-repeat, the library's bf16 / fp16 casts)
-rejects it."""
+autograd, NumPy tril/triu, GQA-by-repeat, the library's bf16 / fp16 casts,
+seqused against the unpadded problem) rejects it."""
 
 import math
 import os
@@ -19,7 +19,8 @@ MUTATIONS = {
     "dq_without_scale": ("dq = scale * (dS @ k)", "dq = dS @ k"),
     "dk_uses_P": ("dk = scale * (dS.T @ q)", "dk = scale * (P.T @ q)"),
     "dv_uses_Y": ("dv = P.T @ dY", "dv = P.T @ Y"),
-    "gqa_interleaved": ("r = head_backward(qb[n1], kb[n2], vb[n2]", "r = head_backward(qb[n1], kb[n1 % N2], vb[n1 % N2]"),
+    "gqa_interleaved": ("r = head_backward(qb[n1, :u1], kb[n2, :u2], vb[n2, :u2]",
+                        "r = head_backward(qb[n1, :u1], kb[n1 % N2, :u2], vb[n1 % N2, :u2]"),
     "lse_log2": ("lse[rows] = m + np.log(", "lse[rows] = m + np.log2("),
     "mask_off_by_one": ("ok &= j <= i + off + right", "ok &= j < i + off + right"),
     "mask_top_left": ("off = s2 - s1\n    i = np.arange(s1)[:, None]", "off = 0\n    i = np.arange(s1)[:, None]"),
@@ -28,6 +29,8 @@ MUTATIONS = {
     "f16_bits": ("quantum = np.ldexp(1.0, e - 11)", "quantum = np.ldexp(1.0, e - 10)"),
     "f16_subnormal_spacing": ("e = np.maximum(e, -13)", "e = np.maximum(e, -14)"),
     "f16_no_overflow": ("np.abs(r) > 65504.0", "np.abs(r) > np.inf"),
+    "seqused_kv_ignored": ("u2 = s2 if seqused_kv is None else", "u2 = s2 if True else"),
+    "seqused_q_unclamped": ("min(max(int(seqused_q[b]), 0), s1)", "max(int(seqused_q[b]), 0)"),
 }
 
 
@@ -114,6 +117,32 @@ def rounding_pin_fails(mod):
     return not np.array_equal(mod.f16_round(x), refh)
 
 
+def seqused_pin_fails(mod):
+    """seqused against the unpadded problem of the used lengths (the mutant's
+    own plain path), with zero gradients on the padding, and an over-long
+    seqused clamped to the sequence."""
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 6, 2, 3))
+    k = rng.standard_normal((2, 7, 1, 3))
+    v = rng.standard_normal((2, 7, 1, 2))
+    dY = rng.standard_normal((2, 6, 2, 2))
+    uq, ukv = np.array([4, 9]), np.array([5, 3])
+    kw = dict(softmax_scale=0.5, mask_mode=1)
+    try:
+        Y, lse = mod.forward(q, k, v, "BSND", **kw, seqused_q=uq, seqused_kv=ukv)
+        g = mod.backward(q, k, v, dY, Y, lse, "BSND", **kw, seqused_q=uq, seqused_kv=ukv)
+    except Exception:
+        return True
+    for b, (u1, u2) in enumerate(((4, 5), (6, 3))):
+        sl = (slice(b, b + 1),)
+        Yt, lt = mod.forward(q[sl][:, :u1], k[sl][:, :u2], v[sl][:, :u2], "BSND", **kw)
+        gt = mod.backward(q[sl][:, :u1], k[sl][:, :u2], v[sl][:, :u2], dY[sl][:, :u1], Yt, lt, "BSND", **kw)
+        for full, part, u in zip(g, gt, (u1, u2, u2)):
+            if not np.allclose(full[b, :u], part[0], atol=1e-12) or np.any(full[b, u:]):
+                return True
+    return False
+
+
 def test_unmutated_oracle_passes_every_pin():
     src = open(SRC, encoding="utf-8").read()
     mod = types.ModuleType("oracle_plain")
@@ -121,9 +150,11 @@ def test_unmutated_oracle_passes_every_pin():
     assert not fd_pin_fails(mod)
     assert not library_pin_fails(mod)
     assert not rounding_pin_fails(mod)
+    assert not seqused_pin_fails(mod)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name):
     mod = load_mutant(name)
-    assert library_pin_fails(mod) or fd_pin_fails(mod) or rounding_pin_fails(mod), f"pins missed mutation {name}"
+    caught = library_pin_fails(mod) or fd_pin_fails(mod) or rounding_pin_fails(mod) or seqused_pin_fails(mod)
+    assert caught, f"pins missed mutation {name}"

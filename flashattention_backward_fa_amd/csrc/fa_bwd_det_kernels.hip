@@ -487,6 +487,14 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) pacc[kb] = mfma32<F16>(ya, lds_load16(v_lane + (kb * 32 * VP + 16 * kk) * 2), pacc[kb]);
     }
+    // instruction grouping for the scheduler (0x100: LDS reads, 0x008: MFMAs):
+    // eight reads ahead, then each MFMA followed by the two reads of a later one
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < (NKQ + NKV) * NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // P, dS (masked when the tile is partial), then dV += P^T dY and dK += dS^T Q
@@ -554,6 +562,13 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32<F16>(da[kb][kc], qb, dKr[kb][nb]);
       }
+    }
+    // the same for the transposing reads: four ahead, then two per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (NBV + NBK) * NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };

@@ -811,6 +811,14 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
           dq[nb] = mfma32<F16>(da[c], kb, dq[nb]);
         }
       }
+      // scheduler grouping (0x100: LDS reads, 0x008: MFMAs): the transposing
+      // reads of two MFMAs ahead, then each MFMA followed by a later one's two
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NBK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
       __builtin_amdgcn_s_setprio(0);
     }
   };

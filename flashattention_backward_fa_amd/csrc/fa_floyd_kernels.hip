@@ -1,0 +1,455 @@
+// gfx950 (MI355X) kernels of Floyd attention, forward and backward.
+//
+// Page "CANN Floyd注意力梯度算子", section 功能说明: the scores add two
+// products, S[n,m,k] = scale * (Q[n,m].K1[n,k] + Q[n,m].K2[k,m]), the first a
+// batch matmul over n and the second one over m; P = softmax_k(S) and
+// Y = P V1 + P V2 with the same two batch axes.  The backward's five
+// gradients reduce over three different axes (dQ over k, dK1 / dV1 over m,
+// dK2 / dV2 over n).
+//
+// Design.  A score element needs one product from each batch orientation, and
+// an MFMA tile of one orientation holds (m, k) for a fixed n while the other
+// holds (n, k) for a fixed m.  The two meet through the fp32 score workspace
+// in HBM, [head][n][m][k]:
+//   1. score_kernel, by n: Q[n] K1[n]^T and dY[n] V1[n]^T into ws_s / ws_p;
+//   2. score_kernel, by m: Q[:,m] K2[:,m]^T and dY[:,m] V2[:,m]^T, and in the
+//      same epilogue, pointwise, S = scale*(both), P = exp(S - max)/sum from
+//      the forward's statistics and dS = P (dP - sfmg), written as 16-bit;
+//   3. gemm_kernel for dV1 = P^T dY and dK1 = scale dS^T Q (batched over n),
+//      dV2, dK2 (batched over m), dQ = scale (dS K1 + dS K2) (two launches,
+//      the second adding the first's fp32 result).
+// No row reduction over k is needed in the backward (the statistics come
+// from the forward), so P and dS are formed where the second score product
+// ends.  Every product is a v_mfma_f32_32x32x16 tile fed from LDS; each
+// operand tile is copied global -> registers -> LDS one k-step ahead
+// (double-buffered LDS, one barrier per step).  An operand whose contraction
+// index t is contiguous in memory is stored [x][t] and read 16 bytes per lane;
+// one whose row index x is contiguous is stored [t][x] and read with
+// ds_read_b64_tr_b16, which hands each lane a column of four rows.
+
+#include <hip/hip_runtime.h>
+
+#include "fa_floyd_internal.h"
+
+namespace ffloyd {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int NT = 256;  // threads per workgroup (4 wavefronts)
+constexpr int BM = 128;  // tile rows (i)
+constexpr int BK = 32;   // contraction step
+
+template <bool F16>
+__device__ __forceinline__ floatx16 mfma(bf16x8 a, bf16x8 b, floatx16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ bf16 to_elem(float x) {
+  if constexpr (F16) return __builtin_bit_cast(bf16, (_Float16)x);
+  else return (bf16)x;
+}
+template <bool F16>
+__device__ __forceinline__ float from_elem(bf16 x) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, x);
+  else return (float)x;
+}
+
+// Operand view of one block: element (x, t) at p[x*sx + t*st]; X rows and T
+// contraction entries exist (both multiples of 8 along the contiguous axis).
+struct Op {
+  const bf16* p;
+  int64_t sx, st;
+  int X, T;
+};
+
+// One operand's tile of BX rows x BK contraction entries.
+//  TC (t contiguous): LDS [x][t], pitch BK + 8 (80 bytes): the 16-byte reads
+//     of 8 consecutive rows fall in distinct banks.
+//  XC (x contiguous): LDS [t][x], pitch 16 banks (mod 64) apart per row
+//     (BX + 32 elements; 48 for BX = 32), so the four rows of one
+//     transposing read of a 16-lane group fall in distinct banks.
+template <bool TC, int BX>
+struct Tile {
+  static constexpr int PITCH = TC ? BK + 8 : (BX == 32 ? 48 : BX + 32);
+  static constexpr int ELEMS = TC ? BX * PITCH : BK * PITCH;
+  static constexpr int CHUNKS = BX * BK / 8;
+  static constexpr int PER = (CHUNKS + NT - 1) / NT;
+  uint4 r[PER];
+
+  __device__ __forceinline__ void chunk_pos(int c, int& x, int& t) const {
+    if constexpr (TC) {
+      x = c / (BK / 8);
+      t = (c % (BK / 8)) * 8;
+    } else {
+      t = c / (BX / 8);
+      x = (c % (BX / 8)) * 8;
+    }
+  }
+  __device__ __forceinline__ void load(const Op& o, int x0, int t0, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + u * NT;
+      int x, t;
+      chunk_pos(c, x, t);
+      const bool ok = c < CHUNKS && x0 + x < o.X && t0 + t < o.T;
+      r[u] = ok ? *reinterpret_cast<const uint4*>(o.p + (int64_t)(x0 + x) * o.sx + (int64_t)(t0 + t) * o.st)
+                : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(bf16* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + u * NT;
+      if (c < CHUNKS) {
+        int x, t;
+        chunk_pos(c, x, t);
+        *reinterpret_cast<uint4*>(lds + (TC ? x * PITCH + t : t * PITCH + x)) = r[u];
+      }
+    }
+  }
+  // MFMA operand of 32-row block bx, contraction slice kk (16 entries): lane l
+  // gets row x = 32*bx + l%32 and t = 16*kk + 8*(l/32) + 0..7.
+  __device__ __forceinline__ bf16x8 frag(const bf16* lds, int bx, int kk, int lane) const {
+    if constexpr (TC) {
+      return *reinterpret_cast<const bf16x8*>(lds + (bx * 32 + (lane & 31)) * PITCH + kk * 16 + 8 * (lane >> 5));
+    } else {
+      // 16-lane group g = lane/16 covers rows x0 .. x0+15, x0 = 32*bx + 16*(g%2);
+      // lane i of the group points at contraction row t + i/4, column x0 + 4*(i%4)
+      // and receives column x0 + i of four contraction rows.
+      const int row = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+      const int col = bx * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const bf16* p = lds + row * PITCH + col;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(p));
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(p + 4 * PITCH));
+      const shortx8 s = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, s);
+    }
+  }
+};
+
+// Wavefront arrangement of a BM x BN tile over 4 wavefronts.
+template <int BN>
+struct Cfg {
+  static constexpr int WN = BN == 128 ? 64 : BN;  // columns per wavefront
+  static constexpr int WAVES_N = BN / WN;
+  static constexpr int WAVES_M = 4 / WAVES_N;
+  static constexpr int WM = BM / WAVES_M;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+};
+
+constexpr int LDS_ELEMS = 2 * 2 * 5120;  // two buffers of the largest A and B tiles
+
+// acc += A(i0.., :) B(:, j0..) over the whole contraction.  Every thread of
+// the workgroup calls it; it ends with a barrier, so the LDS may be reused.
+template <bool ATC, bool BTC, int BN, bool F16>
+__device__ __forceinline__ void gemm_tile(const Op& A, const Op& B, int i0, int j0,
+                                          floatx16 (&acc)[Cfg<BN>::TM][Cfg<BN>::TN], bf16* lds) {
+  using C = Cfg<BN>;
+  using TA = Tile<ATC, BM>;
+  using TB = Tile<BTC, BN>;
+  static_assert(TA::ELEMS <= 5120 && TB::ELEMS <= 5120, "LDS tile size");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  bf16* la[2] = {lds, lds + 5120};
+  bf16* lb[2] = {lds + 2 * 5120, lds + 3 * 5120};
+  TA ta;
+  TB tb;
+  const int nk = (A.T + BK - 1) / BK;
+  ta.load(A, i0, 0, tid);
+  tb.load(B, j0, 0, tid);
+  ta.store(la[0], tid);
+  tb.store(lb[0], tid);
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < nk;
+    if (more) {
+      ta.load(A, i0, (it + 1) * BK, tid);
+      tb.load(B, j0, (it + 1) * BK, tid);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[C::TM], bfr[C::TN];
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) af[tm] = ta.frag(la[cur], wm * C::TM + tm, kk, lane);
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn) bfr[tn] = tb.frag(lb[cur], wn * C::TN + tn, kk, lane);
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = mfma<F16>(af[tm], bfr[tn], acc[tm][tn]);
+    }
+    if (more) {
+      ta.store(la[cur ^ 1], tid);
+      tb.store(lb[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+}
+
+// Workgroup -> (inner batch, tile) with the tiles of one batch entry on one
+// XCD: workgroup w runs on XCD w % 8, so logical index (w % 8) * (n / 8) + w / 8
+// gives every XCD a contiguous range of logical tiles.
+__device__ __forceinline__ int logical_block() {
+  const int w = blockIdx.x, n = gridDim.x;
+  return (n & 7) == 0 ? (w & 7) * (n >> 3) + (w >> 3) : w;
+}
+
+template <bool ATC, bool BTC, int BN, bool F16>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
+  using C = Cfg<BN>;
+  __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
+  const int tiles_j = (g.J + BN - 1) / BN, tiles_i = (g.I + BM - 1) / BM;
+  const int L = logical_block();
+  const int z = L / (tiles_i * tiles_j), tile = L % (tiles_i * tiles_j);
+  const int i0 = (tile / tiles_j) * BM, j0 = (tile % tiles_j) * BN;
+  const int h = blockIdx.y;
+  Op A{static_cast<const bf16*>(g.a) + h * g.a_sh + z * g.a_sz, g.a_si, g.a_st, g.I, g.T};
+  Op B{static_cast<const bf16*>(g.b) + h * g.b_sh + z * g.b_sz, g.b_sj, g.b_st, g.J, g.T};
+  floatx16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = floatx16{};
+  gemm_tile<ATC, BTC, BN, F16>(A, B, i0, j0, acc, lds);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int64_t cb = h * g.c_sh + z * g.c_sz;
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + (wm * C::TM + tm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (i < g.I && j < g.J) {
+          const int64_t off = cb + i * g.c_si + j;
+          float v = g.alpha * acc[tm][tn][r];
+          if (g.addend) v += g.addend[off];
+          if (g.out_f32) static_cast<float*>(g.c)[off] = v;
+          else static_cast<bf16*>(g.c)[off] = to_elem<F16>(v);
+        }
+      }
+    }
+}
+
+// Score products (see ScoreArgs).  Rows i of the tile are m (by n) or n (by
+// m), columns j are keys k; the inner batch index z is n (by n) or m (by m).
+template <bool F16, int EPI>
+__global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
+  using C = Cfg<128>;
+  __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
+  const bool by_m = EPI == 1 || EPI == 3;
+  const int I = by_m ? s.N : s.M, J = s.K;
+  const int tiles_j = (J + 127) / 128, tiles_i = (I + BM - 1) / BM;
+  const int L = logical_block();
+  const int z = L / (tiles_i * tiles_j), tile = L % (tiles_i * tiles_j);
+  const int i0 = (tile / tiles_j) * BM, j0 = (tile % tiles_j) * 128;
+  const int h = blockIdx.y;
+  const int64_t MD = (int64_t)s.M * s.D, NMD = (int64_t)s.N * MD;
+  const int64_t KD = (int64_t)s.K * s.D;
+  // Q / dY rows: by n, row m of batch n at (n*M + m)*D; by m, row n of batch m at n*M*D + m*D
+  const int64_t q_off = h * NMD + (by_m ? (int64_t)z * s.D : (int64_t)z * MD);
+  const int64_t q_sx = by_m ? MD : s.D;
+  // K1/V1 [N][K][D]: by n, row k of batch n at n*K*D + k*D
+  // K2/V2 [K][M][D]: by m, row k of batch m at k*M*D + m*D
+  const int64_t x_off = by_m ? h * (int64_t)s.K * MD + (int64_t)z * s.D : h * (int64_t)s.N * KD + (int64_t)z * KD;
+  const int64_t x_sx = by_m ? MD : s.D;
+
+  floatx16 acs[C::TM][C::TN], acp[C::TM][C::TN];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) acs[tm][tn] = acp[tm][tn] = floatx16{};
+  {
+    Op A{static_cast<const bf16*>(s.q) + q_off, q_sx, 1, I, s.D};
+    Op B{static_cast<const bf16*>(s.x1) + x_off, x_sx, 1, J, s.D};
+    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acs, lds);
+  }
+  if constexpr (EPI == 0 || EPI == 1) {
+    Op A{static_cast<const bf16*>(s.dy) + q_off, q_sx, 1, I, s.D};
+    Op B{static_cast<const bf16*>(s.x2) + x_off, x_sx, 1, J, s.D};
+    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acp, lds);
+  }
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int64_t MK = (int64_t)s.M * s.K, NMK = (int64_t)s.N * MK;
+  // element (i, j) of the tile in the [head][n][m][k] workspace
+  const int64_t wbase = h * NMK + (by_m ? (int64_t)z * s.K : (int64_t)z * MK);
+  const int64_t w_si = by_m ? MK : s.K;
+  const float sl2 = s.scale * kLog2e;
+  const int bb = (s.head0 + h) / s.H;  // batch index of the mask
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + (wm * C::TM + tm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (i >= I || j >= J) continue;
+        const int64_t off = wbase + i * w_si + j;
+        if constexpr (EPI == 0) {
+          s.ws_s[off] = acs[tm][tn][r];
+          s.ws_p[off] = acp[tm][tn][r];
+        } else if constexpr (EPI == 2) {
+          s.ws_s[off] = acs[tm][tn][r];
+        } else if constexpr (EPI == 3) {
+          s.ws_s[off] += acs[tm][tn][r];
+        } else {
+          // i = n, z = m: the row (head, n, m) of the statistics
+          const int64_t row = ((int64_t)h * s.N + i) * s.M + z;
+          const bool live = s.mask == nullptr || s.mask[((int64_t)bb * s.N + i) * s.K + j] == 0;
+          const float sc = acs[tm][tn][r] + s.ws_s[off];
+          const float p = live ? __builtin_amdgcn_exp2f(sc * sl2 - s.lse2[row]) : 0.f;
+          const float dp = acp[tm][tn][r] + s.ws_p[off];
+          static_cast<bf16*>(s.ws_pe)[off] = to_elem<F16>(p);
+          static_cast<bf16*>(s.ws_dse)[off] = to_elem<F16>(p * (dp - s.sfmg[row]));
+        }
+      }
+    }
+}
+
+// 16 lanes per row: sfmg = sum_d dY*Y in fp32, lse2 from the statistics.
+template <bool F16>
+__global__ __launch_bounds__(NT) void rowstats_kernel(RowStatsArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * (NT / 16) + (threadIdx.x >> 4);
+  const int e = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < a.rows) {
+    const bf16* g = static_cast<const bf16*>(a.dy) + row * a.D;
+    const bf16* y = static_cast<const bf16*>(a.y) + row * a.D;
+    for (int d = e; d < a.D; d += 16) acc += from_elem<F16>(g[d]) * from_elem<F16>(y[d]);
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (row < a.rows && e == 0) {
+    a.sfmg[row] = acc;
+    const float mx = a.smax[row * 8], sm = a.ssum[row * 8];
+    const bool live = mx > -__builtin_inff() && sm > 0.f;
+    a.lse2[row] = live ? (mx + __logf(sm)) * kLog2e : __builtin_inff();
+  }
+}
+
+// One wavefront per row (head, n, m): max and sum over the live keys of the
+// scaled scores, then P = exp(S - max) / sum.
+template <bool F16>
+__global__ __launch_bounds__(NT) void softmax_kernel(SoftmaxArgs a) {
+  const int64_t rows = (int64_t)a.heads * a.N * a.M;
+  const int64_t row = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int n = (int)((row / a.M) % a.N), h = (int)(row / ((int64_t)a.M * a.N));
+  const float* srow = a.ws_s + row * a.K;
+  const uint8_t* mrow = a.mask ? a.mask + ((int64_t)((a.head0 + h) / a.H) * a.N + n) * a.K : nullptr;
+  const float sl2 = a.scale * kLog2e;
+  float mx = -__builtin_inff();
+  for (int k = lane; k < a.K; k += 64)
+    if (!mrow || mrow[k] == 0) mx = fmaxf(mx, srow[k] * sl2);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const bool live = mx > -__builtin_inff();
+  float sum = 0.f;
+  if (live)
+    for (int k = lane; k < a.K; k += 64)
+      if (!mrow || mrow[k] == 0) sum += __builtin_amdgcn_exp2f(srow[k] * sl2 - mx);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  const float inv = live ? 1.f / sum : 0.f;
+  bf16* prow = static_cast<bf16*>(a.p) + row * a.K;
+  for (int k = lane; k < a.K; k += 64) {
+    const bool ok = live && (!mrow || mrow[k] == 0);
+    prow[k] = to_elem<F16>(ok ? __builtin_amdgcn_exp2f(srow[k] * sl2 - mx) * inv : 0.f);
+  }
+  if (lane < 8) {
+    // statistics in the natural-log domain: max of scale*S, sum of exp(scale*S - max)
+    a.smax[row * 8 + lane] = live ? mx / kLog2e : -__builtin_inff();
+    a.ssum[row * 8 + lane] = live ? sum : 0.f;
+  }
+}
+
+template <bool ATC, bool BTC, bool F16>
+int launch_gemm_bn(const GemmArgs& g, hipStream_t st) {
+  const int ti = (g.I + BM - 1) / BM;
+  if (g.J <= 32) {
+    const int64_t nx = (int64_t)ti * ((g.J + 31) / 32) * g.nb;
+    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 32, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+  } else if (g.J <= 64) {
+    const int64_t nx = (int64_t)ti * ((g.J + 63) / 64) * g.nb;
+    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 64, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+  } else {
+    const int64_t nx = (int64_t)ti * ((g.J + 127) / 128) * g.nb;
+    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 128, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+  }
+  return (int)hipGetLastError();
+}
+
+template <bool F16>
+int launch_gemm_t(const GemmArgs& g, hipStream_t st) {
+  if (g.a_tc && !g.b_tc) return launch_gemm_bn<true, false, F16>(g, st);
+  if (!g.a_tc && !g.b_tc) return launch_gemm_bn<false, false, F16>(g, st);
+  if (g.a_tc && g.b_tc) return launch_gemm_bn<true, true, F16>(g, st);
+  return launch_gemm_bn<false, true, F16>(g, st);
+}
+
+template <bool F16>
+int launch_scores_t(const ScoreArgs& s, hipStream_t st) {
+  const bool by_m = s.epi == 1 || s.epi == 3;
+  const int I = by_m ? s.N : s.M;
+  const int64_t nx = (int64_t)((I + BM - 1) / BM) * ((s.K + 127) / 128) * (by_m ? s.M : s.N);
+  const dim3 grid((unsigned)nx, s.heads);
+  switch (s.epi) {
+    case 0: hipLaunchKernelGGL((score_kernel<F16, 0>), grid, dim3(NT), 0, st, s); break;
+    case 1: hipLaunchKernelGGL((score_kernel<F16, 1>), grid, dim3(NT), 0, st, s); break;
+    case 2: hipLaunchKernelGGL((score_kernel<F16, 2>), grid, dim3(NT), 0, st, s); break;
+    default: hipLaunchKernelGGL((score_kernel<F16, 3>), grid, dim3(NT), 0, st, s); break;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_gemm(const GemmArgs& g, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return g.f16 ? launch_gemm_t<true>(g, st) : launch_gemm_t<false>(g, st);
+}
+
+int launch_scores(const ScoreArgs& s, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.f16 ? launch_scores_t<true>(s, st) : launch_scores_t<false>(s, st);
+}
+
+int launch_rowstats(const RowStatsArgs& r, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t blocks = (r.rows + NT / 16 - 1) / (NT / 16);
+  if (r.f16) hipLaunchKernelGGL(rowstats_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, st, r);
+  else hipLaunchKernelGGL(rowstats_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, st, r);
+  return (int)hipGetLastError();
+}
+
+int launch_softmax(const SoftmaxArgs& s, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = (int64_t)s.heads * s.N * s.M;
+  const int64_t blocks = (rows + NT / 64 - 1) / (NT / 64);
+  if (s.f16) hipLaunchKernelGGL(softmax_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, st, s);
+  else hipLaunchKernelGGL(softmax_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, st, s);
+  return (int)hipGetLastError();
+}
+
+}  // namespace ffloyd

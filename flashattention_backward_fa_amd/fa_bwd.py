@@ -36,7 +36,8 @@ DTYPE_BF16 = 0
 DTYPE_FP16 = 1
 
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_profile_enable",
-            "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version")
+            "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version",
+            "fa_floyd_workspace_size", "fa_floyd_bwd_run", "fa_floyd_fwd_run")
 
 
 class MaskMode(enum.IntEnum):
@@ -123,6 +124,13 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd_strerror.restype = ctypes.c_char_p
     lib.fa_bwd_abi_version.argtypes = []
     lib.fa_bwd_abi_version.restype = ctypes.c_int
+    # Floyd attention (include/fa_floyd.h); the descriptor is passed by pointer
+    lib.fa_floyd_workspace_size.argtypes = [vp, ctypes.POINTER(sz)]
+    lib.fa_floyd_workspace_size.restype = ctypes.c_int
+    lib.fa_floyd_bwd_run.argtypes = [vp] * 16 + [vp, sz, vp]
+    lib.fa_floyd_bwd_run.restype = ctypes.c_int
+    lib.fa_floyd_fwd_run.argtypes = [vp] * 10 + [vp, sz, vp]
+    lib.fa_floyd_fwd_run.restype = ctypes.c_int
     if lib.fa_bwd_abi_version() != ABI_VERSION:
         raise RuntimeError("libfa_bwd.so ABI version mismatch")
     _lib = lib

@@ -115,3 +115,45 @@ def make_inputs_custom(cfg, seed, dtype=None):
     else:
         out["cu_q"], out["cu_kv"] = None, None
     return out
+
+
+# Floyd attention (page "CANN Floyd注意力梯度算子").  The benchmark workload
+# takes the page's example sizes (S1 = S2 = S3 = 256, D = 128) with 8 heads;
+# the page quotes no workload of its own.  mask_p is the probability that a
+# (n, k) position is masked; masked_rows lists (b, n) rows masked whole.
+FLOYD_CONFIGS = {
+    "floyd": dict(index=11, B=1, H=8, N=256, M=256, K=256, D=128, mask_p=0.0, masked_rows=(), dy_std=1.0),
+    "floyd_small": dict(index=12, B=1, H=2, N=16, M=128, K=128, D=32, mask_p=0.0, masked_rows=(), dy_std=1.0),
+    "floyd_masked": dict(index=13, B=2, H=1, N=32, M=128, K=256, D=64, mask_p=0.2, masked_rows=((0, 5),),
+                         dy_std=1.0),
+    "floyd_n48": dict(index=14, B=1, H=2, N=48, M=128, K=128, D=128, mask_p=0.1, masked_rows=(), dy_std=0.5),
+}
+
+
+def floyd_inputs(cfg, seed=None, dtype=None):
+    """query, key1, value1, key2, value2, dy as CPU torch tensors of `dtype`
+    (default bfloat16) in the page's shapes, and the mask as a numpy uint8
+    array [B, 1, N, 1, K] (None when the workload masks nothing).  Recipe:
+    default_rng(seed); standard normal float32 draws in the order query, key1,
+    value1, key2, value2, dy (dy times dy_std), rounded to the element type;
+    then the mask as uniform draws < mask_p, with the listed rows set whole."""
+    import torch
+
+    dtype = torch.bfloat16 if dtype is None else dtype
+    rng = np.random.default_rng(seed_of(cfg) if seed is None else seed)
+    B, H, N, M, K, D = (cfg[k] for k in ("B", "H", "N", "M", "K", "D"))
+    shp = {"query": (B, H, N, M, D), "key1": (B, H, N, K, D), "value1": (B, H, N, K, D),
+           "key2": (B, H, K, M, D), "value2": (B, H, K, M, D), "dy": (B, H, N, M, D)}
+    out = {}
+    for name, s in shp.items():
+        x = rng.standard_normal(s, dtype=np.float32)
+        if name == "dy":
+            x *= np.float32(cfg["dy_std"])
+        out[name] = torch.from_numpy(x).to(dtype)
+    mask = None
+    if cfg["mask_p"] > 0 or cfg["masked_rows"]:
+        mask = (rng.random((B, 1, N, 1, K)) < cfg["mask_p"]).astype(np.uint8)
+        for (b, n) in cfg["masked_rows"]:
+            mask[b, 0, n, 0, :] = 1
+    out["mask"] = mask
+    return out

@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/fa_bwd.h declares, and fa_bwd_create enforces the constraints of page
+the headers under include/ declare, and fa_bwd_create enforces the constraints of page
 "CANN ops-transformer FlashAttnGrad 算子详解", section 四 4.6, with the error
 classes of the header.  fa_bwd_run's pointer and workspace checks return
 before any device call, so they are exercised here too."""
@@ -25,7 +25,9 @@ def lib():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "fa_bwd.h"), encoding="utf-8").read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f), encoding="utf-8").read() for f in sorted(os.listdir(inc))
+                   if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:int|const char\*|void)\s+(fa_\w+)\s*\(", text, flags=re.M)))
 

@@ -82,15 +82,12 @@ def algorithmic_flops(cfg):
     return 2.0 * (3 * cfg["D"] + 2 * cfg["Dv"]) * cfg["N1"] * visible_pairs(cfg)
 
 
-def kernel_source_hash():
-    from flashattention_backward_fa_amd.profile_summary import kernel_code_hash
-    return kernel_code_hash()
-
-
-def committed_traffic(workload):
+def committed_traffic(workload, path=None, sources="det"):
     """HBM bytes per main-kernel launch from the committed rocprofv3 --pmc
     summary, if it was taken from the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"bwd_dkdv_dq_kernels_{workload}_traffic.txt")
+    from flashattention_backward_fa_amd.profile_summary import SOURCES, kernel_code_hash
+
+    path = path or os.path.join(PROFILE_DIR, f"bwd_dkdv_dq_kernels_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -99,7 +96,7 @@ def committed_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_code_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_code_sha256_16") != kernel_code_hash(SOURCES[sources]):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -300,6 +297,153 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
                 pre_bytes=pre_bytes, settle_steps=settle_steps)
 
 
+FLOYD_WORKLOAD = "floyd"
+
+
+def floyd_stage_units(cfg):
+    """Algorithmic FLOP and HBM bytes of each backward stage of the Floyd
+    attention path on a workload with no mask: T = heads*N*M*K (n, m, k)
+    triples, R = heads*N*M rows.  Each product costs 2*D FLOP per triple; the
+    bytes count every operand read once and every result written once in the
+    path's own decomposition (fp32 scores and dP, 16-bit P and dS, one fp32 dQ
+    partial, in HBM)."""
+    hd = cfg["B"] * cfg["H"]
+    N, M, K, D = cfg["N"], cfg["M"], cfg["K"], cfg["D"]
+    T, R = hd * N * M * K, hd * N * M
+    qsz, k1sz, k2sz = 2 * R * D, 2 * hd * N * K * D, 2 * hd * K * M * D   # bytes of one 16-bit tensor
+    return {
+        "rowstats": (0, 2 * qsz + R * 16),
+        "scores_by_n": (4 * D * T, 2 * qsz + 2 * k1sz + 8 * T),
+        "scores_by_m_softmax_grad": (4 * D * T, 2 * qsz + 2 * k2sz + 8 * T + 4 * T + 8 * R),
+        "dv1": (2 * D * T, 2 * T + qsz + k1sz),
+        "dk1": (2 * D * T, 2 * T + qsz + k1sz),
+        "dv2": (2 * D * T, 2 * T + qsz + k2sz),
+        "dk2": (2 * D * T, 2 * T + qsz + k2sz),
+        "dq_k1": (2 * D * T, 2 * T + k1sz + 2 * qsz),
+        "dq_k2": (2 * D * T, 2 * T + k2sz + 2 * qsz + qsz),
+    }
+
+
+def floyd_leg(steps, warmup, settle_s, with_accuracy):
+    """Floyd attention backward on its benchmark workload: whole-step time from
+    events on the launch stream, per-stage times from the library's timing
+    hook, each stage against its bound, and (optionally) the gradients of one
+    head against the fp64 oracle."""
+    import torch
+    from flashattention_backward_fa_amd import floyd as fl
+    from flashattention_backward_fa_amd import workloads as W
+
+    cfg = W.FLOYD_CONFIGS[FLOYD_WORKLOAD]
+    dev = torch.device("cuda", 0)
+    x = W.floyd_inputs(cfg)
+    names = ("query", "key1", "value1", "key2", "value2")
+    t = [x[n].to(dev) for n in names]
+    dy = x["dy"].to(dev)
+    y, smax, ssum = fl.floyd_attn(*t)   # the step's inputs come from the library's forward
+    desc, *_ = fl._prepare(*t, None)
+    ws = torch.empty(fl.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = tuple(torch.empty_like(a) for a in (t[0], t[1], t[2], t[3], t[4]))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(stage_ms=None):
+        fl.floyd_attn_grad(*t, dy, None, smax, ssum, y, workspace=ws, out=out, stage_ms=stage_ms)
+
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(steps, 1)
+    stage_sum = [0.0] * len(fl.STAGES)
+    reps = 5
+    for _ in range(reps):
+        st = []
+        step(st)
+        stage_sum = [a + b for a, b in zip(stage_sum, st)]
+    stage_ms = [v / reps for v in stage_sum]
+
+    N, M, K, D = cfg["N"], cfg["M"], cfg["K"], cfg["D"]
+    flops = 20.0 * D * cfg["B"] * cfg["H"] * N * M * K
+    units = floyd_stage_units(cfg)
+    stages = {}
+    for name, sms in zip(fl.STAGES, stage_ms):
+        f, b = units[name]
+        t_hbm, t_mfma = b / (PEAK_HBM_GBS * 1e9), f / (PEAK_BF16_TFLOPS * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        gbs, tfs = b / (sms * 1e-3) / 1e9, f / (sms * 1e-3) / 1e12
+        stages[name] = {
+            "ms": round(sms, 4), "bound": bound, "algorithmic_bytes": b, "algorithmic_flop": f,
+            "gb_s": round(gbs, 1), "tflop_s": round(tfs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS if bound == "hbm" else tfs / PEAK_BF16_TFLOPS, 4),
+        }
+    dom = max(stages, key=lambda k: stages[k]["ms"])
+    d = stages[dom]
+    leg = {
+        "workload": FLOYD_WORKLOAD,
+        "config": {k: cfg[k] for k in ("B", "H", "N", "M", "K", "D")} | {"mask": None, "dtype": "bf16"},
+        "ms_per_step": round(ms, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+        "pct_of_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "algorithmic_gflop": round(flops / 1e9, 3),
+        "flop_rule": "20*D per (n, m, k) triple: ten products of 2*D each",
+        "stages": stages,
+        "roofline": {
+            "kernel": dom, "bound": d["bound"],
+            "achieved": d["gb_s"] if d["bound"] == "hbm" else d["tflop_s"],
+            "peak": PEAK_HBM_GBS if d["bound"] == "hbm" else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if d["bound"] == "hbm" else "TFLOP/s", "frac": d["frac"],
+            "traffic": committed_traffic(FLOYD_WORKLOAD, os.path.join(PROFILE_DIR, f"floyd_{dom}_{FLOYD_WORKLOAD}_traffic.txt"),
+                                         "floyd"),
+        },
+        "accuracy": None,
+    }
+    if with_accuracy:
+        leg["accuracy"] = floyd_accuracy(cfg, x)
+    return leg
+
+
+def floyd_accuracy(cfg, x):
+    """One head of the Floyd workload through the library with the oracle
+    forward's Y (rounded to bf16) and statistics (rounded to fp32), against the
+    oracle backward, every element."""
+    import numpy as np
+    import torch
+    import oracle
+    import oracle.floyd as OF
+    from flashattention_backward_fa_amd import floyd as fl
+
+    names = ("query", "key1", "value1", "key2", "value2", "dy")
+    one = {n: x[n][:1, :1].contiguous() for n in names}
+    f = {n: one[n].double().numpy() for n in names}
+    scale = OF.default_scale(cfg["D"])
+    Y, mx, sm = OF.forward(f["query"], f["key1"], f["value1"], f["key2"], f["value2"], scale, None)
+    Yst = oracle.bf16_round(Y)
+    mx32, sm32 = mx.astype(np.float32), sm.astype(np.float32)
+    ref = OF.backward(f["query"], f["key1"], f["value1"], f["key2"], f["value2"], f["dy"], Yst,
+                      mx32.astype(np.float64), sm32.astype(np.float64), scale, None)
+    dev = torch.device("cuda", 0)
+    g = fl.floyd_attn_grad(*(one[n].to(dev) for n in names), None, torch.from_numpy(mx32).to(dev),
+                           torch.from_numpy(sm32).to(dev), torch.from_numpy(Yst).to(torch.bfloat16).to(dev))
+    torch.cuda.synchronize()
+    res = {"reference": "fp64 oracle (oracle.floyd.backward), head 0 of the workload, every element",
+           "tolerance": {"rel_fro": 0.01, "max_abs_ratio": 0.02}}
+    ok = True
+    for name, got, r in zip(("dq", "dk1", "dv1", "dk2", "dv2"), g, ref):
+        rel, mxr = _errors(got.double().cpu().numpy(), r)
+        res[name] = {"rel_fro": round(rel, 6), "max_abs_ratio": round(mxr, 6)}
+        ok = ok and rel <= 0.01 and mxr <= 0.02
+    res["within_tolerance"] = ok
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +458,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32, help="query heads in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration summary")
+    ap.add_argument("--no-floyd", action="store_true", help="skip the Floyd attention backward leg")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -372,6 +517,7 @@ def main():
             "note": "standalone fa_bwd_sfmg entry point; the default step forms sfmg inside dq_kernel",
         },
         "configs": None,
+        "floyd": None,
         "cpu_baseline": None,
         "accuracy": None,
     }
@@ -398,6 +544,11 @@ def main():
                 "algorithmic_gflop": round(f / 1e9, 3),
             }
         line["configs"] = rows
+    if not args.no_floyd:
+        import torch
+
+        torch.cuda.empty_cache()
+        line["floyd"] = floyd_leg(10, 2, args.settle, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         line["cpu_baseline"], sample = cpu_baseline(cfg, args.cpu_heads, name, args.dtype)
         line["accuracy"] = accuracy(sample, name)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <vector>
 
 #include "fa_floyd.h"
 #include "fa_floyd_internal.h"
@@ -103,6 +104,11 @@ GemmArgs gemm_base(const fa_floyd_desc* d, int64_t hc) {
   return g;
 }
 
+int bwd(const fa_floyd_desc* d, const void* query, const void* key1, const void* value1, const void* key2,
+        const void* value2, const void* dy, const uint8_t* atten_mask, const float* softmax_max,
+        const float* softmax_sum, const void* attention_in, void* dq, void* dk1, void* dv1, void* dk2, void* dv2,
+        void* workspace, size_t workspace_bytes, void* stream, float* stage_ms);
+
 }  // namespace
 
 extern "C" {
@@ -121,6 +127,28 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
                      const float* softmax_max, const float* softmax_sum, const void* attention_in, void* dq,
                      void* dk1, void* dv1, void* dk2, void* dv2, void* workspace, size_t workspace_bytes,
                      void* stream) {
+  return bwd(d, query, key1, value1, key2, value2, dy, atten_mask, softmax_max, softmax_sum, attention_in, dq, dk1,
+             dv1, dk2, dv2, workspace, workspace_bytes, stream, nullptr);
+}
+
+int fa_floyd_bwd_run_timed(const fa_floyd_desc* d, const void* query, const void* key1, const void* value1,
+                           const void* key2, const void* value2, const void* dy, const uint8_t* atten_mask,
+                           const float* softmax_max, const float* softmax_sum, const void* attention_in, void* dq,
+                           void* dk1, void* dv1, void* dk2, void* dv2, void* workspace, size_t workspace_bytes,
+                           void* stream, float* stage_ms) {
+  if (!stage_ms) return FA_ERR_NULLPTR;
+  return bwd(d, query, key1, value1, key2, value2, dy, atten_mask, softmax_max, softmax_sum, attention_in, dq, dk1,
+             dv1, dk2, dv2, workspace, workspace_bytes, stream, stage_ms);
+}
+
+}  // extern "C"
+
+namespace {
+
+int bwd(const fa_floyd_desc* d, const void* query, const void* key1, const void* value1, const void* key2,
+        const void* value2, const void* dy, const uint8_t* atten_mask, const float* softmax_max,
+        const float* softmax_sum, const void* attention_in, void* dq, void* dk1, void* dv1, void* dk2, void* dv2,
+        void* workspace, size_t workspace_bytes, void* stream, float* stage_ms) {
   Layout L;
   int rc = plan(d, &L);
   if (rc != FA_OK) return rc;
@@ -142,6 +170,20 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
   float* ws_lse2 = reinterpret_cast<float*>(ws + L.o_lse2);
   const float scale = d->scale_value;
   const int f16 = d->dtype == FA_DTYPE_FP16;
+  const int64_t chunks = (L.heads + L.hc - 1) / L.hc;
+  StageTimer* timer = nullptr;
+  int mark = 0;
+  if (stage_ms) {
+    timer = stage_timer_create((int)(chunks * FA_FLOYD_BWD_STAGES + 1));
+    if (!timer) return FA_ERR_RUNTIME;
+  }
+  // a mark before the first stage and after each one (timed runs only)
+  auto tick = [&]() { return timer ? stage_timer_mark(timer, mark++, stream) : 0; };
+  auto fail = [&]() {
+    stage_timer_destroy(timer);
+    return FA_ERR_RUNTIME;
+  };
+  if (tick()) return fail();
 
   for (int64_t h0 = 0; h0 < L.heads; h0 += L.hc) {
     const int64_t hc = L.heads - h0 < L.hc ? L.heads - h0 : L.hc;
@@ -163,7 +205,8 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
     r.rows = hc * L.NM;
     r.D = d->D;
     r.f16 = f16;
-    if (launch_rowstats(r, stream)) return FA_ERR_RUNTIME;
+    if (launch_rowstats(r, stream)) return fail();
+    if (tick()) return fail();
 
     ScoreArgs s{};
     s.q = q;
@@ -188,12 +231,14 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
     s.x2 = v1;
     s.by_m = 0;
     s.epi = 0;
-    if (launch_scores(s, stream)) return FA_ERR_RUNTIME;
+    if (launch_scores(s, stream)) return fail();
+    if (tick()) return fail();
     s.x1 = k2;
     s.x2 = v2;
     s.by_m = 1;
     s.epi = 1;
-    if (launch_scores(s, stream)) return FA_ERR_RUNTIME;
+    if (launch_scores(s, stream)) return fail();
+    if (tick()) return fail();
 
     // dV1 = P^T dY and dK1 = scale dS^T Q, batched over n: C(k, d), contraction over m
     GemmArgs a = gemm_base(d, hc);
@@ -202,9 +247,11 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
     a.c_si = d->D; a.c_sh = L.NKD; a.c_sz = L.KD;
     a.I = d->K; a.J = d->D; a.T = d->M; a.nb = d->N;
     a.a = ws_pe; a.b = g; a.c = e16(dv1, h0 * L.NKD); a.alpha = 1.f;
-    if (launch_gemm(a, stream)) return FA_ERR_RUNTIME;
+    if (launch_gemm(a, stream)) return fail();
+    if (tick()) return fail();
     a.a = ws_dse; a.b = q; a.c = e16(dk1, h0 * L.NKD); a.alpha = scale;
-    if (launch_gemm(a, stream)) return FA_ERR_RUNTIME;
+    if (launch_gemm(a, stream)) return fail();
+    if (tick()) return fail();
 
     // dV2 and dK2, batched over m: C(k, d) at [k][m][d], contraction over n
     GemmArgs b = gemm_base(d, hc);
@@ -213,9 +260,11 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
     b.c_si = L.MD; b.c_sh = L.KMD; b.c_sz = d->D;
     b.I = d->K; b.J = d->D; b.T = d->N; b.nb = d->M;
     b.a = ws_pe; b.b = g; b.c = e16(dv2, h0 * L.KMD); b.alpha = 1.f;
-    if (launch_gemm(b, stream)) return FA_ERR_RUNTIME;
+    if (launch_gemm(b, stream)) return fail();
+    if (tick()) return fail();
     b.a = ws_dse; b.b = q; b.c = e16(dk2, h0 * L.KMD); b.alpha = scale;
-    if (launch_gemm(b, stream)) return FA_ERR_RUNTIME;
+    if (launch_gemm(b, stream)) return fail();
+    if (tick()) return fail();
 
     // dQ: scale dS K1 (batched over n, fp32 partial), then + scale dS K2 (batched over m)
     GemmArgs c = gemm_base(d, hc);
@@ -224,17 +273,31 @@ int fa_floyd_bwd_run(const fa_floyd_desc* d, const void* query, const void* key1
     c.c_si = d->D; c.c_sh = L.NMD; c.c_sz = L.MD;
     c.I = d->M; c.J = d->D; c.T = d->K; c.nb = d->N;
     c.a = ws_dse; c.b = k1; c.c = ws_dq; c.out_f32 = 1; c.alpha = scale;
-    if (launch_gemm(c, stream)) return FA_ERR_RUNTIME;
+    if (launch_gemm(c, stream)) return fail();
+    if (tick()) return fail();
     GemmArgs e = gemm_base(d, hc);
     e.a_si = L.MK; e.a_st = 1; e.a_sh = L.NMK; e.a_sz = d->K; e.a_tc = 1;
     e.b_sj = 1; e.b_st = L.MD; e.b_sh = L.KMD; e.b_sz = d->D; e.b_tc = 0;
     e.c_si = L.MD; e.c_sh = L.NMD; e.c_sz = d->D;
     e.I = d->N; e.J = d->D; e.T = d->K; e.nb = d->M;
     e.a = ws_dse; e.b = k2; e.c = e16(dq, h0 * L.NMD); e.addend = ws_dq; e.alpha = scale;
-    if (launch_gemm(e, stream)) return FA_ERR_RUNTIME;
+    if (launch_gemm(e, stream)) return fail();
+    if (tick()) return fail();
+  }
+  if (timer) {
+    std::vector<float> ms((size_t)chunks * FA_FLOYD_BWD_STAGES);
+    const int rc = stage_timer_read(timer, ms.data());
+    stage_timer_destroy(timer);
+    if (rc) return FA_ERR_RUNTIME;
+    for (int i = 0; i < FA_FLOYD_BWD_STAGES; ++i) stage_ms[i] = 0.f;
+    for (size_t i = 0; i < ms.size(); ++i) stage_ms[i % FA_FLOYD_BWD_STAGES] += ms[i];
   }
   return FA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int fa_floyd_fwd_run(const fa_floyd_desc* d, const void* query, const void* key1, const void* value1,
                      const void* key2, const void* value2, const uint8_t* atten_mask, void* attention_out,

@@ -91,6 +91,13 @@ struct SoftmaxArgs {
   int32_t f16;
 };
 
+// HIP events between consecutive launches on one stream (timing hook).
+struct StageTimer;
+StageTimer* stage_timer_create(int marks);            // nullptr on failure
+int stage_timer_mark(StageTimer* t, int i, void* stream);
+int stage_timer_read(StageTimer* t, float* ms);       // waits; ms[i] = mark i -> i + 1
+void stage_timer_destroy(StageTimer* t);
+
 int launch_gemm(const GemmArgs& g, void* stream);
 int launch_scores(const ScoreArgs& s, void* stream);
 int launch_rowstats(const RowStatsArgs& r, void* stream);

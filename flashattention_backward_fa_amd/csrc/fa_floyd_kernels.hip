@@ -12,9 +12,10 @@
 // holds (n, k) for a fixed m.  The two meet through the fp32 score workspace
 // in HBM, [head][n][m][k]:
 //   1. score_kernel, by n: Q[n] K1[n]^T and dY[n] V1[n]^T into ws_s / ws_p;
-//   2. score_kernel, by m: Q[:,m] K2[:,m]^T and dY[:,m] V2[:,m]^T, and in the
-//      same epilogue, pointwise, S = scale*(both), P = exp(S - max)/sum from
-//      the forward's statistics and dS = P (dP - sfmg), written as 16-bit;
+//   2. score_grad_kernel, by m: Q[:,m] K2[:,m]^T completes S, and pointwise
+//      P = exp(S - max)/sum from the forward's statistics is written as
+//      16-bit; then dY[:,m] V2[:,m]^T completes dP and dS = P (dP - sfmg)
+//      (with that 16-bit P) is written as 16-bit;
 //   3. gemm_kernel for dV1 = P^T dY and dK1 = scale dS^T Q (batched over n),
 //      dV2, dK2 (batched over m), dQ = scale (dS K1 + dS K2) (two launches,
 //      the second adding the first's fp32 result).
@@ -229,27 +230,46 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int64_t cb = h * g.c_sh + z * g.c_sz;
+  // A tile inside the output (the usual case) issues a block's 16 addend
+  // loads before any store; edge tiles check every element.
+  const bool full = i0 + BM <= g.I && j0 + BN <= g.J;
+  const float* __restrict__ add = g.addend;
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
       const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
+      if (full) {
+        float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i0 + (wm * C::TM + tm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (i < g.I && j < g.J) {
-          const int64_t off = cb + i * g.c_si + j;
-          float v = g.alpha * acc[tm][tn][r];
-          if (g.addend) v += g.addend[off];
-          if (g.out_f32) static_cast<float*>(g.c)[off] = v;
-          else static_cast<bf16*>(g.c)[off] = to_elem<F16>(v);
+        for (int r = 0; r < 16; ++r) v[r] = add ? add[cb + (ib + 8 * (r >> 2) + (r & 3)) * g.c_si + j] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t off = cb + (ib + 8 * (r >> 2) + (r & 3)) * g.c_si + j;
+          const float x = g.alpha * acc[tm][tn][r] + v[r];
+          if (g.out_f32) static_cast<float*>(g.c)[off] = x;
+          else static_cast<bf16*>(g.c)[off] = to_elem<F16>(x);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = ib + 8 * (r >> 2) + (r & 3);
+          if (i < g.I && j < g.J) {
+            const int64_t off = cb + i * g.c_si + j;
+            float x = g.alpha * acc[tm][tn][r];
+            if (add) x += add[off];
+            if (g.out_f32) static_cast<float*>(g.c)[off] = x;
+            else static_cast<bf16*>(g.c)[off] = to_elem<F16>(x);
+          }
         }
       }
     }
 }
 
-// Score products (see ScoreArgs).  Rows i of the tile are m (by n) or n (by
-// m), columns j are keys k; the inner batch index z is n (by n) or m (by m).
+// Score products (see ScoreArgs), epilogues 0, 2 and 3.  Rows i of the tile
+// are m (by n) or n (by m), columns j are keys k; the inner batch index z is
+// n (by n) or m (by m).
 template <bool F16, int EPI>
 __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
   using C = Cfg<128>;
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
     Op B{static_cast<const bf16*>(s.x1) + x_off, x_sx, 1, J, s.D};
     gemm_tile<true, true, 128, F16>(A, B, i0, j0, acs, lds);
   }
-  if constexpr (EPI == 0 || EPI == 1) {
+  if constexpr (EPI == 0) {
     Op A{static_cast<const bf16*>(s.dy) + q_off, q_sx, 1, I, s.D};
     Op B{static_cast<const bf16*>(s.x2) + x_off, x_sx, 1, J, s.D};
     gemm_tile<true, true, 128, F16>(A, B, i0, j0, acp, lds);
@@ -295,33 +315,144 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
   const int64_t w_si = by_m ? MK : s.K;
   const float sl2 = s.scale * kLog2e;
   const int bb = (s.head0 + h) / s.H;  // batch index of the mask
+  float* __restrict__ ws_s = s.ws_s;
+  float* __restrict__ ws_p = s.ws_p;
+  const bool full = i0 + BM <= I && j0 + 128 <= J;
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
       const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
+      auto row_of = [&](int r) { return ib + 8 * (r >> 2) + (r & 3); };
+      auto off_of = [&](int r) { return wbase + row_of(r) * w_si + j; };
+      if constexpr (EPI == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (full || (row_of(r) < I && j < J)) {
+            ws_s[off_of(r)] = acs[tm][tn][r];
+            ws_p[off_of(r)] = acp[tm][tn][r];
+          }
+      } else if constexpr (EPI == 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (full || (row_of(r) < I && j < J)) ws_s[off_of(r)] = acs[tm][tn][r];
+      } else if constexpr (EPI == 3) {
+        if (full) {
+          float old[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) old[r] = ws_s[off_of(r)];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ws_s[off_of(r)] = old[r] + acs[tm][tn][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (row_of(r) < I && j < J) ws_s[off_of(r)] += acs[tm][tn][r];
+        }
+      }
+    }
+}
+
+// Epilogue 1 (backward, by m): for each m, the (n, k) tile of Q K2^T completes
+// the scores with the by-n partial in ws_s, P = exp(scale*S - lse) is stored
+// and kept as 16-bit in registers; then the tile of dY V2^T completes dP with
+// ws_p and dS = P (dP - sfmg) is stored.  Forming P before the second product
+// frees the score accumulators for it.  Every load of a 32x32 block is issued
+// before the block's first store (edge tiles check each element).
+template <bool F16>
+__global__ __launch_bounds__(NT, 2) void score_grad_kernel(ScoreArgs s) {
+  using C = Cfg<128>;
+  __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
+  const int I = s.N, J = s.K;
+  const int tiles_j = (J + 127) / 128, tiles_i = (I + BM - 1) / BM;
+  // consecutive workgroups of an XCD take consecutive m of one (n, k) tile:
+  // their rows of Q, dY and of the workspace lie side by side in memory
+  const int L = logical_block();
+  const int z = L % s.M, tile = L / s.M;
+  const int i0 = (tile / tiles_j) * BM, j0 = (tile % tiles_j) * 128;
+  const int h = blockIdx.y;
+  const int64_t MD = (int64_t)s.M * s.D, NMD = (int64_t)s.N * MD;
+  // Q / dY row n of batch m at n*M*D + m*D; K2 / V2 row k of batch m at k*M*D + m*D
+  const int64_t q_off = h * NMD + (int64_t)z * s.D;
+  const int64_t x_off = h * (int64_t)s.K * MD + (int64_t)z * s.D;
+  const int64_t MK = (int64_t)s.M * s.K, NMK = (int64_t)s.N * MK;
+  const int64_t wbase = h * NMK + (int64_t)z * s.K;   // element (n, m = z, k) at wbase + n*MK + k
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const float sl2 = s.scale * kLog2e;
+  const int bb = (s.head0 + h) / s.H;
+  const bool full = i0 + BM <= I && j0 + 128 <= J;
+  const float* __restrict__ ws_s = s.ws_s;
+  const float* __restrict__ ws_p = s.ws_p;
+  bf16* __restrict__ pe = static_cast<bf16*>(s.ws_pe);
+  bf16* __restrict__ dse = static_cast<bf16*>(s.ws_dse);
+
+  floatx16 acc[C::TM][C::TN];
+  uint32_t pk[C::TM][C::TN][8];  // P as 16-bit pairs (rows r, r + 1 of a block)
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = floatx16{};
+  {
+    Op A{static_cast<const bf16*>(s.q) + q_off, MD, 1, I, s.D};
+    Op B{static_cast<const bf16*>(s.x1) + x_off, MD, 1, J, s.D};
+    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acc, lds);
+  }
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
+      float sv[16], l2[16];
+      bool live[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = i0 + (wm * C::TM + tm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (i >= I || j >= J) continue;
-        const int64_t off = wbase + i * w_si + j;
-        if constexpr (EPI == 0) {
-          s.ws_s[off] = acs[tm][tn][r];
-          s.ws_p[off] = acp[tm][tn][r];
-        } else if constexpr (EPI == 2) {
-          s.ws_s[off] = acs[tm][tn][r];
-        } else if constexpr (EPI == 3) {
-          s.ws_s[off] += acs[tm][tn][r];
-        } else {
-          // i = n, z = m: the row (head, n, m) of the statistics
-          const int64_t row = ((int64_t)h * s.N + i) * s.M + z;
-          const bool live = s.mask == nullptr || s.mask[((int64_t)bb * s.N + i) * s.K + j] == 0;
-          const float sc = acs[tm][tn][r] + s.ws_s[off];
-          const float p = live ? __builtin_amdgcn_exp2f(sc * sl2 - s.lse2[row]) : 0.f;
-          const float dp = acp[tm][tn][r] + s.ws_p[off];
-          static_cast<bf16*>(s.ws_pe)[off] = to_elem<F16>(p);
-          static_cast<bf16*>(s.ws_dse)[off] = to_elem<F16>(p * (dp - s.sfmg[row]));
+        const int i = ib + 8 * (r >> 2) + (r & 3);
+        const bool in = full || (i < I && j < J);
+        sv[r] = in ? ws_s[wbase + i * MK + j] : 0.f;
+        l2[r] = in ? s.lse2[((int64_t)h * s.N + i) * s.M + z] : 0.f;
+        live[r] = in && (s.mask == nullptr || s.mask[((int64_t)bb * s.N + i) * s.K + j] == 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        bf16 e[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = ib + 8 * ((r + u) >> 2) + ((r + u) & 3);
+          const float p = live[r + u] ? __builtin_amdgcn_exp2f((acc[tm][tn][r + u] + sv[r + u]) * sl2 - l2[r + u]) : 0.f;
+          e[u] = to_elem<F16>(p);
+          if (full || (i < I && j < J)) pe[wbase + i * MK + j] = e[u];
         }
+        pk[tm][tn][r >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, e[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, e[1]) << 16);
+      }
+      acc[tm][tn] = floatx16{};
+    }
+  {
+    Op A{static_cast<const bf16*>(s.dy) + q_off, MD, 1, I, s.D};
+    Op B{static_cast<const bf16*>(s.x2) + x_off, MD, 1, J, s.D};
+    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acc, lds);
+  }
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
+      float pv[16], sf[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ib + 8 * (r >> 2) + (r & 3);
+        const bool in = full || (i < I && j < J);
+        pv[r] = in ? ws_p[wbase + i * MK + j] : 0.f;
+        sf[r] = in ? s.sfmg[((int64_t)h * s.N + i) * s.M + z] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ib + 8 * (r >> 2) + (r & 3);
+        const uint16_t bits = (uint16_t)(pk[tm][tn][r >> 1] >> (16 * (r & 1)));
+        const float p = from_elem<F16>(__builtin_bit_cast(bf16, bits));
+        if (full || (i < I && j < J)) dse[wbase + i * MK + j] = to_elem<F16>(p * (acc[tm][tn][r] + pv[r] - sf[r]));
       }
     }
 }
@@ -416,7 +547,7 @@ int launch_scores_t(const ScoreArgs& s, hipStream_t st) {
   const dim3 grid((unsigned)nx, s.heads);
   switch (s.epi) {
     case 0: hipLaunchKernelGGL((score_kernel<F16, 0>), grid, dim3(NT), 0, st, s); break;
-    case 1: hipLaunchKernelGGL((score_kernel<F16, 1>), grid, dim3(NT), 0, st, s); break;
+    case 1: hipLaunchKernelGGL((score_grad_kernel<F16>), grid, dim3(NT), 0, st, s); break;
     case 2: hipLaunchKernelGGL((score_kernel<F16, 2>), grid, dim3(NT), 0, st, s); break;
     default: hipLaunchKernelGGL((score_kernel<F16, 3>), grid, dim3(NT), 0, st, s); break;
   }
@@ -424,6 +555,42 @@ int launch_scores_t(const ScoreArgs& s, hipStream_t st) {
 }
 
 }  // namespace
+
+struct StageTimer {
+  int marks;
+  hipEvent_t* ev;
+};
+
+StageTimer* stage_timer_create(int marks) {
+  StageTimer* t = new StageTimer{marks, new hipEvent_t[marks]};
+  for (int i = 0; i < marks; ++i) {
+    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(t->ev[j]);
+      delete[] t->ev;
+      delete t;
+      return nullptr;
+    }
+  }
+  return t;
+}
+
+int stage_timer_mark(StageTimer* t, int i, void* stream) {
+  return (int)hipEventRecord(t->ev[i], static_cast<hipStream_t>(stream));
+}
+
+int stage_timer_read(StageTimer* t, float* ms) {
+  if (hipEventSynchronize(t->ev[t->marks - 1]) != hipSuccess) return 1;
+  for (int i = 0; i + 1 < t->marks; ++i)
+    if (hipEventElapsedTime(&ms[i], t->ev[i], t->ev[i + 1]) != hipSuccess) return 1;
+  return 0;
+}
+
+void stage_timer_destroy(StageTimer* t) {
+  if (!t) return;
+  for (int i = 0; i < t->marks; ++i) (void)hipEventDestroy(t->ev[i]);
+  delete[] t->ev;
+  delete t;
+}
 
 int launch_gemm(const GemmArgs& g, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -37,7 +37,7 @@ DTYPE_FP16 = 1
 
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_profile_enable",
             "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version",
-            "fa_floyd_workspace_size", "fa_floyd_bwd_run", "fa_floyd_fwd_run")
+            "fa_floyd_workspace_size", "fa_floyd_bwd_run", "fa_floyd_bwd_run_timed", "fa_floyd_fwd_run")
 
 
 class MaskMode(enum.IntEnum):
@@ -129,6 +129,8 @@ def load_library(path=LIB_PATH):
     lib.fa_floyd_workspace_size.restype = ctypes.c_int
     lib.fa_floyd_bwd_run.argtypes = [vp] * 16 + [vp, sz, vp]
     lib.fa_floyd_bwd_run.restype = ctypes.c_int
+    lib.fa_floyd_bwd_run_timed.argtypes = [vp] * 16 + [vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
+    lib.fa_floyd_bwd_run_timed.restype = ctypes.c_int
     lib.fa_floyd_fwd_run.argtypes = [vp] * 10 + [vp, sz, vp]
     lib.fa_floyd_fwd_run.restype = ctypes.c_int
     if lib.fa_bwd_abi_version() != ABI_VERSION:

@@ -127,10 +127,15 @@ def floyd_attn(query, key1, value1, key2, value2, atten_mask=None, scale_value=N
     return out, smax, ssum
 
 
+STAGES = ("rowstats", "scores_by_n", "scores_by_m_softmax_grad", "dv1", "dk1", "dv2", "dk2", "dq_k1", "dq_k2")
+
+
 def floyd_attn_grad(query, key1, value1, key2, value2, dy, atten_mask, softmax_max, softmax_sum, attention_in,
-                    scale_value=None, workspace=None):
+                    scale_value=None, workspace=None, out=None, stage_ms=None):
     """Backward: (dq, dk1, dv1, dk2, dv2) on the current stream, in the
-    inputs' element type."""
+    inputs' element type (written into `out` when given).  With a list
+    `stage_ms` the call goes through fa_floyd_bwd_run_timed, waits, and the
+    list receives the duration of each stage of STAGES in milliseconds."""
     import torch
 
     desc, (B, H, N, M, K, D), q, k1, v1, k2, v2 = _prepare(query, key1, value1, key2, value2, scale_value)
@@ -140,15 +145,25 @@ def floyd_attn_grad(query, key1, value1, key2, value2, dy, atten_mask, softmax_m
     smax = _check("softmax_max", softmax_max, (B, H, N, M, 8), torch.float32, dev)
     ssum = _check("softmax_sum", softmax_sum, (B, H, N, M, 8), torch.float32, dev)
     mask = _mask(atten_mask, B, N, K, dev)
-    dq, dk1, dv1 = torch.empty_like(q), torch.empty_like(k1), torch.empty_like(v1)
-    dk2, dv2 = torch.empty_like(k2), torch.empty_like(v2)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k1), torch.empty_like(v1), torch.empty_like(k2),
+               torch.empty_like(v2))
+    dq, dk1, dv1, dk2, dv2 = out
+    for name, t, ref in (("dq", dq, q), ("dk1", dk1, k1), ("dv1", dv1, v1), ("dk2", dk2, k2), ("dv2", dv2, v2)):
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"out[{name}] must be a contiguous {ref.dtype} tensor of shape {tuple(ref.shape)}")
     ws = _workspace(desc, dev, workspace)
     lib = fb.load_library()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     p = fb._ptr
-    st = lib.fa_floyd_bwd_run(ctypes.byref(desc), p(q), p(k1), p(v1), p(k2), p(v2), p(dy), p(mask), p(smax),
-                              p(ssum), p(y), p(dq), p(dk1), p(dv1), p(dk2), p(dv2), p(ws),
-                              ws.numel() * ws.element_size(), stream)
+    args = (ctypes.byref(desc), p(q), p(k1), p(v1), p(k2), p(v2), p(dy), p(mask), p(smax), p(ssum), p(y), p(dq),
+            p(dk1), p(dv1), p(dk2), p(dv2), p(ws), ws.numel() * ws.element_size(), stream)
+    if stage_ms is None:
+        st = lib.fa_floyd_bwd_run(*args)
+    else:
+        buf = (ctypes.c_float * len(STAGES))()
+        st = lib.fa_floyd_bwd_run_timed(*args, buf)
+        stage_ms[:] = list(buf)
     if st != fb.FA_OK:
         raise fb.FaBwdError(st, "fa_floyd_bwd_run")
     return dq, dk1, dv1, dk2, dv2

@@ -14,6 +14,10 @@ trace: the per-kernel table of a --kernel-trace --stats run (calls, average,
 min and max duration, share of GPU time), with the kernel source hash and,
 when given, the bench.py JSON line of the same build.
 
+--sources selects whose source hash is recorded: the default attention
+kernels ("det") or Floyd attention ("floyd"); trace --match keeps only the
+kernels whose names contain one of the given substrings.
+
 mfma: MFMA-pipe utilisation per kernel from a --pmc GRBM_GUI_ACTIVE
 SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA run.  SQ_VALU_MFMA_BUSY_CYCLES is the
 sum over all 1024 SIMDs (it equals 32 cycles per v_mfma_f32_32x32x16_bf16
@@ -41,6 +45,9 @@ CSRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc")
 # the sources the timed dK/dV and dQ kernels are compiled from
 KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_det_kernels.hip", "fa_bwd_schedule.h",
                                                     "fa_bwd_internal.h"))
+# the sources the Floyd attention kernels are compiled from
+FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h"))
+SOURCES = {"det": KERNEL_SRCS, "floyd": FLOYD_SRCS}
 COPY_BYTES = 256 << 20
 XCDS = 8        # MI355X: 8 XCDs of 32 CUs
 SIMDS = 1024    # 256 CUs x 4 SIMDs
@@ -59,6 +66,12 @@ def kernel_code_hash(paths=KERNEL_SRCS):
     return hashlib.sha256("\n\f\n".join(parts).encode("utf-8")).hexdigest()[:16]
 
 
+def _names(arg):
+    """Kernel name substrings: separated by ';' when one is present (template
+    arguments hold commas), else by ','."""
+    return [n for n in arg.split(";" if ";" in arg else ",") if n]
+
+
 def _rows(d):
     path = os.path.join(d, "run_counter_collection.csv")
     return list(csv.DictReader(open(path)))
@@ -74,7 +87,7 @@ def _per_dispatch(d, counter, match):
 
 
 def traffic(args):
-    names = args.kernels.split(",")
+    names = _names(args.kernels)
     cf = statistics.median(_per_dispatch(args.copy_fetch, "FETCH_SIZE", lambda n: "copyBuffer" in n))
     cw = statistics.median(_per_dispatch(args.copy_write, "WRITE_SIZE", lambda n: "copyBuffer" in n))
     f_scale = COPY_BYTES / (cf * 1024.0)
@@ -87,7 +100,7 @@ def traffic(args):
         fb, wb = f * 1024.0 * f_scale, w * 1024.0 * w_scale
         total += fb + wb
         lines.append(f"# {n}: FETCH_SIZE {f:.0f} KiB -> {fb / 2**20:.1f} MiB, WRITE_SIZE {w:.0f} KiB -> {wb / 2**20:.1f} MiB")
-    src_hash = kernel_code_hash()
+    src_hash = kernel_code_hash(SOURCES[args.sources])
     out = [
         f"# HBM traffic per launch of {'+'.join(names)}, workload {args.workload}",
         f"# command: {args.command}",
@@ -105,14 +118,17 @@ def traffic(args):
 
 
 def _short(name):
-    name = name.replace("fabwd::(anonymous namespace)::", "").replace("fabwd::", "")
+    for ns in ("fabwd", "ffloyd"):
+        name = name.replace(ns + "::(anonymous namespace)::", "").replace(ns + "::", "")
     return name[:64]
 
 
 def trace(args):
     rows = list(csv.DictReader(open(os.path.join(args.stats, "run_kernel_stats.csv"))))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    src_hash = kernel_code_hash()
+    if args.match:
+        rows = [r for r in rows if any(m in r["Name"] for m in _names(args.match))]
+    src_hash = kernel_code_hash(SOURCES[args.sources])
     out = [
         f"# rocprofv3 kernel-trace summary, workload {args.workload}",
         f"# command: {args.command}",
@@ -132,9 +148,9 @@ def trace(args):
 
 
 def mfma(args):
-    names = args.kernels.split(",")
+    names = _names(args.kernels)
     rows = _rows(args.pmc)
-    src_hash = kernel_code_hash()
+    src_hash = kernel_code_hash(SOURCES[args.sources])
     out = [f"# MFMA-pipe utilisation per kernel, workload {args.workload}", f"# command: {args.command}",
            "# columns: kernel | MFMA instructions | MFMA busy cycles (all SIMDs) | elapsed cycles | "
            "utilisation | clock GHz"]
@@ -153,9 +169,9 @@ def mfma(args):
         util = busy / (elapsed * SIMDS)
         tot_busy += busy
         tot_el += elapsed
-        out.append(f"{n:16s} | {insts:12.0f} | {busy:14.0f} | {elapsed:11.0f} | {100 * util:5.1f} % | "
+        out.append(f"{n:40s} | {insts:12.0f} | {busy:14.0f} | {elapsed:11.0f} | {100 * util:5.1f} % | "
                    f"{elapsed / dur_ns:4.2f}")
-    out.append(f"pair_mfma_utilisation: {100 * tot_busy / (tot_el * SIMDS):.1f} %")
+    out.append(f"{'pair' if len(names) == 2 else 'combined'}_mfma_utilisation: {100 * tot_busy / (tot_el * SIMDS):.1f} %")
     out.append(f"kernel_code_sha256_16: {src_hash}")
     text = "\n".join(out) + "\n"
     if args.out:
@@ -171,17 +187,21 @@ def main():
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernels", "--workload"):
         t.add_argument(k, required=True)
     t.add_argument("--out")
+    t.add_argument("--sources", choices=sorted(SOURCES), default="det")
     t.add_argument("--command", default="(see profiles/README.md)")
     tr = sub.add_parser("trace")
     tr.add_argument("--stats", required=True)
     tr.add_argument("--workload", required=True)
     tr.add_argument("--bench-json")
     tr.add_argument("--out")
+    tr.add_argument("--sources", choices=sorted(SOURCES), default="det")
+    tr.add_argument("--match", help="comma-separated substrings: keep only kernels whose name holds one")
     tr.add_argument("--command", default="(see profiles/README.md)")
     m = sub.add_parser("mfma")
     for k in ("--pmc", "--kernels", "--workload"):
         m.add_argument(k, required=True)
     m.add_argument("--out")
+    m.add_argument("--sources", choices=sorted(SOURCES), default="det")
     m.add_argument("--command", default="(see profiles/README.md)")
     args = ap.parse_args()
     if args.cmd == "traffic":

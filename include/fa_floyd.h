@@ -82,6 +82,26 @@ int fa_floyd_bwd_run(const fa_floyd_desc* desc,
                      void* dq, void* dk1, void* dv1, void* dk2, void* dv2,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Timing hook: the same launches as fa_floyd_bwd_run with a HIP event
+ * recorded on `stream` before the first and after each stage; waits for them
+ * and writes the stages' durations in milliseconds (summed over the groups of
+ * heads) to stage_ms[0 .. FA_FLOYD_BWD_STAGES), in this order: row
+ * statistics (sfmg, log-sum-exp), score products batched over n, score
+ * products batched over m with P and dS, dV1, dK1, dV2, dK2, the dQ term of
+ * K1, the dQ term of K2.  Synchronous; for benchmarks.  Errors: those of
+ * fa_floyd_bwd_run, FA_ERR_NULLPTR (stage_ms NULL), FA_ERR_RUNTIME (an event
+ * call failed). */
+#define FA_FLOYD_BWD_STAGES 9
+int fa_floyd_bwd_run_timed(const fa_floyd_desc* desc,
+                           const void* query, const void* key1, const void* value1,
+                           const void* key2, const void* value2, const void* dy,
+                           const uint8_t* atten_mask,
+                           const float* softmax_max, const float* softmax_sum,
+                           const void* attention_in,
+                           void* dq, void* dk1, void* dv1, void* dk2, void* dv2,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           float* stage_ms);
+
 /* The forward that produces the backward's inputs (section 功能说明, forward
  * formula): attention_out (Y, 16-bit, query's shape) and the float32
  * statistics softmax_max (row max of the scaled, masked scores) and

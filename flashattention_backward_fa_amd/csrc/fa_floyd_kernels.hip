@@ -46,7 +46,7 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int NT = 256;  // threads per workgroup (4 wavefronts)
-constexpr int BM = 128;  // tile rows (i)
+constexpr int BM = 128;  // tile rows (i) of every kernel but score_grad_kernel
 constexpr int BK = 32;   // contraction step
 
 template <bool F16>
@@ -141,25 +141,28 @@ struct Tile {
   }
 };
 
-// Wavefront arrangement of a BM x BN tile over 4 wavefronts.
-template <int BN>
+// Wavefront arrangement of a TBM x BN tile over 4 wavefronts.
+template <int BN, int TBM = BM>
 struct Cfg {
-  static constexpr int WN = BN == 128 ? 64 : BN;  // columns per wavefront
-  static constexpr int WAVES_N = BN / WN;
-  static constexpr int WAVES_M = 4 / WAVES_N;
-  static constexpr int WM = BM / WAVES_M;
+  // 128 x 128: 2 x 2 wavefronts of 64 x 64; 128 x 64 and 128 x 32: 4 x 1;
+  // 64 x 128: 2 x 2 of 32 x 64; 32 x 128: 1 x 4 of 32 x 32
+  static constexpr int WAVES_M = TBM / 32 >= 4 ? (BN == 128 ? 2 : 4) : TBM / 32;
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WN = BN / WAVES_N;  // columns per wavefront
+  static constexpr int WM = TBM / WAVES_M;
   static constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1 && WAVES_M * WAVES_N == 4, "wavefront arrangement");
 };
 
 constexpr int LDS_ELEMS = 2 * 2 * 5120;  // two buffers of the largest A and B tiles
 
 // acc += A(i0.., :) B(:, j0..) over the whole contraction.  Every thread of
 // the workgroup calls it; it ends with a barrier, so the LDS may be reused.
-template <bool ATC, bool BTC, int BN, bool F16>
+template <bool ATC, bool BTC, int BN, bool F16, int TBM = BM>
 __device__ __forceinline__ void gemm_tile(const Op& A, const Op& B, int i0, int j0,
-                                          floatx16 (&acc)[Cfg<BN>::TM][Cfg<BN>::TN], bf16* lds) {
-  using C = Cfg<BN>;
-  using TA = Tile<ATC, BM>;
+                                          floatx16 (&acc)[Cfg<BN, TBM>::TM][Cfg<BN, TBM>::TN], bf16* lds) {
+  using C = Cfg<BN, TBM>;
+  using TA = Tile<ATC, TBM>;
   using TB = Tile<BTC, BN>;
   static_assert(TA::ELEMS <= 5120 && TB::ELEMS <= 5120, "LDS tile size");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -357,19 +360,21 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
 // the scores with the by-n partial in ws_s, P = exp(scale*S - lse) is stored
 // and kept as 16-bit in registers; then the tile of dY V2^T completes dP with
 // ws_p and dS = P (dP - sfmg) is stored.  Forming P before the second product
-// frees the score accumulators for it.  Every load of a 32x32 block is issued
-// before the block's first store (edge tiles check each element).
+// frees the score accumulators for it.  Each epilogue's loads are issued
+// before the product that precedes it (edge tiles check each element).
+constexpr int GBM = 64;  // tile rows (n) of score_grad_kernel
+
 template <bool F16>
-__global__ __launch_bounds__(NT, 2) void score_grad_kernel(ScoreArgs s) {
-  using C = Cfg<128>;
+__global__ __launch_bounds__(NT) void score_grad_kernel(ScoreArgs s) {
+  using C = Cfg<128, GBM>;
   __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
   const int I = s.N, J = s.K;
-  const int tiles_j = (J + 127) / 128, tiles_i = (I + BM - 1) / BM;
+  const int tiles_j = (J + 127) / 128, tiles_i = (I + GBM - 1) / GBM;
   // consecutive workgroups of an XCD take consecutive m of one (n, k) tile:
   // their rows of Q, dY and of the workspace lie side by side in memory
   const int L = logical_block();
   const int z = L % s.M, tile = L / s.M;
-  const int i0 = (tile / tiles_j) * BM, j0 = (tile % tiles_j) * 128;
+  const int i0 = (tile / tiles_j) * GBM, j0 = (tile % tiles_j) * 128;
   const int h = blockIdx.y;
   const int64_t MD = (int64_t)s.M * s.D, NMD = (int64_t)s.N * MD;
   // Q / dY row n of batch m at n*M*D + m*D; K2 / V2 row k of batch m at k*M*D + m*D
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(NT, 2) void score_grad_kernel(ScoreArgs s) {
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const float sl2 = s.scale * kLog2e;
   const int bb = (s.head0 + h) / s.H;
-  const bool full = i0 + BM <= I && j0 + 128 <= J;
+  const bool full = i0 + GBM <= I && j0 + 128 <= J;
   const float* __restrict__ ws_s = s.ws_s;
   const float* __restrict__ ws_p = s.ws_p;
   bf16* __restrict__ pe = static_cast<bf16*>(s.ws_pe);
@@ -393,68 +398,86 @@ __global__ __launch_bounds__(NT, 2) void score_grad_kernel(ScoreArgs s) {
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = floatx16{};
+  auto row_of = [&](int tm, int r) { return i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3); };
+  auto col_of = [&](int tn) { return j0 + (wn * C::TN + tn) * 32 + (lane & 31); };
+  auto inside = [&](int tm, int tn, int r) { return full || (row_of(tm, r) < I && col_of(tn) < J); };
+
+  // the by-n partial scores, the rows' log-sum-exp and the mask are loaded
+  // before the first product, so that their latency overlaps it
+  float sv[C::TM][C::TN][16], l2[C::TM][16];
+  bool live[C::TM][C::TN][16];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = row_of(tm, r);
+      l2[tm][r] = (full || i < I) ? s.lse2[((int64_t)h * s.N + i) * s.M + z] : 0.f;
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = row_of(tm, r), j = col_of(tn);
+        const bool in = inside(tm, tn, r);
+        sv[tm][tn][r] = in ? ws_s[wbase + i * MK + j] : 0.f;
+        live[tm][tn][r] = in && (s.mask == nullptr || s.mask[((int64_t)bb * s.N + i) * s.K + j] == 0);
+      }
+  }
   {
     Op A{static_cast<const bf16*>(s.q) + q_off, MD, 1, I, s.D};
     Op B{static_cast<const bf16*>(s.x1) + x_off, MD, 1, J, s.D};
-    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acc, lds);
+    gemm_tile<true, true, 128, F16, GBM>(A, B, i0, j0, acc, lds);
   }
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
-      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
-      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
-      float sv[16], l2[16];
-      bool live[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = ib + 8 * (r >> 2) + (r & 3);
-        const bool in = full || (i < I && j < J);
-        sv[r] = in ? ws_s[wbase + i * MK + j] : 0.f;
-        l2[r] = in ? s.lse2[((int64_t)h * s.N + i) * s.M + z] : 0.f;
-        live[r] = in && (s.mask == nullptr || s.mask[((int64_t)bb * s.N + i) * s.K + j] == 0);
-      }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         bf16 e[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int i = ib + 8 * ((r + u) >> 2) + ((r + u) & 3);
-          const float p = live[r + u] ? __builtin_amdgcn_exp2f((acc[tm][tn][r + u] + sv[r + u]) * sl2 - l2[r + u]) : 0.f;
+          const float p = live[tm][tn][r + u]
+                              ? __builtin_amdgcn_exp2f((acc[tm][tn][r + u] + sv[tm][tn][r + u]) * sl2 - l2[tm][r + u])
+                              : 0.f;
           e[u] = to_elem<F16>(p);
-          if (full || (i < I && j < J)) pe[wbase + i * MK + j] = e[u];
+          if (inside(tm, tn, r + u)) pe[wbase + row_of(tm, r + u) * MK + col_of(tn)] = e[u];
         }
         pk[tm][tn][r >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, e[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, e[1]) << 16);
       }
       acc[tm][tn] = floatx16{};
     }
+  // the by-n partial dP and the rows' sfmg, loaded before the second product
+  float pv[C::TM][C::TN][16], sf[C::TM][16];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = row_of(tm, r);
+      sf[tm][r] = (full || i < I) ? s.sfmg[((int64_t)h * s.N + i) * s.M + z] : 0.f;
+    }
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pv[tm][tn][r] = inside(tm, tn, r) ? ws_p[wbase + row_of(tm, r) * MK + col_of(tn)] : 0.f;
+  }
   {
     Op A{static_cast<const bf16*>(s.dy) + q_off, MD, 1, I, s.D};
     Op B{static_cast<const bf16*>(s.x2) + x_off, MD, 1, J, s.D};
-    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acc, lds);
+    gemm_tile<true, true, 128, F16, GBM>(A, B, i0, j0, acc, lds);
   }
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
-      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
-      float pv[16], sf[16];
+    for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = ib + 8 * (r >> 2) + (r & 3);
-        const bool in = full || (i < I && j < J);
-        pv[r] = in ? ws_p[wbase + i * MK + j] : 0.f;
-        sf[r] = in ? s.sfmg[((int64_t)h * s.N + i) * s.M + z] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = ib + 8 * (r >> 2) + (r & 3);
         const uint16_t bits = (uint16_t)(pk[tm][tn][r >> 1] >> (16 * (r & 1)));
         const float p = from_elem<F16>(__builtin_bit_cast(bf16, bits));
-        if (full || (i < I && j < J)) dse[wbase + i * MK + j] = to_elem<F16>(p * (acc[tm][tn][r] + pv[r] - sf[r]));
+        if (inside(tm, tn, r))
+          dse[wbase + row_of(tm, r) * MK + col_of(tn)] = to_elem<F16>(p * (acc[tm][tn][r] + pv[tm][tn][r] - sf[tm][r]));
       }
-    }
 }
 
 // 16 lanes per row: sfmg = sum_d dY*Y in fp32, lse2 from the statistics.
@@ -542,8 +565,8 @@ int launch_gemm_t(const GemmArgs& g, hipStream_t st) {
 template <bool F16>
 int launch_scores_t(const ScoreArgs& s, hipStream_t st) {
   const bool by_m = s.epi == 1 || s.epi == 3;
-  const int I = by_m ? s.N : s.M;
-  const int64_t nx = (int64_t)((I + BM - 1) / BM) * ((s.K + 127) / 128) * (by_m ? s.M : s.N);
+  const int I = by_m ? s.N : s.M, rows = s.epi == 1 ? GBM : BM;
+  const int64_t nx = (int64_t)((I + rows - 1) / rows) * ((s.K + 127) / 128) * (by_m ? s.M : s.N);
   const dim3 grid((unsigned)nx, s.heads);
   switch (s.epi) {
     case 0: hipLaunchKernelGGL((score_kernel<F16, 0>), grid, dim3(NT), 0, st, s); break;

@@ -15,7 +15,7 @@
 //   2. score_grad_kernel, by m: Q[:,m] K2[:,m]^T completes S, and pointwise
 //      P = exp(S - max)/sum from the forward's statistics is written as
 //      16-bit; then dY[:,m] V2[:,m]^T completes dP and dS = P (dP - sfmg)
-//      (with that 16-bit P) is written as 16-bit;
+//      (P in fp32) is written as 16-bit;
 //   3. gemm_kernel for dV1 = P^T dY and dK1 = scale dS^T Q (batched over n),
 //      dV2, dK2 (batched over m), dQ = scale (dS K1 + dS K2) (two launches,
 //      the second adding the first's fp32 result).
@@ -212,14 +212,14 @@ __device__ __forceinline__ int logical_block() {
   return (n & 7) == 0 ? (w & 7) * (n >> 3) + (w >> 3) : w;
 }
 
-template <bool ATC, bool BTC, int BN, bool F16>
+template <bool ATC, bool BTC, int BN, bool F16, int TBM>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
-  using C = Cfg<BN>;
+  using C = Cfg<BN, TBM>;
   __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
-  const int tiles_j = (g.J + BN - 1) / BN, tiles_i = (g.I + BM - 1) / BM;
+  const int tiles_j = (g.J + BN - 1) / BN, tiles_i = (g.I + TBM - 1) / TBM;
   const int L = logical_block();
   const int z = L / (tiles_i * tiles_j), tile = L % (tiles_i * tiles_j);
-  const int i0 = (tile / tiles_j) * BM, j0 = (tile % tiles_j) * BN;
+  const int i0 = (tile / tiles_j) * TBM, j0 = (tile % tiles_j) * BN;
   const int h = blockIdx.y;
   Op A{static_cast<const bf16*>(g.a) + h * g.a_sh + z * g.a_sz, g.a_si, g.a_st, g.I, g.T};
   Op B{static_cast<const bf16*>(g.b) + h * g.b_sh + z * g.b_sz, g.b_sj, g.b_st, g.J, g.T};
@@ -228,14 +228,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = floatx16{};
-  gemm_tile<ATC, BTC, BN, F16>(A, B, i0, j0, acc, lds);
+  gemm_tile<ATC, BTC, BN, F16, TBM>(A, B, i0, j0, acc, lds);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int64_t cb = h * g.c_sh + z * g.c_sz;
   // A tile inside the output (the usual case) issues a block's 16 addend
   // loads before any store; edge tiles check every element.
-  const bool full = i0 + BM <= g.I && j0 + BN <= g.J;
+  const bool full = i0 + TBM <= g.I && j0 + BN <= g.J;
   const float* __restrict__ add = g.addend;
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
@@ -273,16 +273,18 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
 // Score products (see ScoreArgs), epilogues 0, 2 and 3.  Rows i of the tile
 // are m (by n) or n (by m), columns j are keys k; the inner batch index z is
 // n (by n) or m (by m).
+constexpr int SBM = 128;  // tile rows of score_kernel (64 re-reads K1 / V1 tiles twice as often: slower)
+
 template <bool F16, int EPI>
 __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
-  using C = Cfg<128>;
+  using C = Cfg<128, SBM>;
   __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
   const bool by_m = EPI == 1 || EPI == 3;
   const int I = by_m ? s.N : s.M, J = s.K;
-  const int tiles_j = (J + 127) / 128, tiles_i = (I + BM - 1) / BM;
+  const int tiles_j = (J + 127) / 128, tiles_i = (I + SBM - 1) / SBM;
   const int L = logical_block();
   const int z = L / (tiles_i * tiles_j), tile = L % (tiles_i * tiles_j);
-  const int i0 = (tile / tiles_j) * BM, j0 = (tile % tiles_j) * 128;
+  const int i0 = (tile / tiles_j) * SBM, j0 = (tile % tiles_j) * 128;
   const int h = blockIdx.y;
   const int64_t MD = (int64_t)s.M * s.D, NMD = (int64_t)s.N * MD;
   const int64_t KD = (int64_t)s.K * s.D;
@@ -302,12 +304,12 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
   {
     Op A{static_cast<const bf16*>(s.q) + q_off, q_sx, 1, I, s.D};
     Op B{static_cast<const bf16*>(s.x1) + x_off, x_sx, 1, J, s.D};
-    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acs, lds);
+    gemm_tile<true, true, 128, F16, SBM>(A, B, i0, j0, acs, lds);
   }
   if constexpr (EPI == 0) {
     Op A{static_cast<const bf16*>(s.dy) + q_off, q_sx, 1, I, s.D};
     Op B{static_cast<const bf16*>(s.x2) + x_off, x_sx, 1, J, s.D};
-    gemm_tile<true, true, 128, F16>(A, B, i0, j0, acp, lds);
+    gemm_tile<true, true, 128, F16, SBM>(A, B, i0, j0, acp, lds);
   }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
   const int bb = (s.head0 + h) / s.H;  // batch index of the mask
   float* __restrict__ ws_s = s.ws_s;
   float* __restrict__ ws_p = s.ws_p;
-  const bool full = i0 + BM <= I && j0 + 128 <= J;
+  const bool full = i0 + SBM <= I && j0 + 128 <= J;
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
@@ -358,8 +360,8 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreArgs s) {
 
 // Epilogue 1 (backward, by m): for each m, the (n, k) tile of Q K2^T completes
 // the scores with the by-n partial in ws_s, P = exp(scale*S - lse) is stored
-// and kept as 16-bit in registers; then the tile of dY V2^T completes dP with
-// ws_p and dS = P (dP - sfmg) is stored.  Forming P before the second product
+// as 16-bit and kept in fp32 registers; then the tile of dY V2^T completes dP
+// with ws_p and dS = P (dP - sfmg) is stored.  Forming P before the second product
 // frees the score accumulators for it.  Each epilogue's loads are issued
 // before the product that precedes it (edge tiles check each element).
 constexpr int GBM = 64;  // tile rows (n) of score_grad_kernel
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(NT) void score_grad_kernel(ScoreArgs s) {
   bf16* __restrict__ dse = static_cast<bf16*>(s.ws_dse);
 
   floatx16 acc[C::TM][C::TN];
-  uint32_t pk[C::TM][C::TN][8];  // P as 16-bit pairs (rows r, r + 1 of a block)
+  float pf[C::TM][C::TN][16];  // P in fp32 for dS (the stored P is 16-bit)
 #pragma unroll
   for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
@@ -433,17 +435,11 @@ __global__ __launch_bounds__(NT) void score_grad_kernel(ScoreArgs s) {
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        bf16 e[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float p = live[tm][tn][r + u]
-                              ? __builtin_amdgcn_exp2f((acc[tm][tn][r + u] + sv[tm][tn][r + u]) * sl2 - l2[tm][r + u])
-                              : 0.f;
-          e[u] = to_elem<F16>(p);
-          if (inside(tm, tn, r + u)) pe[wbase + row_of(tm, r + u) * MK + col_of(tn)] = e[u];
-        }
-        pk[tm][tn][r >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, e[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, e[1]) << 16);
+      for (int r = 0; r < 16; ++r) {
+        const float p =
+            live[tm][tn][r] ? __builtin_amdgcn_exp2f((acc[tm][tn][r] + sv[tm][tn][r]) * sl2 - l2[tm][r]) : 0.f;
+        pf[tm][tn][r] = p;
+        if (inside(tm, tn, r)) pe[wbase + row_of(tm, r) * MK + col_of(tn)] = to_elem<F16>(p);
       }
       acc[tm][tn] = floatx16{};
     }
@@ -473,23 +469,34 @@ __global__ __launch_bounds__(NT) void score_grad_kernel(ScoreArgs s) {
     for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint16_t bits = (uint16_t)(pk[tm][tn][r >> 1] >> (16 * (r & 1)));
-        const float p = from_elem<F16>(__builtin_bit_cast(bf16, bits));
         if (inside(tm, tn, r))
-          dse[wbase + row_of(tm, r) * MK + col_of(tn)] = to_elem<F16>(p * (acc[tm][tn][r] + pv[tm][tn][r] - sf[tm][r]));
+          dse[wbase + row_of(tm, r) * MK + col_of(tn)] =
+              to_elem<F16>(pf[tm][tn][r] * (acc[tm][tn][r] + pv[tm][tn][r] - sf[tm][r]));
       }
 }
 
 // 16 lanes per row: sfmg = sum_d dY*Y in fp32, lse2 from the statistics.
+// V = D / 16 contiguous elements of a row per lane, one vector load each.
+template <bool F16, int V>
+__device__ __forceinline__ float row_part(const bf16* g, const bf16* y) {
+  typedef __bf16 vec __attribute__((ext_vector_type(V)));
+  const vec a = *reinterpret_cast<const vec*>(g), b = *reinterpret_cast<const vec*>(y);
+  float acc = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc += from_elem<F16>(a[v]) * from_elem<F16>(b[v]);
+  return acc;
+}
+
 template <bool F16>
 __global__ __launch_bounds__(NT) void rowstats_kernel(RowStatsArgs a) {
   const int64_t row = (int64_t)blockIdx.x * (NT / 16) + (threadIdx.x >> 4);
   const int e = threadIdx.x & 15;
   float acc = 0.f;
   if (row < a.rows) {
-    const bf16* g = static_cast<const bf16*>(a.dy) + row * a.D;
-    const bf16* y = static_cast<const bf16*>(a.y) + row * a.D;
-    for (int d = e; d < a.D; d += 16) acc += from_elem<F16>(g[d]) * from_elem<F16>(y[d]);
+    const int V = a.D / 16;  // D is 32, 64 or 128
+    const bf16* g = static_cast<const bf16*>(a.dy) + row * a.D + e * V;
+    const bf16* y = static_cast<const bf16*>(a.y) + row * a.D + e * V;
+    acc = V == 8 ? row_part<F16, 8>(g, y) : V == 4 ? row_part<F16, 4>(g, y) : row_part<F16, 2>(g, y);
   }
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
@@ -540,16 +547,17 @@ __global__ __launch_bounds__(NT) void softmax_kernel(SoftmaxArgs a) {
 
 template <bool ATC, bool BTC, bool F16>
 int launch_gemm_bn(const GemmArgs& g, hipStream_t st) {
-  const int ti = (g.I + BM - 1) / BM;
+  constexpr int R = BM;
+  const int ti = (g.I + R - 1) / R;
   if (g.J <= 32) {
     const int64_t nx = (int64_t)ti * ((g.J + 31) / 32) * g.nb;
-    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 32, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 32, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
   } else if (g.J <= 64) {
     const int64_t nx = (int64_t)ti * ((g.J + 63) / 64) * g.nb;
-    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 64, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 64, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
   } else {
     const int64_t nx = (int64_t)ti * ((g.J + 127) / 128) * g.nb;
-    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 128, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 128, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
   }
   return (int)hipGetLastError();
 }
@@ -565,7 +573,7 @@ int launch_gemm_t(const GemmArgs& g, hipStream_t st) {
 template <bool F16>
 int launch_scores_t(const ScoreArgs& s, hipStream_t st) {
   const bool by_m = s.epi == 1 || s.epi == 3;
-  const int I = by_m ? s.N : s.M, rows = s.epi == 1 ? GBM : BM;
+  const int I = by_m ? s.N : s.M, rows = s.epi == 1 ? GBM : SBM;
   const int64_t nx = (int64_t)((I + rows - 1) / rows) * ((s.K + 127) / 128) * (by_m ? s.M : s.N);
   const dim3 grid((unsigned)nx, s.heads);
   switch (s.epi) {

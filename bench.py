@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the FlashAttention backward on one MI355X.
 
-One step = one fa_bwd_run over one batch of the workload: the dQ kernel
-(S/P/dP/dS recompute and dQ over query tiles; it also forms sfmg =
-rowsum(dY * Y) for its rows), the dK/dV kernel (S/P recompute, dP, dS, dV, dK
-over key tiles) and the fp32 partial-sum reduce when the plan splits a key
-tile, with every input already resident in HBM.  attn_out and softmax_lse come from the library's own GPU
+One step = one fa_bwd_run over one batch of the workload, with every input
+already resident in HBM.  For the dense layouts (BSND, BNSD) the plan takes
+the stored-dS path: the sfmg preprocess (rowsum(dY * Y)), the dK/dV kernel
+(S/P recompute, dP, dS, dV, dK over key tiles; it also stores dS), the dQ GEMM
+over the stored dS, and the fp32 partial-sum reduce when the plan splits a key
+tile.  For TND it takes the recompute path: the dQ kernel (S/P/dP/dS recompute
+and dQ over query tiles; it also forms sfmg), then the dK/dV kernel and the
+reduce.  attn_out and softmax_lse come from the library's own GPU
 forward (fa_fwd_run), made once before timing.  The default workload is the
 GQA causal one (B=1, N1=32, N2=8, S=4096, D=Dv=128, BSND).
 
 Prints one JSON line: whole-step throughput in TFLOP/s under the standard
 FLOP count (2*(3D+2Dv) per visible (query, key) pair per query head; causal
 with S1 = S2 counted as exactly half of S1*S2); the roofline entry of the
-MFMA-bound kernel pair from HIP events the library records around it inside
+dK/dV + dQ kernel pair from HIP events the library records around it inside
 the timed region; the standalone sfmg preprocess kernel's HBM bandwidth
-(its own timed launches; the default step forms sfmg inside the dQ kernel); the fp64 CPU oracle timed on a bounded sample of the same
+(its own timed launches); the fp64 CPU oracle timed on a bounded sample of the same
 workload; and `accuracy`: the library's gradients on that sample (made from
 the oracle forward's stored Y and lse) against the oracle's, every element,
 so that the speed figure comes with its parity error.
@@ -44,9 +47,19 @@ sys.path.insert(0, ROOT)
 METRIC = "FA-bwd TFLOP/s and % of MI355X bf16 MFMA peak (S=4096, D=128, GQA, causal)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
-# The MFMA-bound part of a step is the dK/dV kernel followed by the dQ kernel;
-# the library records HIP events around that pair on the launch stream.
-MAIN_KERNELS = "dkdv_kernel+dq_kernel"
+# The main part of a step is the dK/dV kernel and the dQ kernel; the library
+# records HIP events around that pair on the launch stream.  Which dQ kernel
+# runs is the plan's choice (fa_bwd_plan_dq_path).
+MAIN_KERNELS = {"stored_ds": "dkdv_kernel+dq_ds_kernel", "recompute": "dkdv_kernel+dq_kernel"}
+DQ_MODES = {
+    "stored_ds": "dK/dV kernel stores dS (bf16 tiles in the workspace), dQ = scale*dS*K by a GEMM kernel "
+                 "(no atomics, deterministic)",
+    "recompute": "separate dQ pass recomputing S and dP (no atomics, deterministic)",
+}
+SFMG_NOTE = {
+    "stored_ds": "standalone fa_bwd_sfmg entry point; the default step launches the same kernel first",
+    "recompute": "standalone fa_bwd_sfmg entry point; the step forms sfmg inside dq_kernel",
+}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -294,7 +307,7 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     torch.cuda.synchronize()
     pre_ms = p0.elapsed_time(p1) / pre_iters
     return dict(ms_per_step=ms_per_step, pair_ms=main_avg, pair_launches=len(main_ms), pre_ms=pre_ms,
-                pre_bytes=pre_bytes, settle_steps=settle_steps)
+                pre_bytes=pre_bytes, settle_steps=settle_steps, dq_path=plan.dq_path())
 
 
 FLOYD_WORKLOAD = "floyd"
@@ -503,10 +516,10 @@ def main():
             "Dv": cfg["Dv"], "mask_mode": cfg["mask_mode"], "win_left": cfg["win_left"],
             "win_right": cfg["win_right"], "global_batch": cfg.get("B", len(cfg.get("lengths", []))),
             "seq_len": cfg.get("S1", int(sum(cfg.get("lengths", [0])))), "parallelism": "single-gpu",
-            "algorithmic_gflop": round(flops / 1e9, 3), "dq_mode": "separate dQ pass (no atomics, deterministic)",
+            "algorithmic_gflop": round(flops / 1e9, 3), "dq_mode": DQ_MODES.get(m["dq_path"], m["dq_path"]),
         },
         "roofline": {
-            "bound": "mfma", "kernel": MAIN_KERNELS, "achieved": round(achieved, 2),
+            "bound": "mfma", "kernel": MAIN_KERNELS.get(m["dq_path"], m["dq_path"]), "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic, "avg_launch_ms": round(main_avg, 5), "launches_timed": m["pair_launches"],
         },
@@ -514,7 +527,7 @@ def main():
             "bound": "hbm", "kernel": "preprocess_kernel (sfmg)", "achieved": round(pre_gbs, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4),
             "bytes_per_launch": pre_bytes, "avg_launch_ms": round(pre_ms, 5),
-            "note": "standalone fa_bwd_sfmg entry point; the default step forms sfmg inside dq_kernel",
+            "note": SFMG_NOTE.get(m["dq_path"], "standalone fa_bwd_sfmg entry point"),
         },
         "configs": None,
         "floyd": None,
@@ -542,6 +555,7 @@ def main():
                 "pair_tflops": round(f / (r["pair_ms"] * 1e-3) / 1e12, 1),
                 "preprocess_gbs": round(r["pre_bytes"] / (r["pre_ms"] * 1e-3) / 1e9, 1),
                 "algorithmic_gflop": round(f / 1e9, 3),
+                "dq_path": r["dq_path"],
             }
         line["configs"] = rows
     if not args.no_floyd:

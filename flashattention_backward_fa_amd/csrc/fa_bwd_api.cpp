@@ -23,7 +23,7 @@ struct fa_bwd_plan_s {
   KernelArgs args;         // pointers left NULL; filled per run
   int64_t q_elems;         // elements of q (and of the fp32 dQ accumulator)
   int64_t lse_elems;       // elements of softmax_lse / sfmg
-  size_t off_dq_acc, off_sfmg, off_dk_acc, off_dv_acc, ws_bytes;
+  size_t off_dq_acc, off_sfmg, off_dk_acc, off_dv_acc, off_ds, ws_bytes;
   fabwd::Profiler* prof = nullptr;  // timing hook, off by default
 };
 
@@ -138,18 +138,31 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   else { a.win_left = d.win_left; a.win_right = d.win_right; }
   a.has_mask = (a.win_left >= 0 || a.win_right >= 0) ? 1 : 0;
 
-  // Kernel choice.  Default: the atomic-free pair (dK/dV kernel over key
-  // tiles, dQ kernel over query tiles); dQ is then bitwise repeatable.
-  // FA_BWD_VARIANT=0/1 selects the fp32-atomic dQ kernels instead (tuning,
-  // bf16 only).
+  // Kernel choice.  Both defaults are free of atomics and bitwise repeatable:
+  //  - dS-store pair (variant 4): the dK/dV kernel also stores dS (2 bytes per
+  //    visible query/key pair, in 32 x 32 tiles laid out by the maximum
+  //    lengths) and a GEMM kernel forms dQ = scale * dS K from it, reading dS
+  //    once instead of recomputing S and dP.  Taken for the dense layouts
+  //    while that dS workspace stays within kDsWorkspaceCap;
+  //  - recompute pair (variant 2): a query-tile-parallel dQ kernel recomputes
+  //    S and dP.  Taken for TND (its tile grid would be laid out by the
+  //    longest sequence) and for problems whose dS would exceed the cap.
+  // FA_BWD_VARIANT=2/4 forces one of them, 0/1 the fp32-atomic dQ kernels
+  // (tuning, bf16 only).
   const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
   const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
-  a.variant = 2;
-  if (const char* e = std::getenv("FA_BWD_VARIANT"); e && !a.f16) {
-    if (e[0] == '0') a.variant = 0;
-    if (e[0] == '1' && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
+  a.ds_nr = (int32_t)((S1 + 127) / 128);
+  a.ds_nks = (int32_t)(4 * ((S2 + 127) / 128));  // every slice of every 128-key tile
+  const double ds_bytes = (double)d.B * (double)N1 * (double)a.ds_nr * (double)a.ds_nks * 8192.0;
+  constexpr double kDsWorkspaceCap = 4.0 * 1024 * 1024 * 1024;
+  a.variant = (!tnd && ds_bytes <= kDsWorkspaceCap) ? 4 : 2;
+  if (const char* e = std::getenv("FA_BWD_VARIANT"); e) {
+    if (e[0] == '2') a.variant = 2;
+    if (e[0] == '0' && !a.f16) a.variant = 0;
+    if (e[0] == '1' && !a.f16 && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
+    if (e[0] == '4') a.variant = 4;
   }
-  if (d.flags & FA_FLAG_DETERMINISTIC) a.variant = 2;
+  if ((d.flags & FA_FLAG_DETERMINISTIC) && a.variant < 2) a.variant = 2;
   if (d.flags & FA_FLAG_FP32_OUT) a.variant = 3;  // fp32 debugging form: sfmg + two VALU kernels
   a.heads_per_job = a.G;
   a.q_splits = 1;
@@ -157,7 +170,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   a.k_part_stride = k_elems;
   a.v_part_stride = v_elems;
   if (a.variant == 1 && a.G > 1) a.heads_per_job = 1;
-  if (a.variant == 2) {
+  if (a.variant == 2 || a.variant == 4) {
     // Enough jobs to balance causal work over the CUs: split the query heads
     // of a GQA group, then the query range of a key tile, until there are at
     // least 2 jobs per CU of an MI355X (256 CUs); each split adds an fp32
@@ -190,12 +203,17 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     cur += align_up((size_t)p.q_elems * sizeof(float));
   }
   p.off_dk_acc = p.off_dv_acc = cur;
-  if (fabwd::split_heads(a) || (a.variant == 2 && a.n_partials > 1)) {
-    const size_t parts = a.variant == 2 ? (size_t)a.n_partials : 1;
+  const bool pair = a.variant == 2 || a.variant == 4;
+  if (fabwd::split_heads(a) || (pair && a.n_partials > 1)) {
+    const size_t parts = pair ? (size_t)a.n_partials : 1;
     p.off_dk_acc = cur;
     cur += align_up(parts * (size_t)k_elems * sizeof(float));
     p.off_dv_acc = cur;
     cur += align_up(parts * (size_t)v_elems * sizeof(float));
+  }
+  p.off_ds = cur;
+  if (a.variant == 4) {  // dS: 4 tiles of 32 x 32 two-byte elements per (128-row group, 32-key slice)
+    cur += align_up((size_t)d.B * (size_t)N1 * (size_t)a.ds_nr * (size_t)a.ds_nks * 8192u);
   }
   p.ws_bytes = cur;
   p.desc = d;
@@ -263,12 +281,24 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   if (a.variant < 2) a.dq_acc = reinterpret_cast<float*>(ws + plan->off_dq_acc);
   a.dk_acc = reinterpret_cast<float*>(ws + plan->off_dk_acc);
   a.dv_acc = reinterpret_cast<float*>(ws + plan->off_dv_acc);
+  a.ds = a.variant == 4 ? ws + plan->off_ds : nullptr;
 
   if (a.variant == 3) {
     if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_f32_debug(a, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    return FA_OK;
+  }
+  if (a.variant == 4) {
+    // sfmg -> dK/dV kernel (which also stores dS) -> dQ GEMM over the stored
+    // dS -> partial-sum reduce (when a key tile is split over jobs)
+    if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_dq_ds(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
     return FA_OK;
   }
   if (a.variant == 2) {
@@ -300,6 +330,17 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
   a.seqused_q = seqused_q; a.seqused_kv = seqused_kv;
   if (fabwd::launch_forward(a, attn_out, softmax_lse, stream) != 0) return FA_ERR_RUNTIME;
+  return FA_OK;
+}
+
+int fa_bwd_plan_dq_path(fa_bwd_plan plan, int* path) {
+  if (!plan || !path) return FA_ERR_NULLPTR;
+  switch (plan->args.variant) {
+    case 4: *path = FA_DQ_STORED_DS; break;
+    case 2: *path = FA_DQ_RECOMPUTE; break;
+    case 3: *path = FA_DQ_FP32_FORM; break;
+    default: *path = FA_DQ_ATOMIC; break;
+  }
   return FA_OK;
 }
 

@@ -106,12 +106,14 @@ __device__ __forceinline__ int swz(int r, int c) {
 // s1, s2: rows / keys that take part; s1a, s2a: rows / keys the sequence
 // holds (they differ only when seqused_q / seqused_kv are given).
 struct SeqBounds {
+  int b;  // sequence index
   int s1, s2, s1a, s2a;
   int64_t qbase, kbase, vbase, obase, lbase;
 };
 
 __device__ __forceinline__ SeqBounds seq_bounds(const KernelArgs& a, int b) {
   SeqBounds r;
+  r.b = b;
   if (a.varlen) {
     const int q0 = a.cu_q[b], k0 = a.cu_kv[b];
     r.s1 = a.cu_q[b + 1] - q0;
@@ -241,6 +243,15 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// The same with the non-temporal hint: for data read once (the stored dS), so
+// that it does not displace reused tiles from the caches.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(uniform_ptr(base)),
+               "s"(m0)
+               : "memory");
+}
+
 // Asynchronous copy of rows [0, ROWS) of a W-column block (columns col0 ..
 // col0+W-1 of the source rows) into a swizzled LDS block: each instruction
 // fills 1 KB of LDS, lane t writing bytes 16t..16t+15, so each lane loads the
@@ -327,6 +338,16 @@ __device__ __forceinline__ void padded_copy(uint32_t lds_tile, const void* g, in
   }
 }
 
+// DS form: whether query block qb (32 rows) sees a key of 32-key slice ks.
+// Only such (block, slice) tiles of dS are stored and read back; the others
+// are zero.
+__device__ __forceinline__ bool ds_tile_visible(int qb, int ks, int s1, int s2, int off, int wl, int wr) {
+  if (ks * 32 >= s2) return false;
+  const fa_sched::Span blks =
+      fa_sched::blocks_covering(fa_sched::rows_seeing(s1, ks * 32, min(ks * 32 + 32, s2), off, wl, wr), 32);
+  return qb >= blks.lo && qb < blks.hi;
+}
+
 // ------------------------------------------------------------------ dK / dV
 
 // QG query groups of NWG wavefronts share one tile of NWG*KPW keys; wavefront
@@ -336,10 +357,13 @@ __device__ __forceinline__ void padded_copy(uint32_t lds_tile, const void* g, in
 // only); Q/dY tiles are swizzled (row reads and transposing reads).
 // Instantiated with NWG = 4, KPW = 32: 8 wavefronts in two query groups (two
 // per SIMD) at D <= 128, 4 wavefronts in one group at D = 192.
-template <int HD, int HDV, int KPW, int NWG, int QG, bool F16>
+// DS: also store each (32-row block, 32-key slice) tile of dS for the dQ GEMM
+// (dq_ds_kernel), as row-major [32 keys][128 rows] tiles of a 128-row group.
+template <int HD, int HDV, int KPW, int NWG, int QG, bool F16, bool DS>
 __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   constexpr int BC = NWG * KPW;       // keys per workgroup
   constexpr int NKB = KPW / 32;       // 32-key blocks per wavefront
+  static_assert(!DS || NKB == 1, "the dS stores assume one 32-key slice per wavefront");
   constexpr int BR = 32;              // query rows per step and group
   constexpr int KP = HD + 8;          // padded pitches of the K and V tiles
   constexpr int VP = HDV + 8;
@@ -463,6 +487,35 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   const uint32_t k_lane = lds_addr(Ks) + ((kw0 + l32) * KP + 8 * hi) * 2;
   const uint32_t v_lane = lds_addr(Vs) + ((kw0 + l32) * VP + 8 * hi) * 2;
 
+  // DS form: the dS of the last item, kept until the next step has passed its
+  // barrier and issued its prefetch, so that the stores have a whole step to
+  // drain before the next s_waitcnt vmcnt(0), which also counts them.
+  bf16x8 ds_keep[NKB][2];
+  int ds_i0 = -1, ds_n1 = 0;
+  // Tile (query block qb, 32-key slice ks) of dS is the register image of the
+  // wavefront that formed it: 2 halves x 64 lanes x 8 elements, half h of lane
+  // p holding rows 16h + 8*(e/4) + 4*(p/32) + e%4 (e = 0..7) of key p%32.
+  // Each half is one 1 KB store instruction.  The 4 tiles of a 128-row query
+  // group and 32-key slice are consecutive ([B][N1][ds_nr][ds_nks][4][1024]).
+  // (The row-group guard keeps the stores inside the workspace even for a
+  // sequence longer than the maximum length the plan was made for.)
+  auto ds_flush = [&]() {
+    if (DS && ds_i0 >= 0 && (ds_i0 >> 7) < a.ds_nr &&
+        ds_tile_visible(ds_i0 >> 5, (j0 + kw0) >> 5, s1, s2, off, wl, wr)) {
+      const int64_t tile0 =
+          ((((int64_t)sb.b * a.N1 + ds_n1) * a.ds_nr + (ds_i0 >> 7)) * a.ds_nks + ((j0 + kw0) >> 5)) * 4 +
+          ((ds_i0 >> 5) & 3);
+      bf16* dsg = static_cast<bf16*>(a.ds) + tile0 * 1024 + lane * 8;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          __builtin_nontemporal_store(ds_keep[kb][h], reinterpret_cast<bf16x8*>(dsg + kb * 4096 + h * 512));
+      }
+    }
+    ds_i0 = -1;
+  };
+
   floatx16 sacc[NKB], pacc[NKB];
   // S = Q K^T and dP = dY V^T for this wavefront's KPW keys
   // Each run of MFMAs raises the wavefront's issue priority, so that on a SIMD
@@ -498,7 +551,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
   // P, dS (masked when the tile is partial), then dV += P^T dY and dK += dS^T Q
-  auto phase_b = [&](int buf, int i0) {
+  auto phase_b = [&](int buf, int i0, int n1) {
     // P = exp(S*scale - lse) (masked), dS = P (dP - sfmg), packed as bf16 A operands.
     // A tile that every (row, key) pair sees takes the unmasked path; otherwise
     // row i is kept iff it lies in [vis_lo, vis_hi] of the lane's key (one
@@ -546,6 +599,16 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
       }
     }
 
+    if constexpr (DS) {  // stored at the start of the next step (ds_flush)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        ds_keep[kb][0] = da[kb][0];
+        ds_keep[kb][1] = da[kb][1];
+      }
+      ds_i0 = i0;
+      ds_n1 = n1;
+    }
+
     // dV += P^T dY, dK += dS^T Q; one transposing read serves all key blocks
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -589,13 +652,15 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
     fetch(cf, t + QG, buf ^ 1);
     step_cursor(cf, QG);
+    if constexpr (DS) ds_flush();
     if (QG == 1 || t < T) {
       phase_a(buf);
-      phase_b(buf, i0);
+      phase_b(buf, i0, n2 * a.G + g0 + cc.h);
     }
     step_cursor(cc, QG);
   };
   for (int it = 0; it < iters; ++it) step(it, it & 1);
+  if constexpr (DS) ds_flush();
   wait_vmem();  // no copy may still be landing when LDS is reused below
 
   // ---- add the other groups' dK/dV into group 0, 32 columns at a time
@@ -836,6 +901,150 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   }
 }
 
+// ------------------------------------------------------------------ dQ from stored dS
+
+// dQ = scale * dS K with dS read back from the tiles the dK/dV kernel stored
+// (DS form): a GEMM per (sequence, query head, 128-row group) over the 32-key
+// slices the group sees, bound by the HBM reads of dS.  One workgroup = 4
+// wavefronts owning 32 query rows (one stored query block) each; a step
+// brings 64 keys: the K rows (swizzled tile) and the 8 dS tiles of the two
+// slices (16 KB, contiguous in the workspace) go straight to LDS,
+// double-buffered.  Both MFMA operands are transposing reads with the same key
+// order inside each 16-key chunk: B = K through SwzTile, A = dS through
+// per-lane addresses into the stored register images (below).
+constexpr int DQS_BK = 64;  // keys per step: two 32-key slices
+
+// LDS placement of a stored dS tile: within each 1 KB half h, the 16-byte
+// chunk c (the lane of the producing wavefront) sits at chunk
+// c ^ 4*(2h + bit 5 of c), which makes the transposing A reads below free of
+// bank conflicts (an involution: the XOR leaves bit 5 alone).
+__device__ __forceinline__ int ds_chunk_slot(int c, int h) { return c ^ (4 * ((2 * h + ((c >> 5) & 1)) & 3)); }
+
+template <int HD, bool F16>
+__global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
+  constexpr int NBK = HD / 32;
+  constexpr int KTB = DQS_BK * HD * 2;  // bytes of one K tile buffer
+  constexpr int STB = 16384;            // bytes of one dS buffer: 2 slices x 4 query blocks x 2 KB
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][DQS_BK * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Ss[2][STB / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // job -> (query group, query head, sequence), the longest groups first
+  const int per_tile = a.N1 * a.B;
+  const int ntiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
+  const int tile = ntiles - 1 - (int)(blockIdx.x / per_tile);
+  const int rem = blockIdx.x % per_tile;
+  const int n1 = rem % a.N1;
+  const int b = rem / a.N1;
+  const int n2 = n1 / a.G;
+
+  const SeqBounds sb = seq_bounds(a, b);
+  const int s1 = sb.s1, s2 = sb.s2;
+  const int i0 = tile * DQ_BQ;
+  if (i0 >= sb.s1a) return;  // no rows of this sequence here
+  const int off = s2 - s1;
+  const int wl = a.win_left, wr = a.win_right;
+  const int qb = tile * 4 + wave;  // this wavefront's 32-row query block
+
+  const bf16* __restrict__ Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
+  const bf16* __restrict__ Sg =
+      static_cast<const bf16*>(a.ds) + (((int64_t)b * a.N1 + n1) * a.ds_nr + tile) * a.ds_nks * 4096;
+
+  // 32-key slices that any row of [i0, i0 + 128) sees (slices past the
+  // workspace's last one, possible only with a sequence longer than the
+  // planned maximum, are left out)
+  const fa_sched::Span ksl = i0 < s1 ? fa_sched::blocks_covering(
+                                            fa_sched::keys_seen(s2, i0, min(i0 + DQ_BQ, s1), off, wl, wr), 32)
+                                      : fa_sched::Span{0, 0};
+  const int ks_end = min(ksl.hi, a.ds_nks);
+  const int nsteps = (ks_end - ksl.lo + 1) / 2;
+
+  TileCopy<HD, DQS_BK, 4> kcp;
+  kcp.init(wave, lane, (int)a.k_ss * 2);
+  // dS copy: instruction u (wavefront u % 4) fills LDS bytes [1024u, 1024u + 1024)
+  // = half u % 2 of tile u / 2; lane t brings the chunk that the placement puts
+  // in slot t.  A lone last slice re-reads itself for the second one.
+  const uint32_t s_voff = (uint32_t)ds_chunk_slot(lane, wave & 1) * 16;
+  auto fetch = [&](int st, int buf) {
+    const int ks = ksl.lo + 2 * st;
+    kcp.issue(lds_addr(Ks) + buf * KTB, Kg + (int64_t)ks * 32 * a.k_ss, s2 - ks * 32, wave, lane);
+    const bf16* src = Sg + (int64_t)ks * 4096;
+    const bool two = ks + 1 < ks_end;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int u = wave + 4 * x;  // half u % 2 == wave % 2 of tile u / 2
+      const int usrc = (u >= 8 && !two) ? u - 8 : u;
+      dma16_nt(src + usrc * 512, s_voff, lds_addr(Ss) + buf * STB + u * 1024);
+    }
+  };
+  if (nsteps > 0) fetch(0, 0);
+
+  SwzTile<HD, DQS_BK> kadr;
+  kadr.init(lds_addr(Ks), lane);
+  // A operand: lane i of a 16-lane group gets, as element e of a transposing
+  // read, element i % 4 of the 8 bytes that lane 4e + i/4 of its group loads.
+  // For query row m = 16*(g % 2) + i (g = lane / 16) and keys
+  // 16kc + 8s + 4*(g / 2) + e, lane L = 4e + q loads rows 16*(g % 2) + 4q + 0..3
+  // of key 16kc + 8s + 4*(g / 2) + e: producer lane 32*(q % 2) + key, half
+  // g % 2, elements 4*(q / 2) + 0..3.
+  uint32_t a_base[2];
+  {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3, h = g & 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 32 * (q & 1) + 8 * s + 4 * (g >> 1) + e;  // chunk at kc = 0
+      a_base[s] = lds_addr(Ss) + wave * 2048 + h * 1024 + ds_chunk_slot(c, h) * 16 + (q >> 1) * 8;
+    }
+  }
+
+  // The tile of (qb, slice ks) was stored iff some row of qb sees a key of the
+  // slice (the dK/dV kernel runs every such pair); otherwise it adds nothing.
+  auto stored = [&](int ks) { return ds_tile_visible(qb, ks, s1, s2, off, wl, wr); };
+
+  floatx16 dq[NBK];
+#pragma unroll
+  for (int nb = 0; nb < NBK; ++nb) dq[nb] = floatx16{};
+
+  auto step = [&](int st, int buf) {
+    wait_vmem();    // this wavefront's copies of step st landed
+    lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
+    if (st + 1 < nsteps) fetch(st + 1, buf ^ 1);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ks = ksl.lo + 2 * st + sl;
+      if (ks < ks_end && stored(ks)) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t ao = buf * STB + sl * 8192 + c * 256;  // slice sl, chunk bit 4 = c
+          const bf16x8 da = join(lds_load_tr(a_base[0] + ao), lds_load_tr(a_base[1] + ao));
+          const int kc = 2 * sl + c;
+#pragma unroll
+          for (int nb = 0; nb < NBK; ++nb) {
+            const bf16x8 kb = join(lds_load_tr(kadr.tr_read(kc, 0, nb, buf * KTB)),
+                                   lds_load_tr(kadr.tr_read(kc, 1, nb, buf * KTB)));
+            dq[nb] = mfma32<F16>(da, kb, dq[nb]);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+  };
+  for (int st = 0; st < nsteps; ++st) step(st, st & 1);
+
+  // dq = bf16(scale * acc): lane holds head-dim column nb*32 + l32 of 16 rows
+  bf16* __restrict__ dQg = static_cast<bf16*>(a.dq) + sb.qbase + (int64_t)n1 * a.q_sn;
+#pragma unroll
+  for (int rg = 0; rg < 16; ++rg) {
+    const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+    if (i < sb.s1a) {  // rows past the used ones hold zeros
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ partial sums
 
 // dk = bf16(sum over parts) and dv likewise in one launch: blocks below
@@ -890,13 +1099,22 @@ int det_keys_per_wave(int D) { (void)D; return 32; }
 
 namespace {
 
-template <bool F16>
+template <bool F16, bool DS>
 int launch_dkdv_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
-  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 4, 2, F16>, grid, dim3(512), s, a);
-  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 4, 2, F16>, grid, dim3(512), s, a);
-  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 4, 2, F16>, grid, dim3(512), s, a);
-  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 4, 1, F16>, grid, dim3(256), s, a);
-  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 4, 1, F16>, grid, dim3(256), s, a);
+  if (a.D == 64 && a.Dv == 64) return launch(dkdv_kernel<64, 64, 32, 4, 2, F16, DS>, grid, dim3(512), s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(dkdv_kernel<128, 64, 32, 4, 2, F16, DS>, grid, dim3(512), s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(dkdv_kernel<128, 128, 32, 4, 2, F16, DS>, grid, dim3(512), s, a);
+  if (a.D == 192 && a.Dv == 64) return launch(dkdv_kernel<192, 64, 32, 4, 1, F16, DS>, grid, dim3(256), s, a);
+  if (a.D == 192 && a.Dv == 128) return launch(dkdv_kernel<192, 128, 32, 4, 1, F16, DS>, grid, dim3(256), s, a);
+  return (int)hipErrorInvalidValue;
+}
+
+template <bool F16>
+int launch_dq_ds_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (a.D == 64) return launch(dq_ds_kernel<64, F16>, grid, block, s, a);
+  if (a.D == 128) return launch(dq_ds_kernel<128, F16>, grid, block, s, a);
+  if (a.D == 192) return launch(dq_ds_kernel<192, F16>, grid, block, s, a);
   return (int)hipErrorInvalidValue;
 }
 
@@ -920,7 +1138,8 @@ int launch_dkdv(const KernelArgs& a, void* stream) {
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)blocks);
-  return a.f16 ? launch_dkdv_t<true>(a, grid, s) : launch_dkdv_t<false>(a, grid, s);
+  if (a.variant == 4) return a.f16 ? launch_dkdv_t<true, true>(a, grid, s) : launch_dkdv_t<false, true>(a, grid, s);
+  return a.f16 ? launch_dkdv_t<true, false>(a, grid, s) : launch_dkdv_t<false, false>(a, grid, s);
 }
 
 int launch_dq(const KernelArgs& a, void* stream) {
@@ -931,6 +1150,16 @@ int launch_dq(const KernelArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)blocks);
   return a.f16 ? launch_dq_t<true>(a, grid, s) : launch_dq_t<false>(a, grid, s);
+}
+
+int launch_dq_ds(const KernelArgs& a, void* stream) {
+  const int64_t tiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
+  const int64_t blocks = tiles * a.N1 * a.B;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks);
+  return a.f16 ? launch_dq_ds_t<true>(a, grid, s) : launch_dq_ds_t<false>(a, grid, s);
 }
 
 int launch_reduce_parts(const KernelArgs& a, void* stream) {

@@ -57,12 +57,20 @@ struct KernelArgs {
 
   int32_t variant;        // 0 = 4-wavefront atomic kernel, 1 = 8-wavefront atomic kernel,
                           // 2 = atomic-free pair (dK/dV kernel + dQ kernel),
-                          // 3 = fp32 debugging form (fp32 outputs)
+                          // 3 = fp32 debugging form (fp32 outputs),
+                          // 4 = dS-store pair (dK/dV kernel storing dS + dQ GEMM)
   int32_t heads_per_job;  // query heads of a GQA group handled by one workgroup
   int32_t q_splits;       // query-range splits of one key tile (atomic-free pair only)
   int32_t n_partials;     // fp32 dK/dV partial sums per key tile (atomic-free pair only)
   int64_t k_part_stride;  // elements between dK partials (= elements of k)
   int64_t v_part_stride;  // elements between dV partials (= elements of v)
+
+  // dS-store form (variant 4): the dK/dV kernel stores dS, bf16 (or fp16), as
+  // [B][N1][ds_nr][ds_nks] tiles of 32 keys x 128 query rows (row-major, keys
+  // as rows); a GEMM kernel then forms dQ = scale * dS K from them.
+  void* ds;
+  int32_t ds_nr;          // 128-row query groups per sequence (ceil(S1 / 128))
+  int32_t ds_nks;         // 32-key slices per sequence (4 * ceil(S2 / 128): whole key tiles)
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups
@@ -79,6 +87,7 @@ bool det_instantiated(int D, int Dv);
 int det_keys_per_wave(int D);
 int launch_dkdv(const KernelArgs& a, void* stream);
 int launch_dq(const KernelArgs& a, void* stream);
+int launch_dq_ds(const KernelArgs& a, void* stream);
 int launch_reduce_parts(const KernelArgs& a, void* stream);
 int launch_dq_finalize(const KernelArgs& a, void* stream);
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream);

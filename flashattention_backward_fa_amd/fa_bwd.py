@@ -35,7 +35,10 @@ FLAG_FP32_OUT = 0x2
 DTYPE_BF16 = 0
 DTYPE_FP16 = 1
 
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_profile_enable",
+# fa_bwd_plan_dq_path values
+DQ_PATHS = {0: "recompute", 1: "stored_ds", 2: "atomic", 3: "fp32_form"}
+
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_plan_dq_path", "fa_bwd_profile_enable",
             "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version",
             "fa_floyd_workspace_size", "fa_floyd_bwd_run", "fa_floyd_bwd_run_timed", "fa_floyd_fwd_run")
 
@@ -113,6 +116,8 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd_sfmg.restype = ctypes.c_int
     lib.fa_fwd_run.argtypes = [vp] * 11
     lib.fa_fwd_run.restype = ctypes.c_int
+    lib.fa_bwd_plan_dq_path.argtypes = [vp, ctypes.POINTER(ctypes.c_int)]
+    lib.fa_bwd_plan_dq_path.restype = ctypes.c_int
     lib.fa_bwd_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.fa_bwd_profile_enable.restype = ctypes.c_int
     lib.fa_bwd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
@@ -196,6 +201,14 @@ class Plan:
         st = self._lib.fa_fwd_run(self.handle, q, k, v, cu_q, cu_kv, seqused_q, seqused_kv, attn_out, lse, stream)
         if st != FA_OK:
             raise FaBwdError(st, "fa_fwd_run")
+
+    def dq_path(self):
+        """One of DQ_PATHS' keys: how this plan forms dQ."""
+        out = ctypes.c_int()
+        st = self._lib.fa_bwd_plan_dq_path(self.handle, ctypes.byref(out))
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_plan_dq_path")
+        return DQ_PATHS[out.value]
 
     def profile_enable(self, slots):
         st = self._lib.fa_bwd_profile_enable(self.handle, int(slots))

@@ -81,7 +81,7 @@ enum { FA_LAYOUT_BSND = 0, FA_LAYOUT_BNSD = 1, FA_LAYOUT_TND = 2 };
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 };
 
 /* flags */
-#define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable results; the default path already is */
+#define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable results; the default paths already are */
 /* fp32 debugging form (not on the page; it checks the arithmetic of section 一
  * at fp32 accuracy): dq, dk, dv are float32 arrays with the shapes and layouts
  * of q, k, v; P and dS are kept in fp32 and every product is an fp32 FMA, so
@@ -116,7 +116,11 @@ typedef struct fa_bwd_desc {
 /* Validate `desc` (all rules of section 四 4.6 that this library enforces) and
  * build a plan.  On success *plan receives a new plan and *workspace_bytes the
  * device workspace size fa_bwd_run needs.  Pure host code: no HIP call, no
- * device memory.  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
+ * device memory.  For BSND/BNSD the workspace holds dS (the page's
+ * dS = P (.) (dP - sfmg), rounded to the element type) for the dQ product,
+ * about 2 * B * N1 * S1 * S2 bytes; where that would exceed 4 GiB, and for
+ * TND, the plan recomputes S and dP for dQ instead and the workspace is small
+ * (sfmg and fp32 dK/dV partial sums).  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
  * FA_ERR_PARAM_INVALID, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED; *plan is left NULL. */
 int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_bytes);
 
@@ -176,8 +180,22 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,
                const int32_t* seqused_q, const int32_t* seqused_kv,
                void* attn_out, float* softmax_lse, void* stream);
 
+/* How a plan forms dQ (fa_bwd_create picks it; see there).  Every path but
+ * FA_DQ_ATOMIC is bitwise repeatable.
+ *   FA_DQ_RECOMPUTE : a query-tile-parallel kernel recomputes S and dP and
+ *                     writes dQ = scale * dS K once (TND; very long BSND/BNSD)
+ *   FA_DQ_STORED_DS : the dK/dV kernel also stores dS (element type) in the
+ *                     workspace and a GEMM kernel reads it back (BSND/BNSD)
+ *   FA_DQ_ATOMIC    : fp32 atomic adds into the workspace (tuning only)
+ *   FA_DQ_FP32_FORM : the fp32 debugging form (FA_FLAG_FP32_OUT)
+ * Writes the path to *path.  Errors: FA_ERR_NULLPTR. */
+enum { FA_DQ_RECOMPUTE = 0, FA_DQ_STORED_DS = 1, FA_DQ_ATOMIC = 2, FA_DQ_FP32_FORM = 3 };
+int fa_bwd_plan_dq_path(fa_bwd_plan plan, int* path);
+
 /* Timing hook.  With slots > 0, every later fa_bwd_run records one pair of
- * HIP events on its stream immediately before and after the main kernel,
+ * HIP events on its stream immediately before and after the main kernels
+ * (the dK/dV kernel and the dQ kernel, or the single kernel of the other
+ * forms),
  * into a ring of `slots` pairs owned by the plan (slots = 0 frees them and
  * stops recording).  Errors: FA_ERR_NULLPTR, FA_ERR_PARAM_INVALID
  * (slots < 0 or > 65536), FA_ERR_RUNTIME (event creation failed). */

@@ -62,17 +62,28 @@ def create(lib, **kw):
 
 def test_valid_problem_and_workspace_size(lib):
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # Enough key tiles x heads for every CU: sfmg only (dQ is written once by
-    # its own kernel, dK/dV by the key-tile kernel).
+    # dS tiles of the dense layouts: 2 bytes per (row, key) of 128-row groups
+    # by whole 128-key tiles, per sequence and query head
+    ds = lambda B, N1, S1, S2: B * N1 * ((S1 + 127) // 128) * 128 * ((S2 + 127) // 128) * 128 * 2  # noqa: E731
+    # Enough key tiles x heads for every CU: sfmg and dS (dK/dV written by the
+    # key-tile kernel, dQ by the GEMM over the stored dS).
     st, ws = create(lib, B=64, N1=8, N2=8, S1=256, S2=256)
     assert st == fb.FA_OK
-    assert ws == rnd(64 * 8 * 256 * 4)
+    assert ws == rnd(64 * 8 * 256 * 4) + rnd(ds(64, 8, 256, 256))
     # A small GQA problem is split over query heads (4) and query ranges (4):
     # 16 fp32 partial sums of dK and of dV per key.
     st, ws = create(lib)
     assert st == fb.FA_OK
     lse, k_elems = 2 * 8 * 128, 2 * 128 * 2 * 128
-    assert ws == rnd(lse * 4) + 2 * rnd(16 * k_elems * 4)
+    assert ws == rnd(lse * 4) + 2 * rnd(16 * k_elems * 4) + rnd(ds(2, 8, 128, 128))
+    # ragged lengths round up to whole tiles
+    st, ws = create(lib, B=64, N1=8, N2=8, S1=200, S2=300)
+    assert st == fb.FA_OK and ws == rnd(64 * 8 * 200 * 4) + rnd(ds(64, 8, 200, 300))
+    # past 4 GiB of dS the plan recomputes S and dP for dQ: sfmg only
+    st, ws = create(lib, B=1, N1=32, N2=32, S1=16384, S2=8192)  # 8 GiB of dS
+    assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4)
+    st, ws = create(lib, B=1, N1=32, N2=32, S1=8192, S2=8192)   # exactly 4 GiB
+    assert st == fb.FA_OK and ws == rnd(32 * 8192 * 4) + rnd(ds(1, 32, 8192, 8192))
     # the fp32 debugging form needs sfmg only
     st, ws = create(lib, flags=fb.FLAG_FP32_OUT)
     assert st == fb.FA_OK
@@ -80,6 +91,48 @@ def test_valid_problem_and_workspace_size(lib):
     # fp16 elements (the page's second binary) plan exactly like bf16
     assert create(lib, dtype=fb.DTYPE_FP16) == create(lib, dtype=fb.DTYPE_BF16)
     assert create(lib, dtype=fb.DTYPE_FP16, flags=fb.FLAG_FP32_OUT)[0] == fb.FA_OK
+
+
+def dq_path(lib, **kw):
+    base = dict(layout="BSND", B=2, N1=8, N2=2, S1=128, S2=128, D=128, Dv=128)
+    base.update(kw)
+    d = fb.make_desc(**base)
+    h, ws, out = ctypes.c_void_p(), ctypes.c_size_t(), ctypes.c_int(-1)
+    assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_OK
+    try:
+        assert lib.fa_bwd_plan_dq_path(h, ctypes.byref(out)) == fb.FA_OK
+    finally:
+        lib.fa_bwd_destroy(h)
+    return fb.DQ_PATHS[out.value]
+
+
+def test_plan_dq_path(lib, monkeypatch):
+    assert dq_path(lib) == "stored_ds"
+    assert dq_path(lib, layout="BNSD", mask_mode=1) == "stored_ds"
+    assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "stored_ds"
+    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "recompute"
+    assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "recompute"  # dS past 4 GiB
+    assert dq_path(lib, flags=fb.FLAG_FP32_OUT) == "fp32_form"
+    monkeypatch.setenv("FA_BWD_VARIANT", "2")
+    assert dq_path(lib) == "recompute"
+    monkeypatch.setenv("FA_BWD_VARIANT", "4")
+    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "stored_ds"
+    monkeypatch.setenv("FA_BWD_VARIANT", "1")
+    assert dq_path(lib) == "atomic"
+    assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "recompute"
+    out = ctypes.c_int()
+    assert lib.fa_bwd_plan_dq_path(None, ctypes.byref(out)) == fb.FA_ERR_NULLPTR
+
+
+def test_tnd_plans_the_recompute_pair(lib):
+    """TND keeps the dQ pass that recomputes S and dP: no dS in the workspace."""
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    st, ws = create(lib, layout="TND", B=4, N1=8, N2=8, S1=1024, S2=1024, T1=4096, T2=4096)
+    assert st == fb.FA_OK
+    # sfmg, then 2 query-range partial sums of dK and dV (8 x 4 key tiles x 8
+    # heads x 2 splits reach 512 jobs)
+    k_elems = 4096 * 8 * 128
+    assert ws == rnd(8 * 4096 * 4) + 2 * rnd(2 * k_elems * 4)
 
 
 @pytest.mark.parametrize("kw,code", [

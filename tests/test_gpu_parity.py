@@ -252,3 +252,37 @@ def test_default_path_is_bitwise_repeatable():
     b = gpu_backward(cfg, x, Yst, lst, deterministic=True)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("variant", ["2", "4"])
+@pytest.mark.parametrize("name", sorted(EDGE_CASES))
+def test_both_pairs_parity(variant, name):
+    """Both atomic-free pairs on every edge case, whatever the plan would pick:
+    FA_BWD_VARIANT=2 (a dQ pass recomputing S and dP, the default for TND) and
+    FA_BWD_VARIANT=4 (the dK/dV kernel stores dS and a GEMM kernel forms dQ
+    from it, the default for BSND/BNSD), against the oracle, every element."""
+    cfg = EDGE_CASES[name]
+    say(f"[parity] variant {variant}: {name}")
+    x = case_inputs(cfg, seed=sorted(EDGE_CASES).index(name))
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    with _env(FA_BWD_VARIANT=variant):
+        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+    qe, ke = empty_rows(cfg, x, gq.shape, gk.shape)
+    assert not np.any(gq[qe]) and not np.any(gk[ke]) and not np.any(gv[ke])
+
+
+@pytest.mark.parametrize("variant", ["2", "4"])
+@pytest.mark.parametrize("split", ["1,1", "2,3", "1,5"])
+def test_both_pairs_split_partials_parity(variant, split):
+    """Both pairs with dK/dV split over query heads and query ranges."""
+    cfg = EDGE_CASES["bsnd_causal_gqa4_ragged"]
+    say(f"[parity] variant {variant}, split {split}")
+    x = case_inputs(cfg, seed=sorted(EDGE_CASES).index("bsnd_causal_gqa4_ragged"))
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    with _env(FA_BWD_VARIANT=variant, FA_BWD_SPLIT=split):
+        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+

@@ -1,5 +1,7 @@
-// gfx950 (MI355X) FlashAttention backward, atomic-free path: one kernel for
-// dK/dV (key tiles in parallel) and one for dQ (query tiles in parallel).
+// gfx950 (MI355X) FlashAttention backward, atomic-free paths: one kernel for
+// dK/dV (key tiles in parallel) and, for dQ (query tiles in parallel), either
+// a GEMM over the dS that the dK/dV kernel stored (dq_ds_kernel, the default
+// for the dense layouts) or a pass that recomputes S and dP (dq_kernel).
 //
 // Formulas: page "CANN ops-transformer FlashAttnGrad 算子详解", section 一
 // (P = exp(scale*QK^T - softmax_lse), dV = P^T dY, dP = dY V^T,
@@ -7,8 +9,9 @@
 // dK = scale*dS^T Q).  The page's own kernel reduces dQ across key tiles with
 // atomic adds into an fp32 workspace (section 五 5.2).  On MI355X fp32
 // atomics reach about 1.35 TB/s against about 7.5 TB/s for plain stores, so
-// here dQ gets its own query-tile-parallel pass that recomputes S and dP
-// (two extra GEMMs) and writes every dQ element once; results are bitwise
+// here dQ gets its own query-tile-parallel pass that writes every dQ element
+// once: from dS stored by the dK/dV kernel (2 bytes per pair written and read
+// back), or by recomputing S and dP (two extra GEMMs); results are bitwise
 // repeatable.
 //
 // dK/dV kernel: one workgroup owns a 128-key tile of one (sequence, key/value

@@ -8,6 +8,7 @@
 
 #include "fa_bwd.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -140,22 +141,33 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
 
   // Kernel choice.  Both defaults are free of atomics and bitwise repeatable:
   //  - dS-store pair (variant 4): the dK/dV kernel also stores dS (2 bytes per
-  //    visible query/key pair, in 32 x 32 tiles laid out by the maximum
-  //    lengths) and a GEMM kernel forms dQ = scale * dS K from it, reading dS
-  //    once instead of recomputing S and dP.  Taken for the dense layouts
-  //    while that dS workspace stays within kDsWorkspaceCap;
+  //    query/key pair of every 32 x 32 tile a 128-row query group sees) and a
+  //    GEMM kernel forms dQ = scale * dS K from it, reading dS once instead of
+  //    recomputing S and dP.  Taken while that dS workspace stays within
+  //    kDsWorkspaceCap;
   //  - recompute pair (variant 2): a query-tile-parallel dQ kernel recomputes
-  //    S and dP.  Taken for TND (its tile grid would be laid out by the
-  //    longest sequence) and for problems whose dS would exceed the cap.
+  //    S and dP.  Taken for problems whose dS would exceed the cap.
   // FA_BWD_VARIANT=2/4 forces one of them, 0/1 the fp32-atomic dQ kernels
   // (tuning, bf16 only).
   const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
   const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
-  a.ds_nr = (int32_t)((S1 + 127) / 128);
-  a.ds_nks = (int32_t)(4 * ((S2 + 127) / 128));  // every slice of every 128-key tile
-  const double ds_bytes = (double)d.B * (double)N1 * (double)a.ds_nr * (double)a.ds_nks * 8192.0;
+  // dS band: a 128-row group sees at most 128 + left + right keys under a
+  // two-sided window, i.e. ceil((128 + left + right) / 32) + 1 slices of 32
+  // (one more for misalignment); otherwise up to every slice of the longest
+  // key sequence.
+  {
+    const int64_t all = (S2 + 31) / 32;
+    int64_t w = all;
+    if (a.win_left >= 0 && a.win_right >= 0)
+      w = std::min<int64_t>(all, (128 + (int64_t)a.win_left + a.win_right + 31) / 32 + 1);
+    a.ds_w = (int32_t)std::max<int64_t>(w, 1);
+    a.ds_nr = (int32_t)((S1 + 127) / 128);
+    // TND group indices cu_q[b] / 128 + b + R stay below T1 / 128 + B + 1
+    a.ds_groups = tnd ? d.T1 / 128 + d.B + 1 : (int64_t)d.B * a.ds_nr;
+  }
+  const double ds_bytes = (double)a.ds_groups * (double)N1 * (double)a.ds_w * 8192.0;
   constexpr double kDsWorkspaceCap = 4.0 * 1024 * 1024 * 1024;
-  a.variant = (!tnd && ds_bytes <= kDsWorkspaceCap) ? 4 : 2;
+  a.variant = ds_bytes <= kDsWorkspaceCap ? 4 : 2;
   if (const char* e = std::getenv("FA_BWD_VARIANT"); e) {
     if (e[0] == '2') a.variant = 2;
     if (e[0] == '0' && !a.f16) a.variant = 0;
@@ -212,8 +224,8 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     cur += align_up(parts * (size_t)v_elems * sizeof(float));
   }
   p.off_ds = cur;
-  if (a.variant == 4) {  // dS: 4 tiles of 32 x 32 two-byte elements per (128-row group, 32-key slice)
-    cur += align_up((size_t)d.B * (size_t)N1 * (size_t)a.ds_nr * (size_t)a.ds_nks * 8192u);
+  if (a.variant == 4) {  // dS: 4 tiles of 32 x 32 two-byte elements per (group, head, slot)
+    cur += align_up((size_t)a.ds_groups * (size_t)N1 * (size_t)a.ds_w * 8192u);
   }
   p.ws_bytes = cur;
   p.desc = d;

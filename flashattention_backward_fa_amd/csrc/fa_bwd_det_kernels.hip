@@ -351,6 +351,15 @@ __device__ __forceinline__ bool ds_tile_visible(int qb, int ks, int s1, int s2, 
   return qb >= blks.lo && qb < blks.hi;
 }
 
+// DS form: workspace group of the 128-row query group R of a sequence, and
+// the first 32-key slice that group sees (the origin of its band of slots).
+__device__ __forceinline__ int64_t ds_group(const KernelArgs& a, const SeqBounds& sb, int R) {
+  return a.varlen ? (sb.lbase >> 7) + sb.b + R : (int64_t)sb.b * a.ds_nr + R;
+}
+__device__ __forceinline__ int ds_band_lo(int R, int s1, int s2, int off, int wl, int wr) {
+  return fa_sched::blocks_covering(fa_sched::keys_seen(s2, R * 128, min(R * 128 + 128, s1), off, wl, wr), 32).lo;
+}
+
 // ------------------------------------------------------------------ dK / dV
 
 // QG query groups of NWG wavefronts share one tile of NWG*KPW keys; wavefront
@@ -499,21 +508,24 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   // wavefront that formed it: 2 halves x 64 lanes x 8 elements, half h of lane
   // p holding rows 16h + 8*(e/4) + 4*(p/32) + e%4 (e = 0..7) of key p%32.
   // Each half is one 1 KB store instruction.  The 4 tiles of a 128-row query
-  // group and 32-key slice are consecutive ([B][N1][ds_nr][ds_nks][4][1024]).
-  // (The row-group guard keeps the stores inside the workspace even for a
+  // group and slice are consecutive, at slot ks - (the group's first slice).
+  // (The group and slot guards keep the stores inside the workspace even for a
   // sequence longer than the maximum length the plan was made for.)
   auto ds_flush = [&]() {
-    if (DS && ds_i0 >= 0 && (ds_i0 >> 7) < a.ds_nr &&
-        ds_tile_visible(ds_i0 >> 5, (j0 + kw0) >> 5, s1, s2, off, wl, wr)) {
-      const int64_t tile0 =
-          ((((int64_t)sb.b * a.N1 + ds_n1) * a.ds_nr + (ds_i0 >> 7)) * a.ds_nks + ((j0 + kw0) >> 5)) * 4 +
-          ((ds_i0 >> 5) & 3);
-      bf16* dsg = static_cast<bf16*>(a.ds) + tile0 * 1024 + lane * 8;
+    if (DS && ds_i0 >= 0) {
+      const int R = ds_i0 >> 7, ks = (j0 + kw0) >> 5;
+      const int slot = ks - ds_band_lo(R, s1, s2, off, wl, wr);
+      const int64_t g = ds_group(a, sb, R);
+      if ((a.varlen || R < a.ds_nr) && g < a.ds_groups && (unsigned)slot < (unsigned)a.ds_w &&
+          ds_tile_visible(ds_i0 >> 5, ks, s1, s2, off, wl, wr)) {
+        const int64_t tile0 = ((g * a.N1 + ds_n1) * a.ds_w + slot) * 4 + ((ds_i0 >> 5) & 3);
+        bf16* dsg = static_cast<bf16*>(a.ds) + tile0 * 1024 + lane * 8;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          __builtin_nontemporal_store(ds_keep[kb][h], reinterpret_cast<bf16x8*>(dsg + kb * 4096 + h * 512));
+          for (int h = 0; h < 2; ++h)
+            __builtin_nontemporal_store(ds_keep[kb][h], reinterpret_cast<bf16x8*>(dsg + kb * 4096 + h * 512));
+        }
       }
     }
     ds_i0 = -1;
@@ -951,16 +963,18 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   const int qb = tile * 4 + wave;  // this wavefront's 32-row query block
 
   const bf16* __restrict__ Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
-  const bf16* __restrict__ Sg =
-      static_cast<const bf16*>(a.ds) + (((int64_t)b * a.N1 + n1) * a.ds_nr + tile) * a.ds_nks * 4096;
+  // this group's band of slices: slot x holds slice ksl.lo + x
+  const int64_t grp = ds_group(a, sb, tile);
+  const bf16* __restrict__ Sg = static_cast<const bf16*>(a.ds) + (grp * a.N1 + n1) * a.ds_w * 4096;
 
-  // 32-key slices that any row of [i0, i0 + 128) sees (slices past the
-  // workspace's last one, possible only with a sequence longer than the
-  // planned maximum, are left out)
+  // 32-key slices that any row of [i0, i0 + 128) sees (slices past the band,
+  // and groups past the workspace, possible only with a sequence longer than
+  // the planned maximum, are left out)
   const fa_sched::Span ksl = i0 < s1 ? fa_sched::blocks_covering(
                                             fa_sched::keys_seen(s2, i0, min(i0 + DQ_BQ, s1), off, wl, wr), 32)
                                       : fa_sched::Span{0, 0};
-  const int ks_end = min(ksl.hi, a.ds_nks);
+  const bool grp_ok = (a.varlen || tile < a.ds_nr) && grp < a.ds_groups;
+  const int ks_end = grp_ok ? min(ksl.hi, ksl.lo + a.ds_w) : ksl.lo;
   const int nsteps = (ks_end - ksl.lo + 1) / 2;
 
   TileCopy<HD, DQS_BK, 4> kcp;
@@ -972,7 +986,7 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   auto fetch = [&](int st, int buf) {
     const int ks = ksl.lo + 2 * st;
     kcp.issue(lds_addr(Ks) + buf * KTB, Kg + (int64_t)ks * 32 * a.k_ss, s2 - ks * 32, wave, lane);
-    const bf16* src = Sg + (int64_t)ks * 4096;
+    const bf16* src = Sg + (int64_t)(ks - ksl.lo) * 4096;
     const bool two = ks + 1 < ks_end;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {

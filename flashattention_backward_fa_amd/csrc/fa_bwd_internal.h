@@ -66,11 +66,17 @@ struct KernelArgs {
   int64_t v_part_stride;  // elements between dV partials (= elements of v)
 
   // dS-store form (variant 4): the dK/dV kernel stores dS, bf16 (or fp16), as
-  // [B][N1][ds_nr][ds_nks] tiles of 32 keys x 128 query rows (row-major, keys
-  // as rows); a GEMM kernel then forms dQ = scale * dS K from them.
+  // [ds_groups][N1][ds_w][4][1024] elements: per 128-row query group, per
+  // query head, per 32-key slice counted from the first slice the group sees
+  // (a band of ds_w slices), the four 32 x 32 tiles of the group's query
+  // blocks; a GEMM kernel then forms dQ = scale * dS K from them.  Group of
+  // row group R of sequence b: b * ds_nr + R (dense layouts) or
+  // cu_q[b] / 128 + b + R (TND; distinct for every (b, R) since cu_q does not
+  // decrease).
   void* ds;
-  int32_t ds_nr;          // 128-row query groups per sequence (ceil(S1 / 128))
-  int32_t ds_nks;         // 32-key slices per sequence (4 * ceil(S2 / 128): whole key tiles)
+  int32_t ds_nr;          // dense layouts: 128-row groups per sequence (ceil(S1 / 128))
+  int32_t ds_w;           // slices per group: a bound on the 32-key slices one group sees
+  int64_t ds_groups;      // groups the workspace holds
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups

@@ -116,11 +116,13 @@ typedef struct fa_bwd_desc {
 /* Validate `desc` (all rules of section 四 4.6 that this library enforces) and
  * build a plan.  On success *plan receives a new plan and *workspace_bytes the
  * device workspace size fa_bwd_run needs.  Pure host code: no HIP call, no
- * device memory.  For BSND/BNSD the workspace holds dS (the page's
- * dS = P (.) (dP - sfmg), rounded to the element type) for the dQ product,
- * about 2 * B * N1 * S1 * S2 bytes; where that would exceed 4 GiB, and for
- * TND, the plan recomputes S and dP for dQ instead and the workspace is small
- * (sfmg and fp32 dK/dV partial sums).  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
+ * device memory.  The workspace holds sfmg, fp32 dK/dV partial sums when the
+ * plan splits a key tile over jobs, and dS (the page's dS = P (.) (dP - sfmg),
+ * rounded to the element type) for the dQ product: 2 bytes per (row, key) of
+ * each 128-row query group and each 32-key slice that group can see (every
+ * slice of the longest key sequence unless both window bounds are given).
+ * Where that dS would exceed 4 GiB the plan recomputes S and dP for dQ
+ * instead and the workspace holds no dS.  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
  * FA_ERR_PARAM_INVALID, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED; *plan is left NULL. */
 int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_bytes);
 
@@ -183,9 +185,10 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,
 /* How a plan forms dQ (fa_bwd_create picks it; see there).  Every path but
  * FA_DQ_ATOMIC is bitwise repeatable.
  *   FA_DQ_RECOMPUTE : a query-tile-parallel kernel recomputes S and dP and
- *                     writes dQ = scale * dS K once (TND; very long BSND/BNSD)
+ *                     writes dQ = scale * dS K once (when the stored dS would
+ *                     exceed 4 GiB)
  *   FA_DQ_STORED_DS : the dK/dV kernel also stores dS (element type) in the
- *                     workspace and a GEMM kernel reads it back (BSND/BNSD)
+ *                     workspace and a GEMM kernel reads it back (default)
  *   FA_DQ_ATOMIC    : fp32 atomic adds into the workspace (tuning only)
  *   FA_DQ_FP32_FORM : the fp32 debugging form (FA_FLAG_FP32_OUT)
  * Writes the path to *path.  Errors: FA_ERR_NULLPTR. */

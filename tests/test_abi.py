@@ -62,9 +62,9 @@ def create(lib, **kw):
 
 def test_valid_problem_and_workspace_size(lib):
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # dS tiles of the dense layouts: 2 bytes per (row, key) of 128-row groups
-    # by whole 128-key tiles, per sequence and query head
-    ds = lambda B, N1, S1, S2: B * N1 * ((S1 + 127) // 128) * 128 * ((S2 + 127) // 128) * 128 * 2  # noqa: E731
+    # dS tiles: 2 bytes per (row, key) of each 128-row group by a band of
+    # 32-key slices (all slices of the key sequence without a two-sided window)
+    ds = lambda B, N1, S1, S2: B * N1 * ((S1 + 127) // 128) * 128 * ((S2 + 31) // 32) * 32 * 2  # noqa: E731
     # Enough key tiles x heads for every CU: sfmg and dS (dK/dV written by the
     # key-tile kernel, dQ by the GEMM over the stored dS).
     st, ws = create(lib, B=64, N1=8, N2=8, S1=256, S2=256)
@@ -79,6 +79,12 @@ def test_valid_problem_and_workspace_size(lib):
     # ragged lengths round up to whole tiles
     st, ws = create(lib, B=64, N1=8, N2=8, S1=200, S2=300)
     assert st == fb.FA_OK and ws == rnd(64 * 8 * 200 * 4) + rnd(ds(64, 8, 200, 300))
+    # a two-sided window bounds the band: ceil((128 + 100 + 20) / 32) + 1 = 9 slices
+    st, ws = create(lib, B=4, N1=8, N2=8, S1=4096, S2=4096, mask_mode=2, win_left=100, win_right=20)
+    assert st == fb.FA_OK and ws == rnd(4 * 8 * 4096 * 4) + rnd(4 * 32 * 8 * 9 * 8192)
+    # causal with a left bound is a two-sided window too: ceil((128 + 1024) / 32) + 1 = 37
+    st, ws = create(lib, B=1, N1=8, N2=8, S1=8192, S2=8192, mask_mode=1, win_left=1024)
+    assert st == fb.FA_OK and ws == rnd(8 * 8192 * 4) + rnd(64 * 8 * 37 * 8192)
     # past 4 GiB of dS the plan recomputes S and dP for dQ: sfmg only
     st, ws = create(lib, B=1, N1=32, N2=32, S1=16384, S2=8192)  # 8 GiB of dS
     assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4)
@@ -110,13 +116,14 @@ def test_plan_dq_path(lib, monkeypatch):
     assert dq_path(lib) == "stored_ds"
     assert dq_path(lib, layout="BNSD", mask_mode=1) == "stored_ds"
     assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "stored_ds"
-    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "recompute"
+    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "stored_ds"
     assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "recompute"  # dS past 4 GiB
     assert dq_path(lib, flags=fb.FLAG_FP32_OUT) == "fp32_form"
     monkeypatch.setenv("FA_BWD_VARIANT", "2")
     assert dq_path(lib) == "recompute"
+    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "recompute"
     monkeypatch.setenv("FA_BWD_VARIANT", "4")
-    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "stored_ds"
+    assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "stored_ds"
     monkeypatch.setenv("FA_BWD_VARIANT", "1")
     assert dq_path(lib) == "atomic"
     assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "recompute"
@@ -124,15 +131,24 @@ def test_plan_dq_path(lib, monkeypatch):
     assert lib.fa_bwd_plan_dq_path(None, ctypes.byref(out)) == fb.FA_ERR_NULLPTR
 
 
-def test_tnd_plans_the_recompute_pair(lib):
-    """TND keeps the dQ pass that recomputes S and dP: no dS in the workspace."""
+def test_tnd_workspace_band(lib):
+    """TND stores dS by 128-row group at index cu_q[b] / 128 + b + R, fewer
+    than T1 / 128 + B + 1 groups, each with a band of 32-key slices."""
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
     st, ws = create(lib, layout="TND", B=4, N1=8, N2=8, S1=1024, S2=1024, T1=4096, T2=4096)
     assert st == fb.FA_OK
-    # sfmg, then 2 query-range partial sums of dK and dV (8 x 4 key tiles x 8
-    # heads x 2 splits reach 512 jobs)
+    # sfmg, then 2 query-range partial sums of dK and dV (8 key tiles x 4
+    # sequences x 8 heads x 2 splits reach 512 jobs), then dS: 37 groups x 8
+    # heads x 32 slices (no window: every slice of the longest sequence)
     k_elems = 4096 * 8 * 128
-    assert ws == rnd(8 * 4096 * 4) + 2 * rnd(2 * k_elems * 4)
+    assert ws == rnd(8 * 4096 * 4) + 2 * rnd(2 * k_elems * 4) + rnd(37 * 8 * 32 * 8192)
+    # the varlen workload's shape: 8 sequences, T = 16437, causal window 1024:
+    # (128 + 8 + 1) groups x 16 heads x 37 slices, 0.66 GB instead of the
+    # 4 GiB of a grid laid out by the longest sequence
+    st, ws = create(lib, layout="TND", B=8, N1=16, N2=16, S1=3594, S2=3594, T1=16437, T2=16437,
+                    mask_mode=1, win_left=1024)
+    assert st == fb.FA_OK
+    assert ws == rnd(16 * 16437 * 4) + rnd(137 * 16 * 37 * 8192)
 
 
 @pytest.mark.parametrize("kw,code", [

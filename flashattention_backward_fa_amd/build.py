@@ -1,7 +1,7 @@
 """Build libfa_bwd.so in-tree for gfx950.
 
 The host planner (csrc/fa_bwd_api.cpp) is plain C++ built with g++; the
-kernels (csrc/fa_bwd_det_kernels.hip: the default dK/dV and dQ kernels;
+kernels (csrc/fa_bwd_det_kernels.hip: the dK/dV kernel and both dQ kernels;
 csrc/fa_bwd_kernels.hip: preprocess and the atomic variants;
 csrc/fa_bwd_f32_kernels.hip: the fp32 debugging form;
 csrc/fa_fwd_kernels.hip: the forward that produces attn_out and

@@ -2,13 +2,13 @@
 
     python -m flashattention_backward_fa_amd.profile_summary traffic \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
-        --kernels dkdv_kernel,dq_kernel --workload gqa_causal --out FILE
+        --kernels dkdv_kernel,dq_ds_kernel --workload gqa_causal --out FILE
 
     python -m flashattention_backward_fa_amd.profile_summary trace \
         --stats DIR --workload gqa_causal --out FILE [--bench-json FILE]
 
     python -m flashattention_backward_fa_amd.profile_summary mfma \
-        --pmc DIR --kernels dkdv_kernel,dq_kernel --workload gqa_causal --out FILE
+        --pmc DIR --kernels dkdv_kernel,dq_ds_kernel --workload gqa_causal --out FILE
 
 trace: the per-kernel table of a --kernel-trace --stats run (calls, average,
 min and max duration, share of GPU time), with the kernel source hash and,

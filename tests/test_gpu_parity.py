@@ -250,14 +250,17 @@ def test_split_partials_parity(split):
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
 
 
-def test_default_path_is_bitwise_repeatable():
-    """No atomics on the default path: two runs give identical bits."""
+@pytest.mark.parametrize("variant", ["plan", "2"])
+def test_default_path_is_bitwise_repeatable(variant):
+    """No atomics on either default chain: two runs give identical bits."""
     cfg = EDGE_CASES["tnd_mixed_lengths"]
     x = case_inputs(cfg, seed=1)
     Yst, lst = oracle_inputs(cfg, x)
-    say("[det] repeat")
-    a = gpu_backward(cfg, x, Yst, lst)
-    b = gpu_backward(cfg, x, Yst, lst, deterministic=True)
+    say(f"[det] repeat ({variant})")
+    env = {} if variant == "plan" else {"FA_BWD_VARIANT": variant}
+    with _env(**env):
+        a = gpu_backward(cfg, x, Yst, lst)
+        b = gpu_backward(cfg, x, Yst, lst, deterministic=True)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
 

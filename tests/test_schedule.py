@@ -203,3 +203,41 @@ def test_check_fails_on_a_planted_off_by_one(sched):
     lo, hi = _pair(sched.sched_rows_seeing, s1, s2, 0, 1, L, R)
     assert (lo, hi) == _span_of(ok[:, 0:1].any(axis=1))
     assert (lo, hi) != _span_of(shifted[:, 0:1].any(axis=1))
+
+
+def test_stored_ds_band_holds_every_group(sched, monkeypatch):
+    """The stored-dS workspace keeps, per 128-row query group, a band of W
+    slots for the 32-key slices the group sees (kernels: slot = slice - first
+    slice of the group, with the same schedule functions as here).  A W below
+    a group's slice count would drop dS tiles.  W is read back from the planned
+    workspace size (no job split: sfmg + groups x W x 8 KB) and checked against
+    every group of many shapes and bands."""
+    from flashattention_backward_fa_amd import build, fa_bwd as fb
+
+    if not os.path.exists(fb.LIB_PATH):
+        build.build()
+    lib = fb.load_library()
+    monkeypatch.setenv("FA_BWD_SPLIT", "1,1")
+    monkeypatch.delenv("FA_BWD_VARIANT", raising=False)
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    lengths = LENGTHS + [(4096, 4096), (3000, 5000), (5000, 3000), (1025, 2047)]
+    bands = _bands() + [(1, 1024, -1), (2, 1024, 1024), (2, 0, 4095), (2, 4095, 0), (2, 100, 20)]
+    checked = 0
+    for s1, s2 in lengths:
+        for mode, wl, wr in bands:
+            d = fb.make_desc("BSND", 1, 1, 1, s1, s2, 64, 64, mask_mode=mode, win_left=wl, win_right=wr)
+            h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+            assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_OK
+            lib.fa_bwd_destroy(h)
+            groups = -(-s1 // 128)
+            rest = ws.value - rnd(4 * s1)
+            assert rest > 0 and rest % (groups * 8192) == 0, (s1, s2, mode, wl, wr)
+            W = rest // (groups * 8192)
+            L, R = oracle.mask_bounds(mode, wl, wr)
+            for i0 in range(0, s1, 128):
+                lo, hi = _pair(sched.sched_query_tile_blocks, s1, s2, i0, 128, 32, L, R)
+                assert hi - lo <= W, (s1, s2, mode, wl, wr, i0, lo, hi, W)
+                checked += 1
+            # the band is no wider than the longest key sequence needs
+            assert W <= max(1, -(-s2 // 32))
+    assert checked > 1000

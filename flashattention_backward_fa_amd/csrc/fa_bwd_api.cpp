@@ -25,6 +25,7 @@ struct fa_bwd_plan_s {
   int64_t q_elems;         // elements of q (and of the fp32 dQ accumulator)
   int64_t lse_elems;       // elements of softmax_lse / sfmg
   size_t off_dq_acc, off_sfmg, off_dk_acc, off_dv_acc, off_ds, ws_bytes;
+  int32_t n2_chunk;        // stored-dS chain: KV heads per dK/dV + dQ launch pair
   fabwd::Profiler* prof = nullptr;  // timing hook, off by default
 };
 
@@ -143,10 +144,11 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   //  - dS-store pair (variant 4): the dK/dV kernel also stores dS (2 bytes per
   //    query/key pair of every 32 x 32 tile a 128-row query group sees) and a
   //    GEMM kernel forms dQ = scale * dS K from it, reading dS once instead of
-  //    recomputing S and dP.  Taken while that dS workspace stays within
-  //    kDsWorkspaceCap;
+  //    recomputing S and dP.  When the whole dS would exceed kDsWorkspaceCap,
+  //    the run handles a chunk of KV heads at a time (a dK/dV and a dQ launch
+  //    per chunk) in a workspace of one chunk;
   //  - recompute pair (variant 2): a query-tile-parallel dQ kernel recomputes
-  //    S and dP.  Taken for problems whose dS would exceed the cap.
+  //    S and dP.  Taken when even one KV head's dS would exceed the cap.
   // FA_BWD_VARIANT=2/4 forces one of them, 0/1 the fp32-atomic dQ kernels
   // (tuning, bf16 only).
   const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
@@ -165,15 +167,26 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     // TND group indices cu_q[b] / 128 + b + R stay below T1 / 128 + B + 1
     a.ds_groups = tnd ? d.T1 / 128 + d.B + 1 : (int64_t)d.B * a.ds_nr;
   }
-  const double ds_bytes = (double)a.ds_groups * (double)N1 * (double)a.ds_w * 8192.0;
-  constexpr double kDsWorkspaceCap = 4.0 * 1024 * 1024 * 1024;
-  a.variant = ds_bytes <= kDsWorkspaceCap ? 4 : 2;
+  // dS bytes of one KV head (its G query heads); FA_BWD_DS_CAP (bytes)
+  // overrides the cap, for tests of the chunked run
+  const double per_kv = (double)a.ds_groups * (double)a.G * (double)a.ds_w * 8192.0;
+  double cap = 4.0 * 1024 * 1024 * 1024;
+  if (const char* e = std::getenv("FA_BWD_DS_CAP")) {
+    const double c = std::atof(e);
+    if (c > 0) cap = c;
+  }
+  p.n2_chunk = (int32_t)std::min<double>((double)N2, std::floor(cap / per_kv));
+  a.variant = p.n2_chunk >= 1 ? 4 : 2;
   if (const char* e = std::getenv("FA_BWD_VARIANT"); e) {
     if (e[0] == '2') a.variant = 2;
     if (e[0] == '0' && !a.f16) a.variant = 0;
     if (e[0] == '1' && !a.f16 && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
     if (e[0] == '4') a.variant = 4;
   }
+  if (p.n2_chunk < 1) p.n2_chunk = 1;  // forced variant 4 past the cap: one KV head at a time
+  a.n2_begin = 0;
+  a.n2_count = (int32_t)N2;
+  a.ds_heads = (int32_t)(a.G * p.n2_chunk);
   if ((d.flags & FA_FLAG_DETERMINISTIC) && a.variant < 2) a.variant = 2;
   if (d.flags & FA_FLAG_FP32_OUT) a.variant = 3;  // fp32 debugging form: sfmg + two VALU kernels
   a.heads_per_job = a.G;
@@ -224,8 +237,8 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     cur += align_up(parts * (size_t)v_elems * sizeof(float));
   }
   p.off_ds = cur;
-  if (a.variant == 4) {  // dS: 4 tiles of 32 x 32 two-byte elements per (group, head, slot)
-    cur += align_up((size_t)a.ds_groups * (size_t)N1 * (size_t)a.ds_w * 8192u);
+  if (a.variant == 4) {  // dS: 4 tiles of 32 x 32 two-byte elements per (group, head of a chunk, slot)
+    cur += align_up((size_t)a.ds_groups * (size_t)a.ds_heads * (size_t)a.ds_w * 8192u);
   }
   p.ws_bytes = cur;
   p.desc = d;
@@ -307,8 +320,14 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
     // dS -> partial-sum reduce (when a key tile is split over jobs)
     if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
-    if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
-    if (fabwd::launch_dq_ds(a, stream) != 0) return FA_ERR_RUNTIME;
+    for (int32_t n2b = 0; n2b < a.N2; n2b += plan->n2_chunk) {  // one pass unless dS is chunked
+      a.n2_begin = n2b;
+      a.n2_count = std::min(plan->n2_chunk, a.N2 - n2b);
+      if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
+      if (fabwd::launch_dq_ds(a, stream) != 0) return FA_ERR_RUNTIME;
+    }
+    a.n2_begin = 0;
+    a.n2_count = a.N2;
     if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
     return FA_OK;

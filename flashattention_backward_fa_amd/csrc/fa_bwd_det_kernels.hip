@@ -406,7 +406,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int HJ = a.G / hpj;
   const int QS = a.q_splits;
   int r = blockIdx.x;
-  const int n2 = r % a.N2; r /= a.N2;
+  const int n2 = a.n2_begin + r % a.n2_count; r /= a.n2_count;
   const int b = r % a.B; r /= a.B;
   const int qs = r % QS; r /= QS;
   const int hslot = r % HJ;
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
       const int64_t g = ds_group(a, sb, R);
       if ((a.varlen || R < a.ds_nr) && g < a.ds_groups && (unsigned)slot < (unsigned)a.ds_w &&
           ds_tile_visible(ds_i0 >> 5, ks, s1, s2, off, wl, wr)) {
-        const int64_t tile0 = ((g * a.N1 + ds_n1) * a.ds_w + slot) * 4 + ((ds_i0 >> 5) & 3);
+        const int64_t tile0 = ((g * a.ds_heads + (ds_n1 - a.n2_begin * a.G)) * a.ds_w + slot) * 4 + ((ds_i0 >> 5) & 3);
         bf16* dsg = static_cast<bf16*>(a.ds) + tile0 * 1024 + lane * 8;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -946,12 +946,14 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // job -> (query group, query head, sequence), the longest groups first
-  const int per_tile = a.N1 * a.B;
+  const int nh = a.G * a.n2_count;  // query heads of this launch's KV heads
+  const int per_tile = nh * a.B;
   const int ntiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
   const int tile = ntiles - 1 - (int)(blockIdx.x / per_tile);
   const int rem = blockIdx.x % per_tile;
-  const int n1 = rem % a.N1;
-  const int b = rem / a.N1;
+  const int hl = rem % nh;          // head within the chunk (its index in the workspace)
+  const int n1 = a.n2_begin * a.G + hl;
+  const int b = rem / nh;
   const int n2 = n1 / a.G;
 
   const SeqBounds sb = seq_bounds(a, b);
@@ -965,7 +967,7 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   const bf16* __restrict__ Kg = static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn;
   // this group's band of slices: slot x holds slice ksl.lo + x
   const int64_t grp = ds_group(a, sb, tile);
-  const bf16* __restrict__ Sg = static_cast<const bf16*>(a.ds) + (grp * a.N1 + n1) * a.ds_w * 4096;
+  const bf16* __restrict__ Sg = static_cast<const bf16*>(a.ds) + (grp * a.ds_heads + hl) * a.ds_w * 4096;
 
   // 32-key slices that any row of [i0, i0 + 128) sees (slices past the band,
   // and groups past the workspace, possible only with a sequence longer than
@@ -1150,7 +1152,7 @@ int launch_dq_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
 
 int launch_dkdv(const KernelArgs& a, void* stream) {
   const int64_t tiles = (a.S2 + 127) / 128;  // 128-key tiles in every shape
-  const int64_t blocks = tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.N2;
+  const int64_t blocks = tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.n2_count;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1171,7 +1173,7 @@ int launch_dq(const KernelArgs& a, void* stream) {
 
 int launch_dq_ds(const KernelArgs& a, void* stream) {
   const int64_t tiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
-  const int64_t blocks = tiles * a.N1 * a.B;
+  const int64_t blocks = tiles * a.G * a.n2_count * a.B;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -77,6 +77,11 @@ struct KernelArgs {
   int32_t ds_nr;          // dense layouts: 128-row groups per sequence (ceil(S1 / 128))
   int32_t ds_w;           // slices per group: a bound on the 32-key slices one group sees
   int64_t ds_groups;      // groups the workspace holds
+  int32_t ds_heads;       // query heads the workspace holds per group (G * KV heads of a chunk)
+  // KV heads [n2_begin, n2_begin + n2_count) handled by one dK/dV launch (and
+  // their query heads by the dQ launch): the whole range, or one chunk when
+  // the stored dS is processed a few KV heads at a time
+  int32_t n2_begin, n2_count;
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups

@@ -85,11 +85,19 @@ def test_valid_problem_and_workspace_size(lib):
     # causal with a left bound is a two-sided window too: ceil((128 + 1024) / 32) + 1 = 37
     st, ws = create(lib, B=1, N1=8, N2=8, S1=8192, S2=8192, mask_mode=1, win_left=1024)
     assert st == fb.FA_OK and ws == rnd(8 * 8192 * 4) + rnd(64 * 8 * 37 * 8192)
-    # past 4 GiB of dS the plan recomputes S and dP for dQ: sfmg only
-    st, ws = create(lib, B=1, N1=32, N2=32, S1=16384, S2=8192)  # 8 GiB of dS
-    assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4)
-    st, ws = create(lib, B=1, N1=32, N2=32, S1=8192, S2=8192)   # exactly 4 GiB
+    # past 4 GiB of dS the run takes a chunk of KV heads at a time, in a
+    # workspace of one chunk: 8 GiB of dS, 256 MiB per KV head -> 16 heads
+    st, ws = create(lib, B=1, N1=32, N2=32, S1=16384, S2=8192)
+    assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4) + rnd(ds(1, 16, 16384, 8192))
+    st, ws = create(lib, B=1, N1=32, N2=32, S1=8192, S2=8192)   # exactly 4 GiB: one pass
     assert st == fb.FA_OK and ws == rnd(32 * 8192 * 4) + rnd(ds(1, 32, 8192, 8192))
+    # GQA: a chunk is whole KV heads (4 query heads each): 8 GiB -> 4 of 8 KV heads
+    st, ws = create(lib, B=1, N1=32, N2=8, S1=16384, S2=8192)
+    assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4) + rnd(ds(1, 16, 16384, 8192))
+    # one KV head past the cap (64 GiB of dS for its 8 query heads): the plan
+    # recomputes S and dP for dQ and the workspace holds sfmg only
+    st, ws = create(lib, B=1, N1=8, N2=1, S1=65536, S2=65536)
+    assert st == fb.FA_OK and ws == rnd(8 * 65536 * 4)
     # the fp32 debugging form needs sfmg only
     st, ws = create(lib, flags=fb.FLAG_FP32_OUT)
     assert st == fb.FA_OK
@@ -117,18 +125,34 @@ def test_plan_dq_path(lib, monkeypatch):
     assert dq_path(lib, layout="BNSD", mask_mode=1) == "stored_ds"
     assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "stored_ds"
     assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "stored_ds"
-    assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "recompute"  # dS past 4 GiB
+    assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "stored_ds"  # chunked
+    assert dq_path(lib, B=1, N1=8, N2=1, S1=65536, S2=65536) == "recompute"  # one KV head past 4 GiB
     assert dq_path(lib, flags=fb.FLAG_FP32_OUT) == "fp32_form"
     monkeypatch.setenv("FA_BWD_VARIANT", "2")
     assert dq_path(lib) == "recompute"
     assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "recompute"
     monkeypatch.setenv("FA_BWD_VARIANT", "4")
-    assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "stored_ds"
+    assert dq_path(lib, B=1, N1=8, N2=1, S1=65536, S2=65536) == "stored_ds"
     monkeypatch.setenv("FA_BWD_VARIANT", "1")
     assert dq_path(lib) == "atomic"
     assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "recompute"
     out = ctypes.c_int()
     assert lib.fa_bwd_plan_dq_path(None, ctypes.byref(out)) == fb.FA_ERR_NULLPTR
+
+
+def test_ds_cap_override_chunks_kv_heads(lib, monkeypatch):
+    """FA_BWD_DS_CAP (bytes) lowers the cap: the workspace then holds the dS
+    of as many whole KV heads as fit (at least one)."""
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # B=2, N1=8, N2=2 (G=4), S=128: 2 groups x 4 slices x 8 KB = 64 KiB per query head
+    per_q = 2 * 4 * 8192
+    base = rnd(2 * 8 * 128 * 4) + 2 * rnd(16 * (2 * 128 * 2 * 128) * 4)  # sfmg + 16 partial sums
+    assert create(lib) == (fb.FA_OK, base + rnd(8 * per_q))
+    monkeypatch.setenv("FA_BWD_DS_CAP", str(4 * per_q))      # exactly one KV head
+    assert create(lib) == (fb.FA_OK, base + rnd(4 * per_q))
+    monkeypatch.setenv("FA_BWD_DS_CAP", str(4 * per_q - 1))  # not even one: recompute
+    assert create(lib) == (fb.FA_OK, base)
+    assert dq_path(lib) == "recompute"
 
 
 def test_tnd_workspace_band(lib):

@@ -297,3 +297,34 @@ def test_both_pairs_split_partials_parity(variant, split):
         gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
 
+
+
+@pytest.mark.parametrize("name", ["bsnd_causal_gqa4_ragged", "tnd_mixed_lengths", "bnsd_batch3_causal",
+                                  "tnd_window_dense_heads", "bsnd_d192_dv64_window"])
+def test_stored_ds_one_kv_head_per_pass(name):
+    """Stored-dS chain run one KV head at a time (the path for dS past the
+    workspace cap; here forced with a 1-byte cap), against the oracle."""
+    cfg = EDGE_CASES[name]
+    say(f"[parity] stored dS, one KV head per pass: {name}")
+    x = case_inputs(cfg, seed=sorted(EDGE_CASES).index(name))
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    with _env(FA_BWD_VARIANT="4", FA_BWD_DS_CAP="1"):
+        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+    qe, ke = empty_rows(cfg, x, gq.shape, gk.shape)
+    assert not np.any(gq[qe]) and not np.any(gk[ke]) and not np.any(gv[ke])
+
+
+def test_stored_ds_uneven_kv_head_chunks():
+    """Three KV heads in chunks of two and one: the cap holds 2.5 KV heads'
+    dS (2 row groups x 2 query heads x 7 slices x 8 KB each)."""
+    cfg = W.custom("BSND", B=1, N1=6, N2=3, S1=200, S2=200, D=128, Dv=128, mask_mode=1)
+    say("[parity] stored dS, KV-head chunks of 2 and 1")
+    x = case_inputs(cfg, seed=11)
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    per_kv = 2 * 2 * 7 * 8192
+    with _env(FA_BWD_DS_CAP=str(per_kv * 5 // 2)):
+        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])

@@ -121,8 +121,10 @@ typedef struct fa_bwd_desc {
  * rounded to the element type) for the dQ product: 2 bytes per (row, key) of
  * each 128-row query group and each 32-key slice that group can see (every
  * slice of the longest key sequence unless both window bounds are given).
- * Where that dS would exceed 4 GiB the plan recomputes S and dP for dQ
- * instead and the workspace holds no dS.  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
+ * Where that dS would exceed 4 GiB the workspace holds the dS of as many
+ * whole key/value heads as fit and fa_bwd_run processes the heads in such
+ * chunks; only where one key/value head's dS alone exceeds 4 GiB does the
+ * plan recompute S and dP for dQ instead, with no dS in the workspace.  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
  * FA_ERR_PARAM_INVALID, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED; *plan is left NULL. */
 int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_bytes);
 
@@ -185,8 +187,8 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,
 /* How a plan forms dQ (fa_bwd_create picks it; see there).  Every path but
  * FA_DQ_ATOMIC is bitwise repeatable.
  *   FA_DQ_RECOMPUTE : a query-tile-parallel kernel recomputes S and dP and
- *                     writes dQ = scale * dS K once (when the stored dS would
- *                     exceed 4 GiB)
+ *                     writes dQ = scale * dS K once (when one key/value
+ *                     head's stored dS would exceed 4 GiB)
  *   FA_DQ_STORED_DS : the dK/dV kernel also stores dS (element type) in the
  *                     workspace and a GEMM kernel reads it back (default)
  *   FA_DQ_ATOMIC    : fp32 atomic adds into the workspace (tuning only)

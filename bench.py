@@ -16,8 +16,10 @@ GQA causal one (B=1, N1=32, N2=8, S=4096, D=Dv=128, BSND).
 Prints one JSON line: whole-step throughput in TFLOP/s under the standard
 FLOP count (2*(3D+2Dv) per visible (query, key) pair per query head; causal
 with S1 = S2 counted as exactly half of S1*S2); the roofline entry of the
-dK/dV + dQ kernel pair from HIP events the library records around it inside
-the timed region; the standalone sfmg preprocess kernel's HBM bandwidth
+dominant kernel, the dK/dV kernel (the four products S, dP, dV, dK it forms:
+2*(2D+2Dv) FLOP per visible pair per query head), timed by HIP events the
+library records around it inside the timed region, with the dK/dV + dQ pair
+beside it; the standalone sfmg preprocess kernel's HBM bandwidth
 (its own timed launches); the fp64 CPU oracle timed on a bounded sample of the same
 workload; and `accuracy`: the library's gradients on that sample (made from
 the oracle forward's stored Y and lse) against the oracle's, every element,
@@ -51,11 +53,14 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # The main part of a step is the dK/dV kernel and the dQ kernel; the library
 # records HIP events around that pair on the launch stream.  Which dQ kernel
 # runs is the plan's choice (fa_bwd_plan_dq_path).
-MAIN_KERNELS = {"stored_ds": "dkdv_kernel+dq_ds_kernel", "recompute": "dkdv_kernel+dq_kernel"}
+MAIN_KERNELS = {"stored_ds": "dkdv_kernel+dq_ds_kernel", "recompute": "dkdv_kernel+dq_kernel",
+                "fused": "fused_kernel"}
+DQ_KERNEL = {"stored_ds": "dq_ds_kernel", "recompute": "dq_kernel"}
 DQ_MODES = {
     "stored_ds": "dK/dV kernel stores dS (bf16 tiles in the workspace), dQ = scale*dS*K by a GEMM kernel "
                  "(no atomics, deterministic)",
     "recompute": "separate dQ pass recomputing S and dP (no atomics, deterministic)",
+    "fused": "one launch per (sequence, KV head): sfmg, dK/dV and dQ in one kernel (no workspace, deterministic)",
 }
 SFMG_NOTE = {
     "stored_ds": "standalone fa_bwd_sfmg entry point; the default step launches the same kernel first",
@@ -96,9 +101,16 @@ def algorithmic_flops(cfg):
     return 2.0 * (3 * cfg["D"] + 2 * cfg["Dv"]) * cfg["N1"] * visible_pairs(cfg)
 
 
-def committed_traffic(workload, path=None, sources="det"):
-    """HBM bytes per main-kernel launch from the committed rocprofv3 --pmc
-    summary, if it was taken from the current kernel source; else None."""
+def dkdv_flops(cfg):
+    """The dK/dV kernel's share: S = QK^T, dP = dY V^T, dV += P^T dY and
+    dK += dS^T Q, 2*(2D + 2Dv) FLOP per visible pair per query head."""
+    return 2.0 * (2 * cfg["D"] + 2 * cfg["Dv"]) * cfg["N1"] * visible_pairs(cfg)
+
+
+def committed_traffic(workload, path=None, sources="det", key="hbm_bytes_per_launch"):
+    """HBM bytes per launch (key: the pair's total, or
+    hbm_bytes_per_launch.<kernel> for one kernel) from the committed rocprofv3
+    --pmc summary, if it was taken from the current kernel source; else None."""
     from flashattention_backward_fa_amd.profile_summary import SOURCES, kernel_code_hash
 
     path = path or os.path.join(PROFILE_DIR, f"bwd_dkdv_dq_kernels_{workload}_traffic.txt")
@@ -113,7 +125,7 @@ def committed_traffic(workload, path=None, sources="det"):
     if vals.get("kernel_code_sha256_16") != kernel_code_hash(SOURCES[sources]):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -215,6 +227,41 @@ def accuracy(sample, name):
     return out
 
 
+def roofline_entry(name, cfg, m):
+    """Roofline of the dominant kernel (the dK/dV kernel; the fused kernel when
+    the plan takes that mode): its algorithmic FLOP per launch over its own
+    average duration from the library's HIP events in the timed region, with
+    the dK/dV + dQ pair (all five products) and the dQ kernel beside it."""
+    flops = algorithmic_flops(cfg)
+    pair_ms = m["pair_ms"]
+    pair = {
+        "kernels": MAIN_KERNELS.get(m["dq_path"], m["dq_path"]),
+        "achieved": round(flops / (pair_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "frac": round(flops / (pair_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_flop_per_launch": flops, "flop_rule": "2*(3D+2Dv) per visible pair per query head",
+        "avg_launch_ms": round(pair_ms, 5), "traffic": committed_traffic(name),
+    }
+    if m["dkdv_ms"] is None:  # one main kernel (fused) or a chunked run: the pair is all there is
+        return {"bound": "mfma", "kernel": pair["kernels"], "achieved": pair["achieved"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": pair["frac"], "traffic": pair["traffic"],
+                "avg_launch_ms": round(pair_ms, 5), "launches_timed": m["pair_launches"],
+                "algorithmic_flop_per_launch": flops, "flop_rule": pair["flop_rule"]}
+    kf = dkdv_flops(cfg)
+    ach = kf / (m["dkdv_ms"] * 1e-3) / 1e12
+    dq = DQ_KERNEL[m["dq_path"]]
+    return {
+        "bound": "mfma", "kernel": "dkdv_kernel", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+        "traffic": committed_traffic(name, key="hbm_bytes_per_launch.dkdv_kernel"),
+        "avg_launch_ms": round(m["dkdv_ms"], 5), "launches_timed": m["pair_launches"],
+        "algorithmic_flop_per_launch": kf,
+        "flop_rule": "2*(2D+2Dv) per visible pair per query head (S, dP, dV, dK)",
+        "pair": pair,
+        "dq_kernel": {"kernel": dq, "avg_launch_ms": round(m["dq_ms"], 5),
+                      "traffic": committed_traffic(name, key=f"hbm_bytes_per_launch.{dq}")},
+    }
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE readings to bytes."""
@@ -284,9 +331,18 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / max(steps, 1)
-    main_ms = plan.profile_read(steps)
+    # the library's events around the two main kernels, split between them
+    split = plan.profile_read_split(steps)
     plan.profile_enable(0)
-    main_avg = sum(main_ms) / max(len(main_ms), 1)
+    n = max(len(split), 1)
+    main_avg = sum(a + b for a, b in split) / n
+    first, second = sum(a for a, _ in split) / n, sum(b for _, b in split) / n
+    path = plan.dq_path()
+    dkdv_ms = dq_ms = None
+    if path == "stored_ds" and all(b > 0 for _, b in split):
+        dkdv_ms, dq_ms = first, second
+    elif path == "recompute":
+        dq_ms, dkdv_ms = first, second
 
     # preprocess alone (sfmg = rowsum(dY * Y)): HBM-bound, timed over its own
     # launches on the same stream; algorithmic bytes = dY and Y read once
@@ -307,20 +363,20 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     p1.record(stream)
     torch.cuda.synchronize()
     pre_ms = p0.elapsed_time(p1) / pre_iters
-    return dict(ms_per_step=ms_per_step, pair_ms=main_avg, pair_launches=len(main_ms), pre_ms=pre_ms,
-                pre_bytes=pre_bytes, settle_steps=settle_steps, dq_path=plan.dq_path())
+    return dict(ms_per_step=ms_per_step, pair_ms=main_avg, pair_launches=len(split), dkdv_ms=dkdv_ms, dq_ms=dq_ms,
+                pre_ms=pre_ms, pre_bytes=pre_bytes, settle_steps=settle_steps, dq_path=path)
 
 
 FLOYD_WORKLOAD = "floyd"
 
 
 def floyd_stage_units(cfg):
-    """Algorithmic FLOP and HBM bytes of each backward stage of the Floyd
-    attention path on a workload with no mask: T = heads*N*M*K (n, m, k)
-    triples, R = heads*N*M rows.  Each product costs 2*D FLOP per triple; the
-    bytes count every operand read once and every result written once in the
-    path's own decomposition (fp32 scores and dP, 16-bit P and dS, one fp32 dQ
-    partial, in HBM)."""
+    """FLOP and HBM bytes of each backward stage of the Floyd attention path on
+    a workload with no mask: T = heads*N*M*K (n, m, k) triples, R = heads*N*M
+    rows.  Each product costs 2*D FLOP per triple.  The bytes are the path's
+    own, not algorithmic: every operand of the stage read once and every result
+    written once in this library's decomposition, which keeps fp32 scores and
+    dP, 16-bit P and dS, and one fp32 dQ partial in HBM between stages."""
     hd = cfg["B"] * cfg["H"]
     N, M, K, D = cfg["N"], cfg["M"], cfg["K"], cfg["D"]
     T, R = hd * N * M * K, hd * N * M
@@ -336,6 +392,21 @@ def floyd_stage_units(cfg):
         "dq_k1": (2 * D * T, 2 * T + k1sz + 2 * qsz),
         "dq_k2": (2 * D * T, 2 * T + k2sz + 2 * qsz + qsz),
     }
+
+
+def floyd_algorithmic_units(cfg):
+    """Algorithmic FLOP and HBM bytes of the whole Floyd backward: ten products
+    of 2*D FLOP per (n, m, k) triple; every input read once (query, key1,
+    value1, key2, value2, dy, attention_in, and the two fp32 row statistics
+    of 8 entries per row) and every gradient written once (dq, dk1, dv1, dk2,
+    dv2).  Nothing the path keeps between its stages counts."""
+    hd = cfg["B"] * cfg["H"]
+    N, M, K, D = cfg["N"], cfg["M"], cfg["K"], cfg["D"]
+    R = hd * N * M
+    qsz, k1sz, k2sz = 2 * R * D, 2 * hd * N * K * D, 2 * hd * K * M * D
+    inputs = 3 * qsz + 2 * k1sz + 2 * k2sz + 2 * R * 8 * 4
+    outputs = qsz + 2 * k1sz + 2 * k2sz
+    return 20.0 * D * hd * N * M * K, inputs + outputs
 
 
 def floyd_leg(steps, warmup, settle_s, with_accuracy):
@@ -394,12 +465,15 @@ def floyd_leg(steps, warmup, settle_s, with_accuracy):
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
         gbs, tfs = b / (sms * 1e-3) / 1e9, f / (sms * 1e-3) / 1e12
         stages[name] = {
-            "ms": round(sms, 4), "bound": bound, "algorithmic_bytes": b, "algorithmic_flop": f,
+            "ms": round(sms, 4), "bound": bound, "path_bytes": b, "flop": f,
             "gb_s": round(gbs, 1), "tflop_s": round(tfs, 1),
-            "frac": round(gbs / PEAK_HBM_GBS if bound == "hbm" else tfs / PEAK_BF16_TFLOPS, 4),
+            "path_frac": round(gbs / PEAK_HBM_GBS if bound == "hbm" else tfs / PEAK_BF16_TFLOPS, 4),
         }
     dom = max(stages, key=lambda k: stages[k]["ms"])
-    d = stages[dom]
+    # the backward as a whole against its algorithmic bound
+    a_flop, a_bytes = floyd_algorithmic_units(cfg)
+    t_hbm, t_mfma = a_bytes / (PEAK_HBM_GBS * 1e9), a_flop / (PEAK_BF16_TFLOPS * 1e12)
+    a_bound = "hbm" if t_hbm >= t_mfma else "mfma"
     leg = {
         "workload": FLOYD_WORKLOAD,
         "config": {k: cfg[k] for k in ("B", "H", "N", "M", "K", "D")} | {"mask": None, "dtype": "bf16"},
@@ -409,12 +483,19 @@ def floyd_leg(steps, warmup, settle_s, with_accuracy):
         "algorithmic_gflop": round(flops / 1e9, 3),
         "flop_rule": "20*D per (n, m, k) triple: ten products of 2*D each",
         "stages": stages,
+        "stage_bytes_note": "path_bytes count the path's own fp32 scores / dP and 16-bit P / dS kept in HBM "
+                            "between stages; they are not algorithmic bytes",
+        "dominant_stage": dom,
         "roofline": {
-            "kernel": dom, "bound": d["bound"],
-            "achieved": d["gb_s"] if d["bound"] == "hbm" else d["tflop_s"],
-            "peak": PEAK_HBM_GBS if d["bound"] == "hbm" else PEAK_BF16_TFLOPS,
-            "unit": "GB/s" if d["bound"] == "hbm" else "TFLOP/s", "frac": d["frac"],
-            "traffic": committed_traffic(FLOYD_WORKLOAD, os.path.join(PROFILE_DIR, f"floyd_{dom}_{FLOYD_WORKLOAD}_traffic.txt"),
+            "kernel": "whole backward (all stages)", "bound": a_bound,
+            "achieved": round(a_bytes / (ms * 1e-3) / 1e9, 1) if a_bound == "hbm" else round(a_flop / (ms * 1e-3) / 1e12, 1),
+            "peak": PEAK_HBM_GBS if a_bound == "hbm" else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if a_bound == "hbm" else "TFLOP/s",
+            "frac": round(max(t_hbm, t_mfma) / (ms * 1e-3), 4),
+            "algorithmic_bytes": a_bytes, "algorithmic_flop": a_flop,
+            "units_rule": "inputs (7 tensors and the 2 row statistics) read once, 5 gradients written once; "
+                          "20*D FLOP per (n, m, k) triple",
+            "traffic": committed_traffic(FLOYD_WORKLOAD, os.path.join(PROFILE_DIR, f"floyd_bwd_kernels_{FLOYD_WORKLOAD}_traffic.txt"),
                                          "floyd"),
         },
         "accuracy": None,
@@ -488,13 +569,12 @@ def main():
     name = args.workload or W.BENCH_WORKLOAD
     cfg = W.CONFIGS[name]
     m = measure(name, args.steps, args.warmup, args.settle, args.dtype)
-    ms_per_step, main_avg, pre_ms, pre_bytes = m["ms_per_step"], m["pair_ms"], m["pre_ms"], m["pre_bytes"]
+    ms_per_step, pre_ms, pre_bytes = m["ms_per_step"], m["pre_ms"], m["pre_bytes"]
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
 
     flops = algorithmic_flops(cfg)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (main_avg * 1e-3) / 1e12
-    traffic = committed_traffic(name)
+    roofline = roofline_entry(name, cfg, m)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -519,11 +599,7 @@ def main():
             "seq_len": cfg.get("S1", int(sum(cfg.get("lengths", [0])))), "parallelism": "single-gpu",
             "algorithmic_gflop": round(flops / 1e9, 3), "dq_mode": DQ_MODES.get(m["dq_path"], m["dq_path"]),
         },
-        "roofline": {
-            "bound": "mfma", "kernel": MAIN_KERNELS.get(m["dq_path"], m["dq_path"]), "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic, "avg_launch_ms": round(main_avg, 5), "launches_timed": m["pair_launches"],
-        },
+        "roofline": roofline,
         "preprocess": {
             "bound": "hbm", "kernel": "preprocess_kernel (sfmg)", "achieved": round(pre_gbs, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pre_gbs / PEAK_HBM_GBS, 4),
@@ -554,6 +630,9 @@ def main():
                 "pct_of_peak": round(100 * f / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                 "pair_ms": round(r["pair_ms"], 4),
                 "pair_tflops": round(f / (r["pair_ms"] * 1e-3) / 1e12, 1),
+                "dkdv_ms": None if r["dkdv_ms"] is None else round(r["dkdv_ms"], 4),
+                "dkdv_frac": None if r["dkdv_ms"] is None else
+                round(dkdv_flops(W.CONFIGS[other]) / (r["dkdv_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "preprocess_gbs": round(r["pre_bytes"] / (r["pre_ms"] * 1e-3) / 1e9, 1),
                 "algorithmic_gflop": round(f / 1e9, 3),
                 "dq_path": r["dq_path"],

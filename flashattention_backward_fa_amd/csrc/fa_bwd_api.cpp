@@ -1,6 +1,7 @@
 // Host side of libfa_bwd.so: validation, planning, workspace sizing and the
 // C ABI declared in include/fa_bwd.h.  Plain C++ (no HIP headers): every
-// device call goes through the launchers of fa_bwd_kernels.hip.
+// device call (the launches and the CU-count query) goes through the
+// functions of the .hip sources declared in fa_bwd_internal.h.
 //
 // The checks follow page "CANN ops-transformer FlashAttnGrad 算子详解",
 // section 四 4.6 (constraints) and section 五 5.1 (host tiling: parse, check,
@@ -34,6 +35,12 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// CU count of the current HIP device (256, an MI355X, when none is visible)
+int device_cus() {
+  const int n = fabwd::device_cu_count();
+  return n > 0 ? n : 256;
+}
+
 bool log_enabled() {
   const char* e = std::getenv("FA_BWD_LOG");
   return e && e[0] == '1';
@@ -60,6 +67,10 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   if (d.mask_mode < FA_MASK_NONE || d.mask_mode > FA_MASK_WINDOW) return FA_ERR_PARAM_INVALID;
   if (!std::isfinite(d.softmax_scale)) return FA_ERR_PARAM_INVALID;
   if (d.flags & ~(FA_FLAG_DETERMINISTIC | FA_FLAG_FP32_OUT)) return FA_ERR_PARAM_INVALID;
+  if (d.dq_mode < FA_DQ_AUTO || d.dq_mode > FA_DQ_FUSED) return FA_ERR_PARAM_INVALID;
+  if (d.num_cus < 0) return FA_ERR_PARAM_INVALID;
+  if ((d.flags & FA_FLAG_FP32_OUT) && d.dq_mode != FA_DQ_AUTO) return FA_ERR_PARAM_INVALID;
+  if ((d.flags & FA_FLAG_DETERMINISTIC) && d.dq_mode == FA_DQ_ATOMIC) return FA_ERR_PARAM_INVALID;
 
   // section 四 4.6: positive sizes, 0 < B < 65536, N1 % N2 == 0, 0 < Dv <= D <= 192
   if (d.B <= 0 || d.B >= 65536) return FA_ERR_SHAPE;
@@ -92,6 +103,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   }
 
   if (!fabwd::main_instantiated(d.D, d.Dv) || !fabwd::det_instantiated(d.D, d.Dv)) return FA_ERR_UNSUPPORTED;
+  if (d.dq_mode == FA_DQ_ATOMIC && d.dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;  // bf16 kernels only
 
   KernelArgs& a = p.args;
   std::memset(&a, 0, sizeof(a));
@@ -140,19 +152,23 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   else { a.win_left = d.win_left; a.win_right = d.win_right; }
   a.has_mask = (a.win_left >= 0 || a.win_right >= 0) ? 1 : 0;
 
-  // Kernel choice.  Both defaults are free of atomics and bitwise repeatable:
-  //  - dS-store pair (variant 4): the dK/dV kernel also stores dS (2 bytes per
-  //    query/key pair of every 32 x 32 tile a 128-row query group sees) and a
-  //    GEMM kernel forms dQ = scale * dS K from it, reading dS once instead of
-  //    recomputing S and dP.  When the whole dS would exceed kDsWorkspaceCap,
-  //    the run handles a chunk of KV heads at a time (a dK/dV and a dQ launch
-  //    per chunk) in a workspace of one chunk;
-  //  - recompute pair (variant 2): a query-tile-parallel dQ kernel recomputes
-  //    S and dP.  Taken when even one KV head's dS would exceed the cap.
-  // FA_BWD_VARIANT=2/4 forces one of them, 0/1 the fp32-atomic dQ kernels
-  // (tuning, bf16 only).
+  // Kernel choice (the dQ modes of include/fa_bwd.h):
+  //  - variant 5, FA_DQ_FUSED: one workgroup per (sequence, KV head) forms
+  //    sfmg, dK, dV and dQ in one launch (small problems: the longest key
+  //    sequence fits one 128-key tile);
+  //  - variant 4, FA_DQ_STORED_DS: the dK/dV kernel also stores dS (2 bytes
+  //    per query/key pair of every 32 x 32 tile a 128-row query group sees)
+  //    and a GEMM kernel forms dQ = scale * dS K from it, reading dS once
+  //    instead of recomputing S and dP.  KV heads are processed in chunks
+  //    whose dS fits the workspace bound (4 GiB per chunk when none is set);
+  //  - variant 2, FA_DQ_RECOMPUTE: a query-tile-parallel dQ kernel recomputes
+  //    S and dP; taken under FA_DQ_AUTO when not even one KV head's dS fits;
+  //  - variants 0/1, FA_DQ_ATOMIC: fp32 atomic adds into a dQ workspace;
+  //  - variant 3: the fp32 debugging form.
   const int64_t k_elems = tnd ? d.T2 * N2 * D : (int64_t)d.B * S2 * N2 * D;
   const int64_t v_elems = tnd ? d.T2 * N2 * Dv : (int64_t)d.B * S2 * N2 * Dv;
+  p.q_elems = tnd ? d.T1 * N1 * D : (int64_t)d.B * S1 * N1 * D;
+  p.lse_elems = tnd ? N1 * d.T1 : (int64_t)d.B * N1 * S1;
   // dS band: a 128-row group sees at most 128 + left + right keys under a
   // two-sided window, i.e. ceil((128 + left + right) / 32) + 1 slices of 32
   // (one more for misalignment); otherwise up to every slice of the longest
@@ -167,46 +183,40 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     // TND group indices cu_q[b] / 128 + b + R stay below T1 / 128 + B + 1
     a.ds_groups = tnd ? d.T1 / 128 + d.B + 1 : (int64_t)d.B * a.ds_nr;
   }
-  // dS bytes of one KV head (its G query heads); FA_BWD_DS_CAP (bytes)
-  // overrides the cap, for tests of the chunked run
-  const double per_kv = (double)a.ds_groups * (double)a.G * (double)a.ds_w * 8192.0;
-  double cap = 4.0 * 1024 * 1024 * 1024;
-  if (const char* e = std::getenv("FA_BWD_DS_CAP")) {
-    const double c = std::atof(e);
-    if (c > 0) cap = c;
-  }
-  p.n2_chunk = (int32_t)std::min<double>((double)N2, std::floor(cap / per_kv));
-  a.variant = p.n2_chunk >= 1 ? 4 : 2;
-  if (const char* e = std::getenv("FA_BWD_VARIANT"); e) {
-    if (e[0] == '2') a.variant = 2;
-    if (e[0] == '0' && !a.f16) a.variant = 0;
-    if (e[0] == '1' && !a.f16 && fabwd::main_v2_instantiated(d.D, d.Dv)) a.variant = 1;
-    if (e[0] == '4') a.variant = 4;
-  }
-  if (p.n2_chunk < 1) p.n2_chunk = 1;  // forced variant 4 past the cap: one KV head at a time
-  a.n2_begin = 0;
-  a.n2_count = (int32_t)N2;
-  a.ds_heads = (int32_t)(a.G * p.n2_chunk);
-  if ((d.flags & FA_FLAG_DETERMINISTIC) && a.variant < 2) a.variant = 2;
-  if (d.flags & FA_FLAG_FP32_OUT) a.variant = 3;  // fp32 debugging form: sfmg + two VALU kernels
-  a.heads_per_job = a.G;
-  a.q_splits = 1;
-  a.n_partials = 1;
-  a.k_part_stride = k_elems;
-  a.v_part_stride = v_elems;
-  if (a.variant == 1 && a.G > 1) a.heads_per_job = 1;
-  if (a.variant == 2 || a.variant == 4) {
-    // Enough jobs to balance causal work over the CUs: split the query heads
-    // of a GQA group, then the query range of a key tile, until there are at
-    // least 2 jobs per CU of an MI355X (256 CUs); each split adds an fp32
-    // partial sum per key that a reduce kernel adds up.
-    const int64_t bc = 4 * fabwd::det_keys_per_wave(d.D);
-    const int64_t tiles = (S2 + bc - 1) / bc;
-    const int64_t target = 2 * 256;
-    while (tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * a.N2 < target) {
-      if (a.heads_per_job > 1 && a.heads_per_job % 2 == 0) a.heads_per_job /= 2;
-      else if (a.q_splits < 4) a.q_splits *= 2;
+  const uint64_t bound = d.max_workspace_bytes;  // 0: no bound
+  const int cus = d.num_cus > 0 ? d.num_cus : device_cus();
+  const size_t sfmg_bytes = align_up((size_t)p.lse_elems * sizeof(float));
+  // the fused kernel holds the whole key range in one tile and the row
+  // statistics of all its (query head, 32-row block) items in LDS
+  const bool fused_ok = fabwd::fused_instantiated(d.D, d.Dv) && S2 <= fabwd::FUSED_MAX_KEYS &&
+                        (int64_t)a.G * ((S1 + 31) / 32) <= fabwd::FUSED_MAX_BLOCKS;
+
+  // Job split of the pair kernels for launches over n2l KV heads: halve the
+  // query heads of a GQA group per job, then split the query range of a key
+  // tile (up to 4 ways), until there are at least 2 jobs per CU, so that
+  // causal work (a 32:1 skew between the first and last key tile at
+  // S = 4096) balances; each split adds an fp32 partial sum of dK and dV per
+  // key that a reduce kernel adds up.  A split whose partials would pass
+  // part_budget bytes (when >= 0) is not taken.
+  const int64_t tiles = (S2 + 127) / 128;  // 128-key tiles of the dK/dV kernel
+  auto partial_bytes = [&](int hpj, int qs) -> size_t {
+    const int64_t np = (int64_t)(a.G / hpj) * qs;
+    return np > 1 ? align_up((size_t)np * (size_t)k_elems * sizeof(float)) +
+                        align_up((size_t)np * (size_t)v_elems * sizeof(float))
+                  : 0;
+  };
+  auto split_for = [&](int64_t n2l, int64_t part_budget) {
+    a.heads_per_job = a.G;
+    a.q_splits = 1;
+    const int64_t target = 2 * (int64_t)cus;
+    while (tiles * (a.G / a.heads_per_job) * a.q_splits * a.B * n2l < target) {
+      int h2 = a.heads_per_job, q2 = a.q_splits;
+      if (h2 > 1 && h2 % 2 == 0) h2 /= 2;
+      else if (q2 < 4) q2 *= 2;
       else break;
+      if (part_budget >= 0 && (int64_t)partial_bytes(h2, q2) > part_budget) break;
+      a.heads_per_job = h2;
+      a.q_splits = q2;
     }
     if (const char* e = std::getenv("FA_BWD_SPLIT")) {  // tuning override "heads_per_job,q_splits"
       int h = 0, q = 0;
@@ -215,20 +225,65 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
         a.q_splits = q;
       }
     }
-    a.n_partials = (a.G / a.heads_per_job) * a.q_splits;
-  }
+  };
+  const double per_kv = (double)a.ds_groups * (double)a.G * (double)a.ds_w * 8192.0;  // dS bytes of one KV head
+  auto ds_bytes = [&](int64_t n2l) {
+    return align_up((size_t)a.ds_groups * (size_t)(a.G * n2l) * (size_t)a.ds_w * 8192u);
+  };
 
-  p.q_elems = tnd ? d.T1 * N1 * D : (int64_t)d.B * S1 * N1 * D;
-  p.lse_elems = tnd ? N1 * d.T1 : (int64_t)d.B * N1 * S1;
+  a.heads_per_job = a.G;
+  a.q_splits = 1;
+  p.n2_chunk = (int32_t)N2;
+  const int mode = d.dq_mode;
+  if (d.flags & FA_FLAG_FP32_OUT) {
+    a.variant = 3;  // fp32 debugging form: sfmg + two VALU kernels
+  } else if (mode == FA_DQ_FUSED || (mode == FA_DQ_AUTO && fused_ok)) {
+    if (!fused_ok) return FA_ERR_UNSUPPORTED;
+    a.variant = 5;
+  } else if (mode == FA_DQ_ATOMIC) {
+    a.variant = fabwd::main_v2_instantiated(d.D, d.Dv) ? 1 : 0;
+    if (a.variant == 1 && a.G > 1) a.heads_per_job = 1;
+  } else {
+    a.variant = 0;
+    if (mode == FA_DQ_STORED_DS || mode == FA_DQ_AUTO) {
+      // the largest chunk of whole KV heads whose dS fits (4 GiB, or what the
+      // bound leaves beside sfmg), then the split for launches of that many
+      // heads in what remains
+      const double room = bound ? (double)bound - (double)sfmg_bytes : 4.0 * 1024 * 1024 * 1024;
+      int64_t chunk = room > 0 ? (int64_t)std::min<double>((double)N2, std::floor(room / per_kv)) : 0;
+      while (chunk >= 1 && bound && (uint64_t)(sfmg_bytes + ds_bytes(chunk)) > bound) --chunk;  // alignment
+      if (chunk < 1 && mode == FA_DQ_STORED_DS && !bound) chunk = 1;  // forced: one KV head at a time
+      if (chunk >= 1) {
+        a.variant = 4;
+        p.n2_chunk = (int32_t)chunk;
+        split_for(chunk, bound ? (int64_t)bound - (int64_t)(sfmg_bytes + ds_bytes(chunk)) : -1);
+      } else if (mode == FA_DQ_STORED_DS) {
+        return FA_ERR_WORKSPACE;
+      }
+    }
+    if (a.variant == 0) {  // recompute: sfmg and the partial sums only
+      if (bound && sfmg_bytes > bound) return FA_ERR_WORKSPACE;
+      a.variant = 2;
+      split_for(N2, bound ? (int64_t)(bound - sfmg_bytes) : -1);
+    }
+  }
+  a.n2_begin = 0;
+  a.n2_count = (int32_t)N2;
+  a.ds_heads = (int32_t)(a.G * p.n2_chunk);
+  const bool pair = a.variant == 2 || a.variant == 4;
+  a.n_partials = pair ? (a.G / a.heads_per_job) * a.q_splits : 1;
+  a.k_part_stride = k_elems;
+  a.v_part_stride = v_elems;
+
+  // workspace: sfmg, [dQ accumulator], [dK / dV partial sums], [dS]
   p.off_sfmg = 0;
   p.off_dq_acc = 0;
-  size_t cur = align_up((size_t)p.lse_elems * sizeof(float));
+  size_t cur = a.variant == 5 ? 0 : sfmg_bytes;  // the fused kernel forms sfmg itself
   if (a.variant < 2) {
     p.off_dq_acc = cur;
     cur += align_up((size_t)p.q_elems * sizeof(float));
   }
   p.off_dk_acc = p.off_dv_acc = cur;
-  const bool pair = a.variant == 2 || a.variant == 4;
   if (fabwd::split_heads(a) || (pair && a.n_partials > 1)) {
     const size_t parts = pair ? (size_t)a.n_partials : 1;
     p.off_dk_acc = cur;
@@ -237,9 +292,8 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     cur += align_up(parts * (size_t)v_elems * sizeof(float));
   }
   p.off_ds = cur;
-  if (a.variant == 4) {  // dS: 4 tiles of 32 x 32 two-byte elements per (group, head of a chunk, slot)
-    cur += align_up((size_t)a.ds_groups * (size_t)a.ds_heads * (size_t)a.ds_w * 8192u);
-  }
+  if (a.variant == 4) cur += ds_bytes(p.n2_chunk);  // 4 tiles of 32 x 32 elements per (group, head of a chunk, slot)
+  if (bound && cur > bound) return FA_ERR_WORKSPACE;  // e.g. the atomic kernels' dQ accumulator
   p.ws_bytes = cur;
   p.desc = d;
   p.desc.S1 = (int32_t)S1;
@@ -276,10 +330,11 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
     const KernelArgs& a = p->args;
     std::fprintf(stderr,
                  "[fa_bwd] plan layout=%d B=%d N1=%d N2=%d S1=%d S2=%d D=%d Dv=%d T1=%lld T2=%lld "
-                 "scale=%g window=(%d,%d) variant=%d heads_per_job=%d q_splits=%d partials=%d workspace=%zu B\n",
+                 "scale=%g window=(%d,%d) variant=%d heads_per_job=%d q_splits=%d partials=%d kv_chunk=%d "
+                 "workspace=%zu B\n",
                  p->desc.layout, a.B, a.N1, a.N2, a.S1, a.S2, a.D, a.Dv, (long long)a.T1,
                  (long long)a.T2, (double)a.scale, a.win_left, a.win_right, a.variant,
-                 a.heads_per_job, a.q_splits, a.n_partials, p->ws_bytes);
+                 a.heads_per_job, a.q_splits, a.n_partials, p->n2_chunk, p->ws_bytes);
   }
   return FA_OK;
 }
@@ -292,8 +347,8 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
     return FA_ERR_NULLPTR;
   int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
   if (st != FA_OK) return st;
-  if (!workspace || workspace_bytes < plan->ws_bytes) return FA_ERR_WORKSPACE;
-  // the tuning-only atomic kernels do not read seqused
+  if (plan->ws_bytes > 0 && (!workspace || workspace_bytes < plan->ws_bytes)) return FA_ERR_WORKSPACE;
+  // the atomic kernels do not read seqused
   if ((seqused_q || seqused_kv) && plan->args.variant < 2) return FA_ERR_UNSUPPORTED;
 
   KernelArgs a = plan->args;
@@ -308,6 +363,12 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   a.dv_acc = reinterpret_cast<float*>(ws + plan->off_dv_acc);
   a.ds = a.variant == 4 ? ws + plan->off_ds : nullptr;
 
+  if (a.variant == 5) {  // one launch: sfmg, dK/dV and dQ per (sequence, KV head)
+    if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    if (fabwd::launch_fused(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    return FA_OK;
+  }
   if (a.variant == 3) {
     if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
@@ -324,6 +385,7 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
       a.n2_begin = n2b;
       a.n2_count = std::min(plan->n2_chunk, a.N2 - n2b);
       if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
+      if (plan->prof && plan->n2_chunk >= a.N2 && fabwd::profiler_mark(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
       if (fabwd::launch_dq_ds(a, stream) != 0) return FA_ERR_RUNTIME;
     }
     a.n2_begin = 0;
@@ -337,6 +399,7 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
     // partial-sum reduce (when a key tile is split over jobs)
     if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_dq(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (plan->prof && fabwd::profiler_mark(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
     if (fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
@@ -367,6 +430,7 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
 int fa_bwd_plan_dq_path(fa_bwd_plan plan, int* path) {
   if (!plan || !path) return FA_ERR_NULLPTR;
   switch (plan->args.variant) {
+    case 5: *path = FA_DQ_FUSED; break;
     case 4: *path = FA_DQ_STORED_DS; break;
     case 2: *path = FA_DQ_RECOMPUTE; break;
     case 3: *path = FA_DQ_FP32_FORM; break;
@@ -389,7 +453,14 @@ int fa_bwd_profile_read(fa_bwd_plan plan, float* ms, int cap, int* count) {
   if (!plan || !ms || !count) return FA_ERR_NULLPTR;
   *count = 0;
   if (!plan->prof) return FA_OK;
-  return fabwd::profiler_read(plan->prof, ms, cap, count) == 0 ? FA_OK : FA_ERR_RUNTIME;
+  return fabwd::profiler_read(plan->prof, ms, nullptr, cap, count) == 0 ? FA_OK : FA_ERR_RUNTIME;
+}
+
+int fa_bwd_profile_read_split(fa_bwd_plan plan, float* first_ms, float* second_ms, int cap, int* count) {
+  if (!plan || !first_ms || !second_ms || !count) return FA_ERR_NULLPTR;
+  *count = 0;
+  if (!plan->prof) return FA_OK;
+  return fabwd::profiler_read(plan->prof, first_ms, second_ms, cap, count) == 0 ? FA_OK : FA_ERR_RUNTIME;
 }
 
 int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,

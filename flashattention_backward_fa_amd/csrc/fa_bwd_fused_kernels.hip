@@ -1,0 +1,317 @@
+// gfx950 (MI355X) FlashAttention backward for short key sequences in one
+// launch: the per-head schedule of page "CANN ops-transformer FlashAttnGrad
+// 算子详解", section 五 5.2 (template flash_attn_grad_bn2: one core per
+// (batch, key/value head), no separate pre- or post-processing pass).
+//
+// One workgroup of 4 wavefronts owns one (sequence, key/value head) and the
+// whole key range of that sequence (at most 128 keys, 32 per wavefront, in
+// LDS).  It forms every quantity of section 一 for the G query heads of the
+// group:
+//   sfmg = rowsum(dY (.) Y)        for all of its query rows, first;
+//   S = scale * Q K^T, P = exp(S - lse), dP = dY V^T, dS = P (.) (dP - sfmg)
+//                                  per 32-row query block;
+//   dV += P^T dY, dK += dS^T Q     in registers over all blocks and heads;
+//   dQ = scale * dS K              per block: the four wavefronts' dS tiles
+//                                  meet in LDS and each wavefront forms 32
+//                                  columns of dQ over all 128 keys.
+// Every dQ row sees its whole key range inside the workgroup, so dQ is
+// written once, with no atomics and no workspace, and the result is bitwise
+// repeatable.  The MFMA layouts are those of the dK/dV kernel
+// (fa_bwd_det_kernels.hip): S and dP put query rows on M and keys on N, so P
+// and dS packed to 16 bits are the A operands of the key-major products; the
+// dQ product reads the dS register images back through transposing LDS reads,
+// like the GEMM over stored dS.
+
+#include <hip/hip_runtime.h>
+
+#include "fa_bwd_tiles.h"
+
+namespace fabwd {
+namespace {
+
+constexpr int FK = FUSED_MAX_KEYS;  // keys per workgroup: 4 wavefronts x 32
+constexpr int FR = 32;              // query rows per step
+static_assert(FK == 128, "one 32-key slice per wavefront");
+
+template <int HD, int HDV, bool F16>
+__global__ __launch_bounds__(256, 1) void fused_kernel(KernelArgs a) {
+  constexpr int NKQ = HD / 16;
+  constexpr int NKV = HDV / 16;
+  constexpr int NBK = HD / 32;
+  constexpr int NBV = HDV / 32;
+  constexpr int QTB = FR * HD * 2;   // bytes of one Q / dY tile buffer
+  constexpr int YTB = FR * HDV * 2;
+  constexpr int MAXR = FUSED_MAX_BLOCKS * FR;  // query rows whose statistics fit
+  static_assert(HD == 64 || HD == 128, "swizzled tiles of 64 or 128 columns");
+
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[FK * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[FK * HDV];
+  __shared__ __attribute__((aligned(1024))) bf16 Qs[2][FR * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Ys[2][FR * HDV];
+  __shared__ __attribute__((aligned(1024))) bf16 Ss[4 * 1024];  // dS images of the 4 key slices, 2 KB each
+  __shared__ __attribute__((aligned(16))) float lse_s[MAXR];    // lse * log2(e) (+inf: row sees nothing)
+  __shared__ __attribute__((aligned(16))) float sfm_s[MAXR];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n2 = blockIdx.x % a.N2;
+  const int b = blockIdx.x / a.N2;
+  const int G = a.G;
+  const SeqBounds sb = seq_bounds(a, b);
+  const int s1 = sb.s1, s2 = sb.s2;
+  const int off = s2 - s1;
+  const int wl = a.win_left, wr = a.win_right;
+  const int kw0 = wave * 32;  // this wavefront's keys within the tile
+
+  bf16* __restrict__ dQ = static_cast<bf16*>(a.dq) + sb.qbase;
+  // blocks of 32 rows over every row the sequence holds (rows past the used
+  // ones are masked and get zero gradients); a sequence longer than the plan's
+  // maximum is cut to what the row statistics hold
+  const int nblk = min((sb.s1a + FR - 1) / FR, FUSED_MAX_BLOCKS / G);
+  const int T = G * nblk;  // items (query head, block), head-major
+
+  if (sb.s2a == 0) {  // no keys at all: every dq row of the group is zero
+    for (int h = 0; h < G; ++h) {
+      const int64_t hb = (int64_t)(n2 * G + h) * a.q_sn;
+      for (int x = tid; x < sb.s1a * HD; x += 256) dQ[hb + (int64_t)(x / HD) * a.q_ss + x % HD] = to_elem<F16>(0.f);
+    }
+    return;
+  }
+
+  // K and V (rows past the sequence's keys repeat its last key; the masks
+  // ignore them), and the first item's Q / dY tiles, asynchronously
+  {
+    TileCopy<HD, FK, 4> kcp;
+    TileCopy<HDV, FK, 4> vcp;
+    kcp.init(wave, lane, (int)a.k_ss * 2);
+    vcp.init(wave, lane, (int)a.v_ss * 2);
+    const int kvalid = min(sb.s2a, FK);
+    kcp.issue(lds_addr(Ks), static_cast<const bf16*>(a.k) + sb.kbase + (int64_t)n2 * a.k_sn, kvalid, wave, lane);
+    vcp.issue(lds_addr(Vs), static_cast<const bf16*>(a.v) + sb.vbase + (int64_t)n2 * a.v_sn, kvalid, wave, lane);
+  }
+  TileCopy<HD, FR, 4> qcp;
+  TileCopy<HDV, FR, 4> ycp;
+  qcp.init(wave, lane, (int)a.q_ss * 2);
+  ycp.init(wave, lane, (int)a.o_ss * 2);
+  auto fetch = [&](int t, int buf) {
+    const int n1 = n2 * G + t / nblk;
+    const int i0 = (t % nblk) * FR;
+    qcp.issue(lds_addr(Qs) + buf * QTB, static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn + (int64_t)i0 * a.q_ss,
+              sb.s1a - i0, wave, lane);
+    ycp.issue(lds_addr(Ys) + buf * YTB,
+              static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i0 * a.o_ss, sb.s1a - i0,
+              wave, lane);
+  };
+  if (T > 0) fetch(0, 0);
+
+  // Row statistics of every item: lse in base 2 (+inf for rows past the used
+  // ones or with lse = -inf, so that their P is 0) and sfmg = rowsum(dY * Y),
+  // HDV / 8 lanes per row with one 16-byte load of each tensor, eight rows in
+  // flight per lane.
+  for (int r = tid; r < T * FR; r += 256) {
+    const int n1 = n2 * G + (r / FR) / nblk;
+    const int i = ((r / FR) % nblk) * FR + r % FR;
+    float l = __builtin_inff();
+    if (i < s1) {
+      const float x = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + i];
+      l = x == -__builtin_inff() ? __builtin_inff() : x * kLog2e;
+    }
+    lse_s[r] = l;
+  }
+  {
+    constexpr int LPR = HDV / 8;      // lanes per row
+    constexpr int RPP = 256 / LPR;    // rows per pass
+    constexpr int UN = 8;             // passes in flight
+    const int part = tid % LPR;
+    for (int r0 = tid / LPR; r0 < T * FR; r0 += RPP * UN) {
+      float acc[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int r = r0 + u * RPP;
+        const int n1 = n2 * G + (r / FR) / nblk;
+        const int i = ((r / FR) % nblk) * FR + r % FR;
+        acc[u] = 0.f;
+        if (r < T * FR && i < sb.s1a) {
+          const int64_t o = sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i * a.o_ss + part * 8;
+          const bf16x8 y = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + o);
+          const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + o);
+          if constexpr (F16) {  // reinterpret whole vectors (element casts of bf16 lanes miscompile)
+            const halfx8 yh = __builtin_bit_cast(halfx8, y), gh = __builtin_bit_cast(halfx8, g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[u] += (float)gh[e] * (float)yh[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[u] += (float)g[e] * (float)y[e];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        float s = acc[u];
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
+        const int r = r0 + u * RPP;
+        if (part == 0 && r < T * FR) sfm_s[r] = s;
+      }
+    }
+  }
+
+  floatx16 dKr[NBK], dVr[NBV];
+#pragma unroll
+  for (int i = 0; i < NBK; ++i) dKr[i] = floatx16{};
+#pragma unroll
+  for (int i = 0; i < NBV; ++i) dVr[i] = floatx16{};
+
+  SwzTile<HD, FK> kadr;
+  SwzTile<HDV, FK> vadr;
+  SwzTile<HD, FR> qadr;
+  SwzTile<HDV, FR> yadr;
+  kadr.init(lds_addr(Ks), lane);
+  vadr.init(lds_addr(Vs), lane);
+  qadr.init(lds_addr(Qs), lane);
+  yadr.init(lds_addr(Ys), lane);
+
+  // A operand of dQ = dS K (query rows on M, keys on K) read back from the dS
+  // register images in Ss: lane i of a 16-lane group receives, as element e
+  // of a transposing read, element i % 4 of the 8 bytes that lane 4e + i/4 of
+  // the group loads; lane L = 4e + q (g = lane / 16) loads rows
+  // 16*(g % 2) + 4q + 0..3 of key 16kc + 8s + 4*(g / 2) + e, which the
+  // producing wavefront's lane 32*(q % 2) + key holds in half g % 2, elements
+  // 4*(q / 2) + 0..3.  Within each 1 KB half h, chunk c (the producer lane)
+  // sits at ds_chunk_slot(c, h), which spreads these reads over all banks.
+  uint32_t a_base[2];
+  {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3, h = g & 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 32 * (q & 1) + 8 * s + 4 * (g >> 1) + e;  // producer chunk at kc = 0
+      a_base[s] = lds_addr(Ss) + h * 1024 + ds_chunk_slot(c, h) * 16 + (q >> 1) * 8;
+    }
+  }
+  // where this lane puts half h of its own dS image
+  const uint32_t s_put = lds_addr(Ss) + wave * 2048;
+
+  wait_vmem();    // K, V, the first tiles and the statistics' loads landed
+  lds_barrier();  // ... everyone's
+
+  const int j_key = kw0 + l32;  // this lane's key (the accumulator column)
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    const int h = t / nblk;
+    const int i0 = (t % nblk) * FR;
+    const int n1 = n2 * G + h;
+    if (t > 0) {
+      wait_vmem();    // this wavefront's copies of item t landed
+      lds_barrier();  // ... and everyone's; buffer buf ^ 1 and Ss are free
+    }
+    if (t + 1 < T) fetch(t + 1, buf ^ 1);
+
+    // S = Q K^T, dP = dY V^T for this wavefront's 32 keys
+    floatx16 sacc = floatx16{}, pacc = floatx16{};
+#pragma unroll
+    for (int kk = 0; kk < NKQ; ++kk)
+      sacc = mfma32<F16>(lds_load16(qadr.row_read(kk, buf * QTB)), lds_load16(kadr.row_read_at(kk, kw0)), sacc);
+#pragma unroll
+    for (int kk = 0; kk < NKV; ++kk)
+      pacc = mfma32<F16>(lds_load16(yadr.row_read(kk, buf * YTB)), lds_load16(vadr.row_read_at(kk, kw0)), pacc);
+
+    // P = exp(S * scale - lse) masked, dS = P (dP - sfmg), packed to 16 bits:
+    // lane = key, element rg of the accumulator = row 8*(rg/4) + 4*hi + rg%4
+    const fa_sched::Window vis = fa_sched::window(fa_sched::rows_of_key(j_key, s1, s2, off, wl, wr), i0);
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int ib = r4 * 8 + hi * 4;
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[t * FR + ib]);
+      const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[t * FR + ib]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rg = r4 * 4 + e;
+        float p = __builtin_amdgcn_exp2f(sacc[rg] * a.scale_log2 - l4[e]);
+        p = fa_sched::in_window(vis, ib + e) ? p : 0.f;
+        pa[rg >> 3][rg & 7] = to_elem<F16>(p);
+        da[rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[rg] - f4[e]));
+      }
+    }
+    // this wavefront's dS image for the dQ product of the block
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *(LDS_AS bf16x8*)(uintptr_t)(s_put + hh * 1024 + ds_chunk_slot(lane, hh) * 16) = da[hh];
+
+    // dV += P^T dY, dK += dS^T Q (B operands: dY and Q read down their columns)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) {
+        const bf16x8 yb = join(lds_load_tr(yadr.tr_read(kc, 0, nb, buf * YTB)), lds_load_tr(yadr.tr_read(kc, 1, nb, buf * YTB)));
+        dVr[nb] = mfma32<F16>(pa[kc], yb, dVr[nb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        const bf16x8 qb = join(lds_load_tr(qadr.tr_read(kc, 0, nb, buf * QTB)), lds_load_tr(qadr.tr_read(kc, 1, nb, buf * QTB)));
+        dKr[nb] = mfma32<F16>(da[kc], qb, dKr[nb]);
+      }
+    }
+
+    lds_barrier();  // the four dS images are in Ss
+
+    // dQ of the block, 32 head-dim columns per wavefront, over all 128 keys
+    if (wave < NBK) {
+      floatx16 dq = floatx16{};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t ao = sl * 2048 + c * 256;  // slice sl, chunk bit 4 = c
+          const bf16x8 dsa = join(lds_load_tr(a_base[0] + ao), lds_load_tr(a_base[1] + ao));
+          const int kc = 2 * sl + c;
+          const bf16x8 kb = join(lds_load_tr(kadr.tr_read(kc, 0, wave)), lds_load_tr(kadr.tr_read(kc, 1, wave)));
+          dq = mfma32<F16>(dsa, kb, dq);
+        }
+      }
+      const int64_t hb = (int64_t)n1 * a.q_sn + wave * 32 + l32;
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) {
+        const int i = i0 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+        if (i < sb.s1a) dQ[hb + (int64_t)i * a.q_ss] = to_elem<F16>(dq[rg] * a.scale);
+      }
+    }
+  }
+
+  // dK = scale * acc, dV = acc for this wavefront's keys (keys past the used
+  // ones hold zeros: no row sees them)
+  bf16* __restrict__ dK = static_cast<bf16*>(a.dk) + sb.kbase + (int64_t)n2 * a.k_sn;
+  bf16* __restrict__ dV = static_cast<bf16*>(a.dv) + sb.vbase + (int64_t)n2 * a.v_sn;
+#pragma unroll
+  for (int rg = 0; rg < 16; ++rg) {
+    const int j = kw0 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+    if (j >= sb.s2a) continue;
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) dK[(int64_t)j * a.k_ss + nb * 32 + l32] = to_elem<F16>(dKr[nb][rg] * a.scale);
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) dV[(int64_t)j * a.v_ss + nb * 32 + l32] = to_elem<F16>(dVr[nb][rg]);
+  }
+}
+
+template <bool F16>
+int launch_fused_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (a.D == 64 && a.Dv == 64) return launch(fused_kernel<64, 64, F16>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 64) return launch(fused_kernel<128, 64, F16>, grid, block, s, a);
+  if (a.D == 128 && a.Dv == 128) return launch(fused_kernel<128, 128, F16>, grid, block, s, a);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool fused_instantiated(int D, int Dv) { return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128)); }
+
+int launch_fused(const KernelArgs& a, void* stream) {
+  const int64_t blocks = (int64_t)a.B * a.N2;
+  if (blocks <= 0) return 0;
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return a.f16 ? launch_fused_t<true>(a, dim3((unsigned)blocks), s) : launch_fused_t<false>(a, dim3((unsigned)blocks), s);
+}
+
+}  // namespace fabwd

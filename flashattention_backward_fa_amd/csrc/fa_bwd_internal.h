@@ -58,7 +58,8 @@ struct KernelArgs {
   int32_t variant;        // 0 = 4-wavefront atomic kernel, 1 = 8-wavefront atomic kernel,
                           // 2 = atomic-free pair (dK/dV kernel + dQ kernel),
                           // 3 = fp32 debugging form (fp32 outputs),
-                          // 4 = dS-store pair (dK/dV kernel storing dS + dQ GEMM)
+                          // 4 = dS-store pair (dK/dV kernel storing dS + dQ GEMM),
+                          // 5 = fused small-sequence kernel (one launch)
   int32_t heads_per_job;  // query heads of a GQA group handled by one workgroup
   int32_t q_splits;       // query-range splits of one key tile (atomic-free pair only)
   int32_t n_partials;     // fp32 dK/dV partial sums per key tile (atomic-free pair only)
@@ -103,6 +104,20 @@ int launch_reduce_parts(const KernelArgs& a, void* stream);
 int launch_dq_finalize(const KernelArgs& a, void* stream);
 int launch_forward(const KernelArgs& a, void* out, float* lse, void* stream);
 
+// Fused small-sequence kernel (fa_bwd_fused_kernels.hip): one workgroup per
+// (sequence, KV head) holds the whole key range (at most FUSED_MAX_KEYS keys)
+// and forms sfmg, dK, dV and dQ for the G query heads in one launch.  The
+// planner takes it by default when a workgroup has at most FUSED_MAX_BLOCKS
+// (query head, 32-row block) items.
+constexpr int FUSED_MAX_KEYS = 128;
+constexpr int FUSED_MAX_BLOCKS = 64;
+bool fused_instantiated(int D, int Dv);
+int launch_fused(const KernelArgs& a, void* stream);
+
+// Compute units of the current HIP device, or 0 when it cannot be read.
+int device_cu_count();
+
+
 // fp32 debugging form (fa_bwd_f32_kernels.hip): dK/dV and dQ, fp32 outputs.
 int launch_f32_debug(const KernelArgs& a, void* stream);
 bool main_instantiated(int D, int Dv);
@@ -112,7 +127,10 @@ struct Profiler;
 Profiler* profiler_create(int slots);   // nullptr on failure
 void profiler_destroy(Profiler* p);
 int profiler_begin(Profiler* p, void* stream);
+int profiler_mark(Profiler* p, void* stream);  // boundary between the two main kernels
 int profiler_end(Profiler* p, void* stream);
-int profiler_read(Profiler* p, float* ms, int cap, int* count);
+// second == nullptr: whole spans into ms; else the parts before and after the
+// mark (ms, second), or the whole span and 0 for runs without a mark
+int profiler_read(Profiler* p, float* ms, float* second, int cap, int* count);
 
 }  // namespace fabwd

@@ -775,6 +775,13 @@ int launch_dq_finalize(const KernelArgs& a, void* stream) {
   return e;
 }
 
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 bool main_instantiated(int D, int Dv) {
   return (D == 64 && Dv == 64) || (D == 128 && (Dv == 64 || Dv == 128)) || (D == 192 && (Dv == 64 || Dv == 128));
 }
@@ -816,17 +823,22 @@ struct Profiler {
   int next = 0;    // slot of the next begin/end pair
   int count = 0;   // recorded pairs not yet read
   hipEvent_t* start = nullptr;
+  hipEvent_t* mid = nullptr;   // boundary between the two main kernels
   hipEvent_t* stop = nullptr;
+  bool* has_mid = nullptr;
 };
 
 Profiler* profiler_create(int slots) {
   Profiler* p = new (std::nothrow) Profiler();
   if (!p) return nullptr;
   p->start = new (std::nothrow) hipEvent_t[slots]();
+  p->mid = new (std::nothrow) hipEvent_t[slots]();
   p->stop = new (std::nothrow) hipEvent_t[slots]();
-  if (!p->start || !p->stop) { profiler_destroy(p); return nullptr; }
+  p->has_mid = new (std::nothrow) bool[slots]();
+  if (!p->start || !p->mid || !p->stop || !p->has_mid) { profiler_destroy(p); return nullptr; }
   for (int i = 0; i < slots; ++i) {
-    if (hipEventCreate(&p->start[i]) != hipSuccess || hipEventCreate(&p->stop[i]) != hipSuccess) {
+    if (hipEventCreate(&p->start[i]) != hipSuccess || hipEventCreate(&p->mid[i]) != hipSuccess ||
+        hipEventCreate(&p->stop[i]) != hipSuccess) {
       p->slots = i + 1;
       profiler_destroy(p);
       return nullptr;
@@ -840,15 +852,24 @@ void profiler_destroy(Profiler* p) {
   if (!p) return;
   for (int i = 0; i < p->slots; ++i) {
     if (p->start && p->start[i]) (void)hipEventDestroy(p->start[i]);
+    if (p->mid && p->mid[i]) (void)hipEventDestroy(p->mid[i]);
     if (p->stop && p->stop[i]) (void)hipEventDestroy(p->stop[i]);
   }
   delete[] p->start;
+  delete[] p->mid;
   delete[] p->stop;
+  delete[] p->has_mid;
   delete p;
 }
 
 int profiler_begin(Profiler* p, void* stream) {
+  p->has_mid[p->next] = false;
   return (int)hipEventRecord(p->start[p->next], static_cast<hipStream_t>(stream));
+}
+
+int profiler_mark(Profiler* p, void* stream) {
+  p->has_mid[p->next] = true;
+  return (int)hipEventRecord(p->mid[p->next], static_cast<hipStream_t>(stream));
 }
 
 int profiler_end(Profiler* p, void* stream) {
@@ -858,13 +879,21 @@ int profiler_end(Profiler* p, void* stream) {
   return e;
 }
 
-int profiler_read(Profiler* p, float* ms, int cap, int* count) {
+int profiler_read(Profiler* p, float* ms, float* second, int cap, int* count) {
   const int n = p->count < cap ? p->count : cap;
   const int first = (p->next - p->count + p->slots) % p->slots;  // oldest recorded slot
   for (int i = 0; i < n; ++i) {
     const int k = (first + (p->count - n) + i) % p->slots;     // newest n, oldest first
     if (hipEventSynchronize(p->stop[k]) != hipSuccess) return 1;
-    if (hipEventElapsedTime(&ms[i], p->start[k], p->stop[k]) != hipSuccess) return 1;
+    if (!second) {
+      if (hipEventElapsedTime(&ms[i], p->start[k], p->stop[k]) != hipSuccess) return 1;
+    } else if (p->has_mid[k]) {
+      if (hipEventElapsedTime(&ms[i], p->start[k], p->mid[k]) != hipSuccess) return 1;
+      if (hipEventElapsedTime(&second[i], p->mid[k], p->stop[k]) != hipSuccess) return 1;
+    } else {
+      if (hipEventElapsedTime(&ms[i], p->start[k], p->stop[k]) != hipSuccess) return 1;
+      second[i] = 0.f;
+    }
   }
   *count = n;
   p->count = 0;

@@ -6,10 +6,11 @@ current stream.  If the library is missing this module raises on use; there
 is no fallback.
 
 The signature of flash_attn_grad follows the page "CANN ops-transformer
-FlashAttnGrad 算子详解", section 四 4.2 (function prototype), without the
-options this library does not build (seqused_q/kv, sinks, attn_mask,
-metadata) and with one layout for q, kv and out (section 四 4.6 requires them
-equal).
+FlashAttnGrad 算子详解", section 四 4.2 (function prototype), with
+seqused_q / seqused_kv, without the options this library does not build
+(sinks, attn_mask, metadata), with one layout for q, kv and out (section 四
+4.6 requires them equal), and with the library's own choices appended: the dQ
+strategy (dq_mode), a workspace bound and the fp32 debugging form.
 """
 
 import ctypes
@@ -19,7 +20,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libfa_bwd.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 FA_OK = 0
 FA_ERR_NULLPTR = 1
@@ -35,11 +36,13 @@ FLAG_FP32_OUT = 0x2
 DTYPE_BF16 = 0
 DTYPE_FP16 = 1
 
-# fa_bwd_plan_dq_path values
-DQ_PATHS = {0: "recompute", 1: "stored_ds", 2: "atomic", 3: "fp32_form"}
+# FA_DQ_* of include/fa_bwd.h: fa_bwd_desc.dq_mode takes the names, and
+# fa_bwd_plan_dq_path reports one of them (never "auto")
+DQ_MODES = {"auto": 0, "stored_ds": 1, "recompute": 2, "atomic": 3, "fused": 4}
+DQ_PATHS = {1: "stored_ds", 2: "recompute", 3: "atomic", 4: "fused", 5: "fp32_form"}
 
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_plan_dq_path", "fa_bwd_profile_enable",
-            "fa_bwd_profile_read", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version",
+            "fa_bwd_profile_read", "fa_bwd_profile_read_split", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version",
             "fa_floyd_workspace_size", "fa_floyd_bwd_run", "fa_floyd_bwd_run_timed", "fa_floyd_fwd_run")
 
 
@@ -80,6 +83,9 @@ class FaBwdDesc(ctypes.Structure):
         ("win_left", ctypes.c_int32),
         ("win_right", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("dq_mode", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("max_workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -123,6 +129,9 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int)]
     lib.fa_bwd_profile_read.restype = ctypes.c_int
+    lib.fa_bwd_profile_read_split.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                              ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.fa_bwd_profile_read_split.restype = ctypes.c_int
     lib.fa_bwd_destroy.argtypes = [vp]
     lib.fa_bwd_destroy.restype = ctypes.c_int
     lib.fa_bwd_strerror.argtypes = [ctypes.c_int]
@@ -148,8 +157,20 @@ def strerror(status):
     return load_library().fa_bwd_strerror(int(status)).decode()
 
 
+def dq_mode_value(m):
+    """FA_DQ_* code of a dq_mode given by name ("auto", "stored_ds",
+    "recompute", "atomic", "fused") or number."""
+    if isinstance(m, str):
+        try:
+            return DQ_MODES[m.lower()]
+        except KeyError:
+            raise ValueError(f"unknown dq_mode {m!r}; one of {sorted(DQ_MODES)}") from None
+    return int(m)
+
+
 def make_desc(layout, B, N1, N2, S1, S2, D, Dv, T1=0, T2=0, softmax_scale=0.0, mask_mode=0,
-              win_left=-1, win_right=-1, flags=0, host_cu_q=None, host_cu_kv=None, dtype=0):
+              win_left=-1, win_right=-1, flags=0, host_cu_q=None, host_cu_kv=None, dtype=0, dq_mode=0,
+              num_cus=0, max_workspace_bytes=0):
     """Fill an fa_bwd_desc.  host_cu_q/kv: optional int32 ctypes arrays kept
     alive by the caller until fa_bwd_create returns."""
     d = FaBwdDesc()
@@ -165,6 +186,9 @@ def make_desc(layout, B, N1, N2, S1, S2, D, Dv, T1=0, T2=0, softmax_scale=0.0, m
     d.mask_mode = mask_mode_value(mask_mode)
     d.win_left, d.win_right = win_left, win_right
     d.flags = flags
+    d.dq_mode = dq_mode_value(dq_mode)
+    d.num_cus = int(num_cus)
+    d.max_workspace_bytes = int(max_workspace_bytes)
     return d
 
 
@@ -222,6 +246,17 @@ class Plan:
         if st != FA_OK:
             raise FaBwdError(st, "fa_bwd_profile_read")
         return [buf[i] for i in range(n.value)]
+
+    def profile_read_split(self, cap):
+        """[(first kernel ms, second kernel ms)] of the recorded runs; see
+        fa_bwd_profile_read_split."""
+        a = (ctypes.c_float * max(int(cap), 1))()
+        b = (ctypes.c_float * max(int(cap), 1))()
+        n = ctypes.c_int()
+        st = self._lib.fa_bwd_profile_read_split(self.handle, a, b, int(cap), ctypes.byref(n))
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_profile_read_split")
+        return [(a[i], b[i]) for i in range(n.value)]
 
     def sfmg(self, dout, attn_out, cu_q, out, stream):
         st = self._lib.fa_bwd_sfmg(self.handle, dout, attn_out, cu_q, out, stream)
@@ -281,12 +316,14 @@ def _check(name, t, dtype, device):
 
 def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0,
              mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1,
-             deterministic=False, host_cu_seqlens=None, fp32_out=False):
+             deterministic=False, host_cu_seqlens=None, fp32_out=False, dq_mode="auto", max_workspace_bytes=0):
     """Create (or reuse) the plan for these shapes, element type and attributes."""
     sh = _shapes(q, k, v, layout)
     dt = _dtype_code(q)
     flags = (FLAG_DETERMINISTIC if deterministic else 0) | (FLAG_FP32_OUT if fp32_out else 0)
     mm = mask_mode_value(mask_mode)
+    dm = dq_mode_value(dq_mode)
+    extra = dict(dq_mode=dm, max_workspace_bytes=int(max_workspace_bytes))
     if layout == "TND":
         if cu_seqlens_q is None or cu_seqlens_kv is None:
             raise ValueError("TND needs cu_seqlens_q and cu_seqlens_kv")
@@ -300,21 +337,22 @@ def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, soft
             hk = [int(x) for x in cu_seqlens_kv.cpu().tolist()]
         key = ("TND", B, sh["N1"], sh["N2"], sh["D"], sh["Dv"], sh["T1"], sh["T2"], max_seqlen_q,
                max_seqlen_kv, tuple(hq) if hq else None, tuple(hk) if hk else None, float(softmax_scale),
-               mm, win_left, win_right, flags, dt)
+               mm, win_left, win_right, flags, dt, dm, int(max_workspace_bytes))
         if key not in _plans:
             aq = (ctypes.c_int32 * len(hq))(*hq) if hq else None
             ak = (ctypes.c_int32 * len(hk))(*hk) if hk else None
             d = make_desc("TND", B, sh["N1"], sh["N2"], max_seqlen_q, max_seqlen_kv, sh["D"], sh["Dv"],
-                          sh["T1"], sh["T2"], softmax_scale, mm, win_left, win_right, flags, aq, ak, dtype=dt)
+                          sh["T1"], sh["T2"], softmax_scale, mm, win_left, win_right, flags, aq, ak, dtype=dt,
+                          **extra)
             _plans[key] = Plan(d)
         return _plans[key]
     if cu_seqlens_q is not None or cu_seqlens_kv is not None:
         raise ValueError("cu_seqlens are only accepted with the TND layout")
     key = (layout, sh["B"], sh["N1"], sh["N2"], sh["S1"], sh["S2"], sh["D"], sh["Dv"], float(softmax_scale), mm,
-           win_left, win_right, flags, dt)
+           win_left, win_right, flags, dt, dm, int(max_workspace_bytes))
     if key not in _plans:
         d = make_desc(layout, sh["B"], sh["N1"], sh["N2"], sh["S1"], sh["S2"], sh["D"], sh["Dv"], 0, 0,
-                      softmax_scale, mm, win_left, win_right, flags, dtype=dt)
+                      softmax_scale, mm, win_left, win_right, flags, dtype=dt, **extra)
         _plans[key] = Plan(d)
     return _plans[key]
 
@@ -322,7 +360,7 @@ def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, soft
 def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None,
                     softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
                     max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None,
-                    fp32_out=False, seqused_q=None, seqused_kv=None):
+                    fp32_out=False, seqused_q=None, seqused_kv=None, dq_mode="auto", max_workspace_bytes=0):
     """dq, dk, dv of attention on the current HIP stream, in the inputs' element
     type (bf16 or fp16).
 
@@ -334,7 +372,10 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
     fp32_out=True selects the fp32 debugging form (float32 outputs, P and dS
     kept in fp32; slow).  seqused_q / seqused_kv: optional int32 device
     tensors [B]; only the first seqused[b] rows / keys of sequence b take part
-    and the gradients of the rest are zero.
+    and the gradients of the rest are zero.  dq_mode: how dQ is formed
+    ("auto", "stored_ds", "recompute", "atomic" or "fused"; see FA_DQ_* in
+    include/fa_bwd.h); max_workspace_bytes: an upper bound on the workspace
+    the plan may ask for (0 = none).
     """
     import torch
 
@@ -354,7 +395,8 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
         raise ValueError("dout and attn_out must have the same shape")
     seqused_q, seqused_kv = _seqused(seqused_q, dev), _seqused(seqused_kv, dev)
     plan = get_plan(q, k, v, layout, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode, win_left, win_right,
-                    max_seqlen_q, max_seqlen_kv, deterministic, fp32_out=fp32_out)
+                    max_seqlen_q, max_seqlen_kv, deterministic, fp32_out=fp32_out, dq_mode=dq_mode,
+                    max_workspace_bytes=max_workspace_bytes)
     odt = torch.float32 if fp32_out else q.dtype
     if out is None:
         dq, dk, dv = (torch.empty(t.shape, dtype=odt, device=dev) for t in (q, k, v))

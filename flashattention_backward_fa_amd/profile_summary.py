@@ -43,8 +43,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc")
 # the sources the timed dK/dV and dQ kernels are compiled from
-KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_det_kernels.hip", "fa_bwd_schedule.h",
-                                                    "fa_bwd_internal.h"))
+KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_det_kernels.hip", "fa_bwd_tiles.h",
+                                                    "fa_bwd_schedule.h", "fa_bwd_internal.h"))
 # the sources the Floyd attention kernels are compiled from
 FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h"))
 SOURCES = {"det": KERNEL_SRCS, "floyd": FLOYD_SRCS}
@@ -93,6 +93,7 @@ def traffic(args):
     f_scale = COPY_BYTES / (cf * 1024.0)
     w_scale = COPY_BYTES / (cw * 1024.0)
     lines = []
+    per_kernel = []
     total = 0.0
     for n in names:
         f = statistics.median(_per_dispatch(args.fetch, "FETCH_SIZE", lambda k, n=n: n in k))
@@ -100,6 +101,7 @@ def traffic(args):
         fb, wb = f * 1024.0 * f_scale, w * 1024.0 * w_scale
         total += fb + wb
         lines.append(f"# {n}: FETCH_SIZE {f:.0f} KiB -> {fb / 2**20:.1f} MiB, WRITE_SIZE {w:.0f} KiB -> {wb / 2**20:.1f} MiB")
+        per_kernel.append(f"hbm_bytes_per_launch.{n}: {fb + wb:.0f}")
     src_hash = kernel_code_hash(SOURCES[args.sources])
     out = [
         f"# HBM traffic per launch of {'+'.join(names)}, workload {args.workload}",
@@ -109,6 +111,7 @@ def traffic(args):
         *lines,
         f"kernel_code_sha256_16: {src_hash}",
         f"hbm_bytes_per_launch: {total:.0f}",
+        *per_kernel,
     ]
     text = "\n".join(out) + "\n"
     if args.out:

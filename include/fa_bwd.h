@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 2
+#define FA_BWD_ABI_VERSION 3
 
 /* Status codes.  The classes mirror the aclnn error families that page
  * "aclnnFusedFloydAttentionGrad" lists (null pointer 161001, invalid
@@ -81,13 +81,56 @@ enum { FA_LAYOUT_BSND = 0, FA_LAYOUT_BNSD = 1, FA_LAYOUT_TND = 2 };
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_WINDOW = 2 };
 
 /* flags */
-#define FA_FLAG_DETERMINISTIC 0x1u /* bitwise-repeatable results; the default paths already are */
+/* Bitwise-repeatable results.  Every dQ mode but FA_DQ_ATOMIC already gives
+ * them; with FA_DQ_AUTO the flag only keeps the plan off the atomic mode, and
+ * asking for FA_DQ_ATOMIC together with it is FA_ERR_PARAM_INVALID. */
+#define FA_FLAG_DETERMINISTIC 0x1u
 /* fp32 debugging form (not on the page; it checks the arithmetic of section 一
  * at fp32 accuracy): dq, dk, dv are float32 arrays with the shapes and layouts
  * of q, k, v; P and dS are kept in fp32 and every product is an fp32 FMA, so
  * the only 16-bit roundings are those of the inputs.  Slow (VALU, untuned);
- * deterministic.  Overrides FA_FLAG_DETERMINISTIC's kernel choice. */
+ * deterministic.  Takes dq_mode FA_DQ_AUTO only. */
 #define FA_FLAG_FP32_OUT 0x2u
+
+/* How dQ = scale * dS K is formed (fa_bwd_desc.dq_mode; fa_bwd_plan_dq_path
+ * reports the plan's choice).  The page's own kernel adds dQ across key tiles
+ * with atomic adds into an fp32 workspace (section 五 5.2); FA_DQ_ATOMIC is
+ * that strategy.  The others write every dQ element once and are bitwise
+ * repeatable.
+ *   FA_DQ_AUTO      : desc only.  fa_bwd_create picks FA_DQ_FUSED for small
+ *                     problems (below), else FA_DQ_STORED_DS when the dS of
+ *                     at least one key/value head fits the workspace bound,
+ *                     else FA_DQ_RECOMPUTE.
+ *   FA_DQ_STORED_DS : the dK/dV kernel also stores dS (the element type, 2
+ *                     bytes per (row, key) of each 32 x 32 tile a 128-row
+ *                     query group sees) in the workspace and a GEMM kernel
+ *                     reads it back; whole key/value heads are processed in
+ *                     chunks that fit the bound.
+ *   FA_DQ_RECOMPUTE : a query-tile-parallel kernel recomputes S and dP and
+ *                     writes dQ; no dS in the workspace (the page's low-memory
+ *                     property: nothing of size S1 x S2 is kept).
+ *   FA_DQ_ATOMIC    : fp32 atomic adds into a dQ workspace, then a cast;
+ *                     not bitwise repeatable; bf16 only and no seqused
+ *                     (FA_ERR_UNSUPPORTED otherwise).
+ *   FA_DQ_FUSED     : the page's per-head small-sequence schedule
+ *                     (flash_attn_grad_bn2, section 五 5.2): one launch, one
+ *                     workgroup per (sequence, key/value head) forms sfmg, dK,
+ *                     dV and dQ for all the head group's query rows, with no
+ *                     workspace.  Needs the longest key sequence <= 128,
+ *                     G * ceil(S1 / 32) <= 64 (G = N1 / N2, S1 the longest
+ *                     query sequence) and (D, Dv) in {(64, 64), (128, 64),
+ *                     (128, 128)}, FA_ERR_UNSUPPORTED otherwise; AUTO takes
+ *                     it whenever these hold.
+ *   FA_DQ_FP32_FORM : reported only: the fp32 debugging form
+ *                     (FA_FLAG_FP32_OUT), which takes FA_DQ_AUTO only. */
+enum {
+  FA_DQ_AUTO = 0,
+  FA_DQ_STORED_DS = 1,
+  FA_DQ_RECOMPUTE = 2,
+  FA_DQ_ATOMIC = 3,
+  FA_DQ_FUSED = 4,
+  FA_DQ_FP32_FORM = 5
+};
 
 typedef struct fa_bwd_plan_s* fa_bwd_plan; /* opaque, host memory only */
 
@@ -111,21 +154,41 @@ typedef struct fa_bwd_desc {
   int32_t mask_mode;     /* FA_MASK_*                                             */
   int32_t win_left, win_right; /* window bounds, -1 = unbounded                  */
   uint32_t flags;        /* FA_FLAG_*                                             */
+  /* ABI version 3 */
+  int32_t dq_mode;       /* FA_DQ_* (FA_DQ_AUTO = 0: the planner's choice)        */
+  int32_t num_cus;       /* compute units the job split fills; 0 = those of the
+                            current HIP device, read once per process (256, an
+                            MI355X, when no device is visible)                  */
+  uint64_t max_workspace_bytes; /* upper bound on the workspace; 0 = none (the
+                            stored dS is then kept below 4 GiB per chunk of
+                            key/value heads).  The planner fits the dS chunk,
+                            then the dK/dV partial sums, inside the bound and
+                            falls back to FA_DQ_RECOMPUTE (under FA_DQ_AUTO)
+                            when not even one head's dS fits              */
 } fa_bwd_desc;
 
 /* Validate `desc` (all rules of section 四 4.6 that this library enforces) and
  * build a plan.  On success *plan receives a new plan and *workspace_bytes the
- * device workspace size fa_bwd_run needs.  Pure host code: no HIP call, no
- * device memory.  The workspace holds sfmg, fp32 dK/dV partial sums when the
- * plan splits a key tile over jobs, and dS (the page's dS = P (.) (dP - sfmg),
- * rounded to the element type) for the dQ product: 2 bytes per (row, key) of
- * each 128-row query group and each 32-key slice that group can see (every
- * slice of the longest key sequence unless both window bounds are given).
- * Where that dS would exceed 4 GiB the workspace holds the dS of as many
- * whole key/value heads as fit and fa_bwd_run processes the heads in such
- * chunks; only where one key/value head's dS alone exceeds 4 GiB does the
- * plan recompute S and dP for dQ instead, with no dS in the workspace.  Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
- * FA_ERR_PARAM_INVALID, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED; *plan is left NULL. */
+ * device workspace size fa_bwd_run needs (never above max_workspace_bytes when
+ * that is set).  Host code only; its one HIP call is the CU-count query when
+ * num_cus = 0 (made once per process).
+ * Workspace (float32 parts, 256-byte aligned, in this order):
+ *   sfmg                 : 4 * (query rows x N1) bytes (not for FA_DQ_FUSED);
+ *   dQ accumulator       : FA_DQ_ATOMIC only, 4 bytes per element of q;
+ *   dK / dV partial sums : when the job split gives a key tile to several
+ *                          workgroups (query heads of a GQA group or query
+ *                          ranges), n_partials fp32 copies of k and of v;
+ *   dS                   : FA_DQ_STORED_DS only, 8 KB per (128-row query
+ *                          group, query head of a chunk, 32-key slice of the
+ *                          group's band); the band is every slice of the
+ *                          longest key sequence unless both window bounds are
+ *                          given.
+ * Errors: FA_ERR_NULLPTR (desc/plan/workspace_bytes NULL),
+ * FA_ERR_PARAM_INVALID (also: dq_mode unknown, FA_DQ_ATOMIC with
+ * FA_FLAG_DETERMINISTIC, an explicit dq_mode with FA_FLAG_FP32_OUT, num_cus
+ * < 0), FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (also: FA_DQ_ATOMIC with fp16,
+ * FA_DQ_FUSED outside its limits), FA_ERR_WORKSPACE (max_workspace_bytes
+ * below what the requested or any mode needs); *plan is left NULL. */
 int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_bytes);
 
 /* Enqueue the backward on `stream` (a hipStream_t; NULL = the null stream).
@@ -145,8 +208,8 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
  *                             used lengths; the rest is padding that nothing
  *                             attends and whose dq / dk / dv rows are written
  *                             as zeros.  NULL: every row takes part.  Any layout.
- *                             Not available with the tuning-only atomic kernels
- *                             (FA_ERR_UNSUPPORTED).
+ *                             Not available with FA_DQ_ATOMIC
+ *                             (FA_ERR_UNSUPPORTED, returned before any launch).
  *   dq, dk, dv              : outputs of the plan's element type, shapes of
  *                             q, k, v
  *   workspace               : device memory of at least *workspace_bytes from
@@ -184,17 +247,9 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v,
                const int32_t* seqused_q, const int32_t* seqused_kv,
                void* attn_out, float* softmax_lse, void* stream);
 
-/* How a plan forms dQ (fa_bwd_create picks it; see there).  Every path but
- * FA_DQ_ATOMIC is bitwise repeatable.
- *   FA_DQ_RECOMPUTE : a query-tile-parallel kernel recomputes S and dP and
- *                     writes dQ = scale * dS K once (when one key/value
- *                     head's stored dS would exceed 4 GiB)
- *   FA_DQ_STORED_DS : the dK/dV kernel also stores dS (element type) in the
- *                     workspace and a GEMM kernel reads it back (default)
- *   FA_DQ_ATOMIC    : fp32 atomic adds into the workspace (tuning only)
- *   FA_DQ_FP32_FORM : the fp32 debugging form (FA_FLAG_FP32_OUT)
- * Writes the path to *path.  Errors: FA_ERR_NULLPTR. */
-enum { FA_DQ_RECOMPUTE = 0, FA_DQ_STORED_DS = 1, FA_DQ_ATOMIC = 2, FA_DQ_FP32_FORM = 3 };
+/* How the plan forms dQ: one of FA_DQ_STORED_DS, FA_DQ_RECOMPUTE,
+ * FA_DQ_ATOMIC, FA_DQ_FUSED, FA_DQ_FP32_FORM (see fa_bwd_desc.dq_mode).
+ * Writes it to *path.  Errors: FA_ERR_NULLPTR. */
 int fa_bwd_plan_dq_path(fa_bwd_plan plan, int* path);
 
 /* Timing hook.  With slots > 0, every later fa_bwd_run records one pair of
@@ -211,6 +266,16 @@ int fa_bwd_profile_enable(fa_bwd_plan plan, int slots);
  * most `slots` entries); the ring is then emptied.  Errors: FA_ERR_NULLPTR,
  * FA_ERR_RUNTIME (an event query failed). */
 int fa_bwd_profile_read(fa_bwd_plan plan, float* ms, int cap, int* count);
+
+/* The same recorded runs as fa_bwd_profile_read (and the same emptying of
+ * the ring), each split at the boundary between its two main kernels, where
+ * the run records a third event: first_ms[i] is the first kernel (the dK/dV
+ * kernel under FA_DQ_STORED_DS, the dQ kernel under FA_DQ_RECOMPUTE) and
+ * second_ms[i] the other.  Runs with a single main kernel (FA_DQ_FUSED,
+ * FA_DQ_ATOMIC, the fp32 form) or with dS processed in several chunks of
+ * key/value heads record no boundary: their whole span goes to first_ms[i]
+ * and second_ms[i] is 0.  Errors: FA_ERR_NULLPTR, FA_ERR_RUNTIME. */
+int fa_bwd_profile_read_split(fa_bwd_plan plan, float* first_ms, float* second_ms, int cap, int* count);
 
 /* Free a plan (and its timing events).  NULL is a no-op.  Returns FA_OK. */
 int fa_bwd_destroy(fa_bwd_plan plan);

@@ -40,14 +40,14 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.fa_bwd_abi_version() == fb.ABI_VERSION == 2
+    assert lib.fa_bwd_abi_version() == fb.ABI_VERSION == 3
     for st in range(0, 7):
         assert len(fb.strerror(st)) > 0
     assert fb.strerror(99) == "unknown status"
 
 
 def create(lib, **kw):
-    base = dict(layout="BSND", B=2, N1=8, N2=2, S1=128, S2=128, D=128, Dv=128)
+    base = dict(layout="BSND", B=2, N1=8, N2=2, S1=256, S2=256, D=128, Dv=128, num_cus=256)
     base.update(kw)
     d = fb.make_desc(**base)
     h = ctypes.c_void_p()
@@ -74,8 +74,8 @@ def test_valid_problem_and_workspace_size(lib):
     # 16 fp32 partial sums of dK and of dV per key.
     st, ws = create(lib)
     assert st == fb.FA_OK
-    lse, k_elems = 2 * 8 * 128, 2 * 128 * 2 * 128
-    assert ws == rnd(lse * 4) + 2 * rnd(16 * k_elems * 4) + rnd(ds(2, 8, 128, 128))
+    lse, k_elems = 2 * 8 * 256, 2 * 256 * 2 * 128
+    assert ws == rnd(lse * 4) + 2 * rnd(16 * k_elems * 4) + rnd(ds(2, 8, 256, 256))
     # ragged lengths round up to whole tiles
     st, ws = create(lib, B=64, N1=8, N2=8, S1=200, S2=300)
     assert st == fb.FA_OK and ws == rnd(64 * 8 * 200 * 4) + rnd(ds(64, 8, 200, 300))
@@ -91,9 +91,12 @@ def test_valid_problem_and_workspace_size(lib):
     assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4) + rnd(ds(1, 16, 16384, 8192))
     st, ws = create(lib, B=1, N1=32, N2=32, S1=8192, S2=8192)   # exactly 4 GiB: one pass
     assert st == fb.FA_OK and ws == rnd(32 * 8192 * 4) + rnd(ds(1, 32, 8192, 8192))
-    # GQA: a chunk is whole KV heads (4 query heads each): 8 GiB -> 4 of 8 KV heads
+    # GQA: a chunk is whole KV heads (4 query heads each): 8 GiB -> 4 of 8 KV
+    # heads; the job split is sized for the 4 heads of one launch (64 tiles x
+    # 4 heads x 2 query-head slots = 512 jobs), so 2 partial sums of dK and dV
     st, ws = create(lib, B=1, N1=32, N2=8, S1=16384, S2=8192)
-    assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4) + rnd(ds(1, 16, 16384, 8192))
+    kv = rnd(8192 * 8 * 128 * 4)
+    assert st == fb.FA_OK and ws == rnd(32 * 16384 * 4) + 2 * 2 * kv + rnd(ds(1, 16, 16384, 8192))
     # one KV head past the cap (64 GiB of dS for its 8 query heads): the plan
     # recomputes S and dP for dQ and the workspace holds sfmg only
     st, ws = create(lib, B=1, N1=8, N2=1, S1=65536, S2=65536)
@@ -108,7 +111,7 @@ def test_valid_problem_and_workspace_size(lib):
 
 
 def dq_path(lib, **kw):
-    base = dict(layout="BSND", B=2, N1=8, N2=2, S1=128, S2=128, D=128, Dv=128)
+    base = dict(layout="BSND", B=2, N1=8, N2=2, S1=256, S2=256, D=128, Dv=128)
     base.update(kw)
     d = fb.make_desc(**base)
     h, ws, out = ctypes.c_void_p(), ctypes.c_size_t(), ctypes.c_int(-1)
@@ -120,39 +123,107 @@ def dq_path(lib, **kw):
     return fb.DQ_PATHS[out.value]
 
 
-def test_plan_dq_path(lib, monkeypatch):
+def test_plan_dq_path(lib):
     assert dq_path(lib) == "stored_ds"
     assert dq_path(lib, layout="BNSD", mask_mode=1) == "stored_ds"
     assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "stored_ds"
-    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "stored_ds"
+    assert dq_path(lib, layout="TND", S1=256, S2=256, T1=1024, T2=1024) == "stored_ds"
     assert dq_path(lib, B=1, N1=32, N2=32, S1=16384, S2=8192) == "stored_ds"  # chunked
     assert dq_path(lib, B=1, N1=8, N2=1, S1=65536, S2=65536) == "recompute"  # one KV head past 4 GiB
     assert dq_path(lib, flags=fb.FLAG_FP32_OUT) == "fp32_form"
-    monkeypatch.setenv("FA_BWD_VARIANT", "2")
-    assert dq_path(lib) == "recompute"
-    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "recompute"
-    monkeypatch.setenv("FA_BWD_VARIANT", "4")
-    assert dq_path(lib, B=1, N1=8, N2=1, S1=65536, S2=65536) == "stored_ds"
-    monkeypatch.setenv("FA_BWD_VARIANT", "1")
-    assert dq_path(lib) == "atomic"
-    assert dq_path(lib, flags=fb.FLAG_DETERMINISTIC) == "recompute"
+    # short key sequences: one launch per (sequence, KV head)
+    assert dq_path(lib, S1=128, S2=128, D=64, Dv=64, B=1, N1=2, N2=2) == "fused"
+    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256) == "fused"
+    assert dq_path(lib, S1=2048, S2=128, N1=2, N2=2) == "fused"             # 64 (head, block) items
+    assert dq_path(lib, S1=2049, S2=128, N1=2, N2=2) == "stored_ds"         # 65
+    assert dq_path(lib, S1=128, S2=129) == "stored_ds"                       # two key tiles
+    assert dq_path(lib, S1=128, S2=128, D=192, Dv=128) == "stored_ds"        # not instantiated
+    # explicit modes
+    assert dq_path(lib, dq_mode="recompute") == "recompute"
+    assert dq_path(lib, layout="TND", S1=64, S2=64, T1=256, T2=256, dq_mode="recompute") == "recompute"
+    assert dq_path(lib, B=1, N1=8, N2=1, S1=65536, S2=65536, dq_mode="stored_ds") == "stored_ds"
+    assert dq_path(lib, dq_mode="atomic") == "atomic"
+    assert dq_path(lib, S1=128, S2=128, dq_mode="fused") == "fused"
+    assert dq_path(lib, S1=256, S2=256, dq_mode="stored_ds") == "stored_ds"
     out = ctypes.c_int()
     assert lib.fa_bwd_plan_dq_path(None, ctypes.byref(out)) == fb.FA_ERR_NULLPTR
 
 
-def test_ds_cap_override_chunks_kv_heads(lib, monkeypatch):
-    """FA_BWD_DS_CAP (bytes) lowers the cap: the workspace then holds the dS
-    of as many whole KV heads as fit (at least one)."""
+def test_dq_mode_rules(lib):
+    """dq_mode, num_cus and the determinism flag are checked in fa_bwd_create."""
+    assert create(lib, dq_mode=5)[0] == fb.FA_ERR_PARAM_INVALID                 # FP32_FORM is reported only
+    assert create(lib, dq_mode=-1)[0] == fb.FA_ERR_PARAM_INVALID
+    assert create(lib, dq_mode="atomic", flags=fb.FLAG_DETERMINISTIC)[0] == fb.FA_ERR_PARAM_INVALID
+    assert create(lib, dq_mode="recompute", flags=fb.FLAG_FP32_OUT)[0] == fb.FA_ERR_PARAM_INVALID
+    assert create(lib, dq_mode="atomic", dtype=fb.DTYPE_FP16)[0] == fb.FA_ERR_UNSUPPORTED
+    assert create(lib, dq_mode="fused", S1=256, S2=256)[0] == fb.FA_ERR_UNSUPPORTED      # keys past one tile
+    assert create(lib, dq_mode="fused", S1=4096, S2=128, N1=2, N2=2)[0] == fb.FA_ERR_UNSUPPORTED  # 128 items
+    assert create(lib, dq_mode="fused", S1=128, S2=128, D=192, Dv=128)[0] == fb.FA_ERR_UNSUPPORTED
+    assert create(lib, num_cus=-1)[0] == fb.FA_ERR_PARAM_INVALID
+    for m in ("stored_ds", "recompute", "fused"):
+        assert create(lib, dq_mode=m, flags=fb.FLAG_DETERMINISTIC, S1=128, S2=128)[0] == fb.FA_OK
+    # the fused kernel needs no workspace at all
+    assert create(lib, dq_mode="fused", S1=128, S2=128) == (fb.FA_OK, 0)
+
+
+def test_atomic_mode_rejects_seqused_before_any_launch(lib):
+    plan = fb.Plan(fb.make_desc("BSND", 1, 2, 2, 256, 256, 64, 64, dq_mode="atomic"))
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the check fails first
+    args = [fake] * 6 + [None, None] + [fake, None] + [fake] * 3
+    assert lib.fa_bwd_run(plan.handle, *args, fake, plan.workspace_bytes, None) == fb.FA_ERR_UNSUPPORTED
+    args = [fake] * 6 + [None, None] + [None, fake] + [fake] * 3
+    assert lib.fa_bwd_run(plan.handle, *args, fake, plan.workspace_bytes, None) == fb.FA_ERR_UNSUPPORTED
+
+
+def test_job_split_follows_num_cus(lib):
+    """The split targets two jobs per CU: more CUs, more partial sums."""
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # B=2, N1=8, N2=2 (G=4), S=128: 2 groups x 4 slices x 8 KB = 64 KiB per query head
-    per_q = 2 * 4 * 8192
-    base = rnd(2 * 8 * 128 * 4) + 2 * rnd(16 * (2 * 128 * 2 * 128) * 4)  # sfmg + 16 partial sums
-    assert create(lib) == (fb.FA_OK, base + rnd(8 * per_q))
-    monkeypatch.setenv("FA_BWD_DS_CAP", str(4 * per_q))      # exactly one KV head
-    assert create(lib) == (fb.FA_OK, base + rnd(4 * per_q))
-    monkeypatch.setenv("FA_BWD_DS_CAP", str(4 * per_q - 1))  # not even one: recompute
-    assert create(lib) == (fb.FA_OK, base)
-    assert dq_path(lib) == "recompute"
+    kw = dict(B=1, N1=32, N2=8, S1=4096, S2=4096, mask_mode=1)
+    lse, kv = rnd(32 * 4096 * 4), rnd(4096 * 8 * 128 * 4)
+    ds = rnd(32 * 32 * 128 * 8192)
+    # 256 CUs: 32 tiles x 8 KV heads x 2 query-head slots = 512 jobs, 2 partials
+    assert create(lib, num_cus=256, **kw) == (fb.FA_OK, lse + 2 * 2 * kv + ds)
+    # 128 CUs: 32 x 8 = 256 jobs already, no split and no partials
+    assert create(lib, num_cus=128, **kw) == (fb.FA_OK, lse + ds)
+    # 1024 CUs: 4 query-head slots x 2 query splits = 8 partials
+    assert create(lib, num_cus=1024, **kw) == (fb.FA_OK, lse + 2 * 8 * kv + ds)
+
+
+def test_workspace_bound_chunks_kv_heads(lib):
+    """max_workspace_bytes bounds the workspace: the dS chunk (whole KV heads)
+    shrinks to fit, then the split partials; below one KV head's dS the plan
+    recomputes S and dP for dQ (AUTO) or refuses (stored_ds forced)."""
+    rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # B=2, N1=8, N2=2 (G=4), S=256: 4 groups x 8 slices x 8 KB per query head
+    kw = dict(num_cus=256, S1=256, S2=256)
+    per_q = 4 * 8 * 8192
+    sf = rnd(2 * 8 * 256 * 4)
+    kv = rnd(2 * 256 * 2 * 128 * 4)              # one fp32 copy of k (or v)
+    # unbounded: both KV heads, 2 key tiles x 2 heads x 2 batches = 8 jobs -> 4 x 4 = 16 partials
+    st, ws = create(lib, **kw)
+    assert st == fb.FA_OK and ws == sf + 2 * 16 * kv + rnd(8 * per_q)
+    assert dq_path(lib, **kw) == "stored_ds"
+    # room for exactly one KV head's dS and nothing else: chunk of 1, no split
+    st, ws = create(lib, max_workspace_bytes=sf + 4 * per_q, **kw)
+    assert st == fb.FA_OK and ws == sf + 4 * per_q
+    # room for both KV heads' dS: the chunk is filled first, the split gets the rest
+    st, ws = create(lib, max_workspace_bytes=sf + 4 * per_q + 2 * 2 * kv, **kw)
+    assert st == fb.FA_OK and ws == sf + 8 * per_q
+    # both KV heads and two partial sums of dK and of dV (four do not fit)
+    st, ws = create(lib, max_workspace_bytes=sf + 8 * per_q + 2 * 2 * kv, **kw)
+    assert st == fb.FA_OK and ws == sf + 8 * per_q + 2 * 2 * kv
+    # not one KV head: AUTO recomputes, with as many partials as fit
+    st, ws = create(lib, max_workspace_bytes=sf + 4 * per_q - 1, **kw)
+    assert st == fb.FA_OK and ws <= sf + 4 * per_q - 1
+    assert dq_path(lib, max_workspace_bytes=sf + 4 * per_q - 1, **kw) == "recompute"
+    assert create(lib, max_workspace_bytes=sf, **kw) == (fb.FA_OK, sf)   # sfmg only: no split
+    assert create(lib, max_workspace_bytes=sf + 4 * per_q - 1, dq_mode="stored_ds", **kw)[0] == fb.FA_ERR_WORKSPACE
+    assert create(lib, max_workspace_bytes=sf - 1, **kw)[0] == fb.FA_ERR_WORKSPACE
+    assert create(lib, max_workspace_bytes=sf - 1, dq_mode="recompute", **kw)[0] == fb.FA_ERR_WORKSPACE
+    # the atomic mode's fp32 dQ accumulator must fit too
+    q_acc = rnd(2 * 256 * 8 * 128 * 4)
+    assert create(lib, dq_mode="atomic", max_workspace_bytes=sf + q_acc - 1, **kw)[0] == fb.FA_ERR_WORKSPACE
+    assert create(lib, dq_mode="fused", S1=128, S2=128, max_workspace_bytes=1)[0] == fb.FA_OK
 
 
 def test_tnd_workspace_band(lib):
@@ -265,7 +336,8 @@ def test_tnd_decreasing_cu_rejected(lib):
 
 
 def test_run_checks_before_any_device_call(lib):
-    plan = fb.Plan(fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64))
+    plan = fb.Plan(fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64, dq_mode="stored_ds"))
+    assert plan.workspace_bytes > 0
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every check below fails first
     # q k v dout attn_out lse | cu_q cu_kv | seqused_q seqused_kv | dq dk dv
     args = [fake] * 6 + [None, None] + [None, None] + [fake] * 3

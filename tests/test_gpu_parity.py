@@ -2,10 +2,12 @@
 
 Tolerance (bf16 outputs, per tensor, against the stored-mode oracle):
 relative Frobenius error <= 1e-2 and max |err| <= 2e-2 * max |ref|.
-Small cases compare every element; the four large workloads compare the
-sfmg preprocess on every row and dq/dk/dv on sampled rows that the oracle
-evaluates one by one (backward_rows), in the same launch configuration the
-benchmark times."""
+Every test compares every element of dq, dk and dv: the small edge cases,
+and the four large workloads at their full sizes in the launch configuration
+the benchmark times (the plan's own dQ mode) and through the recompute mode;
+the large workloads also check the sfmg preprocess on every row and, as a
+second, independent route, sampled rows that the oracle evaluates one by
+one (backward_rows)."""
 
 import math
 
@@ -118,15 +120,21 @@ def test_layouts_agree_bitwise_on_dk_dv():
 _cache = {}
 
 
-def big(name):
+def big(name, with_ref=True):
+    """Inputs, the oracle forward's stored Y / lse and (with_ref) the oracle's
+    whole backward of a named workload; one workload is cached at a time."""
     if name not in _cache:
         cfg = W.CONFIGS[name]
         x = W.make_inputs(cfg)
         say(f"[parity] {name}: oracle forward")
         Yst, lst = oracle_inputs(cfg, x)
         _cache.clear()
-        _cache[name] = (cfg, x, Yst, lst)
-    return _cache[name]
+        _cache[name] = {"cfg": cfg, "x": x, "Yst": Yst, "lst": lst, "ref": None}
+    c = _cache[name]
+    if with_ref and c["ref"] is None:
+        say(f"[parity] {name}: oracle backward (whole tensors)")
+        c["ref"] = oracle_backward(c["cfg"], c["x"], c["Yst"], c["lst"])
+    return c
 
 
 def sample_rows(cfg, x, n=40, seed=0):
@@ -156,48 +164,66 @@ def pick(arr, cfg, x, b, n, i, kind):
     return arr[b, n, i]
 
 
-@pytest.mark.parametrize("variant", ["plan", "2"])
-@pytest.mark.parametrize("name", ["mha_causal", "gqa_causal", "varlen_window", "wide_qk"])
-def test_parity_large_workload_sampled(name, variant):
-    """variant "plan": the chain fa_bwd_create picks (stored dS on these
-    workloads); "2": the recompute chain, which the plan takes only past 4 GiB
-    of dS, forced here at the benchmark's sizes."""
+LARGE = ["mha_causal", "gqa_causal", "varlen_window", "wide_qk"]
+
+
+def test_sfmg_preprocess_large_workloads():
+    """The preprocess kernel alone, every row of each large workload."""
     import torch
-    cfg, x, Yst, lst = big(name)
-    say(f"[parity] {name}: sfmg preprocess")
     import flashattention_backward_fa_amd as fa
     dev = torch.device("cuda", 0)
-    cu = torch.from_numpy(x["cu_q"]).to(dev) if cfg["layout"] == "TND" else None
-    mq, _ = max_lengths(cfg, x)
-    attn_out = torch.from_numpy(Yst).to(torch.bfloat16).to(dev)
-    s_gpu = fa.sfmg(x["dout"].to(dev), attn_out, cfg["layout"], cu, max_seqlen_q=mq).cpu().double().numpy()
-    s_ref = oracle.sfmg(f64(x["dout"]), Yst, cfg["layout"], x["cu_q"])
-    bound = 1e-5 * oracle.sfmg(np.abs(f64(x["dout"])), np.abs(Yst), cfg["layout"], x["cu_q"]) + 1e-30
-    assert np.all(np.abs(s_gpu - s_ref) <= bound)
+    for name in LARGE:
+        c = big(name, with_ref=False)
+        cfg, x, Yst = c["cfg"], c["x"], c["Yst"]
+        say(f"[parity] {name}: sfmg preprocess")
+        cu = torch.from_numpy(x["cu_q"]).to(dev) if cfg["layout"] == "TND" else None
+        mq, _ = max_lengths(cfg, x)
+        attn_out = torch.from_numpy(Yst).to(torch.bfloat16).to(dev)
+        s_gpu = fa.sfmg(x["dout"].to(dev), attn_out, cfg["layout"], cu, max_seqlen_q=mq).cpu().double().numpy()
+        s_ref = oracle.sfmg(f64(x["dout"]), Yst, cfg["layout"], x["cu_q"])
+        bound = 1e-5 * oracle.sfmg(np.abs(f64(x["dout"])), np.abs(Yst), cfg["layout"], x["cu_q"]) + 1e-30
+        assert np.all(np.abs(s_gpu - s_ref) <= bound)
 
-    say(f"[parity] {name}: backward ({variant})")
-    if variant == "plan":
-        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
-    else:
-        with _env(FA_BWD_VARIANT=variant):
-            gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+
+@pytest.mark.parametrize("name,dq_mode", [(n, m) for n in LARGE for m in ("auto", "recompute")])
+def test_parity_large_workload_full(name, dq_mode):
+    """Every element of dq, dk, dv of the full-size workload against the
+    oracle's whole backward.  dq_mode "auto": the plan fa_bwd_create picks
+    (stored dS on these workloads, as benchmarked); "recompute": the mode that
+    keeps no dS, forced here at the benchmark's sizes."""
+    import torch  # noqa: F401
+    import flashattention_backward_fa_amd as fa
+    c = big(name)
+    cfg, x, Yst, lst = c["cfg"], c["x"], c["Yst"], c["lst"]
+    say(f"[parity] {name}: backward ({dq_mode}) on the GPU")
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, dq_mode=dq_mode)
+    if dq_mode == "auto":
+        mq, mk = max_lengths(cfg, x)
+        plan = fa.fa_bwd.get_plan(x["q"].to("meta"), x["k"].to("meta"), x["v"].to("meta"), cfg["layout"],
+                                  *((None, None) if cfg["layout"] != "TND" else
+                                    (torch.from_numpy(x["cu_q"]), torch.from_numpy(x["cu_kv"]))),
+                                  cfg["softmax_scale"], cfg["mask_mode"], cfg["win_left"], cfg["win_right"], mq, mk)
+        assert plan.dq_path() == "stored_ds"
+    rq, rk, rv = c["ref"]
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+    assert np.all(np.isfinite(gq)) and np.all(np.isfinite(gk)) and np.all(np.isfinite(gv))
+    # a second route to the same numbers: rows the oracle evaluates one by one
     q_rows, kv_rows = sample_rows(cfg, x)
-    rq, rk, rv = oracle.backward_rows(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"]), Yst, lst, q_rows,
+    sq, sk, sv = oracle.backward_rows(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"]), Yst, lst, q_rows,
                                       kv_rows, cfg["layout"], x["cu_q"], x["cu_kv"], cfg["softmax_scale"],
                                       cfg["mask_mode"], cfg["win_left"], cfg["win_right"])
-    got_q = np.stack([pick(gq, cfg, x, b, n, i, "q") for (b, n, i) in q_rows])
-    got_k = np.stack([pick(gk, cfg, x, b, n, j, "kv") for (b, n, j) in kv_rows])
-    got_v = np.stack([pick(gv, cfg, x, b, n, j, "kv") for (b, n, j) in kv_rows])
-    assert_all_close([(got_q, np.stack(rq), "dq (sampled rows)"), (got_k, np.stack(rk), "dk (sampled rows)"),
-                      (got_v, np.stack(rv), "dv (sampled rows)")])
-    assert np.all(np.isfinite(gq)) and np.all(np.isfinite(gk)) and np.all(np.isfinite(gv))
+    for (b, n, i), r in zip(q_rows, sq):
+        assert np.allclose(pick(rq, cfg, x, b, n, i, "q"), r, rtol=1e-9, atol=1e-12)
+    for (b, n, j), r1, r2 in zip(kv_rows, sk, sv):
+        assert np.allclose(pick(rk, cfg, x, b, n, j, "kv"), r1, rtol=1e-9, atol=1e-12)
+        assert np.allclose(pick(rv, cfg, x, b, n, j, "kv"), r2, rtol=1e-9, atol=1e-12)
 
 
 # ------------------------------------------------------------------ kernel paths
 
 class _env:
-    """Set environment variables read by fa_bwd_create (kernel choice,
-    split override) and drop cached plans around the block."""
+    """Set environment variables read by fa_bwd_create (the job-split tuning
+    override) and drop cached plans around the block."""
 
     def __init__(self, **kv):
         self.kv = kv
@@ -223,17 +249,16 @@ class _env:
 ATOMIC_CASES = ["bsnd_causal_gqa4_ragged", "tnd_mixed_lengths", "bnsd_causal_s1_lt_s2_d192"]
 
 
-@pytest.mark.parametrize("variant", ["0", "1"])
 @pytest.mark.parametrize("name", ATOMIC_CASES)
-def test_atomic_dq_kernels_parity(variant, name):
-    """The fp32-atomic dQ kernels (kept for comparison) against the oracle."""
+def test_atomic_dq_mode_parity(name):
+    """dq_mode "atomic" (the page's fp32 atomic dQ, section 五 5.2) against the
+    oracle: the 8-wavefront kernel at D <= 128, the 4-wavefront one at D = 192."""
     cfg = EDGE_CASES[name]
-    say(f"[parity] atomic variant {variant}: {name}")
+    say(f"[parity] atomic dQ: {name}")
     x = case_inputs(cfg, seed=sorted(EDGE_CASES).index(name))
     Yst, lst = oracle_inputs(cfg, x)
     rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
-    with _env(FA_BWD_VARIANT=variant):
-        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, dq_mode="atomic")
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
 
 
@@ -250,81 +275,154 @@ def test_split_partials_parity(split):
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
 
 
-@pytest.mark.parametrize("variant", ["plan", "2"])
-def test_default_path_is_bitwise_repeatable(variant):
-    """No atomics on either default chain: two runs give identical bits."""
-    cfg = EDGE_CASES["tnd_mixed_lengths"]
+@pytest.mark.parametrize("dq_mode", ["auto", "recompute", "stored_ds", "fused"])
+def test_default_path_is_bitwise_repeatable(dq_mode):
+    """No atomics in any of these modes: two runs give identical bits (the
+    second with the determinism flag, which must not change the plan)."""
+    cfg = EDGE_CASES["tnd_mixed_lengths"] if dq_mode != "fused" else EDGE_CASES["tnd_window_dense_heads"]
     x = case_inputs(cfg, seed=1)
     Yst, lst = oracle_inputs(cfg, x)
-    say(f"[det] repeat ({variant})")
-    env = {} if variant == "plan" else {"FA_BWD_VARIANT": variant}
-    with _env(**env):
-        a = gpu_backward(cfg, x, Yst, lst)
-        b = gpu_backward(cfg, x, Yst, lst, deterministic=True)
+    say(f"[det] repeat ({dq_mode})")
+    a = gpu_backward(cfg, x, Yst, lst, dq_mode=dq_mode)
+    b = gpu_backward(cfg, x, Yst, lst, dq_mode=dq_mode, deterministic=True)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
 
 
-@pytest.mark.parametrize("variant", ["2", "4"])
-@pytest.mark.parametrize("name", sorted(EDGE_CASES))
-def test_both_pairs_parity(variant, name):
-    """Both atomic-free pairs on every edge case, whatever the plan would pick:
-    FA_BWD_VARIANT=2 (a dQ pass recomputing S and dP, the default for TND) and
-    FA_BWD_VARIANT=4 (the dK/dV kernel stores dS and a GEMM kernel forms dQ
-    from it, the default for BSND/BNSD), against the oracle, every element."""
+# edge cases whose longest key sequence fits the fused kernel's one tile
+FUSED_CASES = sorted(n for n, c in EDGE_CASES.items()
+                     if c["D"] in (64, 128) and max(c.get("lengths_kv", c.get("lengths", [c.get("S2", 0)]))) <= 128
+                     and (c["layout"] == "TND" or c["S2"] <= 128))
+
+
+@pytest.mark.parametrize("dq_mode,name", [(m, n) for m in ("recompute", "stored_ds") for n in sorted(EDGE_CASES)]
+                         + [("fused", n) for n in FUSED_CASES])
+def test_every_mode_parity(dq_mode, name):
+    """Each deterministic dQ mode on every edge case it takes, whatever the
+    plan would pick, against the oracle, every element: "recompute" (a dQ pass
+    recomputing S and dP), "stored_ds" (the dK/dV kernel stores dS and a GEMM
+    kernel forms dQ from it) and "fused" (one launch per sequence and KV head)."""
     cfg = EDGE_CASES[name]
-    say(f"[parity] variant {variant}: {name}")
+    say(f"[parity] {dq_mode}: {name}")
     x = case_inputs(cfg, seed=sorted(EDGE_CASES).index(name))
     Yst, lst = oracle_inputs(cfg, x)
     rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
-    with _env(FA_BWD_VARIANT=variant):
-        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, dq_mode=dq_mode)
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
     qe, ke = empty_rows(cfg, x, gq.shape, gk.shape)
     assert not np.any(gq[qe]) and not np.any(gk[ke]) and not np.any(gv[ke])
 
 
-@pytest.mark.parametrize("variant", ["2", "4"])
+FUSED_EXTRA = {
+    "fused_gqa8_s1_256_s2_96": W.custom("BSND", B=1, N1=8, N2=1, S1=256, S2=96, D=128, Dv=128, mask_mode=1),
+    "fused_long_queries": W.custom("BNSD", B=2, N1=2, N2=2, S1=1000, S2=128, D=64, Dv=64, mask_mode=0),
+    "fused_tnd_window": W.custom("TND", N1=4, N2=1, D=128, Dv=64, mask_mode=2, win_left=17, win_right=3,
+                                 lengths=[0, 128, 7, 100, 33], lengths_kv=[5, 128, 0, 90, 33]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_EXTRA))
+def test_fused_kernel_shapes(name):
+    """The fused kernel at its limits: GQA 8 (the head loop), many query
+    blocks, Dv < D, empty key and query sequences, windows."""
+    cfg = FUSED_EXTRA[name]
+    say(f"[parity] fused: {name}")
+    x = case_inputs(cfg, seed=5)
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, dq_mode="fused")
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+    qe, ke = empty_rows(cfg, x, gq.shape, gk.shape)
+    assert not np.any(gq[qe]) and not np.any(gk[ke]) and not np.any(gv[ke])
+
+
+@pytest.mark.parametrize("dq_mode", ["recompute", "stored_ds"])
 @pytest.mark.parametrize("split", ["1,1", "2,3", "1,5"])
-def test_both_pairs_split_partials_parity(variant, split):
+def test_both_pairs_split_partials_parity(dq_mode, split):
     """Both pairs with dK/dV split over query heads and query ranges."""
     cfg = EDGE_CASES["bsnd_causal_gqa4_ragged"]
-    say(f"[parity] variant {variant}, split {split}")
+    say(f"[parity] {dq_mode}, split {split}")
     x = case_inputs(cfg, seed=sorted(EDGE_CASES).index("bsnd_causal_gqa4_ragged"))
     Yst, lst = oracle_inputs(cfg, x)
     rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
-    with _env(FA_BWD_VARIANT=variant, FA_BWD_SPLIT=split):
-        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    with _env(FA_BWD_SPLIT=split):
+        gq, gk, gv = gpu_backward(cfg, x, Yst, lst, dq_mode=dq_mode)
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
 
+
+def _min_stored_ds_bound(cfg, x):
+    """The smallest max_workspace_bytes a stored-dS plan accepts (bisection on
+    fa_bwd_create's answer): it holds sfmg and the dS of one KV head."""
+    import torch
+    from flashattention_backward_fa_amd import fa_bwd as fb
+    mq, mk = max_lengths(cfg, x)
+    cu = (None, None) if cfg["layout"] != "TND" else (torch.from_numpy(x["cu_q"]), torch.from_numpy(x["cu_kv"]))
+    args = (x["q"].to("meta"), x["k"].to("meta"), x["v"].to("meta"), cfg["layout"], *cu, cfg["softmax_scale"],
+            cfg["mask_mode"], cfg["win_left"], cfg["win_right"], mq, mk)
+
+    def ok(bound):
+        try:
+            fb.get_plan(*args, dq_mode="stored_ds", max_workspace_bytes=bound)
+            return True
+        except fb.FaBwdError as e:
+            assert e.status == fb.FA_ERR_WORKSPACE
+            return False
+
+    hi = fb.get_plan(*args, dq_mode="stored_ds").workspace_bytes
+    lo = 1
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if ok(mid):
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
 
 
 @pytest.mark.parametrize("name", ["bsnd_causal_gqa4_ragged", "tnd_mixed_lengths", "bnsd_batch3_causal",
                                   "tnd_window_dense_heads", "bsnd_d192_dv64_window"])
 def test_stored_ds_one_kv_head_per_pass(name):
-    """Stored-dS chain run one KV head at a time (the path for dS past the
-    workspace cap; here forced with a 1-byte cap), against the oracle."""
+    """Stored-dS mode under the smallest workspace bound it accepts: one KV
+    head's dS per pass (the dK/dV and dQ launches repeat per head), against
+    the oracle."""
     cfg = EDGE_CASES[name]
     say(f"[parity] stored dS, one KV head per pass: {name}")
     x = case_inputs(cfg, seed=sorted(EDGE_CASES).index(name))
     Yst, lst = oracle_inputs(cfg, x)
     rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
-    with _env(FA_BWD_VARIANT="4", FA_BWD_DS_CAP="1"):
-        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    bound = _min_stored_ds_bound(cfg, x)
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, dq_mode="stored_ds", max_workspace_bytes=bound)
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
     qe, ke = empty_rows(cfg, x, gq.shape, gk.shape)
     assert not np.any(gq[qe]) and not np.any(gk[ke]) and not np.any(gv[ke])
 
 
 def test_stored_ds_uneven_kv_head_chunks():
-    """Three KV heads in chunks of two and one: the cap holds 2.5 KV heads'
-    dS (2 row groups x 2 query heads x 7 slices x 8 KB each)."""
+    """Three KV heads in chunks of two and one: the bound holds sfmg and 2.5
+    KV heads' dS (2 row groups x 2 query heads x 7 slices x 8 KB each)."""
     cfg = W.custom("BSND", B=1, N1=6, N2=3, S1=200, S2=200, D=128, Dv=128, mask_mode=1)
     say("[parity] stored dS, KV-head chunks of 2 and 1")
     x = case_inputs(cfg, seed=11)
     Yst, lst = oracle_inputs(cfg, x)
     rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
     per_kv = 2 * 2 * 7 * 8192
-    with _env(FA_BWD_DS_CAP=str(per_kv * 5 // 2)):
-        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+    sfmg = (6 * 200 * 4 + 255) // 256 * 256
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, max_workspace_bytes=sfmg + per_kv * 5 // 2)
+    assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+
+
+def test_workspace_bound_falls_back_to_recompute():
+    """A bound below one KV head's dS: the plan recomputes S and dP for dQ,
+    with no partial sums when even those do not fit."""
+    from flashattention_backward_fa_amd import fa_bwd as fb
+    cfg = EDGE_CASES["bsnd_causal_gqa4_ragged"]
+    x = case_inputs(cfg, seed=sorted(EDGE_CASES).index("bsnd_causal_gqa4_ragged"))
+    Yst, lst = oracle_inputs(cfg, x)
+    rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+    sfmg = (8 * 300 * 4 + 255) // 256 * 256
+    plan = fb.get_plan(x["q"].to("meta"), x["k"].to("meta"), x["v"].to("meta"), "BSND", None, None, 0.0, 1, -1, -1,
+                       max_workspace_bytes=sfmg)
+    assert plan.dq_path() == "recompute" and plan.workspace_bytes == sfmg
+    say("[parity] workspace bound = sfmg only")
+    gq, gk, gv = gpu_backward(cfg, x, Yst, lst, max_workspace_bytes=sfmg)
     assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])

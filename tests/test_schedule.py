@@ -218,14 +218,14 @@ def test_stored_ds_band_holds_every_group(sched, monkeypatch):
         build.build()
     lib = fb.load_library()
     monkeypatch.setenv("FA_BWD_SPLIT", "1,1")
-    monkeypatch.delenv("FA_BWD_VARIANT", raising=False)
     rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
     lengths = LENGTHS + [(4096, 4096), (3000, 5000), (5000, 3000), (1025, 2047)]
     bands = _bands() + [(1, 1024, -1), (2, 1024, 1024), (2, 0, 4095), (2, 4095, 0), (2, 100, 20)]
     checked = 0
     for s1, s2 in lengths:
         for mode, wl, wr in bands:
-            d = fb.make_desc("BSND", 1, 1, 1, s1, s2, 64, 64, mask_mode=mode, win_left=wl, win_right=wr)
+            d = fb.make_desc("BSND", 1, 1, 1, s1, s2, 64, 64, mask_mode=mode, win_left=wl, win_right=wr,
+                             dq_mode="stored_ds")
             h, ws = ctypes.c_void_p(), ctypes.c_size_t()
             assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_OK
             lib.fa_bwd_destroy(h)

@@ -4,6 +4,7 @@ The host planner (csrc/fa_bwd_api.cpp) is plain C++ built with g++; the
 kernels (csrc/fa_bwd_det_kernels.hip: the dK/dV kernel and both dQ kernels;
 csrc/fa_bwd_kernels.hip: preprocess and the atomic variants;
 csrc/fa_bwd_fused_kernels.hip: the one-launch kernel for short key sequences;
+csrc/fa_bwd_scratch.hip: the device scratch of the entry point that allocates nothing;
 csrc/fa_bwd_f32_kernels.hip: the fp32 debugging form;
 csrc/fa_fwd_kernels.hip: the forward that produces attn_out and
 softmax_lse; csrc/fa_floyd_kernels.hip: Floyd attention, whose host side is
@@ -69,6 +70,7 @@ def build(verbose=False):
     det_o = os.path.join(BUILDDIR, "fa_bwd_det_kernels.o")
     f32_o = os.path.join(BUILDDIR, "fa_bwd_f32_kernels.o")
     fus_o = os.path.join(BUILDDIR, "fa_bwd_fused_kernels.o")
+    scr_o = os.path.join(BUILDDIR, "fa_bwd_scratch.o")
     fapi_o = os.path.join(BUILDDIR, "fa_floyd_api.o")
     fker_o = os.path.join(BUILDDIR, "fa_floyd_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
@@ -83,13 +85,15 @@ def build(verbose=False):
           "-o", f32_o], verbose)
     _run([hipcc, *HIP_FLAGS, *DET_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
           os.path.join(CSRC, "fa_bwd_fused_kernels.hip"), "-o", fus_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_scratch.hip"),
+          "-o", scr_o], verbose)
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
           "-c", os.path.join(CSRC, "fa_floyd_api.cpp"), "-o", fapi_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_floyd_kernels.hip"),
           "-o", fker_o], verbose)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o, det_o, f32_o, fus_o,
-          fapi_o, fker_o], verbose)
+          scr_o, fapi_o, fker_o], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -413,6 +413,24 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   return FA_OK;
 }
 
+int fa_bwd_run_noalloc(fa_bwd_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                       const void* attn_out, const float* softmax_lse, const int32_t* cu_seqlens_q,
+                       const int32_t* cu_seqlens_kv, const int32_t* seqused_q, const int32_t* seqused_kv, void* dq,
+                       void* dk, void* dv, void* stream) {
+  static_assert(fabwd::SCRATCH_BYTES == FA_BWD_SCRATCH_BYTES, "one scratch size");
+  if (!plan) return FA_ERR_NULLPTR;
+  if (plan->ws_bytes > FA_BWD_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  // the argument checks of fa_bwd_run come first, before any device call
+  if (!q || !k || !v || !dout || !attn_out || !softmax_lse || !dq || !dk || !dv) return FA_ERR_NULLPTR;
+  const int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
+  if (st != FA_OK) return st;
+  if ((seqused_q || seqused_kv) && plan->args.variant < 2) return FA_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (plan->ws_bytes > 0 && fabwd::scratch_ptr(&scratch) != 0) return FA_ERR_RUNTIME;
+  return fa_bwd_run(plan, q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q, cu_seqlens_kv, seqused_q, seqused_kv,
+                    dq, dk, dv, scratch, plan->ws_bytes > 0 ? FA_BWD_SCRATCH_BYTES : 0, stream);
+}
+
 int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                const int32_t* cu_seqlens_kv, const int32_t* seqused_q, const int32_t* seqused_kv, void* attn_out,
                float* softmax_lse, void* stream) {

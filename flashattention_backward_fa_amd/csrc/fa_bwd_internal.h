@@ -117,6 +117,11 @@ int launch_fused(const KernelArgs& a, void* stream);
 // Compute units of the current HIP device, or 0 when it cannot be read.
 int device_cu_count();
 
+// Library-owned device scratch of fa_bwd_run_noalloc (fa_bwd_scratch.hip):
+// SCRATCH_BYTES on each device, its device address on the current device
+// looked up once per device.  Returns 0 or a hipError_t value.
+constexpr size_t SCRATCH_BYTES = size_t(64) << 20;
+int scratch_ptr(void** ptr);
 
 // fp32 debugging form (fa_bwd_f32_kernels.hip): dK/dV and dQ, fp32 outputs.
 int launch_f32_debug(const KernelArgs& a, void* stream);

@@ -30,6 +30,8 @@ FA_ERR_UNSUPPORTED = 4
 FA_ERR_WORKSPACE = 5
 FA_ERR_RUNTIME = 6
 
+SCRATCH_BYTES = 64 << 20  # FA_BWD_SCRATCH_BYTES: the device scratch of fa_bwd_run_noalloc
+
 LAYOUTS = {"BSND": 0, "BNSD": 1, "TND": 2}
 FLAG_DETERMINISTIC = 0x1
 FLAG_FP32_OUT = 0x2
@@ -41,7 +43,7 @@ DTYPE_FP16 = 1
 DQ_MODES = {"auto": 0, "stored_ds": 1, "recompute": 2, "atomic": 3, "fused": 4}
 DQ_PATHS = {1: "stored_ds", 2: "recompute", 3: "atomic", 4: "fused", 5: "fp32_form"}
 
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_plan_dq_path", "fa_bwd_profile_enable",
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_noalloc", "fa_bwd_sfmg", "fa_fwd_run", "fa_bwd_plan_dq_path", "fa_bwd_profile_enable",
             "fa_bwd_profile_read", "fa_bwd_profile_read_split", "fa_bwd_destroy", "fa_bwd_strerror", "fa_bwd_abi_version",
             "fa_floyd_workspace_size", "fa_floyd_bwd_run", "fa_floyd_bwd_run_timed", "fa_floyd_fwd_run")
 
@@ -118,6 +120,8 @@ def load_library(path=LIB_PATH):
     lib.fa_bwd_create.restype = ctypes.c_int
     lib.fa_bwd_run.argtypes = [vp] * 11 + [vp] * 3 + [vp, sz, vp]
     lib.fa_bwd_run.restype = ctypes.c_int
+    lib.fa_bwd_run_noalloc.argtypes = [vp] * 11 + [vp] * 3 + [vp]
+    lib.fa_bwd_run_noalloc.restype = ctypes.c_int
     lib.fa_bwd_sfmg.argtypes = [vp] * 6
     lib.fa_bwd_sfmg.restype = ctypes.c_int
     lib.fa_fwd_run.argtypes = [vp] * 11

@@ -227,6 +227,33 @@ int fa_bwd_run(fa_bwd_plan plan,
                void* dq, void* dk, void* dv,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the library-owned device scratch that fa_bwd_run_noalloc uses in
+ * place of a caller workspace (64 MiB on each device the library runs on,
+ * held until the process ends). */
+#define FA_BWD_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* fa_bwd_run for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results as fa_bwd_run, without the workspace: the
+ * kernels use a library-owned device array of FA_BWD_SCRATCH_BYTES on the
+ * current device instead.  The call allocates nothing (no hipMalloc, no
+ * library routine that allocates).  Create the plan with
+ * max_workspace_bytes <= FA_BWD_SCRATCH_BYTES so that it fits; a plan whose
+ * workspace is larger is refused with FA_ERR_WORKSPACE before any launch.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (several streams, host threads or processes' worth of
+ * plans on the same array) race and must be ordered by the caller.  Nothing
+ * in the array needs to start at zero: every part the kernels read is
+ * written earlier in the same call.  Errors: those of fa_bwd_run, and
+ * FA_ERR_RUNTIME when the array's address cannot be found on the current
+ * device. */
+int fa_bwd_run_noalloc(fa_bwd_plan plan,
+                       const void* q, const void* k, const void* v,
+                       const void* dout, const void* attn_out, const float* softmax_lse,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                       const int32_t* seqused_q, const int32_t* seqused_kv,
+                       void* dq, void* dk, void* dv, void* stream);
+
 /* The preprocess step alone (the page's first vector stage, section 五 5.2:
  * sfmg = rowsum(dY (.) Y)): writes float32 sfmg in softmax_lse's layout
  * ([B, N1, S1] or [N1, T1]) to `sfmg`, a caller buffer of that size.

@@ -358,6 +358,23 @@ def test_run_checks_before_any_device_call(lib):
     assert lib.fa_bwd_sfmg(plan.handle, None, fake, None, fake, None) == fb.FA_ERR_NULLPTR
 
 
+def test_noalloc_refuses_plans_past_the_scratch(lib):
+    """fa_bwd_run_noalloc checks the plan against the library's device scratch
+    (FA_BWD_SCRATCH_BYTES) before anything touches a device."""
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every check below fails first
+    args = [fake] * 6 + [None, None] + [None, None] + [fake] * 3
+    big = fb.Plan(fb.make_desc("BSND", 1, 32, 8, 4096, 4096, 128, 128, mask_mode=1))
+    assert big.workspace_bytes > fb.SCRATCH_BYTES
+    assert lib.fa_bwd_run_noalloc(big.handle, *args, None) == fb.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_run_noalloc(None, *args, None) == fb.FA_ERR_NULLPTR
+    # bounded by the scratch size, the same problem plans within it
+    fit = fb.Plan(fb.make_desc("BSND", 1, 32, 8, 4096, 4096, 128, 128, mask_mode=1,
+                               max_workspace_bytes=fb.SCRATCH_BYTES))
+    assert 0 < fit.workspace_bytes <= fb.SCRATCH_BYTES
+    st = lib.fa_bwd_run_noalloc(fit.handle, None, *args[1:], None)
+    assert st == fb.FA_ERR_NULLPTR
+
+
 def test_mask_mode_names():
     assert fb.mask_mode_value("Causal") == 1
     assert fb.mask_mode_value("window") == 2

@@ -282,8 +282,10 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     untimed steps for at least `settle_s` seconds (the shader clock ramps up
     over the first tens of milliseconds of load, and drops again while the host
     builds the next workload's inputs) and then `warmup` untimed ones:
-    whole-step time from events around the loop, the dK/dV + dQ pair from the
-    library's events, and the preprocess kernel over its own launches.
+    whole-step time from events around the loop; then `steps` more steps with
+    the library's events around and between the dK/dV and dQ kernels (kept
+    out of the first loop so that they add nothing to the step time); then
+    the preprocess kernel over its own launches.
     Returns times in ms, the preprocess bytes and the settle step count."""
     import torch
     from flashattention_backward_fa_amd import fa_bwd as fb
@@ -321,7 +323,7 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    plan.profile_enable(max(steps, 1))
+    # whole steps, with no event inside them
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -331,7 +333,12 @@ def measure(name, steps, warmup, settle_s=0.0, dtype="bf16"):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / max(steps, 1)
-    # the library's events around the two main kernels, split between them
+    # the same steps again with the library's events around the two main
+    # kernels and between them
+    plan.profile_enable(max(steps, 1))
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     split = plan.profile_read_split(steps)
     plan.profile_enable(0)
     n = max(len(split), 1)

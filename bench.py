@@ -242,8 +242,12 @@ def roofline_entry(name, cfg, m):
         "avg_launch_ms": round(pair_ms, 5), "traffic": committed_traffic(name),
     }
     if m["dkdv_ms"] is None:  # one main kernel (fused) or a chunked run: the pair is all there is
+        traffic = pair["traffic"]
+        if m["dq_path"] == "fused":
+            traffic = committed_traffic(name, os.path.join(PROFILE_DIR, f"bwd_fused_kernel_{name}_traffic.txt"),
+                                        "fused")
         return {"bound": "mfma", "kernel": pair["kernels"], "achieved": pair["achieved"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": pair["frac"], "traffic": pair["traffic"],
+                "unit": "TFLOP/s", "frac": pair["frac"], "traffic": traffic,
                 "avg_launch_ms": round(pair_ms, 5), "launches_timed": m["pair_launches"],
                 "algorithmic_flop_per_launch": flops, "flop_rule": pair["flop_rule"]}
     kf = dkdv_flops(cfg)

@@ -188,8 +188,10 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   const size_t sfmg_bytes = align_up((size_t)p.lse_elems * sizeof(float));
   // the fused kernel holds the whole key range in one tile and the row
   // statistics of all its (query head, 32-row block) items in LDS
+  // (and addresses a head's dq rows by 32-bit byte offsets)
   const bool fused_ok = fabwd::fused_instantiated(d.D, d.Dv) && S2 <= fabwd::FUSED_MAX_KEYS &&
-                        (int64_t)a.G * ((S1 + 31) / 32) <= fabwd::FUSED_MAX_BLOCKS;
+                        (int64_t)a.G * ((S1 + 31) / 32) <= fabwd::FUSED_MAX_BLOCKS &&
+                        (S1 + 32) * a.q_ss * 2 < (int64_t(1) << 31);
 
   // Job split of the pair kernels for launches over n2l KV heads: halve the
   // query heads of a GQA group per job, then split the query range of a key

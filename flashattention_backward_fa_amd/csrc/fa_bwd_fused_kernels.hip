@@ -29,6 +29,15 @@
 namespace fabwd {
 namespace {
 
+// s_waitcnt vmcnt(N): all but this wavefront's N most recent vector-memory
+// instructions have completed (gfx9 retires loads and stores in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
+}
+
 constexpr int FK = FUSED_MAX_KEYS;  // keys per workgroup: 4 wavefronts x 32
 constexpr int FR = 32;              // query rows per step
 static_assert(FK == 128, "one 32-key slice per wavefront");
@@ -105,53 +114,54 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(KernelArgs a) {
   if (T > 0) fetch(0, 0);
 
   // Row statistics of every item: lse in base 2 (+inf for rows past the used
-  // ones or with lse = -inf, so that their P is 0) and sfmg = rowsum(dY * Y),
-  // HDV / 8 lanes per row with one 16-byte load of each tensor, eight rows in
-  // flight per lane.
-  for (int r = tid; r < T * FR; r += 256) {
-    const int n1 = n2 * G + (r / FR) / nblk;
-    const int i = ((r / FR) % nblk) * FR + r % FR;
-    float l = __builtin_inff();
-    if (i < s1) {
-      const float x = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + i];
-      l = x == -__builtin_inff() ? __builtin_inff() : x * kLog2e;
-    }
-    lse_s[r] = l;
-  }
+  // ones or with lse = -inf, so that their P is 0) and sfmg = rowsum(dY * Y).
+  // Every load is issued unconditionally (rows clamped into the sequence) and
+  // the row's validity applied to the value, so that a lane's loads are all
+  // in flight together.
+  const int R = T * FR;  // statistics rows: item r / 32, row r % 32 of its block
+  auto row_of = [&](int r, int& n1, int& i) {
+    const int rc = min(r, R - 1);
+    n1 = n2 * G + (rc / FR) / nblk;
+    i = ((rc / FR) % nblk) * FR + rc % FR;
+  };
   {
     constexpr int LPR = HDV / 8;      // lanes per row
     constexpr int RPP = 256 / LPR;    // rows per pass
     constexpr int UN = 8;             // passes in flight
     const int part = tid % LPR;
-    for (int r0 = tid / LPR; r0 < T * FR; r0 += RPP * UN) {
-      float acc[UN];
+    for (int r0 = tid / LPR; r0 < R; r0 += RPP * UN) {
+      bf16x8 y[UN], g[UN];
+      float x[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const int r = r0 + u * RPP;
-        const int n1 = n2 * G + (r / FR) / nblk;
-        const int i = ((r / FR) % nblk) * FR + r % FR;
-        acc[u] = 0.f;
-        if (r < T * FR && i < sb.s1a) {
-          const int64_t o = sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i * a.o_ss + part * 8;
-          const bf16x8 y = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + o);
-          const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + o);
-          if constexpr (F16) {  // reinterpret whole vectors (element casts of bf16 lanes miscompile)
-            const halfx8 yh = __builtin_bit_cast(halfx8, y), gh = __builtin_bit_cast(halfx8, g);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[u] += (float)gh[e] * (float)yh[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[u] += (float)g[e] * (float)y[e];
-          }
-        }
+        int n1, i;
+        row_of(r0 + u * RPP, n1, i);
+        const int ic = max(min(i, sb.s1a - 1), 0);
+        const int64_t o = sb.obase + (int64_t)n1 * a.o_sn + (int64_t)ic * a.o_ss + part * 8;
+        y[u] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + o);
+        g[u] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + o);
+        x[u] = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + ic];
       }
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        float s = acc[u];
+        float acc = 0.f;
+        if constexpr (F16) {  // reinterpret whole vectors (element casts of bf16 lanes miscompile)
+          const halfx8 yh = __builtin_bit_cast(halfx8, y[u]), gh = __builtin_bit_cast(halfx8, g[u]);
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
+          for (int e = 0; e < 8; ++e) acc += (float)gh[e] * (float)yh[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc += (float)g[u][e] * (float)y[u][e];
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+        int n1, i;
         const int r = r0 + u * RPP;
-        if (part == 0 && r < T * FR) sfm_s[r] = s;
+        row_of(r, n1, i);
+        if (part == 0 && r < R) {
+          sfm_s[r] = i < sb.s1a ? acc : 0.f;
+          lse_s[r] = (i < s1 && x[u] != -__builtin_inff()) ? x[u] * kLog2e : __builtin_inff();
+        }
       }
     }
   }
@@ -190,6 +200,12 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(KernelArgs a) {
   }
   // where this lane puts half h of its own dS image
   const uint32_t s_put = lds_addr(Ss) + wave * 2048;
+  // dq rows of a head leave as buffer stores whose range ends with the last
+  // row the sequence holds, so that rows past it are dropped by the range
+  // check: every lane issues the same 16 store instructions per item, and the
+  // next item's wait can leave exactly those in flight (the planner keeps
+  // the byte offsets below 2^31)
+  const int64_t dq_bytes = sb.s1a > 0 ? ((int64_t)(sb.s1a - 1) * a.q_ss + HD) * 2 : 0;
 
   wait_vmem();    // K, V, the first tiles and the statistics' loads landed
   lds_barrier();  // ... everyone's
@@ -201,7 +217,10 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(KernelArgs a) {
     const int i0 = (t % nblk) * FR;
     const int n1 = n2 * G + h;
     if (t > 0) {
-      wait_vmem();    // this wavefront's copies of item t landed
+      // this wavefront's copies of item t landed (the dq stores of item t - 1,
+      // issued after them, may still be in flight)
+      if (wave < NBK) wait_vmem_keep<16>();
+      else wait_vmem();
       lds_barrier();  // ... and everyone's; buffer buf ^ 1 and Ss are free
     }
     if (t + 1 < T) fetch(t + 1, buf ^ 1);
@@ -269,11 +288,14 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(KernelArgs a) {
           dq = mfma32<F16>(dsa, kb, dq);
         }
       }
-      const int64_t hb = (int64_t)n1 * a.q_sn + wave * 32 + l32;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(dQ + (int64_t)n1 * a.q_sn, (short)0, (int)dq_bytes, 0x00020000);
 #pragma unroll
       for (int rg = 0; rg < 16; ++rg) {
         const int i = i0 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
-        if (i < sb.s1a) dQ[hb + (int64_t)i * a.q_ss] = to_elem<F16>(dq[rg] * a.scale);
+        const uint32_t off = (uint32_t)(((int64_t)i * a.q_ss + wave * 32 + l32) * 2);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_elem<F16>(dq[rg] * a.scale)), rsrc,
+                                              (int)off, 0, 0);
       }
     }
   }

@@ -10,6 +10,9 @@
     python -m flashattention_backward_fa_amd.profile_summary mfma \
         --pmc DIR --kernels dkdv_kernel,dq_ds_kernel --workload gqa_causal --out FILE
 
+    python -m flashattention_backward_fa_amd.profile_summary counters \
+        --pmc DIR --kernels dkdv_kernel,dq_ds_kernel --workload gqa_causal --out FILE
+
 trace: the per-kernel table of a --kernel-trace --stats run (calls, average,
 min and max duration, share of GPU time), with the kernel source hash and,
 when given, the bench.py JSON line of the same build.
@@ -47,7 +50,10 @@ KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_det_kernels.hip", "f
                                                     "fa_bwd_schedule.h", "fa_bwd_internal.h"))
 # the sources the Floyd attention kernels are compiled from
 FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h"))
-SOURCES = {"det": KERNEL_SRCS, "floyd": FLOYD_SRCS}
+# the sources of the fused small-sequence kernel
+FUSED_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_fused_kernels.hip", "fa_bwd_tiles.h",
+                                                   "fa_bwd_schedule.h", "fa_bwd_internal.h"))
+SOURCES = {"det": KERNEL_SRCS, "floyd": FLOYD_SRCS, "fused": FUSED_SRCS}
 COPY_BYTES = 256 << 20
 XCDS = 8        # MI355X: 8 XCDs of 32 CUs
 SIMDS = 1024    # 256 CUs x 4 SIMDs
@@ -183,6 +189,25 @@ def mfma(args):
     sys.stdout.write(text)
 
 
+def counters(args):
+    """Median per dispatch of every counter of a --pmc run, per named kernel."""
+    names = _names(args.kernels)
+    rows = _rows(args.pmc)
+    src_hash = kernel_code_hash(SOURCES[args.sources])
+    cnames = sorted({r["Counter_Name"] for r in rows})
+    out = [f"# counters per dispatch (median over dispatches), workload {args.workload}", f"# command: {args.command}",
+           "# columns: kernel | " + " | ".join(cnames)]
+    for n in names:
+        vals = [statistics.median(_per_dispatch(args.pmc, c, lambda k, n=n: n in k)) for c in cnames]
+        out.append(f"{n:24s} | " + " | ".join(f"{v:.0f}" for v in vals))
+    out.append(f"kernel_code_sha256_16: {src_hash}")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -206,8 +231,16 @@ def main():
     m.add_argument("--out")
     m.add_argument("--sources", choices=sorted(SOURCES), default="det")
     m.add_argument("--command", default="(see profiles/README.md)")
+    c = sub.add_parser("counters")
+    for k in ("--pmc", "--kernels", "--workload"):
+        c.add_argument(k, required=True)
+    c.add_argument("--out")
+    c.add_argument("--sources", choices=sorted(SOURCES), default="det")
+    c.add_argument("--command", default="(see profiles/README.md)")
     args = ap.parse_args()
-    if args.cmd == "traffic":
+    if args.cmd == "counters":
+        counters(args)
+    elif args.cmd == "traffic":
         traffic(args)
     elif args.cmd == "trace":
         trace(args)

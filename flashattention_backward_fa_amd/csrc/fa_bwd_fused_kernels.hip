@@ -26,6 +26,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "fa_bwd_tiles.h"
 
 namespace fabwd {
@@ -131,6 +133,20 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) float lse_s[MAXR];    // lse * log2(e) (+inf: row sees nothing)
   __shared__ __attribute__((aligned(16))) float sfm_s[MAXR];
 
+  // one load per 64-byte line of the argument block, waited for in the same
+  // statement: the argument loads below, which the compiler spreads over
+  // several dependent waits, then hit the scalar cache instead of memory
+  {
+    static_assert(sizeof(KernelArgs) > 6 * 64 && sizeof(KernelArgs) <= 7 * 64, "seven lines");
+    uint32_t x0, x1, x2, x3, x4, x5, x6;
+    asm volatile(
+        "s_load_dword %0, %7, 0x0\n\ts_load_dword %1, %7, 0x40\n\ts_load_dword %2, %7, 0x80\n\t"
+        "s_load_dword %3, %7, 0xc0\n\ts_load_dword %4, %7, 0x100\n\ts_load_dword %5, %7, 0x140\n\t"
+        "s_load_dword %6, %7, 0x180\n\ts_waitcnt lgkmcnt(0)"
+        : "=s"(x0), "=s"(x1), "=s"(x2), "=s"(x3), "=s"(x4), "=s"(x5), "=s"(x6)
+        : "s"(__builtin_amdgcn_kernarg_segment_ptr()));
+    asm volatile("" ::"s"(x0 | x1 | x2 | x3 | x4 | x5 | x6));
+  }
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave >> 2;   // query group
@@ -200,43 +216,51 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
   {
     constexpr int LPR = HDV / 8;      // lanes per row
     constexpr int RPP = NT / LPR;     // rows per pass
-    constexpr int UN = 8;             // passes in flight
     const int part = tid % LPR;
-    for (int r0 = tid / LPR; r0 < R; r0 += RPP * UN) {
-      bf16x8 y[UN], g[UN];
-      float x[UN];
+    // UN passes in flight per round: no more than the rows need (a clamped
+    // pass would only repeat the last row's loads)
+    auto stats = [&](auto un) {
+      constexpr int UN = decltype(un)::value;
+      for (int r0 = tid / LPR; r0 < R; r0 += RPP * UN) {
+        bf16x8 y[UN], g[UN];
+        float x[UN];
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        int n1, i;
-        row_of(r0 + u * RPP, n1, i);
-        const int ic = max(min(i, sb.s1a - 1), 0);
-        const int64_t o = sb.obase + (int64_t)n1 * a.o_sn + (int64_t)ic * a.o_ss + part * 8;
-        y[u] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + o);
-        g[u] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + o);
-        x[u] = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + ic];
-      }
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        float acc = 0.f;
-        if constexpr (F16) {  // reinterpret whole vectors (element casts of bf16 lanes miscompile)
-          const halfx8 yh = __builtin_bit_cast(halfx8, y[u]), gh = __builtin_bit_cast(halfx8, g[u]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc += (float)gh[e] * (float)yh[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc += (float)g[u][e] * (float)y[u][e];
+        for (int u = 0; u < UN; ++u) {
+          int n1, i;
+          row_of(r0 + u * RPP, n1, i);
+          const int ic = max(min(i, sb.s1a - 1), 0);
+          const int64_t o = sb.obase + (int64_t)n1 * a.o_sn + (int64_t)ic * a.o_ss + part * 8;
+          y[u] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + o);
+          g[u] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + o);
+          x[u] = a.lse[sb.lbase + (int64_t)n1 * a.l_sn + ic];
         }
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-        int n1, i;
-        const int r = r0 + u * RPP;
-        row_of(r, n1, i);
-        if (part == 0 && r < R) {
-          sfm_s[r] = i < sb.s1a ? acc : 0.f;
-          lse_s[r] = (i < s1 && x[u] != -__builtin_inff()) ? x[u] * kLog2e : __builtin_inff();
+        for (int u = 0; u < UN; ++u) {
+          float acc = 0.f;
+          if constexpr (F16) {  // reinterpret whole vectors (element casts of bf16 lanes miscompile)
+            const halfx8 yh = __builtin_bit_cast(halfx8, y[u]), gh = __builtin_bit_cast(halfx8, g[u]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += (float)gh[e] * (float)yh[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += (float)g[u][e] * (float)y[u][e];
+          }
+#pragma unroll
+          for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+          int n1, i;
+          const int r = r0 + u * RPP;
+          row_of(r, n1, i);
+          if (part == 0 && r < R) {
+            sfm_s[r] = i < sb.s1a ? acc : 0.f;
+            lse_s[r] = (i < s1 && x[u] != -__builtin_inff()) ? x[u] * kLog2e : __builtin_inff();
+          }
         }
       }
-    }
+    };
+    if (R <= RPP) stats(std::integral_constant<int, 1>{});
+    else if (R <= 2 * RPP) stats(std::integral_constant<int, 2>{});
+    else if (R <= 4 * RPP) stats(std::integral_constant<int, 4>{});
+    else stats(std::integral_constant<int, 8>{});
   }
 
   // dK and dV accumulate transposed (lane = key, elements = columns), so

@@ -13,9 +13,9 @@
 //                                  per 32-row query block;
 //   dV += P^T dY, dK += dS^T Q     in registers over all blocks and heads;
 //   dQ = scale * dS K              per block: the four wavefronts' dS tiles
-//                                  meet in LDS and each of the first D / 32
-//                                  wavefronts forms 32 columns of dQ over
-//                                  all 128 keys.
+//                                  meet in LDS and D / 32 of the four
+//                                  wavefronts form 32 columns of dQ each
+//                                  over all 128 keys.
 // Every dQ row sees its whole key range inside the workgroup, so dQ is
 // written once, with no atomics and no workspace, and the result is bitwise
 // repeatable.  The MFMA layouts are those of the dK/dV kernel
@@ -159,6 +159,10 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
   const int off = s2 - s1;
   const int wl = a.win_left, wr = a.win_right;
   const int kw0 = kw * 32;  // this wavefront's keys within the tile
+  // the 32-column block of dQ this wavefront forms (when below D / 32): with
+  // two groups at D = 64, group 1 uses wavefronts 2 and 3, so that every SIMD
+  // runs one dQ product per step
+  const int cb = (kw - qg * NBK) & 3;
 
   bf16* __restrict__ dQ = static_cast<bf16*>(a.dq) + sb.qbase;
   // blocks of 32 rows over every row the sequence holds (rows past the used
@@ -326,14 +330,14 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
       // this wavefront's copies of item t landed; its dq stores of step
       // k - 1, issued after those copies, may stay in flight (at step 1 it
       // has stored nothing yet)
-      if (kw < NBK && k >= 2) wait_vmem_keep<NST>();
+      if (cb < NBK && k >= 2) wait_vmem_keep<NST>();
       else wait_vmem();
       lds_barrier();  // ... everyone's, and every dS image of step k - 1
     }
     if (k < nsteps && t + QG < T) fetch(t + QG, buf ^ 1);
 
     // dQ^T of item tp, 32 head-dim columns per wavefront, over all 128 keys
-    if (hasp && kw < NBK) {
+    if (hasp && cb < NBK) {
       floatx16 dq = floatx16{};
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
           const uint32_t ao = (buf ^ 1) * 8192 + sl * 2048 + c * 256;  // buffer, slice sl, chunk bit 4 = c
           const bf16x8 dsb = join(lds_load_tr(a_base[0] + ao), lds_load_tr(a_base[1] + ao));
           const int kc = 2 * sl + c;
-          const bf16x8 ka = join(lds_load_tr(kadr.tr_read(kc, 0, kw)), lds_load_tr(kadr.tr_read(kc, 1, kw)));
+          const bf16x8 ka = join(lds_load_tr(kadr.tr_read(kc, 0, cb)), lds_load_tr(kadr.tr_read(kc, 1, cb)));
           dq = mfma32<F16>(ka, dsb, dq);
         }
       }
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
           __builtin_amdgcn_make_buffer_rsrc(dQ + (int64_t)n1p * a.q_sn, (short)0, (int)dq_bytes, 0x00020000);
 #pragma unroll
       for (int pc = 0; pc < NST; ++pc) {
-        const uint32_t off = (uint32_t)(((int64_t)ip * a.q_ss + kw * 32 + pc * 16 + hi * 8) * 2);
+        const uint32_t off = (uint32_t)(((int64_t)ip * a.q_ss + cb * 32 + pc * 16 + hi * 8) * 2);
         __builtin_amdgcn_raw_buffer_store_b128(piece[pc], rsrc, (int)off, 0, 0);
       }
     }

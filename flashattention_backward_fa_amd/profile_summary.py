@@ -148,7 +148,8 @@ def trace(args):
                    f"{float(r['MinNs']) / 1e3:9.1f} | {float(r['MaxNs']) / 1e3:9.1f} | {float(r['Percentage']):5.1f}%")
     out.append(f"kernel_code_sha256_16: {src_hash}")
     if args.bench_json:
-        out.append("bench.py line of this build: " + open(args.bench_json).read().strip().splitlines()[-1])
+        lines = [ln for ln in open(args.bench_json).read().splitlines() if ln.startswith("{")]
+        out.append("bench.py line of this build: " + (lines[-1] if lines else "(none)"))
     text = "\n".join(out) + "\n"
     if args.out:
         with open(args.out, "w") as fh:
@@ -180,6 +181,9 @@ def mfma(args):
         tot_el += elapsed
         out.append(f"{n:40s} | {insts:12.0f} | {busy:14.0f} | {elapsed:11.0f} | {100 * util:5.1f} % | "
                    f"{elapsed / dur_ns:4.2f}")
+        if dur_ns < 50_000:
+            out.append(f"# {n}: a {dur_ns / 1000:.1f} us dispatch; the counters' window around it is longer than "
+                       "the dispatch, so elapsed cycles and clock are overstated and utilisation understated")
     out.append(f"{'pair' if len(names) == 2 else 'combined'}_mfma_utilisation: {100 * tot_busy / (tot_el * SIMDS):.1f} %")
     out.append(f"kernel_code_sha256_16: {src_hash}")
     text = "\n".join(out) + "\n"

@@ -28,6 +28,7 @@
 
 #include <type_traits>
 
+#include "fa_bwd_kernarg.h"
 #include "fa_bwd_tiles.h"
 
 namespace fabwd {
@@ -133,20 +134,7 @@ __global__ __launch_bounds__(256 * QG, 1) void fused_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) float lse_s[MAXR];    // lse * log2(e) (+inf: row sees nothing)
   __shared__ __attribute__((aligned(16))) float sfm_s[MAXR];
 
-  // one load per 64-byte line of the argument block, waited for in the same
-  // statement: the argument loads below, which the compiler spreads over
-  // several dependent waits, then hit the scalar cache instead of memory
-  {
-    static_assert(sizeof(KernelArgs) > 6 * 64 && sizeof(KernelArgs) <= 7 * 64, "seven lines");
-    uint32_t x0, x1, x2, x3, x4, x5, x6;
-    asm volatile(
-        "s_load_dword %0, %7, 0x0\n\ts_load_dword %1, %7, 0x40\n\ts_load_dword %2, %7, 0x80\n\t"
-        "s_load_dword %3, %7, 0xc0\n\ts_load_dword %4, %7, 0x100\n\ts_load_dword %5, %7, 0x140\n\t"
-        "s_load_dword %6, %7, 0x180\n\ts_waitcnt lgkmcnt(0)"
-        : "=s"(x0), "=s"(x1), "=s"(x2), "=s"(x3), "=s"(x4), "=s"(x5), "=s"(x6)
-        : "s"(__builtin_amdgcn_kernarg_segment_ptr()));
-    asm volatile("" ::"s"(x0 | x1 | x2 | x3 | x4 | x5 | x6));
-  }
+  prefetch_args();
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave >> 2;   // query group

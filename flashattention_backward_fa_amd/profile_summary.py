@@ -52,7 +52,7 @@ KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_det_kernels.hip", "f
 FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h"))
 # the sources of the fused small-sequence kernel
 FUSED_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_fused_kernels.hip", "fa_bwd_tiles.h",
-                                                   "fa_bwd_schedule.h", "fa_bwd_internal.h"))
+                                                   "fa_bwd_schedule.h", "fa_bwd_internal.h", "fa_bwd_kernarg.h"))
 SOURCES = {"det": KERNEL_SRCS, "floyd": FLOYD_SRCS, "fused": FUSED_SRCS}
 COPY_BYTES = 256 << 20
 XCDS = 8        # MI355X: 8 XCDs of 32 CUs

@@ -361,26 +361,12 @@ def get_plan(q, k, v, layout="BSND", cu_seqlens_q=None, cu_seqlens_kv=None, soft
     return _plans[key]
 
 
-def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None,
-                    softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
-                    max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None,
-                    fp32_out=False, seqused_q=None, seqused_kv=None, dq_mode="auto", max_workspace_bytes=0):
-    """dq, dk, dv of attention on the current HIP stream, in the inputs' element
-    type (bf16 or fp16).
-
-    q, k, v, dout, attn_out: bf16 or fp16 CUDA(HIP) tensors of one type in
-    `layout`; softmax_lse:
-    float32, (B, N1, S1) or (N1, T1); cu_seqlens_*: int32 device tensors for
-    TND only.  Non-contiguous inputs are made contiguous first.  `workspace`
-    (uint8 tensor) and `out` ((dq, dk, dv)) may be passed to avoid allocation.
-    fp32_out=True selects the fp32 debugging form (float32 outputs, P and dS
-    kept in fp32; slow).  seqused_q / seqused_kv: optional int32 device
-    tensors [B]; only the first seqused[b] rows / keys of sequence b take part
-    and the gradients of the rest are zero.  dq_mode: how dQ is formed
-    ("auto", "stored_ds", "recompute", "atomic" or "fused"; see FA_DQ_* in
-    include/fa_bwd.h); max_workspace_bytes: an upper bound on the workspace
-    the plan may ask for (0 = none).
-    """
+def _bind_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q, cu_seqlens_kv, softmax_scale, mask_mode,
+               win_left, win_right, max_seqlen_q, max_seqlen_kv, layout, deterministic, workspace, out, fp32_out,
+               seqused_q, seqused_kv, dq_mode, max_workspace_bytes):
+    """Validation, plan lookup and allocation shared by flash_attn_grad and
+    prepare_grad: (plan, run arguments before the stream, outputs, tensors to
+    keep alive)."""
     import torch
 
     if layout not in LAYOUTS:
@@ -412,11 +398,92 @@ def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_
                 raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(ref.shape)}")
     if workspace is None or workspace.numel() < plan.workspace_bytes:
         workspace = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    plan.run(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(attn_out), _ptr(softmax_lse), _ptr(cu_seqlens_q),
-             _ptr(cu_seqlens_kv), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), stream,
-             _ptr(seqused_q), _ptr(seqused_kv))
-    return dq, dk, dv
+    args = (plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(attn_out), _ptr(softmax_lse),
+            _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(seqused_q), _ptr(seqused_kv), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()))
+    keep = (q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q, cu_seqlens_kv, seqused_q, seqused_kv, workspace)
+    return plan, args, (dq, dk, dv), keep
+
+
+def flash_attn_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None,
+                    softmax_scale=0.0, mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1,
+                    max_seqlen_kv=-1, layout="BSND", deterministic=False, workspace=None, out=None,
+                    fp32_out=False, seqused_q=None, seqused_kv=None, dq_mode="auto", max_workspace_bytes=0):
+    """dq, dk, dv of attention on the current HIP stream, in the inputs' element
+    type (bf16 or fp16).
+
+    q, k, v, dout, attn_out: bf16 or fp16 CUDA(HIP) tensors of one type in
+    `layout`; softmax_lse:
+    float32, (B, N1, S1) or (N1, T1); cu_seqlens_*: int32 device tensors for
+    TND only.  Non-contiguous inputs are made contiguous first.  `workspace`
+    (uint8 tensor) and `out` ((dq, dk, dv)) may be passed to avoid allocation.
+    fp32_out=True selects the fp32 debugging form (float32 outputs, P and dS
+    kept in fp32; slow).  seqused_q / seqused_kv: optional int32 device
+    tensors [B]; only the first seqused[b] rows / keys of sequence b take part
+    and the gradients of the rest are zero.  dq_mode: how dQ is formed
+    ("auto", "stored_ds", "recompute", "atomic" or "fused"; see FA_DQ_* in
+    include/fa_bwd.h); max_workspace_bytes: an upper bound on the workspace
+    the plan may ask for (0 = none).
+    """
+    import torch
+
+    plan, args, outs, _keep = _bind_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q, cu_seqlens_kv,
+                                         softmax_scale, mask_mode, win_left, win_right, max_seqlen_q, max_seqlen_kv,
+                                         layout, deterministic, workspace, out, fp32_out, seqused_q, seqused_kv,
+                                         dq_mode, max_workspace_bytes)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    st = plan._lib.fa_bwd_run(*args, stream)
+    if st != FA_OK:
+        raise FaBwdError(st, "fa_bwd_run")
+    return outs
+
+
+class PreparedGrad:
+    """The backward bound to fixed tensors (from prepare_grad): validation,
+    plan lookup, output / workspace allocation and pointer marshalling are done
+    once, and each call only enqueues fa_bwd_run.  The bound tensors may change
+    in value between calls but not be reallocated; the object keeps them alive.
+    Calling it returns (dq, dk, dv), the same tensors every time."""
+
+    def __init__(self, plan, args, outs, keep, device, stream):
+        self.plan = plan
+        self.outputs = outs
+        self._run = plan._lib.fa_bwd_run
+        self._args = args
+        self._keep = keep
+        self._device = device
+        self._stream = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+
+    def __call__(self, stream=None):
+        """Enqueue one backward on `stream` (a torch stream), else on the stream
+        fixed at preparation, else on the current stream."""
+        if stream is not None:
+            s = ctypes.c_void_p(stream.cuda_stream)
+        elif self._stream is not None:
+            s = self._stream
+        else:
+            import torch
+
+            s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream)
+        st = self._run(*self._args, s)
+        if st != FA_OK:
+            raise FaBwdError(st, "fa_bwd_run")
+        return self.outputs
+
+
+def prepare_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0,
+                 mask_mode=0, win_left=-1, win_right=-1, max_seqlen_q=-1, max_seqlen_kv=-1, layout="BSND",
+                 deterministic=False, workspace=None, out=None, fp32_out=False, seqused_q=None, seqused_kv=None,
+                 dq_mode="auto", max_workspace_bytes=0, stream=None):
+    """flash_attn_grad's arguments bound once into a PreparedGrad, for loops
+    that run the same backward many times (the per-call host cost of
+    flash_attn_grad is a large share of a short backward).  `stream`: a torch
+    stream to enqueue on (default: the current stream at each call)."""
+    plan, args, outs, keep = _bind_grad(q, k, v, dout, attn_out, softmax_lse, cu_seqlens_q, cu_seqlens_kv,
+                                        softmax_scale, mask_mode, win_left, win_right, max_seqlen_q, max_seqlen_kv,
+                                        layout, deterministic, workspace, out, fp32_out, seqused_q, seqused_kv,
+                                        dq_mode, max_workspace_bytes)
+    return PreparedGrad(plan, args, outs, keep, q.device, stream)
 
 
 def flash_attn(q, k, v, cu_seqlens_q=None, cu_seqlens_kv=None, softmax_scale=0.0, mask_mode=0, win_left=-1,

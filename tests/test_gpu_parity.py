@@ -318,13 +318,21 @@ FUSED_EXTRA = {
     "fused_long_queries": W.custom("BNSD", B=2, N1=2, N2=2, S1=1000, S2=128, D=64, Dv=64, mask_mode=0),
     "fused_tnd_window": W.custom("TND", N1=4, N2=1, D=128, Dv=64, mask_mode=2, win_left=17, win_right=3,
                                  lengths=[0, 128, 7, 100, 33], lengths_kv=[5, 128, 0, 90, 33]),
+    # D = 64 runs two query groups over alternate items: an odd item count
+    # (3 heads x 3 blocks) leaves group 1 idle in the last step
+    "fused_d64_gqa3_odd_items": W.custom("BSND", B=2, N1=6, N2=2, S1=80, S2=100, D=64, Dv=64, mask_mode=1),
+    # one item in all: group 1 never has work, its dK / dV stay zero
+    "fused_d64_single_item": W.custom("BNSD", B=1, N1=1, N2=1, S1=20, S2=128, D=64, Dv=64, mask_mode=2,
+                                      win_left=5, win_right=40),
+    "fused_d128_single_item": W.custom("BNSD", B=1, N1=1, N2=1, S1=31, S2=77, D=128, Dv=128, mask_mode=0),
 }
 
 
 @pytest.mark.parametrize("name", sorted(FUSED_EXTRA))
 def test_fused_kernel_shapes(name):
     """The fused kernel at its limits: GQA 8 (the head loop), many query
-    blocks, Dv < D, empty key and query sequences, windows."""
+    blocks, Dv < D, empty key and query sequences, windows, odd and single
+    item counts for the two query groups at D = 64."""
     cfg = FUSED_EXTRA[name]
     say(f"[parity] fused: {name}")
     x = case_inputs(cfg, seed=5)

@@ -28,6 +28,9 @@ CASES = {
     "bsnd_d192_causal_left": (W.custom("BSND", B=2, N1=2, N2=1, S1=260, S2=140, D=192, Dv=128, mask_mode=1,
                                        win_left=50), [259, 33], [140, 90]),
     "kv_only": (W.custom("BSND", B=2, N1=4, N2=4, S1=129, S2=257, D=128, Dv=64, mask_mode=1), None, [200, 128]),
+    # short keys: the plan takes the fused one-launch kernel
+    "fused_d64": (W.custom("BSND", B=3, N1=4, N2=2, S1=100, S2=128, D=64, Dv=64, mask_mode=1),
+                  [100, 37, 0], [128, 90, 5]),
 }
 
 
@@ -61,6 +64,9 @@ def padding_masks(cfg, x, q_shape, k_shape, uq, ukv):
 def run_case(name, dtype=None, store="bf16", tol=None, **extra):
     import torch
 
+    if name.startswith("fused"):
+        extra.setdefault("dq_mode", "fused")
+
     cfg, uq, ukv = CASES[name]
     x = case_inputs(cfg, seed=sorted(CASES).index(name), dtype=dtype)
     args = (cfg["layout"], x["cu_q"], x["cu_kv"], cfg["softmax_scale"], cfg["mask_mode"], cfg["win_left"],
@@ -90,10 +96,11 @@ def test_seqused_parity(name):
     run_case(name)
 
 
-def test_seqused_fp16():
+@pytest.mark.parametrize("name", ["bsnd_gqa_causal", "fused_d64"])
+def test_seqused_fp16(name):
     import torch
 
-    run_case("bsnd_gqa_causal", dtype=torch.float16, store="fp16", tol=(1.25e-3, 2.5e-3))
+    run_case(name, dtype=torch.float16, store="fp16", tol=(1.25e-3, 2.5e-3))
 
 
 def test_seqused_fp32_debug_form():

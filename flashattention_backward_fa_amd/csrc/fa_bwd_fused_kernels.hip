@@ -12,17 +12,18 @@
 //   S = scale * Q K^T, P = exp(S - lse), dP = dY V^T, dS = P (.) (dP - sfmg)
 //                                  per 32-row query block;
 //   dV += P^T dY, dK += dS^T Q     in registers over all blocks and heads;
-//   dQ = scale * dS K              per block: the four wavefronts' dS tiles
-//                                  meet in LDS and D / 32 of the four
-//                                  wavefronts form 32 columns of dQ each
-//                                  over all 128 keys.
+//   dQ = scale * dS K              per block, one step later: the four
+//                                  wavefronts' dS tiles meet in LDS and D / 32
+//                                  of the four wavefronts form 32 columns of
+//                                  dQ each over all 128 keys.
 // Every dQ row sees its whole key range inside the workgroup, so dQ is
 // written once, with no atomics and no workspace, and the result is bitwise
-// repeatable.  The MFMA layouts are those of the dK/dV kernel
-// (fa_bwd_det_kernels.hip): S and dP put query rows on M and keys on N, so P
-// and dS packed to 16 bits are the A operands of the key-major products; the
-// dQ product reads the dS register images back through transposing LDS reads,
-// like the GEMM over stored dS.
+// repeatable.  S and dP put query rows on M and keys on N, as in the dK/dV
+// kernel (fa_bwd_det_kernels.hip), so P and dS packed to 16 bits are MFMA
+// operands of the key products as they stand.  dV, dK and dQ accumulate
+// transposed (the key or query row on N), so that every lane ends with
+// 16-byte pieces of its own row; the dQ product reads the dS register images
+// back through transposing LDS reads, like the GEMM over stored dS.
 
 #include <hip/hip_runtime.h>
 

@@ -383,17 +383,21 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
     // dS -> partial-sum reduce (when a key tile is split over jobs)
     if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;
     if (plan->prof && fabwd::profiler_begin(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+    // unchunked, the dQ GEMM launch also adds the partial sums (in its last
+    // workgroups); chunked, the reduce runs once after the last chunk
+    const bool one_pass = plan->n2_chunk >= a.N2;
+    a.reduce_tail = one_pass && a.n_partials > 1 ? 1 : 0;
     for (int32_t n2b = 0; n2b < a.N2; n2b += plan->n2_chunk) {  // one pass unless dS is chunked
       a.n2_begin = n2b;
       a.n2_count = std::min(plan->n2_chunk, a.N2 - n2b);
       if (fabwd::launch_dkdv(a, stream) != 0) return FA_ERR_RUNTIME;
-      if (plan->prof && plan->n2_chunk >= a.N2 && fabwd::profiler_mark(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
+      if (plan->prof && one_pass && fabwd::profiler_mark(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
       if (fabwd::launch_dq_ds(a, stream) != 0) return FA_ERR_RUNTIME;
     }
     a.n2_begin = 0;
     a.n2_count = a.N2;
     if (plan->prof && fabwd::profiler_end(plan->prof, stream) != 0) return FA_ERR_RUNTIME;
-    if (fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
+    if (!a.reduce_tail && fabwd::launch_reduce_parts(a, stream) != 0) return FA_ERR_RUNTIME;
     return FA_OK;
   }
   if (a.variant == 2) {

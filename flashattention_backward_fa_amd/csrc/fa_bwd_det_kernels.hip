@@ -598,6 +598,55 @@ __global__ __launch_bounds__(256, HD > 128 ? 1 : 2) void dq_kernel(KernelArgs a)
   }
 }
 
+// ------------------------------------------------------------------ partial sums
+
+// dk = bf16(sum over parts) and dv likewise: blocks [0, kblocks) of the
+// nblocks take dK, the rest dV; 8 elements per thread, parts added in index
+// order (so the result is repeatable).
+template <bool F16>
+__device__ __forceinline__ void reduce_parts_body(const float* __restrict__ kpart, int64_t k_stride,
+                                                  bf16* __restrict__ kout, const float* __restrict__ vpart,
+                                                  int64_t v_stride, bf16* __restrict__ vout, int nparts, int kblocks,
+                                                  int blk_id, int nblocks) {
+  const bool is_k = blk_id < kblocks;
+  const float* __restrict__ part = is_k ? kpart : vpart;
+  const int64_t stride = is_k ? k_stride : v_stride;
+  bf16* __restrict__ out = is_k ? kout : vout;
+  const int64_t n8 = stride / 8;
+  const int64_t nblk = is_k ? kblocks : (int64_t)nblocks - kblocks;
+  const int64_t blk = is_k ? blk_id : blk_id - kblocks;
+  for (int64_t i = blk * 256 + threadIdx.x; i < n8; i += nblk * 256) {
+    floatx4 s0 = reinterpret_cast<const floatx4*>(part)[2 * i];
+    floatx4 s1 = reinterpret_cast<const floatx4*>(part)[2 * i + 1];
+    for (int p = 1; p < nparts; ++p) {
+      const float* q = part + (int64_t)p * stride;
+      s0 += reinterpret_cast<const floatx4*>(q)[2 * i];
+      s1 += reinterpret_cast<const floatx4*>(q)[2 * i + 1];
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = to_elem<F16>(s0[e]);
+      o[e + 4] = to_elem<F16>(s1[e]);
+    }
+    reinterpret_cast<bf16x8*>(out)[i] = o;
+  }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ kpart, int64_t k_stride,
+                                                           bf16* __restrict__ kout, const float* __restrict__ vpart,
+                                                           int64_t v_stride, bf16* __restrict__ vout, int nparts,
+                                                           int kblocks) {
+  reduce_parts_body<F16>(kpart, k_stride, kout, vpart, v_stride, vout, nparts, kblocks, blockIdx.x, gridDim.x);
+}
+
+// Blocks of the reduce: at most 4096 per tensor, 8 elements per thread.
+__host__ __device__ inline int64_t reduce_blocks(int64_t elems) {
+  const int64_t b = (elems / 8 + 255) / 256;
+  return b > 4096 ? 4096 : b;
+}
+
 // ------------------------------------------------------------------ dQ from stored dS
 
 // dQ = scale * dS K with dS read back from the tiles the dK/dV kernel stored
@@ -626,6 +675,15 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   const int nh = a.G * a.n2_count;  // query heads of this launch's KV heads
   const int per_tile = nh * a.B;
   const int ntiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
+  if (a.reduce_tail) {  // workgroups past the GEMM's add the dK/dV partial sums
+    const int gemm_blocks = ntiles * per_tile;
+    if ((int)blockIdx.x >= gemm_blocks) {
+      reduce_parts_body<F16>(a.dk_acc, a.k_part_stride, static_cast<bf16*>(a.dk), a.dv_acc, a.v_part_stride,
+                             static_cast<bf16*>(a.dv), a.n_partials, (int)reduce_blocks(a.k_part_stride),
+                             (int)blockIdx.x - gemm_blocks, (int)gridDim.x - gemm_blocks);
+      return;
+    }
+  }
   const int tile = ntiles - 1 - (int)(blockIdx.x / per_tile);
   const int rem = blockIdx.x % per_tile;
   const int hl = rem % nh;          // head within the chunk (its index in the workspace)
@@ -741,42 +799,6 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ partial sums
-
-// dk = bf16(sum over parts) and dv likewise in one launch: blocks below
-// `kblocks` take dK, the rest dV; 8 elements per thread, parts added in index
-// order (so the result is repeatable).
-template <bool F16>
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* __restrict__ kpart, int64_t k_stride,
-                                                           bf16* __restrict__ kout, const float* __restrict__ vpart,
-                                                           int64_t v_stride, bf16* __restrict__ vout, int nparts,
-                                                           int kblocks) {
-  const bool is_k = (int)blockIdx.x < kblocks;
-  const float* __restrict__ part = is_k ? kpart : vpart;
-  const int64_t stride = is_k ? k_stride : v_stride;
-  bf16* __restrict__ out = is_k ? kout : vout;
-  const int64_t n8 = stride / 8;
-  const int64_t nblk = is_k ? kblocks : (int64_t)gridDim.x - kblocks;
-  const int64_t blk = is_k ? blockIdx.x : blockIdx.x - kblocks;
-  for (int64_t i = blk * 256 + threadIdx.x; i < n8; i += nblk * 256) {
-    floatx4 s0 = reinterpret_cast<const floatx4*>(part)[2 * i];
-    floatx4 s1 = reinterpret_cast<const floatx4*>(part)[2 * i + 1];
-    for (int p = 1; p < nparts; ++p) {
-      const float* q = part + (int64_t)p * stride;
-      s0 += reinterpret_cast<const floatx4*>(q)[2 * i];
-      s1 += reinterpret_cast<const floatx4*>(q)[2 * i + 1];
-    }
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[e] = to_elem<F16>(s0[e]);
-      o[e + 4] = to_elem<F16>(s1[e]);
-    }
-    reinterpret_cast<bf16x8*>(out)[i] = o;
-  }
-}
-
-
 }  // namespace
 
 bool det_instantiated(int D, int Dv) {
@@ -844,7 +866,8 @@ int launch_dq(const KernelArgs& a, void* stream) {
 
 int launch_dq_ds(const KernelArgs& a, void* stream) {
   const int64_t tiles = (a.S1 + DQ_BQ - 1) / DQ_BQ;
-  const int64_t blocks = tiles * a.G * a.n2_count * a.B;
+  const int64_t blocks = tiles * a.G * a.n2_count * a.B +
+                         (a.reduce_tail ? reduce_blocks(a.k_part_stride) + reduce_blocks(a.v_part_stride) : 0);
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -855,11 +878,7 @@ int launch_dq_ds(const KernelArgs& a, void* stream) {
 int launch_reduce_parts(const KernelArgs& a, void* stream) {
   if (a.n_partials <= 1) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto blocks = [](int64_t elems) -> int64_t {
-    const int64_t b = (elems / 8 + 255) / 256;
-    return b > 4096 ? 4096 : b;
-  };
-  const int64_t kb = blocks(a.k_part_stride), vb = blocks(a.v_part_stride);
+  const int64_t kb = reduce_blocks(a.k_part_stride), vb = reduce_blocks(a.v_part_stride);
   if (kb <= 0 || vb <= 0) return 0;
   return launch(a.f16 ? reduce_parts_kernel<true> : reduce_parts_kernel<false>, dim3((unsigned)(kb + vb)), dim3(256), s,
                 (const float*)a.dk_acc, a.k_part_stride, static_cast<bf16*>(a.dk), (const float*)a.dv_acc,

@@ -83,6 +83,10 @@ struct KernelArgs {
   // their query heads by the dQ launch): the whole range, or one chunk when
   // the stored dS is processed a few KV heads at a time
   int32_t n2_begin, n2_count;
+  // 1: the dQ GEMM launch also adds the fp32 dK/dV partial sums (extra
+  // workgroups after the GEMM's, which the dispatcher starts as the GEMM's
+  // last ones drain), in place of a separate reduce launch
+  int32_t reduce_tail;
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups

@@ -4,8 +4,9 @@
 One step = one fa_bwd_run over one batch of the workload, with every input
 already resident in HBM.  The plan takes the stored-dS path: the sfmg
 preprocess (rowsum(dY * Y)), the dK/dV kernel (S/P recompute, dP, dS, dV, dK
-over key tiles; it also stores dS), the dQ GEMM over the stored dS, and the
-fp32 partial-sum reduce when the plan splits a key tile.  (Past 4 GiB of dS
+over key tiles; it also stores dS), the dQ GEMM over the stored dS, whose
+launch also adds the fp32 dK/dV partial sums when the plan splits a key tile
+(its last workgroups).  (Past 4 GiB of dS
 the dK/dV and dQ launches repeat per chunk of KV heads; only where one KV
 head's dS alone would not fit does it take the recompute path: the dQ kernel
 recomputes S/P/dP/dS over query tiles and forms sfmg, then the dK/dV kernel

@@ -360,34 +360,40 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   if constexpr (DS) ds_flush();
   wait_vmem();  // no copy may still be landing when LDS is reused below
 
-  // ---- add the other groups' dK/dV into group 0, 32 columns at a time
+  // ---- QG = 2: the groups swap halves through LDS (group 1 hands its dK to
+  // group 0, group 0 its dV to group 1); each adds the half it received and
+  // stores it.  The K, V, Q and dY tiles are no longer read; 32-column block c
+  // of [dK | dV] takes 16 KB in the first of them with room left.
   if constexpr (QG > 1) {
-    float* red = reinterpret_cast<float*>(Ks);  // K/V tiles are no longer read
+    static_assert(QG == 2 && NKB == 1, "two groups of one 32-key slice per wavefront");
+    constexpr int CH = NWG * 16 * 64 * 4;
+    constexpr int nK = (int)sizeof(Ks) / CH, nV = (int)sizeof(Vs) / CH, nQ = (int)sizeof(Qs) / CH;
+    static_assert(nK + nV + nQ + (int)sizeof(Ys) / CH >= NBK + NBV, "LDS room for one group's dK and dV");
+    auto chunk = [&](int c) -> float* {
+      char* p = c < nK             ? reinterpret_cast<char*>(Ks) + c * CH
+                : c < nK + nV      ? reinterpret_cast<char*>(Vs) + (c - nK) * CH
+                : c < nK + nV + nQ ? reinterpret_cast<char*>(&Qs[0][0][0]) + (c - nK - nV) * CH
+                                   : reinterpret_cast<char*>(&Ys[0][0][0]) + (c - nK - nV - nQ) * CH;
+      return reinterpret_cast<float*>(p);
+    };
+    __syncthreads();
+    if (qg == 1) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int nb = 0; nb < NBK; ++nb) xput(chunk(nb), kw, lane, dKr[0][nb]);
+    } else {
 #pragma unroll
-      for (int nb = 0; nb < NBK + NBV; ++nb) {
-        __syncthreads();
-        if (qg != 0) {
-#pragma unroll
-          for (int rg = 0; rg < 16; ++rg)
-            red[(((qg - 1) * NWG + kw) * 16 + rg) * 64 + lane] = nb < NBK ? dKr[kb][nb][rg] : dVr[kb][nb - NBK][rg];
-        }
-        __syncthreads();
-        if (qg == 0) {
-#pragma unroll
-          for (int g = 1; g < QG; ++g) {
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) {
-              const float x = red[(((g - 1) * NWG + kw) * 16 + rg) * 64 + lane];
-              if (nb < NBK) dKr[kb][nb][rg] += x; else dVr[kb][nb - NBK][rg] += x;
-            }
-          }
-        }
-      }
+      for (int nb = 0; nb < NBV; ++nb) xput(chunk(NBK + nb), kw, lane, dVr[0][nb]);
     }
-    if (qg != 0) return;
+    __syncthreads();
+    if (qg == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) xadd(chunk(nb), kw, lane, dKr[0][nb]);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) xadd(chunk(NBK + nb), kw, lane, dVr[0][nb]);
+    }
   }
+  const bool st_k = QG == 1 || qg == 0, st_v = QG == 1 || qg == 1;
 
   // ---- output: bf16 when this job alone covers the key tile, else fp32 partials
   const bool partial = a.n_partials > 1;
@@ -402,15 +408,23 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
       const int64_t ko = sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
       const int64_t vo = sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
       if (partial) {
+        if (st_k) {
 #pragma unroll
-        for (int nb = 0; nb < NBK; ++nb) a.dk_acc[kpart + ko + nb * 32 + l32] = dKr[kb][nb][rg] * a.scale;
+          for (int nb = 0; nb < NBK; ++nb) a.dk_acc[kpart + ko + nb * 32 + l32] = dKr[kb][nb][rg] * a.scale;
+        }
+        if (st_v) {
 #pragma unroll
-        for (int nb = 0; nb < NBV; ++nb) a.dv_acc[vpart + vo + nb * 32 + l32] = dVr[kb][nb][rg];
+          for (int nb = 0; nb < NBV; ++nb) a.dv_acc[vpart + vo + nb * 32 + l32] = dVr[kb][nb][rg];
+        }
       } else {
+        if (st_k) {
 #pragma unroll
-        for (int nb = 0; nb < NBK; ++nb) static_cast<bf16*>(a.dk)[ko + nb * 32 + l32] = to_elem<F16>(dKr[kb][nb][rg] * a.scale);
+          for (int nb = 0; nb < NBK; ++nb) static_cast<bf16*>(a.dk)[ko + nb * 32 + l32] = to_elem<F16>(dKr[kb][nb][rg] * a.scale);
+        }
+        if (st_v) {
 #pragma unroll
-        for (int nb = 0; nb < NBV; ++nb) static_cast<bf16*>(a.dv)[vo + nb * 32 + l32] = to_elem<F16>(dVr[kb][nb][rg]);
+          for (int nb = 0; nb < NBV; ++nb) static_cast<bf16*>(a.dv)[vo + nb * 32 + l32] = to_elem<F16>(dVr[kb][nb][rg]);
+        }
       }
     }
   }

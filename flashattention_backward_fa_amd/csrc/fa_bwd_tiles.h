@@ -180,6 +180,24 @@ struct SwzTile {
   }
 };
 
+// A 32 x 32 fp32 block of each of the 4 wavefronts of a group in 16 KB of
+// LDS: lane-contiguous 16-byte pieces, element rg of lane l of wavefront w at
+// float 4 * ((4w + rg/4) * 64 + l) + rg % 4.
+__device__ __forceinline__ void xput(float* area, int w, int lane, const floatx16& acc) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+    *reinterpret_cast<floatx4*>(area + 4 * ((4 * w + r4) * 64 + lane)) =
+        floatx4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+}
+__device__ __forceinline__ void xadd(const float* area, int w, int lane, floatx16& acc) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const floatx4 x = *reinterpret_cast<const floatx4*>(area + 4 * ((4 * w + r4) * 64 + lane));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[4 * r4 + e] += x[e];
+  }
+}
+
 // Workgroup barrier for LDS-only hand-offs: waits for this wavefront's own LDS
 // operations, then s_barrier.  Unlike __syncthreads it does not drain
 // outstanding global loads (the compiler's release fence would), so a

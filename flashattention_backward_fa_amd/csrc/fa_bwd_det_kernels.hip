@@ -395,37 +395,50 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   }
   const bool st_k = QG == 1 || qg == 0, st_v = QG == 1 || qg == 1;
 
-  // ---- output: bf16 when this job alone covers the key tile, else fp32 partials
-  const bool partial = a.n_partials > 1;
+  // ---- output: 16-bit dK / dV when this job alone covers the key tile, as
+  // 16-byte row pieces (the accumulators transposed on MFMA first); else fp32
+  // partial sums, one column per lane
+  static_assert(NKB == 1, "one 32-key slice per wavefront");
+  if (a.n_partials == 1) {
+    bf16x8 eye[2];
+    eye_operand<F16>(lane, eye);
+    const int jr = j0 + kw0 + l32;  // the key of this lane's row
+    const bool ok = jr < sb.s2a;    // keys past the used ones hold zeros
+    auto put = [&](bf16* row, const floatx16& acc, float mul, int nb) {
+      u32x4 piece[2];
+      row_pieces<F16>(transpose_acc<F16>(acc, mul, eye), 1.f, piece);
+      if (ok) {
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) *reinterpret_cast<u32x4*>(row + nb * 32 + pc * 16 + hi * 8) = piece[pc];
+      }
+    };
+    if (st_k) {
+      bf16* row = static_cast<bf16*>(a.dk) + sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)jr * a.k_ss;
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) put(row, dKr[0][nb], a.scale, nb);
+    }
+    if (st_v) {
+      bf16* row = static_cast<bf16*>(a.dv) + sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)jr * a.v_ss;
+#pragma unroll
+      for (int nb = 0; nb < NBV; ++nb) put(row, dVr[0][nb], 1.f, nb);
+    }
+    return;
+  }
   const int64_t kpart = (int64_t)part * a.k_part_stride;
   const int64_t vpart = (int64_t)part * a.v_part_stride;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
+  for (int rg = 0; rg < 16; ++rg) {
+    const int j = j0 + kw0 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+    if (j >= sb.s2a) continue;  // keys past the used ones hold zeros
+    const int64_t ko = sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
+    const int64_t vo = sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
+    if (st_k) {
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) {
-      const int j = j0 + kw0 + kb * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
-      if (j >= sb.s2a) continue;  // keys past the used ones hold zeros
-      const int64_t ko = sb.kbase + (int64_t)n2 * a.k_sn + (int64_t)j * a.k_ss;
-      const int64_t vo = sb.vbase + (int64_t)n2 * a.v_sn + (int64_t)j * a.v_ss;
-      if (partial) {
-        if (st_k) {
+      for (int nb = 0; nb < NBK; ++nb) a.dk_acc[kpart + ko + nb * 32 + l32] = dKr[0][nb][rg] * a.scale;
+    }
+    if (st_v) {
 #pragma unroll
-          for (int nb = 0; nb < NBK; ++nb) a.dk_acc[kpart + ko + nb * 32 + l32] = dKr[kb][nb][rg] * a.scale;
-        }
-        if (st_v) {
-#pragma unroll
-          for (int nb = 0; nb < NBV; ++nb) a.dv_acc[vpart + vo + nb * 32 + l32] = dVr[kb][nb][rg];
-        }
-      } else {
-        if (st_k) {
-#pragma unroll
-          for (int nb = 0; nb < NBK; ++nb) static_cast<bf16*>(a.dk)[ko + nb * 32 + l32] = to_elem<F16>(dKr[kb][nb][rg] * a.scale);
-        }
-        if (st_v) {
-#pragma unroll
-          for (int nb = 0; nb < NBV; ++nb) static_cast<bf16*>(a.dv)[vo + nb * 32 + l32] = to_elem<F16>(dVr[kb][nb][rg]);
-        }
-      }
+      for (int nb = 0; nb < NBV; ++nb) a.dv_acc[vpart + vo + nb * 32 + l32] = dVr[0][nb][rg];
     }
   }
 }

@@ -44,49 +44,6 @@ __device__ __forceinline__ void wait_vmem_keep() {
   asm volatile("" ::: "memory");
 }
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t pack2(bf16 lo, bf16 hi) {
-  return (uint32_t)__builtin_bit_cast(unsigned short, lo) | ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
-}
-
-// A 32 x 32 block held transposed (lane = row l % 32, element rg = column
-// 8*(rg/4) + 4*(l/32) + rg%4), times mul, as two 16-byte pieces per lane:
-// after a swap of halves between lanes l and l + 32, piece p of lane l holds
-// columns 16p + 8*(l/32) .. +7 of its row.
-template <bool F16>
-__device__ __forceinline__ void row_pieces(const floatx16& acc, float mul, u32x4 (&piece)[2]) {
-  uint32_t w[8];  // w[2*c4 + e]: columns 8*c4 + 4*hi + 2e, +1
-#pragma unroll
-  for (int x = 0; x < 8; ++x) w[x] = pack2(to_elem<F16>(acc[2 * x] * mul), to_elem<F16>(acc[2 * x + 1] * mul));
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      // lanes 32..63 of the first operand trade places with lanes 0..31 of the second
-      const auto r = __builtin_amdgcn_permlane32_swap(w[4 * p + e], w[4 * p + 2 + e], false, false);
-      w[4 * p + e] = r[0];
-      w[4 * p + 2 + e] = r[1];
-    }
-    piece[p] = u32x4{w[4 * p], w[4 * p + 1], w[4 * p + 2], w[4 * p + 3]};
-  }
-}
-
-// One key row of a transposed accumulator of NB 32-column blocks, times mul,
-// in 16-byte pieces at row (when ok).
-template <bool F16, int NB>
-__device__ __forceinline__ void store_rows(bf16* row, const floatx16 (&acc)[NB], float mul, int hi, bool ok) {
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    u32x4 piece[2];
-    row_pieces<F16>(acc[nb], mul, piece);
-    if (ok) {
-#pragma unroll
-      for (int pc = 0; pc < 2; ++pc) *reinterpret_cast<u32x4*>(row + nb * 32 + pc * 16 + hi * 8) = piece[pc];
-    }
-  }
-}
-
 constexpr int FK = FUSED_MAX_KEYS;  // keys per workgroup: 4 wavefronts x 32
 constexpr int FR = 32;              // query rows per step
 static_assert(FK == 128, "one 32-key slice per wavefront");

@@ -180,6 +180,83 @@ struct SwzTile {
   }
 };
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pack2(bf16 lo, bf16 hi) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, lo) | ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
+}
+
+// A 32 x 32 block held transposed (lane = row l % 32, element rg = column
+// 8*(rg/4) + 4*(l/32) + rg%4), times mul, as two 16-byte pieces per lane:
+// after a swap of halves between lanes l and l + 32, piece p of lane l holds
+// columns 16p + 8*(l/32) .. +7 of its row.
+template <bool F16>
+__device__ __forceinline__ void row_pieces(const floatx16& acc, float mul, u32x4 (&piece)[2]) {
+  uint32_t w[8];  // w[2*c4 + e]: columns 8*c4 + 4*hi + 2e, +1
+#pragma unroll
+  for (int x = 0; x < 8; ++x) w[x] = pack2(to_elem<F16>(acc[2 * x] * mul), to_elem<F16>(acc[2 * x + 1] * mul));
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      // lanes 32..63 of the first operand trade places with lanes 0..31 of the second
+      const auto r = __builtin_amdgcn_permlane32_swap(w[4 * p + e], w[4 * p + 2 + e], false, false);
+      w[4 * p + e] = r[0];
+      w[4 * p + 2 + e] = r[1];
+    }
+    piece[p] = u32x4{w[4 * p], w[4 * p + 1], w[4 * p + 2], w[4 * p + 3]};
+  }
+}
+
+// One key row of a transposed accumulator of NB 32-column blocks, times mul,
+// in 16-byte pieces at row (when ok).
+template <bool F16, int NB>
+__device__ __forceinline__ void store_rows(bf16* row, const floatx16 (&acc)[NB], float mul, int hi, bool ok) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    u32x4 piece[2];
+    row_pieces<F16>(acc[nb], mul, piece);
+    if (ok) {
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc) *reinterpret_cast<u32x4*>(row + nb * 32 + pc * 16 + hi * 8) = piece[pc];
+    }
+  }
+}
+
+// A key-major 32 x 32 accumulator (lane = column l % 32, element rg = key
+// 8*(rg/4) + 4*(l/32) + rg%4), times mul and rounded to 16 bits, in the
+// transposed form that row_pieces takes (lane = key).  Two MFMAs against a
+// permutation of the identity: A is the accumulator as it stands (column =
+// M, key = K; rg 8s..8s+7 are the K-slots of product s), and each output
+// element is one input times 1 plus zeros, so the values come through
+// unchanged.  eye[s] is this lane's B operand of product s (eye_operand).
+template <bool F16>
+__device__ __forceinline__ floatx16 transpose_acc(const floatx16& acc, float mul, const bf16x8 (&eye)[2]) {
+  floatx16 d = floatx16{};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8 x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = to_elem<F16>(acc[8 * s + j] * mul);
+    d = mfma32<F16>(x, eye[s], d);
+  }
+  return d;
+}
+// B operand of product s of transpose_acc for lane `lane`: K-slot 8*(lane/32)
+// + j holds key 16s + 8*(j/4) + 4*(lane/32) + j%4; column n = lane % 32 takes
+// a 1 at the slot of key n.
+template <bool F16>
+__device__ __forceinline__ void eye_operand(int lane, bf16x8 (&eye)[2]) {
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int m = n - 16 * s;
+    const int jj = (m >= 0 && m < 16 && ((m >> 2) & 1) == h) ? 4 * (m >> 3) + (m & 3) : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) eye[s][j] = to_elem<F16>(j == jj ? 1.f : 0.f);
+  }
+}
+
 // A 32 x 32 fp32 block of each of the 4 wavefronts of a group in 16 KB of
 // LDS: lane-contiguous 16-byte pieces, element rg of lane l of wavefront w at
 // float 4 * ((4w + rg/4) * 64 + l) + rg % 4.

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 
 #include "fa_bwd_internal.h"
@@ -312,6 +313,17 @@ int check_run_pointers(const fa_bwd_plan_s& p, const int32_t* cu_q, const int32_
   return FA_OK;
 }
 
+// Element tensors move in 16-byte pieces (copies to LDS, vector loads, row
+// stores); float32 and int32 arrays in 4-byte words.  NULL passes (optional
+// arrays).
+bool aligned(std::initializer_list<const void*> t16, std::initializer_list<const void*> t4) {
+  for (const void* p : t16)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  for (const void* p : t4)
+    if (reinterpret_cast<uintptr_t>(p) & 3) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -349,6 +361,8 @@ int fa_bwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
     return FA_ERR_NULLPTR;
   int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
   if (st != FA_OK) return st;
+  if (!aligned({q, k, v, dout, attn_out, dq, dk, dv}, {softmax_lse, cu_seqlens_q, cu_seqlens_kv, seqused_q, seqused_kv}))
+    return FA_ERR_PARAM_INVALID;
   if (plan->ws_bytes > 0 && (!workspace || workspace_bytes < plan->ws_bytes)) return FA_ERR_WORKSPACE;
   // the atomic kernels do not read seqused
   if ((seqused_q || seqused_kv) && plan->args.variant < 2) return FA_ERR_UNSUPPORTED;
@@ -430,6 +444,8 @@ int fa_bwd_run_noalloc(fa_bwd_plan plan, const void* q, const void* k, const voi
   if (!q || !k || !v || !dout || !attn_out || !softmax_lse || !dq || !dk || !dv) return FA_ERR_NULLPTR;
   const int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
   if (st != FA_OK) return st;
+  if (!aligned({q, k, v, dout, attn_out, dq, dk, dv}, {softmax_lse, cu_seqlens_q, cu_seqlens_kv, seqused_q, seqused_kv}))
+    return FA_ERR_PARAM_INVALID;
   if ((seqused_q || seqused_kv) && plan->args.variant < 2) return FA_ERR_UNSUPPORTED;
   void* scratch = nullptr;
   if (plan->ws_bytes > 0 && fabwd::scratch_ptr(&scratch) != 0) return FA_ERR_RUNTIME;
@@ -443,6 +459,8 @@ int fa_fwd_run(fa_bwd_plan plan, const void* q, const void* k, const void* v, co
   if (!plan || !q || !k || !v || !attn_out || !softmax_lse) return FA_ERR_NULLPTR;
   int st = check_run_pointers(*plan, cu_seqlens_q, cu_seqlens_kv);
   if (st != FA_OK) return st;
+  if (!aligned({q, k, v, attn_out}, {softmax_lse, cu_seqlens_q, cu_seqlens_kv, seqused_q, seqused_kv}))
+    return FA_ERR_PARAM_INVALID;
   KernelArgs a = plan->args;
   a.q = q; a.k = k; a.v = v;
   a.cu_q = cu_seqlens_q; a.cu_kv = cu_seqlens_kv;
@@ -492,6 +510,7 @@ int fa_bwd_sfmg(fa_bwd_plan plan, const void* dout, const void* attn_out,
   if (!plan || !dout || !attn_out || !sfmg) return FA_ERR_NULLPTR;
   const bool tnd = plan->desc.layout == FA_LAYOUT_TND;
   if (tnd != (cu_seqlens_q != nullptr)) return FA_ERR_SHAPE;
+  if (!aligned({dout, attn_out}, {cu_seqlens_q, sfmg})) return FA_ERR_PARAM_INVALID;
   KernelArgs a = plan->args;
   a.dout = dout; a.out = attn_out; a.cu_q = cu_seqlens_q; a.sfmg = sfmg;
   if (fabwd::launch_preprocess(a, false, stream) != 0) return FA_ERR_RUNTIME;

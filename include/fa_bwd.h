@@ -22,6 +22,10 @@
  *  - All tensors are dense, row-major, contiguous, in device memory, owned by
  *    the caller.  Inputs are only read.  dq, dk, dv are fully overwritten
  *    (rows that receive no gradient are written as zeros).
+ *  - The kernels move q, k, v, dout, attn_out, dq, dk and dv in 16-byte
+ *    pieces: their pointers must be 16-byte aligned, and softmax_lse and the
+ *    int32 arrays 4-byte aligned (FA_ERR_PARAM_INVALID otherwise, returned
+ *    before any launch).
  *  - Element types (section 五 5.4 registers both): bf16 and IEEE fp16.  q, k,
  *    v, dout, attn_out and dq, dk, dv share the plan's type; softmax_lse and
  *    the workspace are float32.
@@ -216,7 +220,8 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
  *                             fa_bwd_create, exclusively owned by this call
  *                             until it completes on `stream`
  * Errors: FA_ERR_NULLPTR (plan or a tensor pointer NULL), FA_ERR_SHAPE
- * (cu_seqlens given or missing against the layout), FA_ERR_WORKSPACE,
+ * (cu_seqlens given or missing against the layout), FA_ERR_PARAM_INVALID (a
+ * pointer misaligned, see the conventions above), FA_ERR_WORKSPACE,
  * FA_ERR_RUNTIME (a launch failed).  Device cu_seqlens are trusted: they must
  * agree with T1/T2 and the max lengths in the plan. */
 int fa_bwd_run(fa_bwd_plan plan,

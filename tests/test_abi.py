@@ -328,6 +328,33 @@ def test_tnd_rules(lib):
     assert lib.fa_bwd_create(ctypes.byref(d), ctypes.byref(h), ctypes.byref(ws)) == fb.FA_ERR_SHAPE
 
 
+def test_misaligned_pointers_rejected_before_any_device_call(lib):
+    """Element tensors move in 16-byte pieces, float32 / int32 arrays in words:
+    a misaligned pointer is FA_ERR_PARAM_INVALID from every run entry point,
+    before anything is launched (the fake addresses are never dereferenced)."""
+    plan = fb.Plan(fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64, dq_mode="stored_ds"))
+    fake, half = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    lse_odd = ctypes.c_void_p(0x1002)
+    ws = plan.workspace_bytes
+    none4 = [None] * 4  # cu_q cu_kv seqused_q seqused_kv
+    for i in (0, 1, 2, 3, 4):  # q k v dout attn_out
+        args = [fake] * 6
+        args[i] = half
+        assert lib.fa_bwd_run(plan.handle, *args, *none4, fake, fake, fake, fake, ws, None) == fb.FA_ERR_PARAM_INVALID
+    for i in range(3):  # dq dk dv
+        outs = [fake] * 3
+        outs[i] = half
+        assert lib.fa_bwd_run(plan.handle, *([fake] * 6), *none4, *outs, fake, ws, None) == fb.FA_ERR_PARAM_INVALID
+        assert lib.fa_bwd_run_noalloc(plan.handle, *([fake] * 6), *none4, *outs, None) == fb.FA_ERR_PARAM_INVALID
+    assert lib.fa_bwd_run(plan.handle, *([fake] * 5), lse_odd, *none4, fake, fake, fake, fake, ws,
+                          None) == fb.FA_ERR_PARAM_INVALID
+    assert lib.fa_fwd_run(plan.handle, half, fake, fake, None, None, None, None, fake, fake,
+                          None) == fb.FA_ERR_PARAM_INVALID
+    assert lib.fa_fwd_run(plan.handle, fake, fake, fake, None, None, None, None, fake, lse_odd,
+                          None) == fb.FA_ERR_PARAM_INVALID
+    assert lib.fa_bwd_sfmg(plan.handle, half, fake, None, fake, None) == fb.FA_ERR_PARAM_INVALID
+
+
 def test_tnd_decreasing_cu_rejected(lib):
     aq = (ctypes.c_int32 * 3)(0, 6, 4)
     d = fb.make_desc("TND", 2, 2, 2, -1, -1, 64, 64, 4, 4, host_cu_q=aq, host_cu_kv=aq)

@@ -277,6 +277,15 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   a.n_partials = pair ? (a.G / a.heads_per_job) * a.q_splits : 1;
   a.k_part_stride = k_elems;
   a.v_part_stride = v_elems;
+  // dQ GEMM: two step groups per workgroup when its grid fits one round of two
+  // workgroups per CU (the longest row groups of a causal mask then take half
+  // as long) and no partial-sum reduce runs in its tail
+  a.dq_groups = 1;
+  if (a.variant == 4 && d.D <= 128) {
+    const bool tail = p.n2_chunk >= N2 && a.n_partials > 1;
+    const int64_t wgs = (S1 + 127) / 128 * a.G * p.n2_chunk * d.B;
+    if (!tail && wgs <= 2 * (int64_t)cus) a.dq_groups = 2;
+  }
 
   // workspace: sfmg, [dQ accumulator], [dK / dV partial sums], [dS]
   p.off_sfmg = 0;

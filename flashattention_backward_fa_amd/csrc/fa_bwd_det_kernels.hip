@@ -685,19 +685,26 @@ __host__ __device__ inline int64_t reduce_blocks(int64_t elems) {
 // double-buffered.  Both MFMA operands are transposing reads with the same key
 // order inside each 16-key chunk: B = K through SwzTile, A = dS through
 // per-lane addresses into the stored register images (below).
+// QG = 2 (grids of at most one round): two such groups of 4 wavefronts share
+// the row group and take alternate steps, each with its own buffers; at the end
+// they swap halves of the columns through LDS and each stores its half.  The
+// longest row groups of a causal mask then take half as long.
 constexpr int DQS_BK = 64;  // keys per step: two 32-key slices
 
 
-template <int HD, bool F16>
-__global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
+template <int HD, int QG, bool F16>
+__global__ __launch_bounds__(256 * QG, 2 / QG) void dq_ds_kernel(KernelArgs a) {
   constexpr int NBK = HD / 32;
   constexpr int KTB = DQS_BK * HD * 2;  // bytes of one K tile buffer
   constexpr int STB = 16384;            // bytes of one dS buffer: 2 slices x 4 query blocks x 2 KB
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][DQS_BK * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 Ss[2][STB / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[QG][2][DQS_BK * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Ss[QG][2][STB / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wv >> 2;   // step group: takes steps qg, qg + QG, ...
+  const int wave = wv & 3;  // query block of the row group
+  const uint32_t ks_lds = lds_addr(Ks) + qg * 2 * KTB, ss_lds = lds_addr(Ss) + qg * 2 * STB;
   // job -> (query group, query head, sequence), the longest groups first
   const int nh = a.G * a.n2_count;  // query heads of this launch's KV heads
   const int per_tile = nh * a.B;
@@ -749,20 +756,20 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
   const uint32_t s_voff = (uint32_t)ds_chunk_slot(lane, wave & 1) * 16;
   auto fetch = [&](int st, int buf) {
     const int ks = ksl.lo + 2 * st;
-    kcp.issue(lds_addr(Ks) + buf * KTB, Kg + (int64_t)ks * 32 * a.k_ss, s2 - ks * 32, wave, lane);
+    kcp.issue(ks_lds + buf * KTB, Kg + (int64_t)ks * 32 * a.k_ss, s2 - ks * 32, wave, lane);
     const bf16* src = Sg + (int64_t)(ks - ksl.lo) * 4096;
     const bool two = ks + 1 < ks_end;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int u = wave + 4 * x;  // half u % 2 == wave % 2 of tile u / 2
       const int usrc = (u >= 8 && !two) ? u - 8 : u;
-      dma16_nt(src + usrc * 512, s_voff, lds_addr(Ss) + buf * STB + u * 1024);
+      dma16_nt(src + usrc * 512, s_voff, ss_lds + buf * STB + u * 1024);
     }
   };
-  if (nsteps > 0) fetch(0, 0);
+  if (qg < nsteps) fetch(qg, 0);
 
   SwzTile<HD, DQS_BK> kadr;
-  kadr.init(lds_addr(Ks), lane);
+  kadr.init(ks_lds, lane);
   // A operand: lane i of a 16-lane group gets, as element e of a transposing
   // read, element i % 4 of the 8 bytes that lane 4e + i/4 of its group loads.
   // For query row m = 16*(g % 2) + i (g = lane / 16) and keys
@@ -775,7 +782,7 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = 32 * (q & 1) + 8 * s + 4 * (g >> 1) + e;  // chunk at kc = 0
-      a_base[s] = lds_addr(Ss) + wave * 2048 + h * 1024 + ds_chunk_slot(c, h) * 16 + (q >> 1) * 8;
+      a_base[s] = ss_lds + wave * 2048 + h * 1024 + ds_chunk_slot(c, h) * 16 + (q >> 1) * 8;
     }
   }
 
@@ -787,10 +794,12 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NBK; ++nb) dq[nb] = floatx16{};
 
+  // iteration it: group qg computes step st = it * QG + qg (if there is one)
   auto step = [&](int st, int buf) {
     wait_vmem();    // this wavefront's copies of step st landed
     lds_barrier();  // ... and everyone's; buffer buf ^ 1 is no longer read
-    if (st + 1 < nsteps) fetch(st + 1, buf ^ 1);
+    if (st + QG < nsteps) fetch(st + QG, buf ^ 1);
+    if (st >= nsteps) return;
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       const int ks = ksl.lo + 2 * st + sl;
@@ -812,7 +821,35 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
       }
     }
   };
-  for (int st = 0; st < nsteps; ++st) step(st, st & 1);
+  const int iters = (nsteps + QG - 1) / QG;
+  for (int it = 0; it < iters; ++it) step(it * QG + qg, it & 1);
+
+  // QG = 2: group 1 hands column blocks [0, NBK/2) to group 0, group 0 hands
+  // the rest to group 1 (16 KB of LDS per block); each adds what it received
+  constexpr int NLO = QG > 1 ? NBK / 2 : NBK;  // blocks that group 0 stores
+  if constexpr (QG > 1) {
+    static_assert(NBK % 2 == 0 && QG == 2, "two halves");
+    static_assert(sizeof(Ks) >= (size_t)NBK * 16384, "LDS room for the swap");
+    wait_vmem();
+    __syncthreads();  // every LDS read of the steps is done
+    float* area = reinterpret_cast<float*>(&Ks[0][0][0]);
+    if (qg == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NLO; ++nb) xput(area + nb * 4096, wave, lane, dq[nb]);
+    } else {
+#pragma unroll
+      for (int nb = NLO; nb < NBK; ++nb) xput(area + nb * 4096, wave, lane, dq[nb]);
+    }
+    __syncthreads();
+    if (qg == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NLO; ++nb) xadd(area + nb * 4096, wave, lane, dq[nb]);
+    } else {
+#pragma unroll
+      for (int nb = NLO; nb < NBK; ++nb) xadd(area + nb * 4096, wave, lane, dq[nb]);
+    }
+  }
+  const int nb_lo = qg == 0 ? 0 : NLO, nb_hi = qg == 0 ? NLO : NBK;
 
   // dq = bf16(scale * acc): lane holds head-dim column nb*32 + l32 of 16 rows
   bf16* __restrict__ dQg = static_cast<bf16*>(a.dq) + sb.qbase + (int64_t)n1 * a.q_sn;
@@ -821,7 +858,8 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(KernelArgs a) {
     const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
     if (i < sb.s1a) {  // rows past the used ones hold zeros
 #pragma unroll
-      for (int nb = 0; nb < NBK; ++nb) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
+      for (int nb = 0; nb < NBK; ++nb)
+        if (nb >= nb_lo && nb < nb_hi) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
     }
   }
 }
@@ -850,10 +888,12 @@ int launch_dkdv_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
 
 template <bool F16>
 int launch_dq_ds_t(const KernelArgs& a, dim3 grid, hipStream_t s) {
-  const dim3 block(256);
-  if (a.D == 64) return launch(dq_ds_kernel<64, F16>, grid, block, s, a);
-  if (a.D == 128) return launch(dq_ds_kernel<128, F16>, grid, block, s, a);
-  if (a.D == 192) return launch(dq_ds_kernel<192, F16>, grid, block, s, a);
+  const bool two = a.dq_groups == 2;
+  const dim3 b1(256), b2(512);
+  if (a.D == 64) return two ? launch(dq_ds_kernel<64, 2, F16>, grid, b2, s, a) : launch(dq_ds_kernel<64, 1, F16>, grid, b1, s, a);
+  if (a.D == 128)
+    return two ? launch(dq_ds_kernel<128, 2, F16>, grid, b2, s, a) : launch(dq_ds_kernel<128, 1, F16>, grid, b1, s, a);
+  if (a.D == 192 && !two) return launch(dq_ds_kernel<192, 1, F16>, grid, b1, s, a);
   return (int)hipErrorInvalidValue;
 }
 

@@ -87,6 +87,9 @@ struct KernelArgs {
   // workgroups after the GEMM's, which the dispatcher starts as the GEMM's
   // last ones drain), in place of a separate reduce launch
   int32_t reduce_tail;
+  // dQ GEMM workgroups: 1 = 4 wavefronts; 2 = two groups of 4 that share a row
+  // group and take alternate key steps (D <= 128, no reduce tail)
+  int32_t dq_groups;
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups

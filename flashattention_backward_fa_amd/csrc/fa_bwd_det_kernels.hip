@@ -227,13 +227,13 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < NKQ; ++kk) {
-      const bf16x8 qa = lds_load16(qadr.row_read(kk, buf * QTB));
+      const bf16x8 qa = lds_load16(qadr.row_read_c(kk, buf * QTB));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32<F16>(qa, lds_load16(k_lane + (kb * 32 * KP + 16 * kk) * 2), sacc[kb]);
     }
 #pragma unroll
     for (int kk = 0; kk < NKV; ++kk) {
-      const bf16x8 ya = lds_load16(yadr.row_read(kk, buf * YTB));
+      const bf16x8 ya = lds_load16(yadr.row_read_c(kk, buf * YTB));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) pacc[kb] = mfma32<F16>(ya, lds_load16(v_lane + (kb * 32 * VP + 16 * kk) * 2), pacc[kb]);
     }
@@ -312,13 +312,13 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
       for (int nb = 0; nb < NBV; ++nb) {
-        const bf16x8 yb = join(lds_load_tr(yadr.tr_read(kc, 0, nb, buf * YTB)), lds_load_tr(yadr.tr_read(kc, 1, nb, buf * YTB)));
+        const bf16x8 yb = join(lds_load_tr(yadr.tr_read_c(kc, 0, nb, buf * YTB)), lds_load_tr(yadr.tr_read_c(kc, 1, nb, buf * YTB)));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) dVr[kb][nb] = mfma32<F16>(pa[kb][kc], yb, dVr[kb][nb]);
       }
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
-        const bf16x8 qb = join(lds_load_tr(qadr.tr_read(kc, 0, nb, buf * QTB)), lds_load_tr(qadr.tr_read(kc, 1, nb, buf * QTB)));
+        const bf16x8 qb = join(lds_load_tr(qadr.tr_read_c(kc, 0, nb, buf * QTB)), lds_load_tr(qadr.tr_read_c(kc, 1, nb, buf * QTB)));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) dKr[kb][nb] = mfma32<F16>(da[kb][kc], qb, dKr[kb][nb]);
       }
@@ -356,7 +356,13 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
     }
     step_cursor(cc, QG);
   };
-  for (int it = 0; it < iters; ++it) step(it, it & 1);
+  // two steps per iteration, so that the buffer offsets are constants
+  int it = 0;
+  for (; it + 1 < iters; it += 2) {
+    step(it, 0);
+    step(it + 1, 1);
+  }
+  if (it < iters) step(it, 0);
   if constexpr (DS) ds_flush();
   wait_vmem();  // no copy may still be landing when LDS is reused below
 

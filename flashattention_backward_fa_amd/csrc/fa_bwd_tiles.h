@@ -169,6 +169,13 @@ struct SwzTile {
     if constexpr (COLS == 192) return kk < 8 ? row_read(kk, boff) + r0 * 256 : row_read(kk, boff) + r0 * 128;
     else return row_read(kk, boff) + r0 * W0 * 2;
   }
+  // The same two reads with boff added after the XOR (equal, since boff is a
+  // multiple of 512 and the XOR acts on bits 5..7 only), for loops whose
+  // buffer offset is a constant: it then becomes the instruction's offset.
+  __device__ __forceinline__ uint32_t row_read_c(int kk, uint32_t boff) const { return row_read(kk) + boff; }
+  __device__ __forceinline__ uint32_t tr_read_c(int kc, int s, int nb, uint32_t boff) const {
+    return tr_read(kc, s, nb) + boff;
+  }
   // LDS address of the transposing read for row chunk kc, half s, column block nb
   __device__ __forceinline__ uint32_t tr_read(int kc, int s, int nb, uint32_t boff = 0) const {
     if constexpr (COLS == 192) {

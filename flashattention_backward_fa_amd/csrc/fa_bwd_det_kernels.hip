@@ -818,8 +818,8 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void dq_ds_kernel(KernelArgs a) {
           const int kc = 2 * sl + c;
 #pragma unroll
           for (int nb = 0; nb < NBK; ++nb) {
-            const bf16x8 kb = join(lds_load_tr(kadr.tr_read(kc, 0, nb, buf * KTB)),
-                                   lds_load_tr(kadr.tr_read(kc, 1, nb, buf * KTB)));
+            const bf16x8 kb = join(lds_load_tr(kadr.tr_read_c(kc, 0, nb, buf * KTB)),
+                                   lds_load_tr(kadr.tr_read_c(kc, 1, nb, buf * KTB)));
             dq[nb] = mfma32<F16>(da, kb, dq[nb]);
           }
         }
@@ -828,7 +828,12 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void dq_ds_kernel(KernelArgs a) {
     }
   };
   const int iters = (nsteps + QG - 1) / QG;
-  for (int it = 0; it < iters; ++it) step(it * QG + qg, it & 1);
+  int it = 0;  // two steps per iteration, so that the buffer offsets are constants
+  for (; it + 1 < iters; it += 2) {
+    step(it * QG + qg, 0);
+    step((it + 1) * QG + qg, 1);
+  }
+  if (it < iters) step(it * QG + qg, 0);
 
   // QG = 2: group 1 hands column blocks [0, NBK/2) to group 0, group 0 hands
   // the rest to group 1 (16 KB of LDS per block); each adds what it received

@@ -215,14 +215,22 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   // group and slice are consecutive, at slot ks - (the group's first slice).
   // (The group and slot guards keep the stores inside the workspace even for a
   // sequence longer than the maximum length the plan was made for.)
+  // Per job: this wavefront's slice, the query blocks that see a key of it
+  // (the tiles that are stored), the group of row group 0 and the group stride.
+  const int ds_ks = (j0 + kw0) >> 5;
+  const fa_sched::Span ds_vis =
+      ds_ks * 32 < s2 ? fa_sched::blocks_covering(fa_sched::rows_seeing(s1, ds_ks * 32, min(ds_ks * 32 + 32, s2), off, wl, wr), 32)
+                      : fa_sched::Span{0, 0};
+  const int64_t ds_g0 = ds_group(a, sb, 0);  // the group of row group R is ds_g0 + R
+  const int64_t ds_gstride = (int64_t)a.ds_heads * a.ds_w * 4;
   auto ds_flush = [&]() {
     if (DS && ds_i0 >= 0) {
-      const int R = ds_i0 >> 7, ks = (j0 + kw0) >> 5;
-      const int slot = ks - ds_band_lo(R, s1, s2, off, wl, wr);
-      const int64_t g = ds_group(a, sb, R);
-      if ((a.varlen || R < a.ds_nr) && g < a.ds_groups && (unsigned)slot < (unsigned)a.ds_w &&
-          ds_tile_visible(ds_i0 >> 5, ks, s1, s2, off, wl, wr)) {
-        const int64_t tile0 = ((g * a.ds_heads + (ds_n1 - a.n2_begin * a.G)) * a.ds_w + slot) * 4 + ((ds_i0 >> 5) & 3);
+      const int qb = ds_i0 >> 5, R = ds_i0 >> 7;
+      const int slot = ds_ks - ds_band_lo(R, s1, s2, off, wl, wr);
+      const int64_t g = ds_g0 + R;
+      if ((a.varlen || R < a.ds_nr) && g < a.ds_groups && (unsigned)slot < (unsigned)a.ds_w && qb >= ds_vis.lo &&
+          qb < ds_vis.hi) {
+        const int64_t tile0 = g * ds_gstride + (int64_t)(((ds_n1 - a.n2_begin * a.G) * a.ds_w + slot) * 4 + (qb & 3));
         bf16* dsg = static_cast<bf16*>(a.ds) + tile0 * 1024 + lane * 8;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {

@@ -140,41 +140,43 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   qcp.init(kw, lane, (int)a.q_ss * 2);
   ycp.init(kw, lane, (int)a.o_ss * 2);
   float pl = 0.f, pf = 0.f;
-  // The fetch side walks its items with running element offsets of the Q and
-  // dY tiles and of the head's lse / sfmg rows, advanced by additions only.
-  struct FetchCursor { int h, blk; int64_t qo, yo, lh; };
+  // The fetch side walks its items with running pointers to the Q and dY
+  // tiles and to the head's lse / sfmg rows, advanced by additions only.
+  struct FetchCursor { int h, blk; const bf16* qp; const bf16* yp; const float* lp; const float* sp; };
   const int64_t q_adv = (int64_t)QG * BR * a.q_ss, y_adv = (int64_t)QG * BR * a.o_ss;
   const int64_t q_wrap = a.q_sn - (int64_t)nblk * BR * a.q_ss, y_wrap = a.o_sn - (int64_t)nblk * BR * a.o_ss;
   auto fc_init = [&](FetchCursor& f) {
     const int n1 = n2 * a.G + g0 + f.h;
     const int i0 = (bs_lo + f.blk) * BR;
-    f.qo = sb.qbase + (int64_t)n1 * a.q_sn + (int64_t)i0 * a.q_ss;
-    f.yo = sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i0 * a.o_ss;
-    f.lh = sb.lbase + (int64_t)n1 * a.l_sn;
+    f.qp = static_cast<const bf16*>(a.q) + sb.qbase + (int64_t)n1 * a.q_sn + (int64_t)i0 * a.q_ss;
+    f.yp = static_cast<const bf16*>(a.dout) + sb.obase + (int64_t)n1 * a.o_sn + (int64_t)i0 * a.o_ss;
+    f.lp = a.lse + sb.lbase + (int64_t)n1 * a.l_sn;
+    f.sp = a.sfmg + sb.lbase + (int64_t)n1 * a.l_sn;
   };
   auto fc_step = [&](FetchCursor& f) {  // to the group's next item
     if (nblk == 0) return;  // no items at all (the loop below would not end)
     f.blk += QG;
-    f.qo += q_adv;
-    f.yo += y_adv;
+    f.qp += q_adv;
+    f.yp += y_adv;
     while (f.blk >= nblk) {
       f.blk -= nblk;
       ++f.h;
-      f.qo += q_wrap;
-      f.yo += y_wrap;
-      f.lh += a.l_sn;
+      f.qp += q_wrap;
+      f.yp += y_wrap;
+      f.lp += a.l_sn;
+      f.sp += a.l_sn;
     }
   };
   auto fetch = [&](const FetchCursor& f, int t, int buf) {
     if (t < T) {
       const int i0 = (bs_lo + f.blk) * BR;
       if (kw == 0) {
-        const int64_t lrow = f.lh + min(i0 + l32, s1 - 1);
-        pl = a.lse[lrow];
-        pf = a.sfmg[lrow];
+        const int lrow = min(i0 + l32, s1 - 1);
+        pl = f.lp[lrow];
+        pf = f.sp[lrow];
       }
-      qcp.issue(q_lds + buf * QTB, static_cast<const bf16*>(a.q) + f.qo, s1 - i0, kw, lane);
-      ycp.issue(y_lds + buf * YTB, static_cast<const bf16*>(a.dout) + f.yo, s1 - i0, kw, lane);
+      qcp.issue(q_lds + buf * QTB, f.qp, s1 - i0, kw, lane);
+      ycp.issue(y_lds + buf * YTB, f.yp, s1 - i0, kw, lane);
     }
   };
   // lse in base 2 for the rows of the block at i0; a row past the end or an
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   // the other buffer, compute item t.
   const int iters = (T + QG - 1) / QG;
   Cursor cc{0, qg};                  // item t being computed
-  FetchCursor cf{0, qg, 0, 0, 0};    // item being fetched
+  FetchCursor cf{0, qg, nullptr, nullptr, nullptr, nullptr};  // item being fetched
   step_cursor(cc, 0);
   {
     Cursor c0{0, qg};

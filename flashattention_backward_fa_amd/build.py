@@ -1,7 +1,8 @@
 """Build libfa_bwd.so in-tree for gfx950.
 
 The host planner (csrc/fa_bwd_api.cpp) is plain C++ built with g++; the
-kernels (csrc/fa_bwd_dkdv_kernels.hip: the dK/dV kernel;
+kernels (csrc/fa_bwd_dkdv.h with csrc/fa_bwd_dkdv_kernels.hip and
+csrc/fa_bwd_dkdv192_kernels.hip: the dK/dV kernel;
 csrc/fa_bwd_det_kernels.hip: both dQ kernels and the partial-sum reduce;
 csrc/fa_bwd_kernels.hip: preprocess and the atomic variants;
 csrc/fa_bwd_fused_kernels.hip: the one-launch kernel for short key sequences;
@@ -45,6 +46,9 @@ DET_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 # minimises register pressure (GQA -2.3 %, MHA -1.7 %, varlen -1.4 % against
 # iterative ILP; the dQ GEMM is 1 % slower under it, so it keeps ILP).
 DKDV_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]
+# Its D = 192 instantiations (one wavefront per SIMD) under the iterative
+# occupancy strategy: wide_qk -2.1 % against ILP, where minreg changes nothing.
+DKDV192_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-maxocc"]
 
 
 def _hipcc():
@@ -75,6 +79,7 @@ def build(verbose=False):
     fwd_o = os.path.join(BUILDDIR, "fa_fwd_kernels.o")
     det_o = os.path.join(BUILDDIR, "fa_bwd_det_kernels.o")
     dkdv_o = os.path.join(BUILDDIR, "fa_bwd_dkdv_kernels.o")
+    dkdv192_o = os.path.join(BUILDDIR, "fa_bwd_dkdv192_kernels.o")
     f32_o = os.path.join(BUILDDIR, "fa_bwd_f32_kernels.o")
     fus_o = os.path.join(BUILDDIR, "fa_bwd_fused_kernels.o")
     scr_o = os.path.join(BUILDDIR, "fa_bwd_scratch.o")
@@ -90,6 +95,8 @@ def build(verbose=False):
           os.path.join(CSRC, "fa_bwd_det_kernels.hip"), "-o", det_o], verbose)
     _run([hipcc, *HIP_FLAGS, *DKDV_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
           os.path.join(CSRC, "fa_bwd_dkdv_kernels.hip"), "-o", dkdv_o], verbose)
+    _run([hipcc, *HIP_FLAGS, *DKDV192_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+          os.path.join(CSRC, "fa_bwd_dkdv192_kernels.hip"), "-o", dkdv192_o], verbose)
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_bwd_f32_kernels.hip"),
           "-o", f32_o], verbose)
     _run([hipcc, *HIP_FLAGS, *DET_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
@@ -101,7 +108,7 @@ def build(verbose=False):
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "fa_floyd_kernels.hip"),
           "-o", fker_o], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o, det_o, dkdv_o, f32_o, fus_o,
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o, fwd_o, det_o, dkdv_o, dkdv192_o, f32_o, fus_o,
           scr_o, fapi_o, fker_o], verbose)
     os.replace(tmp, LIB)
     return LIB

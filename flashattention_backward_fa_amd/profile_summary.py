@@ -46,7 +46,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "flashattention_backward_fa_amd", "csrc")
 # the sources the timed dK/dV and dQ kernels are compiled from
-KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_dkdv_kernels.hip", "fa_bwd_det_kernels.hip",
+KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_dkdv.h", "fa_bwd_dkdv_kernels.hip",
+                                                    "fa_bwd_dkdv192_kernels.hip", "fa_bwd_det_kernels.hip",
                                                     "fa_bwd_tiles.h", "fa_bwd_schedule.h", "fa_bwd_internal.h"))
 # the sources the Floyd attention kernels are compiled from
 FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h"))

@@ -34,6 +34,7 @@ struct fa_bwd_plan_s {
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxSeqLen = int64_t(1) << 29;  // bound on S1, S2 (exclusive)
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // CU count of the current HIP device (256, an MI355X, when none is visible)
@@ -102,6 +103,8 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     if (d.host_cu_seqlens_q || d.host_cu_seqlens_kv) return FA_ERR_SHAPE;
     if (S1 <= 0 || S2 <= 0) return FA_ERR_SHAPE;
   }
+  // row and key indices, their differences and window sums are 32-bit
+  if (S1 >= kMaxSeqLen || S2 >= kMaxSeqLen) return FA_ERR_SHAPE;
 
   if (!fabwd::main_instantiated(d.D, d.Dv) || !fabwd::det_instantiated(d.D, d.Dv)) return FA_ERR_UNSUPPORTED;
   if (d.dq_mode == FA_DQ_ATOMIC && d.dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;  // bf16 kernels only
@@ -151,6 +154,12 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
   if (d.mask_mode == FA_MASK_NONE) { a.win_left = -1; a.win_right = -1; }
   else if (d.mask_mode == FA_MASK_CAUSAL) { a.win_left = d.win_left; a.win_right = 0; }
   else { a.win_left = d.win_left; a.win_right = d.win_right; }
+  // A left bound of at least S2 - 1 (a right bound of at least S1 - 1) masks
+  // nothing that the sequence ends do not: clamp wider bounds to S2 (S1), so
+  // that the kernels' index sums i + (s2 - s1) +- bound stay within 32 bits
+  // (with S1, S2 < 2^29 they stay below 3 * 2^29).
+  if (a.win_left > a.S2) a.win_left = a.S2;
+  if (a.win_right > a.S1) a.win_right = a.S1;
   a.has_mask = (a.win_left >= 0 || a.win_right >= 0) ? 1 : 0;
 
   // Kernel choice (the dQ modes of include/fa_bwd.h):

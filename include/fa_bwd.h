@@ -147,7 +147,7 @@ typedef struct fa_bwd_desc {
   int32_t N1, N2;        /* query heads, key/value heads; N1 % N2 == 0           */
   int32_t S1, S2;        /* BSND/BNSD: sequence lengths (> 0).  TND: max_seqlen_q /
                             max_seqlen_kv, or -1 to derive them from the host
-                            cu_seqlens copies below                              */
+                            cu_seqlens copies below.  Both below 2^29            */
   int32_t D, Dv;         /* head dims, 0 < Dv <= D <= 192                         */
   int64_t T1, T2;        /* TND: total query / key rows (> 0); ignored otherwise  */
   const int32_t* host_cu_seqlens_q;  /* TND, optional: host copy of cu_seqlens_q
@@ -156,7 +156,9 @@ typedef struct fa_bwd_desc {
   const int32_t* host_cu_seqlens_kv; /* TND, optional: same for cu_seqlens_kv    */
   float softmax_scale;   /* 0 selects 1/sqrt(D) (section 一, scale rule)         */
   int32_t mask_mode;     /* FA_MASK_*                                             */
-  int32_t win_left, win_right; /* window bounds, -1 = unbounded                  */
+  int32_t win_left, win_right; /* window bounds, -1 = unbounded; a bound wider
+                                  than the sequences (left > S2, right > S1)
+                                  acts as that width                          */
   uint32_t flags;        /* FA_FLAG_*                                             */
   /* ABI version 3 */
   int32_t dq_mode;       /* FA_DQ_* (FA_DQ_AUTO = 0: the planner's choice)        */

@@ -254,6 +254,8 @@ def test_tnd_workspace_band(lib):
     (dict(D=128, Dv=192), fb.FA_ERR_SHAPE),          # Dv <= D
     (dict(D=256, Dv=128), fb.FA_ERR_SHAPE),          # D <= 192
     (dict(S1=0), fb.FA_ERR_SHAPE),
+    (dict(S1=2**29), fb.FA_ERR_SHAPE),               # index sums must fit 32 bits
+    (dict(S2=2**29, N1=1, N2=1, D=64, Dv=64), fb.FA_ERR_SHAPE),
     (dict(mask_mode=0, win_left=5), fb.FA_ERR_SHAPE),  # dense needs no window
     (dict(mask_mode=1, win_right=3), fb.FA_ERR_SHAPE),
     (dict(mask_mode=2, win_left=-2), fb.FA_ERR_SHAPE),
@@ -277,6 +279,19 @@ def test_create_rejects(lib, kw, code):
 ])
 def test_create_accepts(lib, kw):
     assert create(lib, **kw)[0] == fb.FA_OK
+
+
+def test_wide_windows_are_clamped_to_the_sequences(lib, monkeypatch, capfd):
+    """A left bound past S2 (a right bound past S1) masks nothing that the
+    sequence ends do not; the plan clamps it to that width, so a bound of
+    2^31 - 1 cannot wrap the kernels' 32-bit sums i + (s2 - s1) + bound."""
+    monkeypatch.setenv("FA_BWD_LOG", "1")
+    big = 2**31 - 1
+    assert create(lib, mask_mode=2, win_left=big, win_right=big, S1=200, S2=300)[0] == fb.FA_OK
+    assert create(lib, mask_mode=1, win_left=big, S1=200, S2=300)[0] == fb.FA_OK
+    assert create(lib, mask_mode=2, win_left=299, win_right=199, S1=200, S2=300)[0] == fb.FA_OK
+    windows = re.findall(r"window=\((-?\d+),(-?\d+)\)", capfd.readouterr().err)
+    assert windows == [("300", "200"), ("300", "0"), ("299", "199")]
 
 
 def test_abi_version_mismatch(lib):

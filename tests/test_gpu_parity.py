@@ -70,6 +70,30 @@ def test_zero_upstream_gradient_gives_exact_zeros():
         assert not np.any(g)
 
 
+def test_windows_wider_than_the_sequences_mask_nothing_more():
+    """Bounds of 2^31 - 1 act as the sequence widths (the plan clamps them,
+    so no 32-bit index sum wraps): bitwise equal to an unbounded left side
+    under causal, and the oracle's results under a two-sided window."""
+    big = 2**31 - 1
+    cfg = W.custom("BSND", B=1, N1=4, N2=2, S1=260, S2=300, D=128, Dv=128, mask_mode=1)
+    x = case_inputs(cfg, 5)
+    Yst, lst = oracle_inputs(cfg, x)
+    say("[parity] causal, left bound 2^31 - 1")
+    a = gpu_backward(cfg, x, Yst, lst)
+    b = gpu_backward(dict(cfg, win_left=big), x, Yst, lst)
+    assert all(np.array_equal(u, w) for u, w in zip(a, b))
+    for cfg in (W.custom("BSND", B=1, N1=4, N2=2, S1=260, S2=300, D=128, Dv=128, mask_mode=2, win_left=big,
+                         win_right=big),
+                W.custom("TND", N1=2, N2=2, D=64, Dv=64, mask_mode=2, win_left=big, win_right=big,
+                         lengths=[77, 128, 3], lengths_kv=[90, 40, 3])):
+        x = case_inputs(cfg, 6)
+        Yst, lst = oracle_inputs(cfg, x)
+        rq, rk, rv = oracle_backward(cfg, x, Yst, lst)
+        say(f"[parity] window 2^31 - 1 both sides: {cfg['layout']}")
+        gq, gk, gv = gpu_backward(cfg, x, Yst, lst)
+        assert_all_close([(gq, rq, "dq"), (gk, rk, "dk"), (gv, rv, "dv")])
+
+
 def _metamorphic_inputs():
     cfg = W.custom("BSND", B=1, N1=4, N2=2, S1=200, S2=200, D=128, Dv=128, mask_mode=1)
     x = case_inputs(cfg, 4)

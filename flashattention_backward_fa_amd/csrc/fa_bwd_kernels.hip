@@ -35,7 +35,9 @@
 #include <hip/hip_runtime.h>
 
 #include <new>
+#include <type_traits>
 
+#include "fa_bwd.h"
 #include "fa_bwd_internal.h"
 #include "fa_bwd_schedule.h"
 
@@ -74,17 +76,36 @@ __device__ __forceinline__ bf16x8 join(shortx4 lo, shortx4 hi) {
 // ---------------------------------------------------------------- preprocess
 
 // One row = Dv contiguous bf16 of dout / attn_out.  DV/8 lanes per row, each
-// with one 16-byte load of each tensor.
-template <int DV, bool F16>
-__global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t rows, int zero_dq,
+// with one 16-byte load of each tensor.  BNSD and TND: a block takes RPB
+// consecutive rows.  BSND: a block takes RPB consecutive rows of one (batch,
+// head) pair, the pair the faster block index, so that its sfmg values
+// ([b][n][s]) are one contiguous store instead of RPB scattered 4-byte ones
+// while the blocks in flight together still read whole rows of heads
+// (measured: GQA 13.8 -> 12.3 us, MHA 8.7 -> 7.1 us; the same for TND, or
+// the pair as the slower index, made varlen and BNSD slower).  One
+// instantiation per layout; TND and BNSD form the sfmg index after the loads.
+template <int DV, bool F16, int LAYOUT>
+__global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t rows, uint32_t pairs, int zero_dq,
                                                           int64_t dq_elems, int64_t dk_elems, int64_t dv_elems) {
   constexpr int LPR = DV / 8;             // lanes per row
   constexpr int RPB = 256 / LPR;          // rows per block
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  int64_t row, o = 0;  // the row's index in dout / attn_out (rows of Dv elements) and in sfmg
+  bool ok;
+  if constexpr (LAYOUT == FA_LAYOUT_BSND) {  // block -> (chunk, pair = b * N1 + n); row (b * S1 + s) * N1 + n
+    const uint32_t chunk = blockIdx.x / pairs, pair = blockIdx.x - chunk * pairs;
+    const uint32_t b = pair / (uint32_t)a.N1, n = pair - b * (uint32_t)a.N1;
+    const int64_t si = (int64_t)chunk * RPB + tid / LPR;
+    row = ((int64_t)b * a.S1 + si) * a.N1 + n;
+    o = (int64_t)pair * a.S1 + si;  // [b][n][s]: l_sb = N1 * S1, l_sn = S1
+    ok = si < a.S1;
+  } else {
+    row = (int64_t)blockIdx.x * RPB + tid / LPR;
+    ok = row < rows;
+  }
   const int part = tid % LPR;
   float s = 0.f;
-  if (row < rows) {
+  if (ok) {
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.out) + row * DV + part * 8);
     const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.dout) + row * DV + part * 8);
     if constexpr (F16) {  // fp16 in the same storage: reinterpret whole vectors (element-wise casts of
@@ -100,15 +121,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(KernelArgs a, int64_t r
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
-  if (row < rows && part == 0) {
-    int64_t o;
-    if (a.layout == 0) {  // BSND: row = (b*S1 + s)*N1 + n  ->  [b][n][s]
-      const int64_t n = row % a.N1, bs = row / a.N1;
-      const int64_t b = bs / a.S1, si = bs % a.S1;
-      o = b * a.l_sb + n * a.l_sn + si;
-    } else if (a.layout == 1) {  // BNSD: row = (b*N1 + n)*S1 + s  ->  same order
+  if (ok && part == 0) {  // (the other layouts' sfmg index is formed after the loads)
+    if constexpr (LAYOUT == FA_LAYOUT_BNSD) {  // row = (b*N1 + n)*S1 + s  ->  same order
       o = row;
-    } else {  // TND: row = t*N1 + n  ->  [n][t]
+    } else if constexpr (LAYOUT == FA_LAYOUT_TND) {  // row = t*N1 + n  ->  [n][t]
       const int64_t n = row % a.N1, t = row / a.N1;
       o = n * a.l_sn + t;
     }
@@ -734,29 +750,37 @@ int64_t k_elems(const KernelArgs& a) {
 int64_t v_elems(const KernelArgs& a) {
   return a.varlen ? a.T2 * a.N2 * a.Dv : (int64_t)a.B * a.S2 * a.N2 * a.Dv;
 }
-int64_t out_rows(const KernelArgs& a) {
-  return a.varlen ? a.T1 * a.N1 : (int64_t)a.B * a.S1 * a.N1;
-}
 }  // namespace
 
 int launch_preprocess(const KernelArgs& a, bool zero_dq_acc, void* stream) {
-  const int64_t rows = out_rows(a);
   const int lpr = a.Dv / 8;
   const int64_t rpb = 256 / lpr;
-  const int64_t blocks = (rows + rpb - 1) / rpb;
+  const int64_t rows = a.varlen ? a.T1 * a.N1 : (int64_t)a.B * a.S1 * a.N1;
+  // BSND: blocks of rpb rows of one (batch, head) pair; otherwise of rpb rows
+  const int64_t pairs = (int64_t)a.B * a.N1;
+  const int64_t blocks = a.layout == 0 ? pairs * ((a.S1 + rpb - 1) / rpb) : (rows + rpb - 1) / rpb;
   if (blocks <= 0) return 0;
+  if (blocks > UINT32_MAX) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t dqe = zero_dq_acc ? q_elems(a) : 0;
   const int64_t dke = zero_dq_acc && split_heads(a) ? k_elems(a) : 0;
   const int64_t dve = zero_dq_acc && split_heads(a) ? v_elems(a) : 0;
   const dim3 grid((unsigned)blocks), block(256);
   const int z = zero_dq_acc ? 1 : 0;
-  if (a.Dv == 128)
-    return launch(a.f16 ? preprocess_kernel<128, true> : preprocess_kernel<128, false>, grid, block, s, a, rows, z, dqe,
-                  dke, dve);
-  if (a.Dv == 64)
-    return launch(a.f16 ? preprocess_kernel<64, true> : preprocess_kernel<64, false>, grid, block, s, a, rows, z, dqe,
-                  dke, dve);
+  auto go = [&](auto kernel) { return launch(kernel, grid, block, s, a, rows, (uint32_t)pairs, z, dqe, dke, dve); };
+  auto by_layout = [&](auto dv, auto f16) {
+    constexpr int DV = decltype(dv)::value;
+    constexpr bool F16 = decltype(f16)::value;
+    if (a.layout == FA_LAYOUT_BSND) return go(preprocess_kernel<DV, F16, FA_LAYOUT_BSND>);
+    if (a.layout == FA_LAYOUT_BNSD) return go(preprocess_kernel<DV, F16, FA_LAYOUT_BNSD>);
+    return go(preprocess_kernel<DV, F16, FA_LAYOUT_TND>);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  if (a.Dv == 128) return a.f16 ? by_layout(D128{}, T{}) : by_layout(D128{}, F{});
+  if (a.Dv == 64) return a.f16 ? by_layout(D64{}, T{}) : by_layout(D64{}, F{});
   return (int)hipErrorInvalidValue;
 }
 

@@ -295,6 +295,7 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     const int64_t wgs = (S1 + 127) / 128 * a.G * p.n2_chunk * d.B;
     if (!tail && wgs <= 2 * (int64_t)cus) a.dq_groups = 2;
   }
+  a.round_wgs = pair ? cus : 0;  // the dK/dV kernel holds one workgroup per CU
 
   // workspace: sfmg, [dQ accumulator], [dK / dV partial sums], [dS]
   p.off_sfmg = 0;

@@ -90,6 +90,9 @@ struct KernelArgs {
   // dQ GEMM workgroups: 1 = 4 wavefronts; 2 = two groups of 4 that share a row
   // group and take alternate key steps (D <= 128, no reduce tail)
   int32_t dq_groups;
+  // dK/dV kernel: workgroups that the device holds at once (one per CU), the
+  // unit of the engine-order reversal of its job order; 0 = no reversal
+  int32_t round_wgs;
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups

@@ -303,8 +303,13 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void dq_ds_kernel(KernelArgs a) {
       return;
     }
   }
-  const int tile = ntiles - 1 - (int)(blockIdx.x / per_tile);
-  const int rem = blockIdx.x % per_tile;
+  // engines in reverse in even rounds, as in the dK/dV grid (rounds of one
+  // workgroup per CU at QG = 2, two at QG = 1)
+  int bid = blockIdx.x;
+  const int rw = a.round_wgs * (2 / QG);
+  if (rw > 0 && ((bid / rw) & 1) == 0 && (bid | 31) < ntiles * per_tile) bid ^= 24;
+  const int tile = ntiles - 1 - bid / per_tile;
+  const int rem = bid % per_tile;
   const int hl = rem % nh;          // head within the chunk (its index in the workspace)
   const int n1 = a.n2_begin * a.G + hl;
   const int b = rem / nh;

@@ -30,6 +30,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fa_bwd_tiles.h"
 #include "fa_floyd_internal.h"
 
 namespace ffloyd {
@@ -475,6 +476,125 @@ __global__ __launch_bounds__(NT) void score_grad_kernel(ScoreArgs s) {
       }
 }
 
+// The same stage with its product operands copied straight to LDS, each
+// tile whole (the contraction is D <= 128 deep), as in the attention
+// kernels' swizzled tiles: Q, K2 and dY are in flight together, V2 is
+// fetched while the first epilogue runs.  The plain form above fetches each
+// operand one 32-deep step ahead through registers, a memory round trip per
+// step.  D = 64 or 128; the tile's row offsets must fit 32 bits.
+template <bool F16, int HD>
+__global__ __launch_bounds__(NT) void score_grad_dma_kernel(ScoreArgs s) {
+  using C = Cfg<128, GBM>;
+  static_assert(C::TM == 1 && C::TN == 2 && C::WAVES_N == 2, "2 x 2 wavefronts of 32 x 64");
+  constexpr int ATB = GBM * HD * 2;  // bytes of an n-row tile (Q or dY)
+  __shared__ __attribute__((aligned(1024))) bf16 As[2][GBM * HD];  // Q, dY
+  __shared__ __attribute__((aligned(1024))) bf16 Bs[128 * HD];     // K2, then V2
+  const int I = s.N, J = s.K;
+  const int tiles_j = (J + 127) / 128;
+  const int L = logical_block();
+  const int z = L % s.M, tile = L / s.M;
+  const int i0 = (tile / tiles_j) * GBM, j0 = (tile % tiles_j) * 128;
+  const int h = blockIdx.y;
+  const int64_t MD = (int64_t)s.M * s.D, NMD = (int64_t)s.N * MD;
+  const int64_t q_off = h * NMD + (int64_t)z * s.D + (int64_t)i0 * MD;               // row n = i0 of batch m = z
+  const int64_t x_off = h * (int64_t)s.K * MD + (int64_t)z * s.D + (int64_t)j0 * MD;  // row k = j0 of batch m = z
+  const int64_t MK = (int64_t)s.M * s.K, NMK = (int64_t)s.N * MK;
+  const int64_t wbase = h * NMK + (int64_t)z * s.K;  // element (n, m = z, k) at wbase + n*MK + k
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const float sl2 = s.scale * kLog2e;
+  const int bb = (s.head0 + h) / s.H;
+  const bool full = i0 + GBM <= I && j0 + 128 <= J;
+  const float* __restrict__ ws_s = s.ws_s;
+  const float* __restrict__ ws_p = s.ws_p;
+  bf16* __restrict__ pe = static_cast<bf16*>(s.ws_pe);
+  bf16* __restrict__ dse = static_cast<bf16*>(s.ws_dse);
+  auto row_of = [&](int r) { return i0 + wm * 32 + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3); };
+  auto col_of = [&](int tn) { return j0 + (wn * C::TN + tn) * 32 + (lane & 31); };
+  auto inside = [&](int tn, int r) { return full || (row_of(r) < I && col_of(tn) < J); };
+
+  // the first epilogue's by-n partial scores, log-sum-exp and mask, loaded
+  // before the operand copies (they complete first)
+  float sv[C::TN][16], l2[16];
+  bool live[C::TN][16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = row_of(r);
+    l2[r] = (full || i < I) ? s.lse2[((int64_t)h * s.N + i) * s.M + z] : 0.f;
+  }
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = row_of(r), j = col_of(tn);
+      const bool in = inside(tn, r);
+      sv[tn][r] = in ? ws_s[wbase + i * MK + j] : 0.f;
+      live[tn][r] = in && (s.mask == nullptr || s.mask[((int64_t)bb * s.N + i) * s.K + j] == 0);
+    }
+
+  // operand tiles, rows past the end repeating the last one (masked above)
+  fabwd::TileCopy<HD, GBM, 4> acp;
+  fabwd::TileCopy<HD, 128, 4> bcp;
+  acp.init(wave, lane, (int)(MD * 2));
+  bcp.init(wave, lane, (int)(MD * 2));
+  const uint32_t a_lds = fabwd::lds_addr(As), b_lds = fabwd::lds_addr(Bs);
+  acp.issue(a_lds, static_cast<const bf16*>(s.q) + q_off, I - i0, wave, lane);
+  bcp.issue(b_lds, static_cast<const bf16*>(s.x1) + x_off, J - j0, wave, lane);
+  acp.issue(a_lds + ATB, static_cast<const bf16*>(s.dy) + q_off, I - i0, wave, lane);
+  fabwd::SwzTile<HD, GBM> aadr;
+  fabwd::SwzTile<HD, 128> badr;
+  aadr.init(a_lds, lane);
+  badr.init(b_lds, lane);
+  // acc += A (rows 32*wm..) B^T (rows 64*wn + 32*tn..), both 16-byte row reads
+  auto product = [&](floatx16 (&acc)[C::TN], uint32_t a_off) {
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) {
+      const bf16x8 a = fabwd::lds_load16(aadr.row_read_at(kk, 32 * wm, a_off));
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn)
+        acc[tn] = fabwd::mfma32<F16>(a, fabwd::lds_load16(badr.row_read_at(kk, 64 * wn + 32 * tn)), acc[tn]);
+    }
+  };
+  fabwd::wait_vmem();
+  fabwd::lds_barrier();
+  floatx16 acc[C::TN] = {floatx16{}, floatx16{}};
+  product(acc, 0);
+  fabwd::lds_barrier();  // every wavefront's reads of K2 are done
+  bcp.issue(b_lds, static_cast<const bf16*>(s.x2) + x_off, J - j0, wave, lane);
+  // the second epilogue's by-n partial dP and the rows' sfmg
+  float pv[C::TN][16], sf[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = row_of(r);
+    sf[r] = (full || i < I) ? s.sfmg[((int64_t)h * s.N + i) * s.M + z] : 0.f;
+  }
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[tn][r] = inside(tn, r) ? ws_p[wbase + row_of(r) * MK + col_of(tn)] : 0.f;
+  // P = exp(scale*S - lse), stored 16-bit, kept in fp32 for dS
+  float pf[C::TN][16];
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = live[tn][r] ? __builtin_amdgcn_exp2f((acc[tn][r] + sv[tn][r]) * sl2 - l2[r]) : 0.f;
+      pf[tn][r] = p;
+      if (inside(tn, r)) pe[wbase + row_of(r) * MK + col_of(tn)] = to_elem<F16>(p);
+    }
+    acc[tn] = floatx16{};
+  }
+  fabwd::wait_vmem();
+  fabwd::lds_barrier();
+  product(acc, ATB);
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (inside(tn, r))
+        dse[wbase + row_of(r) * MK + col_of(tn)] = to_elem<F16>(pf[tn][r] * (acc[tn][r] + pv[tn][r] - sf[r]));
+}
+
 // 16 lanes per row: sfmg = sum_d dY*Y in fp32, lse2 from the statistics.
 // V = D / 16 contiguous elements of a row per lane, one vector load each.
 template <bool F16, int V>
@@ -578,7 +698,16 @@ int launch_scores_t(const ScoreArgs& s, hipStream_t st) {
   const dim3 grid((unsigned)nx, s.heads);
   switch (s.epi) {
     case 0: hipLaunchKernelGGL((score_kernel<F16, 0>), grid, dim3(NT), 0, st, s); break;
-    case 1: hipLaunchKernelGGL((score_grad_kernel<F16>), grid, dim3(NT), 0, st, s); break;
+    case 1:
+      // operand tiles straight to LDS when D allows it and a tile's row
+      // offsets (128 rows of M*D elements) fit 32 bits
+      if ((s.D == 64 || s.D == 128) && 128 * (int64_t)s.M * s.D * 2 < (int64_t(1) << 31)) {
+        if (s.D == 128) hipLaunchKernelGGL((score_grad_dma_kernel<F16, 128>), grid, dim3(NT), 0, st, s);
+        else hipLaunchKernelGGL((score_grad_dma_kernel<F16, 64>), grid, dim3(NT), 0, st, s);
+      } else {
+        hipLaunchKernelGGL((score_grad_kernel<F16>), grid, dim3(NT), 0, st, s);
+      }
+      break;
     case 2: hipLaunchKernelGGL((score_kernel<F16, 2>), grid, dim3(NT), 0, st, s); break;
     default: hipLaunchKernelGGL((score_kernel<F16, 3>), grid, dim3(NT), 0, st, s); break;
   }

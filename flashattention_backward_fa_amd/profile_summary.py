@@ -50,7 +50,8 @@ KERNEL_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_dkdv.h", "fa_bwd_dkd
                                                     "fa_bwd_dkdv192_kernels.hip", "fa_bwd_det_kernels.hip",
                                                     "fa_bwd_tiles.h", "fa_bwd_schedule.h", "fa_bwd_internal.h"))
 # the sources the Floyd attention kernels are compiled from
-FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h"))
+FLOYD_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_floyd_kernels.hip", "fa_floyd_internal.h", "fa_bwd_tiles.h",
+                                                   "fa_bwd_schedule.h", "fa_bwd_internal.h"))
 # the sources of the fused small-sequence kernel
 FUSED_SRCS = tuple(os.path.join(CSRC, f) for f in ("fa_bwd_fused_kernels.hip", "fa_bwd_tiles.h",
                                                    "fa_bwd_schedule.h", "fa_bwd_internal.h", "fa_bwd_kernarg.h"))

@@ -490,9 +490,12 @@ __global__ __launch_bounds__(NT) void score_grad_dma_kernel(ScoreArgs s) {
   __shared__ __attribute__((aligned(1024))) bf16 As[2][GBM * HD];  // Q, dY
   __shared__ __attribute__((aligned(1024))) bf16 Bs[128 * HD];     // K2, then V2
   const int I = s.N, J = s.K;
-  const int tiles_j = (J + 127) / 128;
+  const int tiles_j = (J + 127) / 128, tiles = ((I + GBM - 1) / GBM) * tiles_j;
+  // consecutive workgroups of an XCD take the (n, k) tiles of one m: each Q /
+  // dY tile is read by the tiles_j of them and each K2 / V2 tile by the n
+  // tiles while it is still in the XCD's L2
   const int L = logical_block();
-  const int z = L % s.M, tile = L / s.M;
+  const int z = L / tiles, tile = L % tiles;
   const int i0 = (tile / tiles_j) * GBM, j0 = (tile % tiles_j) * 128;
   const int h = blockIdx.y;
   const int64_t MD = (int64_t)s.M * s.D, NMD = (int64_t)s.N * MD;

@@ -271,6 +271,98 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
     }
 }
 
+// The same product for operands whose row index x is contiguous in memory
+// (A[x][t] at x + t*a_st, B likewise: dV1, dK1, dV2, dK2), on whole 128 x 128
+// tiles with a contraction that is a multiple of 64: each 64-deep step of
+// both operands goes straight to LDS as a swizzled [t][x] tile (the
+// attention kernels' copy), double-buffered, the next step's copy issued as
+// soon as every wavefront has finished the previous one; both MFMA operands
+// are transposing reads with one key order inside each 16-deep chunk.
+constexpr int GKB = 64;  // contraction per step of gemm_dma_kernel
+
+template <bool F16>
+__global__ __launch_bounds__(NT, 2) void gemm_dma_kernel(GemmArgs g) {
+  using C = Cfg<128, 128>;
+  static_assert(C::TM == 2 && C::TN == 2 && C::WAVES_N == 2, "2 x 2 wavefronts of 64 x 64");
+  constexpr int TB = GKB * 128 * 2;  // bytes of one operand tile
+  __shared__ __attribute__((aligned(1024))) bf16 As[2][GKB * 128];
+  __shared__ __attribute__((aligned(1024))) bf16 Bs[2][GKB * 128];
+  const int tiles_j = g.J / 128, tiles_i = g.I / 128;
+  const int L = logical_block();
+  const int z = L / (tiles_i * tiles_j), tile = L % (tiles_i * tiles_j);
+  const int i0 = (tile / tiles_j) * 128, j0 = (tile % tiles_j) * 128;
+  const int h = blockIdx.y;
+  const bf16* __restrict__ Ag = static_cast<const bf16*>(g.a) + h * g.a_sh + z * g.a_sz + i0;
+  const bf16* __restrict__ Bg = static_cast<const bf16*>(g.b) + h * g.b_sh + z * g.b_sz + j0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  fabwd::TileCopy<128, GKB, 4> acp, bcp;
+  acp.init(wave, lane, (int)(g.a_st * 2));
+  bcp.init(wave, lane, (int)(g.b_st * 2));
+  const uint32_t a_lds = fabwd::lds_addr(As), b_lds = fabwd::lds_addr(Bs);
+  fabwd::SwzTile<128, GKB> aadr, badr;
+  aadr.init(a_lds, lane);
+  badr.init(b_lds, lane);
+  auto fetch = [&](int st, int buf) {
+    acp.issue(a_lds + buf * TB, Ag + (int64_t)st * GKB * g.a_st, GKB, wave, lane);
+    bcp.issue(b_lds + buf * TB, Bg + (int64_t)st * GKB * g.b_st, GKB, wave, lane);
+  };
+  floatx16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = floatx16{};
+  const int nk = g.T / GKB;
+  fetch(0, 0);
+  auto step = [&](int st, int buf) {
+    fabwd::wait_vmem();     // this wavefront's copies of step st landed
+    fabwd::lds_barrier();   // ... and everyone's; buffer buf ^ 1 is no longer read
+    if (st + 1 < nk) fetch(st + 1, buf ^ 1);
+#pragma unroll
+    for (int kc = 0; kc < GKB / 16; ++kc) {
+      bf16x8 af[C::TM], bfr[C::TN];
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+        af[tm] = fabwd::join(fabwd::lds_load_tr(aadr.tr_read_c(kc, 0, 2 * wm + tm, buf * TB)),
+                             fabwd::lds_load_tr(aadr.tr_read_c(kc, 1, 2 * wm + tm, buf * TB)));
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn)
+        bfr[tn] = fabwd::join(fabwd::lds_load_tr(badr.tr_read_c(kc, 0, 2 * wn + tn, buf * TB)),
+                              fabwd::lds_load_tr(badr.tr_read_c(kc, 1, 2 * wn + tn, buf * TB)));
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = fabwd::mfma32<F16>(af[tm], bfr[tn], acc[tm][tn]);
+    }
+  };
+  int st = 0;  // two steps per iteration, so that the buffer offsets are constants
+  for (; st + 1 < nk; st += 2) {
+    step(st, 0);
+    step(st + 1, 1);
+  }
+  if (st < nk) step(st, 0);
+
+  const int64_t cb = h * g.c_sh + z * g.c_sz;
+  const float* __restrict__ add = g.addend;
+#pragma unroll
+  for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int j = j0 + (wn * C::TN + tn) * 32 + (lane & 31);
+      const int ib = i0 + (wm * C::TM + tm) * 32 + 4 * (lane >> 5);
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = add ? add[cb + (ib + 8 * (r >> 2) + (r & 3)) * g.c_si + j] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t off = cb + (ib + 8 * (r >> 2) + (r & 3)) * g.c_si + j;
+        const float x = g.alpha * acc[tm][tn][r] + v[r];
+        if (g.out_f32) static_cast<float*>(g.c)[off] = x;
+        else static_cast<bf16*>(g.c)[off] = to_elem<F16>(x);
+      }
+    }
+}
+
 // Score products (see ScoreArgs), epilogues 0, 2 and 3.  Rows i of the tile
 // are m (by n) or n (by m), columns j are keys k; the inner batch index z is
 // n (by n) or m (by m).
@@ -680,7 +772,13 @@ int launch_gemm_bn(const GemmArgs& g, hipStream_t st) {
     hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 64, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
   } else {
     const int64_t nx = (int64_t)ti * ((g.J + 127) / 128) * g.nb;
-    hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 128, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+    // both operands row-contiguous, whole tiles, 64-deep steps, and a step's
+    // 64 rows addressed by 32-bit byte offsets: copies straight to LDS
+    const bool dma = !ATC && !BTC && g.a_si == 1 && g.b_sj == 1 && g.I % 128 == 0 && g.J % 128 == 0 &&
+                     g.T % GKB == 0 && (int64_t)GKB * g.a_st * 2 < (int64_t(1) << 31) &&
+                     (int64_t)GKB * g.b_st * 2 < (int64_t(1) << 31);
+    if (dma) hipLaunchKernelGGL((gemm_dma_kernel<F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+    else hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 128, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
   }
   return (int)hipGetLastError();
 }

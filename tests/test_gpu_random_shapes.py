@@ -64,6 +64,22 @@ def draw_case(i):
     if rng.random() < 0.3:
         used = (np.array([int(rng.integers(0, L + 20)) for L in lens_q]),
                 np.array([int(rng.integers(0, L + 20)) for L in lens_k]))
+    # The same holds when no sequence has more than one key taking part (S2 = 1, or
+    # seqused_kv <= 1 everywhere): every row sees at most one key, P = 1 and dS = 0
+    # exactly in fp64, and the whole reference is zero.  Such draws get a second key
+    # (after every draw, so the other cases keep theirs).
+    keys = [min(L, int(u)) for L, u in zip(lens_k, used[1])] if used is not None else lens_k
+    if max(keys) == 1:
+        if used is not None:
+            used[1][:] = np.minimum(np.maximum(used[1], 2), [max(L, 1) for L in lens_k])
+            keys = [min(L, int(u)) for L, u in zip(lens_k, used[1])]
+        if max(keys) == 1:  # allocated lengths of one key: widen the allocation
+            if cfg["layout"] == "TND":
+                cfg["lengths_kv"] = [max(L, 2) if L == 1 else L for L in cfg["lengths_kv"]]
+            else:
+                cfg["S2"] = 2
+            if used is not None:
+                used[1][:] = np.maximum(used[1], 2)
     return cfg, fp16, used
 
 

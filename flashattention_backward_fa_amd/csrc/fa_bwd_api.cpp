@@ -296,6 +296,11 @@ int validate_and_plan(const fa_bwd_desc& d, fa_bwd_plan_s& p) {
     if (!tail && wgs <= 2 * (int64_t)cus) a.dq_groups = 2;
   }
   a.round_wgs = pair ? cus : 0;  // the dK/dV kernel holds one workgroup per CU
+  // Varlen grids run each sequence's key tiles together: sequences of unequal
+  // lengths then spread over every shader engine (in key-tile order the
+  // sequence index alone picks the engine pair), and neighbouring tiles of a
+  // sequence share their query rows in L2.
+  a.seq_major = pair && tnd ? 1 : 0;
 
   // workspace: sfmg, [dQ accumulator], [dK / dV partial sums], [dS]
   p.off_sfmg = 0;

@@ -72,7 +72,10 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // job = ((((tile * HJ + hslot) * QS + qs) * B + b) * N2 + n2), longest first.
+  // job = ((((tile * HJ + hslot) * QS + qs) * B + b) * N2 + n2), longest first
+  // under a causal mask, or for varlen grids (seq_major)
+  // ((((b * HJ + hslot) * QS + qs) * tiles + tile) * N2 + n2), so that a
+  // sequence's tiles run together.
   // The dispatcher sends workgroup i to XCD i % 8 and, within the XCD, to its
   // four shader engines in turn ((i / 8) % 4), each workgroup waiting for a CU
   // of its own engine while the XCD's later ones wait behind it.  In the even
@@ -85,11 +88,16 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int QS = a.q_splits;
   int r = blockIdx.x;
   if (a.round_wgs > 0 && ((r / a.round_wgs) & 1) == 0 && (r | 31) < (int)gridDim.x) r ^= 24;
+  // The two orders differ only in which of (b, tile) is the fast index, so one
+  // decomposition serves both (selects, no branches).
+  const int nfast = a.seq_major ? (a.S2 + BC - 1) / BC : a.B;
   const int n2 = a.n2_begin + r % a.n2_count; r /= a.n2_count;
-  const int b = r % a.B; r /= a.B;
+  const int fast = r % nfast; r /= nfast;
   const int qs = r % QS; r /= QS;
   const int hslot = r % HJ;
-  const int tile = r / HJ;
+  const int slow = r / HJ;
+  const int b = a.seq_major ? slow : fast;
+  const int tile = a.seq_major ? fast : slow;
   const int part = hslot * QS + qs;
 
   const SeqBounds sb = seq_bounds(a, b);

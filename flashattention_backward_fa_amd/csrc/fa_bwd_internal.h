@@ -93,6 +93,10 @@ struct KernelArgs {
   // dK/dV kernel: workgroups that the device holds at once (one per CU), the
   // unit of the engine-order reversal of its job order; 0 = no reversal
   int32_t round_wgs;
+  // dK/dV kernel job order: 0 = key tile slowest (longest first under a causal
+  // mask), 1 = sequence slowest and key tile fastest (varlen: a sequence's
+  // tiles are consecutive)
+  int32_t seq_major;
 };
 
 // True when dK/dV of one key/value head are summed over several workgroups

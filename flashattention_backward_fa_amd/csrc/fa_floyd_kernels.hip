@@ -21,12 +21,15 @@
 //      the second adding the first's fp32 result).
 // No row reduction over k is needed in the backward (the statistics come
 // from the forward), so P and dS are formed where the second score product
-// ends.  Every product is a v_mfma_f32_32x32x16 tile fed from LDS; each
-// operand tile is copied global -> registers -> LDS one k-step ahead
-// (double-buffered LDS, one barrier per step).  An operand whose contraction
-// index t is contiguous in memory is stored [x][t] and read 16 bytes per lane;
-// one whose row index x is contiguous is stored [t][x] and read with
-// ds_read_b64_tr_b16, which hands each lane a column of four rows.
+// ends.  Every product is a v_mfma_f32_32x32x16 tile fed from LDS.  In the
+// general kernels each operand tile is copied global -> registers -> LDS one
+// k-step ahead (double-buffered LDS, one barrier per step): an operand whose
+// contraction index t is contiguous in memory is stored [x][t] and read 16
+// bytes per lane; one whose row index x is contiguous is stored [t][x] and
+// read with ds_read_b64_tr_b16, which hands each lane a column of four rows.
+// The fixed-m score kernel (D = 64, 128) and the gradient GEMMs whose
+// operands are both row-contiguous copy their tiles straight to LDS instead
+// (global_load_lds into the attention kernels' swizzled tiles).
 
 #include <hip/hip_runtime.h>
 

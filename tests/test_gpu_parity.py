@@ -209,6 +209,27 @@ def test_sfmg_preprocess_large_workloads():
         assert np.all(np.abs(s_gpu - s_ref) <= bound)
 
 
+@pytest.mark.parametrize("Dv,N1,T", [(128, 16, 1000), (128, 32, 77), (64, 32, 1003), (64, 64, 5), (64, 16, 300),
+                                      (128, 48, 17)])
+def test_sfmg_preprocess_tnd_shapes(Dv, N1, T):
+    """The TND preprocess (rows t * N1 + n, sfmg [n][t]) for several head
+    counts and both Dv, with T not a multiple of a block's rows and a
+    sequence boundary inside a block: every row against the oracle."""
+    import torch
+    import flashattention_backward_fa_amd as fa
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(700 + Dv + N1 + T)
+    dy = torch.from_numpy(rng.standard_normal((T, N1, Dv), dtype=np.float32)).to(torch.bfloat16)
+    y = torch.from_numpy(rng.standard_normal((T, N1, Dv), dtype=np.float32)).to(torch.bfloat16)
+    cu = np.array([0, T // 3, T], dtype=np.int32)
+    say(f"[parity] TND sfmg Dv={Dv} N1={N1} T={T}")
+    s_gpu = fa.sfmg(dy.to(dev), y.to(dev), "TND", torch.from_numpy(cu).to(dev),
+                    max_seqlen_q=int(np.diff(cu).max())).cpu().double().numpy()
+    s_ref = oracle.sfmg(f64(dy), f64(y), "TND", cu)
+    bound = 1e-5 * oracle.sfmg(np.abs(f64(dy)), np.abs(f64(y)), "TND", cu) + 1e-30
+    assert s_gpu.shape == s_ref.shape and np.all(np.abs(s_gpu - s_ref) <= bound)
+
+
 @pytest.mark.parametrize("name,dq_mode", [(n, m) for n in LARGE for m in ("auto", "recompute")])
 def test_parity_large_workload_full(name, dq_mode):
     """Every element of dq, dk, dv of the full-size workload against the

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
   const int HJ = a.G / hpj;
   const int QS = a.q_splits;
   int r = blockIdx.x;
-  if (a.round_wgs > 0 && ((r / a.round_wgs) & 1) == 0 && (r | 31) < (int)gridDim.x) r ^= 24;
+  if (a.round_wgs > 0 && !a.seq_major && ((r / a.round_wgs) & 1) == 0 && (r | 31) < (int)gridDim.x) r ^= 24;
   // The two orders differ only in which of (b, tile) is the fast index, so one
   // decomposition serves both (selects, no branches).
   const int nfast = a.seq_major ? (a.S2 + BC - 1) / BC : a.B;

@@ -274,16 +274,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
     }
 }
 
-// The same product for operands whose row index x is contiguous in memory
-// (A[x][t] at x + t*a_st, B likewise: dV1, dK1, dV2, dK2), on whole 128 x 128
-// tiles with a contraction that is a multiple of 64: each 64-deep step of
-// both operands goes straight to LDS as a swizzled [t][x] tile (the
+// The same product for B operands whose row index x is contiguous in memory
+// (B[x][t] at x + t*b_st) and A operands of either kind (A[x][t] at x +
+// t*a_st: dV1, dK1, dV2, dK2; or at x*a_si + t, ATC: the dQ terms), on whole
+// 128 x 128 tiles with a contraction that is a multiple of 64: each 64-deep
+// step of both operands goes straight to LDS as a swizzled tile (the
 // attention kernels' copy), double-buffered, the next step's copy issued as
-// soon as every wavefront has finished the previous one; both MFMA operands
-// are transposing reads with one key order inside each 16-deep chunk.
+// soon as every wavefront has finished the previous one.  B, and an A of the
+// first kind, are transposing reads of [t][x] tiles; an ATC A is read from its
+// [x][t] tile in the same order of t inside each 16-deep chunk (two 8-byte
+// reads: t = 4h..4h+3 and 8+4h..8+4h+3 for lane half h).
 constexpr int GKB = 64;  // contraction per step of gemm_dma_kernel
 
-template <bool F16>
+template <bool ATC, bool F16>
 __global__ __launch_bounds__(NT, 2) void gemm_dma_kernel(GemmArgs g) {
   using C = Cfg<128, 128>;
   static_assert(C::TM == 2 && C::TN == 2 && C::WAVES_N == 2, "2 x 2 wavefronts of 64 x 64");
@@ -295,19 +298,22 @@ __global__ __launch_bounds__(NT, 2) void gemm_dma_kernel(GemmArgs g) {
   const int z = L / (tiles_i * tiles_j), tile = L % (tiles_i * tiles_j);
   const int i0 = (tile / tiles_j) * 128, j0 = (tile % tiles_j) * 128;
   const int h = blockIdx.y;
-  const bf16* __restrict__ Ag = static_cast<const bf16*>(g.a) + h * g.a_sh + z * g.a_sz + i0;
+  const bf16* __restrict__ Ag = static_cast<const bf16*>(g.a) + h * g.a_sh + z * g.a_sz + i0 * (ATC ? g.a_si : 1);
   const bf16* __restrict__ Bg = static_cast<const bf16*>(g.b) + h * g.b_sh + z * g.b_sz + j0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  fabwd::TileCopy<128, GKB, 4> acp, bcp;
-  acp.init(wave, lane, (int)(g.a_st * 2));
+  // A: rows t, 128 columns x (or, ATC, rows x, 64 columns t); B: rows t
+  fabwd::TileCopy<ATC ? GKB : 128, ATC ? 128 : GKB, 4> acp;
+  fabwd::TileCopy<128, GKB, 4> bcp;
+  acp.init(wave, lane, (int)((ATC ? g.a_si : g.a_st) * 2));
   bcp.init(wave, lane, (int)(g.b_st * 2));
   const uint32_t a_lds = fabwd::lds_addr(As), b_lds = fabwd::lds_addr(Bs);
-  fabwd::SwzTile<128, GKB> aadr, badr;
+  fabwd::SwzTile<ATC ? GKB : 128, ATC ? 128 : GKB> aadr;
+  fabwd::SwzTile<128, GKB> badr;
   aadr.init(a_lds, lane);
   badr.init(b_lds, lane);
   auto fetch = [&](int st, int buf) {
-    acp.issue(a_lds + buf * TB, Ag + (int64_t)st * GKB * g.a_st, GKB, wave, lane);
+    acp.issue(a_lds + buf * TB, Ag + (int64_t)st * GKB * (ATC ? 1 : g.a_st), ATC ? 128 : GKB, wave, lane);
     bcp.issue(b_lds + buf * TB, Bg + (int64_t)st * GKB * g.b_st, GKB, wave, lane);
   };
   floatx16 acc[C::TM][C::TN];
@@ -325,9 +331,20 @@ __global__ __launch_bounds__(NT, 2) void gemm_dma_kernel(GemmArgs g) {
     for (int kc = 0; kc < GKB / 16; ++kc) {
       bf16x8 af[C::TM], bfr[C::TN];
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm)
-        af[tm] = fabwd::join(fabwd::lds_load_tr(aadr.tr_read_c(kc, 0, 2 * wm + tm, buf * TB)),
-                             fabwd::lds_load_tr(aadr.tr_read_c(kc, 1, 2 * wm + tm, buf * TB)));
+      for (int tm = 0; tm < C::TM; ++tm) {
+        if constexpr (ATC) {
+          // logical 16-byte chunk 2kc (t = 16kc..16kc+7) of row 64wm + 32tm + l32
+          // and chunk 2kc + 1, each read at the lane half's 8-byte half
+          const int hi = lane >> 5;
+          const uint32_t c0 = aadr.row_read_at(kc, 64 * wm + 32 * tm, buf * TB) ^ (16 * hi);
+          const shortx4 lo4 = *(LDS_AS const shortx4*)(uintptr_t)(c0 + 8 * hi);
+          const shortx4 hi4 = *(LDS_AS const shortx4*)(uintptr_t)((c0 ^ 16) + 8 * hi);
+          af[tm] = fabwd::join(lo4, hi4);
+        } else {
+          af[tm] = fabwd::join(fabwd::lds_load_tr(aadr.tr_read_c(kc, 0, 2 * wm + tm, buf * TB)),
+                               fabwd::lds_load_tr(aadr.tr_read_c(kc, 1, 2 * wm + tm, buf * TB)));
+        }
+      }
 #pragma unroll
       for (int tn = 0; tn < C::TN; ++tn)
         bfr[tn] = fabwd::join(fabwd::lds_load_tr(badr.tr_read_c(kc, 0, 2 * wn + tn, buf * TB)),
@@ -777,10 +794,11 @@ int launch_gemm_bn(const GemmArgs& g, hipStream_t st) {
     const int64_t nx = (int64_t)ti * ((g.J + 127) / 128) * g.nb;
     // both operands row-contiguous, whole tiles, 64-deep steps, and a step's
     // 64 rows addressed by 32-bit byte offsets: copies straight to LDS
-    const bool dma = !ATC && !BTC && g.a_si == 1 && g.b_sj == 1 && g.I % 128 == 0 && g.J % 128 == 0 &&
-                     g.T % GKB == 0 && (int64_t)GKB * g.a_st * 2 < (int64_t(1) << 31) &&
+    const bool dma = !BTC && (ATC ? g.a_st == 1 : g.a_si == 1) && g.b_sj == 1 && g.I % 128 == 0 &&
+                     g.J % 128 == 0 && g.T % GKB == 0 &&
+                     (int64_t)(ATC ? 128 * g.a_si : GKB * g.a_st) * 2 < (int64_t(1) << 31) &&
                      (int64_t)GKB * g.b_st * 2 < (int64_t(1) << 31);
-    if (dma) hipLaunchKernelGGL((gemm_dma_kernel<F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
+    if (dma) hipLaunchKernelGGL((gemm_dma_kernel<ATC, F16>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
     else hipLaunchKernelGGL((gemm_kernel<ATC, BTC, 128, F16, R>), dim3((unsigned)nx, g.heads), dim3(NT), 0, st, g);
   }
   return (int)hipGetLastError();

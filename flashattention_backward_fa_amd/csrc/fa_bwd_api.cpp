@@ -369,10 +369,11 @@ int fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_plan* plan, size_t* workspace_
     std::fprintf(stderr,
                  "[fa_bwd] plan layout=%d B=%d N1=%d N2=%d S1=%d S2=%d D=%d Dv=%d T1=%lld T2=%lld "
                  "scale=%g window=(%d,%d) variant=%d heads_per_job=%d q_splits=%d partials=%d kv_chunk=%d "
-                 "workspace=%zu B\n",
+                 "dq_groups=%d round_wgs=%d seq_major=%d workspace=%zu B\n",
                  p->desc.layout, a.B, a.N1, a.N2, a.S1, a.S2, a.D, a.Dv, (long long)a.T1,
                  (long long)a.T2, (double)a.scale, a.win_left, a.win_right, a.variant,
-                 a.heads_per_job, a.q_splits, a.n_partials, p->n2_chunk, p->ws_bytes);
+                 a.heads_per_job, a.q_splits, a.n_partials, p->n2_chunk, a.dq_groups, a.round_wgs, a.seq_major,
+                 p->ws_bytes);
   }
   return FA_OK;
 }

@@ -294,6 +294,19 @@ def test_wide_windows_are_clamped_to_the_sequences(lib, monkeypatch, capfd):
     assert windows == [("300", "200"), ("300", "0"), ("299", "199")]
 
 
+def test_launch_order_fields_of_the_plan(lib, monkeypatch, capfd):
+    """The stored-dS and recompute chains order the dK/dV grid for the
+    dispatcher (engine reversal over rounds of one workgroup per CU) and take
+    varlen grids sequence by sequence; the fused and atomic forms use neither."""
+    monkeypatch.setenv("FA_BWD_LOG", "1")
+    assert create(lib, mask_mode=1, num_cus=200)[0] == fb.FA_OK                      # dense, stored dS
+    assert tnd_create(lib, [300, 500], [300, 500], mask_mode=1, num_cus=256) == fb.FA_OK  # varlen
+    assert create(lib, S1=128, S2=128, mask_mode=1)[0] == fb.FA_OK                    # fused
+    assert create(lib, mask_mode=1, dq_mode="atomic")[0] == fb.FA_OK                  # atomic
+    logs = re.findall(r"variant=(\d+) .*dq_groups=(\d+) round_wgs=(\d+) seq_major=(\d+)", capfd.readouterr().err)
+    assert [(int(v), int(r), int(m)) for v, _, r, m in logs] == [(4, 200, 0), (4, 256, 1), (5, 0, 0), (1, 0, 0)]
+
+
 def test_abi_version_mismatch(lib):
     d = fb.make_desc("BSND", 1, 2, 2, 64, 64, 64, 64)
     d.abi_version = 7

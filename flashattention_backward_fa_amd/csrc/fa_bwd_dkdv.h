@@ -316,12 +316,24 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
         const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][buf][ib]);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
+          if constexpr (F16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int rg = r4 * 4 + e;
-            const float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
-            pa[kb][rg >> 3][rg & 7] = to_elem<F16>(p);
-            da[kb][rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[kb][rg] - f4[e]));
+            for (int e = 0; e < 4; e += 2) {
+              const int rg = r4 * 4 + e;
+              const float p0 = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+              const float p1 = __builtin_amdgcn_exp2f(sacc[kb][rg + 1] * a.scale_log2 - l4[e + 1]);
+              put_f16_pair(pa[kb][rg >> 3], (rg & 7) >> 1, p0, p1);
+              put_f16_pair(da[kb][rg >> 3], (rg & 7) >> 1, p0 * (pacc[kb][rg] - f4[e]),
+                           p1 * (pacc[kb][rg + 1] - f4[e + 1]));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rg = r4 * 4 + e;
+              const float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+              pa[kb][rg >> 3][rg & 7] = to_elem<F16>(p);
+              da[kb][rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[kb][rg] - f4[e]));
+            }
           }
         }
       }
@@ -337,13 +349,27 @@ __global__ __launch_bounds__(64 * NWG * QG, 1) void dkdv_kernel(KernelArgs a) {
         const floatx4 f4 = *reinterpret_cast<const floatx4*>(&sfm_s[qg][buf][ib]);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
+          if constexpr (F16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int rg = r4 * 4 + e;
-            float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
-            p = fa_sched::in_window(vis[kb], ib + e) ? p : 0.f;
-            pa[kb][rg >> 3][rg & 7] = to_elem<F16>(p);
-            da[kb][rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[kb][rg] - f4[e]));
+            for (int e = 0; e < 4; e += 2) {
+              const int rg = r4 * 4 + e;
+              float p0 = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+              float p1 = __builtin_amdgcn_exp2f(sacc[kb][rg + 1] * a.scale_log2 - l4[e + 1]);
+              p0 = fa_sched::in_window(vis[kb], ib + e) ? p0 : 0.f;
+              p1 = fa_sched::in_window(vis[kb], ib + e + 1) ? p1 : 0.f;
+              put_f16_pair(pa[kb][rg >> 3], (rg & 7) >> 1, p0, p1);
+              put_f16_pair(da[kb][rg >> 3], (rg & 7) >> 1, p0 * (pacc[kb][rg] - f4[e]),
+                           p1 * (pacc[kb][rg + 1] - f4[e + 1]));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rg = r4 * 4 + e;
+              float p = __builtin_amdgcn_exp2f(sacc[kb][rg] * a.scale_log2 - l4[e]);
+              p = fa_sched::in_window(vis[kb], ib + e) ? p : 0.f;
+              pa[kb][rg >> 3][rg & 7] = to_elem<F16>(p);
+              da[kb][rg >> 3][rg & 7] = to_elem<F16>(p * (pacc[kb][rg] - f4[e]));
+            }
           }
         }
       }

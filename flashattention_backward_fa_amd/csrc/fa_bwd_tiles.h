@@ -189,6 +189,19 @@ struct SwzTile {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// Elements 2k and 2k + 1 of an fp16 operand held in the 16-bit vector type:
+// a and b rounded to nearest even as one packed conversion
+// (v_cvt_pk_f16_f32), which element-wise conversions through the storage
+// type do not always become.
+__device__ __forceinline__ void put_f16_pair(bf16x8& v, int k, float a, float b) {
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+  w[k] = __builtin_bit_cast(unsigned, __builtin_convertvector((float2_t){a, b}, half2_t));
+  v = __builtin_bit_cast(bf16x8, w);
+}
+
 __device__ __forceinline__ uint32_t pack2(bf16 lo, bf16 hi) {
   return (uint32_t)__builtin_bit_cast(unsigned short, lo) | ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
 }

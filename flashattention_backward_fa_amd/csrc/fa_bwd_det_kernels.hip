@@ -446,15 +446,39 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void dq_ds_kernel(KernelArgs a) {
   }
   const int nb_lo = qg == 0 ? 0 : NLO, nb_hi = qg == 0 ? NLO : NBK;
 
-  // dq = bf16(scale * acc): lane holds head-dim column nb*32 + l32 of 16 rows
   bf16* __restrict__ dQg = static_cast<bf16*>(a.dq) + sb.qbase + (int64_t)n1 * a.q_sn;
+  if constexpr (QG > 1) {
+    // dq = bf16(scale * acc), each 32 x 32 block turned row-major by two MFMAs
+    // against a permuted identity (exact: every output is one input times 1),
+    // then stored as 16-byte row pieces (lane = query row).  Measured faster
+    // only for the one-round grids of this form (MHA -3.5 %; the QG = 1 grids
+    // of GQA, varlen and wide_qk +0.5 to +2.6 %).
+    bf16x8 eye[2];
+    eye_operand<F16>(lane, eye);
+    const int row = i0 + wave * 32 + l32;
+    bf16* __restrict__ dq_row = dQg + (int64_t)row * a.q_ss;
+    const bool row_ok = row < sb.s1a;  // rows past the used ones hold zeros
 #pragma unroll
-  for (int rg = 0; rg < 16; ++rg) {
-    const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
-    if (i < sb.s1a) {  // rows past the used ones hold zeros
+    for (int nb = 0; nb < NBK; ++nb) {
+      if (nb >= nb_lo && nb < nb_hi) {
+        u32x4 piece[2];
+        row_pieces<F16>(transpose_acc<F16>(dq[nb], a.scale, eye), 1.f, piece);
+        if (row_ok) {
 #pragma unroll
-      for (int nb = 0; nb < NBK; ++nb)
-        if (nb >= nb_lo && nb < nb_hi) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
+          for (int pc = 0; pc < 2; ++pc) *reinterpret_cast<u32x4*>(dq_row + nb * 32 + pc * 16 + hi * 8) = piece[pc];
+        }
+      }
+    }
+  } else {
+    // dq = bf16(scale * acc): lane holds head-dim column nb*32 + l32 of 16 rows
+#pragma unroll
+    for (int rg = 0; rg < 16; ++rg) {
+      const int i = i0 + wave * 32 + (rg >> 2) * 8 + hi * 4 + (rg & 3);
+      if (i < sb.s1a) {  // rows past the used ones hold zeros
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb)
+          if (nb >= nb_lo && nb < nb_hi) dQg[(int64_t)i * a.q_ss + nb * 32 + l32] = to_elem<F16>(dq[nb][rg] * a.scale);
+      }
     }
   }
 }
